@@ -1,0 +1,173 @@
+"""fp64 CPU oracle for the selective-scan (S6) forward and decode step.
+
+TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` may import this package. It never imports or calls the GPU library,
+and the GPU library never imports it.
+
+The arithmetic lives in ``ss_oracle.c`` (plain sequential loops in IEEE double, one
+independent recurrence per (batch, channel)); this module only compiles it with gcc and
+marshals numpy arrays. Inputs are numpy arrays: ``float32`` for fp32 data, ``uint16``
+holding bf16 bit patterns for bf16 data (u, delta, z, B, C share one of the two);
+A, D and delta_bias are ``float32``. Results are ``float64``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ss_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libss_oracle.so")
+_lib = None
+
+F32 = 0
+BF16 = 1
+
+
+CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-std=c11", "-Wall",
+          "-Wextra", "-shared", "-fPIC"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc the given C file into a shared library at ``out``."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast math, no contraction, OpenMP over channels)."""
+    if force or not os.path.exists(_LIB_PATH):
+        compile_source(_SRC, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(path):
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.ss_oracle_fwd.restype = i32
+    lib.ss_oracle_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                  i64, i64, i64, i64, i32, vp, vp, i64, i32]
+    lib.ss_oracle_step.restype = i32
+    lib.ss_oracle_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                   i64, i64, i64, i32, i32]
+    lib.ss_oracle_max_threads.restype = i32
+    lib.ss_oracle_max_threads.argtypes = []
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = _bind(_LIB_PATH)
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().ss_oracle_max_threads())
+
+
+def _dtype_of(*arrays) -> int:
+    kinds = {a.dtype for a in arrays if a is not None}
+    if kinds == {np.dtype(np.float32)}:
+        return F32
+    if kinds == {np.dtype(np.uint16)}:
+        return BF16
+    raise TypeError(f"u, delta, z, B, C must all be float32 or all uint16 (bf16 bits), got {kinds}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if dtype is not None and a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=None,
+        channels=None, nthreads=0, want_y=True, _lib=None):
+    """Forward scan. Shapes: u, delta, z (batch, L, dim); B, C (batch, L, N); A (dim, N);
+    D, delta_bias (dim,); h0 (batch, dim, N) float64 or None.
+
+    channels: None for every channel, else an int array of shape (k, 2) of (b, d) pairs;
+    then y is (k, L) and last_state is (k, N).
+    Returns (y, last_state) as float64 arrays (y is None when want_y is False).
+    """
+    u, delta, B, C, z = _c(u), _c(delta), _c(B), _c(C), _c(z)
+    A, D, delta_bias = _c(A, np.float32), _c(D, np.float32), _c(delta_bias, np.float32)
+    dt = _dtype_of(u, delta, B, C, z)
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    if delta.shape != u.shape or (z is not None and z.shape != u.shape):
+        raise ValueError("u, delta and z must share a shape")
+    if B.shape != (batch, L, N) or C.shape != (batch, L, N) or A.shape != (dim, N):
+        raise ValueError("bad B, C or A shape")
+    if h0 is not None:
+        h0 = _c(h0, np.float64)
+        if h0.shape != (batch, dim, N):
+            raise ValueError("bad h0 shape")
+    if channels is None:
+        nchan, cb, cd = 0, None, None
+        y = np.empty((batch, L, dim), np.float64) if want_y else None
+        st = np.empty((batch, dim, N), np.float64)
+    else:
+        ch = np.ascontiguousarray(np.asarray(channels, dtype=np.int64).reshape(-1, 2))
+        nchan = ch.shape[0]
+        cb, cd = np.ascontiguousarray(ch[:, 0]), np.ascontiguousarray(ch[:, 1])
+        y = np.empty((nchan, L), np.float64) if want_y else None
+        st = np.empty((nchan, N), np.float64)
+        if nchan == 0:
+            return y, st
+    rc = (_lib or _load()).ss_oracle_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(delta_bias), int(bool(softplus)), _ptr(h0), _ptr(y), _ptr(st),
+                               batch, L, dim, N, dt, _ptr(cb), _ptr(cd), nchan, int(nthreads))
+    if rc != 0:
+        raise ValueError("ss_oracle_fwd rejected its arguments")
+    return y, st
+
+
+def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, nthreads=0,
+         _lib=None):
+    """One decode step, state (batch, dim, N) float64 updated in place. u, delta, z are
+    (batch, dim); B, C are (batch, N). Returns y (batch, dim) float64."""
+    if state.dtype != np.float64 or not state.flags.c_contiguous:
+        raise TypeError("state must be a C-contiguous float64 array")
+    u, delta, B, C, z = _c(u), _c(delta), _c(B), _c(C), _c(z)
+    A, D, delta_bias = _c(A, np.float32), _c(D, np.float32), _c(delta_bias, np.float32)
+    dt = _dtype_of(u, delta, B, C, z)
+    batch, dim = u.shape
+    N = A.shape[1]
+    if state.shape != (batch, dim, N) or B.shape != (batch, N) or C.shape != (batch, N):
+        raise ValueError("bad state, B or C shape")
+    y = np.empty((batch, dim), np.float64)
+    rc = (_lib or _load()).ss_oracle_step(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(y),
+                                batch, dim, N, dt, int(nthreads))
+    if rc != 0:
+        raise ValueError("ss_oracle_step rejected its arguments")
+    return y
+
+
+class Library:
+    """The oracle API bound to another build of the same C source (used by the tests that
+    plant mistakes in a copy of the oracle and check that the pins catch them)."""
+
+    def __init__(self, path):
+        self._h = _bind(path)
+
+    def fwd(self, *a, **k):
+        return fwd(*a, _lib=self._h, **k)
+
+    def step(self, *a, **k):
+        return step(*a, _lib=self._h, **k)

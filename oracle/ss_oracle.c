@@ -1,0 +1,184 @@
+/*
+ * ss_oracle.c -- plain fp64 CPU oracle for the selective state-space scan (S6).
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark may load this library. It shares no code, header or table with the
+ * GPU library, and never calls it.
+ *
+ * What it computes (one independent recurrence per batch row b and channel d):
+ *
+ *   x      = delta[b,t,d] + bias[d]                        (bias absent -> 0)
+ *   dt     = softplus(x) if softplus_flag else x
+ *   for each state n:
+ *     abar = exp(dt * A[d,n])                               (zero-order-hold decay)
+ *     h[n] = abar * h[n] + (dt * B[b,t,n]) * u[b,t,d]
+ *   y[b,t,d] = (sum_n C[b,t,n] * h[n] + D[d] * u[b,t,d]) * silu(z[b,t,d])
+ *   last_state[b,d,n] = h[n] after the last step
+ *
+ * Sources (web pages on the Mamba selective SSM):
+ *  - "Mamba：选择性状态空间模型入门教程" (jindou-blog tutorial), section
+ *    "状态空间模型（SSM）的直觉": recurrence h = A h + B x, output y = C h + D x;
+ *    section "Mamba 的关键创新：选择性机制": B, C and the step size are functions of
+ *    the input, the step size passes through softplus, the state is discretised with
+ *    the step and y is read from the updated state.
+ *  - "Mamba：选择性状态空间的线性时间序列建模" (wiki note on arXiv 2312.00752),
+ *    table "算法对比（核心直觉）", row S6: B_t and C_t have shape (batch, L, N) and the
+ *    step is tau(Delta + s_Delta(x_t)), i.e. the bias is added before softplus;
+ *    section "架构：极简设计": the SSM branch is multiplied by a SiLU branch.
+ *  - "架构变体：Mamba/SSM" (aiqz.cc), section "离散化": zero-order hold with step Delta;
+ *    section "Python 演示": state starts at zero.
+ * Readings where the pages are silent or disagree (all in the design notes):
+ *  - discretised input term is dt * B (not the exact ZOH (exp(dt A) - 1)/A * B);
+ *  - y reads the post-update state; the D term is included; the SiLU gate multiplies
+ *    the whole output including the D term; the bias is added before softplus;
+ *  - A is a diagonal (dim, dstate) array; B and C carry no channel index.
+ *
+ * Arithmetic: every input is converted exactly to double (bf16 -> fp32 -> fp64 is
+ * exact), all arithmetic is IEEE double with libm exp/log1p, compiled without fast
+ * math. Work is split over (b, d) channels with OpenMP; each channel runs the plain
+ * sequential loop above, so the result does not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* element types of u, delta, z, B and C */
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+static double in_at(const void* p, int dtype, int64_t i) {
+  if (dtype == ORACLE_F32) return (double)((const float*)p)[i];
+  uint32_t w = (uint32_t)((const uint16_t*)p)[i] << 16; /* bf16 is the top half of an fp32 */
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return (double)f;
+}
+
+/* softplus(x) = log(1 + e^x), written so that neither branch overflows */
+static double softplus(double x) {
+  if (x > 0.0) return x + log1p(exp(-x));
+  return log1p(exp(x));
+}
+
+/* silu(z) = z * sigmoid(z) */
+static double silu(double z) {
+  if (z >= 0.0) return z / (1.0 + exp(-z));
+  double e = exp(z);
+  return z * e / (1.0 + e);
+}
+
+/* One channel (b, d) over t in [0, seqlen). h holds the state on entry and exit.
+   y_out[t * y_stride] receives y[b,t,d]. */
+static void scan_channel(const void* u, const void* delta, const float* A, const void* B,
+                         const void* C, const float* D, const void* z, const float* bias,
+                         int softplus_flag, int64_t b, int64_t d, int64_t seqlen, int64_t dim,
+                         int64_t dstate, int dtype, double* h, double* y_out, int64_t y_stride) {
+  const double bias_d = bias ? (double)bias[d] : 0.0;
+  const double D_d = D ? (double)D[d] : 0.0;
+  for (int64_t t = 0; t < seqlen; ++t) {
+    const int64_t e = (b * seqlen + t) * dim + d;  /* index into (batch, seqlen, dim) */
+    const int64_t bc = (b * seqlen + t) * dstate;  /* row of (batch, seqlen, dstate) */
+    const double x = in_at(delta, dtype, e) + bias_d;
+    const double dt = softplus_flag ? softplus(x) : x;
+    const double uv = in_at(u, dtype, e);
+    double acc = 0.0;
+    for (int64_t n = 0; n < dstate; ++n) {
+      const double abar = exp(dt * (double)A[d * dstate + n]);
+      h[n] = abar * h[n] + (dt * in_at(B, dtype, bc + n)) * uv;
+      acc += in_at(C, dtype, bc + n) * h[n];
+    }
+    double yv = acc + D_d * uv;
+    if (z) yv *= silu(in_at(z, dtype, e));
+    if (y_out) y_out[t * y_stride] = yv;
+  }
+}
+
+/*
+ * Full forward over every (b, d), or over a listed subset of channels.
+ *   h0          optional (batch, dim, dstate) initial state; NULL means zeros.
+ *   nchan == 0  all channels: y is (batch, seqlen, dim), last_state is (batch, dim, dstate).
+ *   nchan  > 0  only the channels (chan_b[i], chan_d[i]): y is (nchan, seqlen) and
+ *               last_state is (nchan, dstate); h0 is still indexed as (batch, dim, dstate).
+ * y and last_state may be NULL. Returns 0, or -1 on a bad argument.
+ */
+int ss_oracle_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                  const double* h0, double* y, double* last_state, int64_t batch, int64_t seqlen,
+                  int64_t dim, int64_t dstate, int dtype, const int64_t* chan_b,
+                  const int64_t* chan_d, int64_t nchan, int nthreads) {
+  if (!u || !delta || !A || !B || !C) return -1;
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || nchan < 0) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (nchan > 0 && (!chan_b || !chan_d)) return -1;
+  const int64_t njobs = nchan > 0 ? nchan : batch * dim;
+  int bad = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t j = 0; j < njobs; ++j) {
+    const int64_t b = nchan > 0 ? chan_b[j] : j / dim;
+    const int64_t d = nchan > 0 ? chan_d[j] : j % dim;
+    if (b < 0 || b >= batch || d < 0 || d >= dim) { bad = 1; continue; }
+    double* h = (double*)calloc((size_t)dstate, sizeof(double));
+    if (!h) { bad = 1; continue; }
+    if (h0)
+      for (int64_t n = 0; n < dstate; ++n) h[n] = h0[(b * dim + d) * dstate + n];
+    double* yo = NULL;
+    int64_t ys = 0;
+    if (y) {
+      if (nchan > 0) { yo = y + j * seqlen; ys = 1; }
+      else { yo = y + b * seqlen * dim + d; ys = dim; }
+    }
+    scan_channel(u, delta, A, B, C, D, z, delta_bias, softplus_flag, b, d, seqlen, dim, dstate,
+                 dtype, h, yo, ys);
+    if (last_state) {
+      double* dst = nchan > 0 ? last_state + j * dstate : last_state + (b * dim + d) * dstate;
+      for (int64_t n = 0; n < dstate; ++n) dst[n] = h[n];
+    }
+    free(h);
+  }
+  return bad ? -1 : 0;
+}
+
+/*
+ * One decode step for every (b, d): the loop body above for a single time index,
+ * with the state carried in place (fp64). u, delta, z, y are (batch, dim);
+ * B and C are (batch, dstate); state is (batch, dim, dstate).
+ */
+int ss_oracle_step(double* state, const void* u, const void* delta, const float* A, const void* B,
+                   const void* C, const float* D, const void* z, const float* delta_bias,
+                   int softplus_flag, double* y, int64_t batch, int64_t dim, int64_t dstate,
+                   int dtype, int nthreads) {
+  if (!state || !u || !delta || !A || !B || !C) return -1;
+  if (batch < 0 || dim < 0 || dstate < 1) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < batch * dim; ++j) {
+    const int64_t b = j / dim, d = j % dim;
+    /* a step is a length-1 sequence: (batch, 1, dim) and (batch, 1, dstate) index the
+       same memory as (batch, dim) and (batch, dstate) */
+    scan_channel(u, delta, A, B, C, D, z, delta_bias, softplus_flag, b, d, 1, dim, dstate, dtype,
+                 state + j * dstate, y ? y + j : NULL, 1);
+  }
+  return 0;
+}
+
+int ss_oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

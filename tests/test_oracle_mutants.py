@@ -1,0 +1,82 @@
+"""Plant plausible mistakes in a copy of the oracle's C source (on the CPU) and check
+that the pins in test_oracle_pins.py catch every one of them."""
+import os
+import shutil
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ss_oracle.c")
+
+# (name, [(original text, planted text), ...]) -- each original must occur in the source
+MUTANTS = [
+    ("drop_D_term", [("double yv = acc + D_d * uv;", "double yv = acc;")]),
+    ("bias_after_softplus", [("const double x = in_at(delta, dtype, e) + bias_d;",
+                              "const double x = in_at(delta, dtype, e);"),
+                             ("const double dt = softplus_flag ? softplus(x) : x;",
+                              "const double dt = (softplus_flag ? softplus(x) : x) + bias_d;")]),
+    ("no_softplus", [("const double dt = softplus_flag ? softplus(x) : x;", "const double dt = x;")]),
+    ("y_reads_old_state", [("      h[n] = abar * h[n] + (dt * in_at(B, dtype, bc + n)) * uv;\n"
+                            "      acc += in_at(C, dtype, bc + n) * h[n];",
+                            "      acc += in_at(C, dtype, bc + n) * h[n];\n"
+                            "      h[n] = abar * h[n] + (dt * in_at(B, dtype, bc + n)) * uv;")]),
+    ("A_transposed", [("(double)A[d * dstate + n]", "(double)A[n * dim + d]")]),
+    ("B_C_swapped", [("(dt * in_at(B, dtype, bc + n))", "(dt * in_at(C, dtype, bc + n))"),
+                     ("acc += in_at(C, dtype, bc + n) * h[n];", "acc += in_at(B, dtype, bc + n) * h[n];")]),
+    ("decay_sign", [("exp(dt * (double)A[d * dstate + n])", "exp(-dt * (double)A[d * dstate + n])")]),
+    ("input_term_without_dt", [("(dt * in_at(B, dtype, bc + n)) * uv", "in_at(B, dtype, bc + n) * uv")]),
+    ("gate_skips_D_term", [("    double yv = acc + D_d * uv;\n    if (z) yv *= silu(in_at(z, dtype, e));",
+                            "    double yv = acc;\n    if (z) yv *= silu(in_at(z, dtype, e));\n    yv += D_d * uv;")]),
+    ("gate_is_sigmoid", [("if (z >= 0.0) return z / (1.0 + exp(-z));", "if (z >= 0.0) return 1.0 / (1.0 + exp(-z));"),
+                         ("return z * e / (1.0 + e);", "return e / (1.0 + e);")]),
+    ("B_ignores_batch", [("const int64_t bc = (b * seqlen + t) * dstate;", "const int64_t bc = t * dstate;")]),
+    ("bf16_decode_shift", [("<< 16;", "<< 15;")]),
+    ("state_not_carried_in_step", [("state + j * dstate, y ? y + j : NULL, 1);",
+                                    "state + 0 * dstate, y ? y + j : NULL, 1);")]),
+]
+
+
+def pin_suite(lib):
+    """Run the pins against ``lib``; return the names of the pins that fail."""
+    failed = []
+    checks = [
+        ("brute", lambda: pins.test_brute_force_unrolled_sum(lib, True, True)),
+        ("brute_ungated", lambda: pins.test_brute_force_unrolled_sum(lib, False, True)),
+        ("brute_no_softplus", lambda: pins.test_brute_force_no_softplus_no_bias(lib)),
+        ("brute_bf16", lambda: pins.test_brute_force_bf16_inputs(lib)),
+        ("conv", lambda: pins.test_lti_equals_convolution(lib, True)),
+        ("geometric", lambda: pins.test_geometric_series_constant_inputs(lib)),
+        ("zero_step", lambda: pins.test_zero_step_keeps_state_exactly(lib)),
+        ("huge_step", lambda: pins.test_huge_step_resets_state(lib)),
+        ("page5", lambda: pins.test_page5_worked_example(lib)),
+        ("step", lambda: pins.test_step_by_step_matches_forward(lib)),
+    ]
+    for name, fn in checks:
+        try:
+            fn()
+        except AssertionError:
+            failed.append(name)
+    return failed
+
+
+def test_unmodified_copy_passes(tmp_path):
+    src = tmp_path / "ss_oracle.c"
+    shutil.copy(SRC, src)
+    lib = oracle.Library(oracle.compile_source(str(src), str(tmp_path / "lib.so")))
+    assert pin_suite(lib) == []
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, edits):
+    text = open(SRC).read()
+    for old, new in edits:
+        assert text.count(old) == 1, f"mutation anchor not found once: {old!r}"
+        text = text.replace(old, new)
+    src = tmp_path / "ss_oracle_mutant.c"
+    src.write_text(text)
+    lib = oracle.Library(oracle.compile_source(str(src), str(tmp_path / "mutant.so")))
+    failed = pin_suite(lib)
+    assert failed, f"planted mistake {name} passed every pin"
