@@ -1,0 +1,111 @@
+/*
+ * ss.h -- C ABI of libss, the gfx950 (MI355X) selective state-space scan (S6).
+ *
+ * The operation (for every batch row b, channel d and state n):
+ *
+ *   dt        = softplus(delta[b,t,d] + delta_bias[d])   (or without softplus)
+ *   abar      = exp(dt * A[d,n])
+ *   h[n]      = abar * h[n] + (dt * B[b,t,n]) * u[b,t,d]
+ *   y[b,t,d]  = (sum_n C[b,t,n] * h[n] + D[d] * u[b,t,d]) * silu(z[b,t,d])
+ *
+ * Sources: "Mamba：选择性状态空间的线性时间序列建模" (wiki note on arXiv 2312.00752),
+ * table "算法对比（核心直觉）" row S6 -- B and C are input-dependent with shape
+ * (batch, L, N) and the step is tau(Delta + s_Delta(x)); section "第二个创新：硬件感知
+ * 算法" -- the scan runs as one fused kernel whose expanded state never reaches HBM.
+ * "Mamba：选择性状态空间模型入门教程" (jindou-blog tutorial), sections
+ * "状态空间模型（SSM）的直觉" (h = A h + B x, y = C h + D x) and "Mamba 的关键创新：
+ * 选择性机制" (softplus step, discretised A and B, y read from the updated state).
+ * "架构变体：Mamba/SSM" (aiqz.cc), section "离散化" (zero-order hold with step Delta).
+ *
+ * Conventions shared by every entry point:
+ *  - All data pointers are DEVICE pointers on the current HIP device, owned by the
+ *    caller. The library allocates and frees nothing, keeps no per-call state, and is
+ *    safe to call from several host threads.
+ *  - Tensors are dense, row-major, with no padding or strides.
+ *  - in_dtype selects the element type of u, delta, z, B and C (all the same);
+ *    A, D, delta_bias, y and the state are always fp32.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null stream).
+ *    Arguments are validated before anything is enqueued; on a validation error the
+ *    call returns the code and writes nothing. A launch failure returns SS_ERR_HIP.
+ *    Faults during execution surface at the caller's next synchronisation.
+ *  - Outputs must not alias inputs. NaN and Inf propagate unchecked.
+ */
+#ifndef SS_H_
+#define SS_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SS_ABI_VERSION 1
+#define SS_MAX_DSTATE 16
+
+typedef enum {
+  SS_OK = 0,
+  SS_ERR_NULL_ARG = 1,      /* a required pointer is NULL */
+  SS_ERR_BAD_SHAPE = 2,     /* a size is < 1 (batch, dim, dstate) or < 0 (seqlen), or too large */
+  SS_ERR_BAD_DTYPE = 3,     /* in_dtype is not one of ss_dtype */
+  SS_ERR_UNSUPPORTED_N = 4, /* dstate > SS_MAX_DSTATE */
+  SS_ERR_MISALIGNED = 5,    /* a pointer is not aligned to its element size */
+  SS_ERR_HIP = 6,           /* a HIP runtime call or kernel launch failed */
+  SS_ERR_DEVICE = 7         /* the current device is not a gfx950 GPU */
+} ss_status;
+
+typedef enum {
+  SS_DTYPE_F32 = 0,  /* IEEE binary32 */
+  SS_DTYPE_BF16 = 1  /* bfloat16: the upper 16 bits of a binary32 */
+} ss_dtype;
+
+/* SS_ABI_VERSION of the built library. */
+int ss_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* ss_status_string(int status);
+
+/*
+ * ss_fwd -- selective-scan forward over a whole sequence, from a zero initial state.
+ *
+ *   u, delta, z   (batch, seqlen, dim)     in_dtype. delta is the raw step before bias.
+ *                                          z may be NULL: no SiLU gate.
+ *   A             (dim, dstate)            fp32, the diagonal state matrix per channel
+ *                                          (normally negative; any finite value is used as is).
+ *   B, C          (batch, seqlen, dstate)  in_dtype, shared by all channels of a batch row.
+ *   D             (dim)                    fp32, may be NULL: no skip term.
+ *   delta_bias    (dim)                    fp32, may be NULL: zero bias. Added before softplus.
+ *   softplus_flag                          non-zero: dt = softplus(delta + bias); else dt = delta + bias.
+ *   y             (batch, seqlen, dim)     fp32 output.
+ *   last_state    (batch, dim, dstate)     fp32 output, may be NULL: the state after the last token.
+ *   seqlen == 0 is allowed: no token is read, y is not written, last_state is set to
+ *   zero; u, delta, z, B, C and y may then be NULL (A is still required).
+ * Limits: dstate <= 16; batch * seqlen * dim < 2^62.
+ */
+int ss_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+           const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
+           float* last_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+           int in_dtype, void* stream);
+
+/*
+ * ss_step -- one decode step: the same update for a single token, with the state
+ * carried across calls and updated in place (streaming inference, O(1) per token:
+ * "Mamba：选择性状态空间模型入门教程", table "Mamba vs Transformer vs RNN").
+ *
+ *   state         (batch, dim, dstate)     fp32, read and written in place.
+ *   u, delta, z   (batch, dim)             in_dtype; z may be NULL.
+ *   B, C          (batch, dstate)          in_dtype.
+ *   A, D, delta_bias, softplus_flag        as in ss_fwd.
+ *   y             (batch, dim)             fp32 output.
+ * Running ss_step for t = 0..L-1 from a zero state gives the same y and final state as
+ * ss_fwd over the L tokens, up to fp32 rounding.
+ */
+int ss_step(float* state, const void* u, const void* delta, const float* A, const void* B,
+            const void* C, const float* D, const void* z, const float* delta_bias,
+            int softplus_flag, float* y, int64_t batch, int64_t dim, int64_t dstate, int in_dtype,
+            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_H_ */

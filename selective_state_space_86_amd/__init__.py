@@ -1,0 +1,10 @@
+"""MI355X (gfx950) selective state-space scan (S6): Python binding of libss.
+
+Every step of the scan runs in the HIP kernels of ``libss.so``; this package only
+marshals torch device tensors into the C ABI declared in ``include/ss.h``
+(``ss_fwd``, ``ss_step``). The library is loaded on first use and a missing or
+unloadable build raises: there is no fallback path.
+"""
+from ._binding import SSError, fwd, lib_path, load_library, step  # noqa: F401
+
+__all__ = ["fwd", "step", "SSError", "load_library", "lib_path"]

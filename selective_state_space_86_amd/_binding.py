@@ -1,0 +1,138 @@
+"""ctypes binding of libss (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libss.so")
+_lib = None
+
+F32, BF16 = 0, 1
+EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_step")
+
+
+class SSError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {status_string(status)}")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libss.so (built in-tree by __graft_entry__.build()); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.ss_abi_version.restype = i32
+    lib.ss_abi_version.argtypes = []
+    lib.ss_status_string.restype = ctypes.c_char_p
+    lib.ss_status_string.argtypes = [i32]
+    lib.ss_fwd.restype = i32
+    lib.ss_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.ss_step.restype = i32
+    lib.ss_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, vp]
+    _lib = lib
+    return lib
+
+
+def status_string(s: int) -> str:
+    return load_library().ss_status_string(int(s)).decode()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _in_dtype(*ts) -> int:
+    kinds = {t.dtype for t in ts if t is not None}
+    if kinds == {torch.float32}:
+        return F32
+    if kinds == {torch.bfloat16}:
+        return BF16
+    raise TypeError(f"u, delta, z, B, C must all be float32 or all bfloat16, got {kinds}")
+
+
+def _check(t, name, device, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a device tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=None,
+        last_state=None, return_last_state=True, stream=None):
+    """Selective-scan forward (``ss_fwd``). u, delta, z: (batch, L, dim); B, C: (batch, L, N);
+    A: (dim, N) fp32; D, delta_bias: (dim,) fp32. Returns y (fp32) and, unless
+    return_last_state is False, the final state (batch, dim, N) fp32."""
+    dev = u.device
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    dt = _in_dtype(u, delta, B, C, z)
+    _check(u, "u", dev)
+    _check(delta, "delta", dev, shape=u.shape)
+    _check(z, "z", dev, shape=u.shape)
+    _check(B, "B", dev, shape=(batch, L, N))
+    _check(C, "C", dev, shape=(batch, L, N))
+    _check(A, "A", dev, torch.float32, (dim, N))
+    _check(D, "D", dev, torch.float32, (dim,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (dim,))
+    if y is None:
+        y = torch.empty((batch, L, dim), dtype=torch.float32, device=dev)
+    _check(y, "y", dev, torch.float32, (batch, L, dim))
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", dev, torch.float32, (batch, dim, N))
+    rc = load_library().ss_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(delta_bias), int(bool(softplus)), _ptr(y), _ptr(last_state),
+                               batch, L, dim, N, dt, _stream(dev, stream))
+    if rc != 0:
+        raise SSError(rc, "ss_fwd")
+    return (y, last_state) if return_last_state else y
+
+
+def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=None,
+         stream=None):
+    """One decode step (``ss_step``); state (batch, dim, N) fp32 is updated in place.
+    u, delta, z: (batch, dim); B, C: (batch, N). Returns y (batch, dim) fp32."""
+    dev = state.device
+    batch, dim, N = state.shape
+    dt = _in_dtype(u, delta, B, C, z)
+    _check(state, "state", dev, torch.float32)
+    _check(u, "u", dev, shape=(batch, dim))
+    _check(delta, "delta", dev, shape=(batch, dim))
+    _check(z, "z", dev, shape=(batch, dim))
+    _check(B, "B", dev, shape=(batch, N))
+    _check(C, "C", dev, shape=(batch, N))
+    _check(A, "A", dev, torch.float32, (dim, N))
+    _check(D, "D", dev, torch.float32, (dim,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (dim,))
+    if y is None:
+        y = torch.empty((batch, dim), dtype=torch.float32, device=dev)
+    _check(y, "y", dev, torch.float32, (batch, dim))
+    rc = load_library().ss_step(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(y),
+                                batch, dim, N, dt, _stream(dev, stream))
+    if rc != 0:
+        raise SSError(rc, "ss_step")
+    return y

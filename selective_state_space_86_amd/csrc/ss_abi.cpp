@@ -1,0 +1,117 @@
+// ss_abi.cpp -- the extern "C" entry points of libss: argument validation, device check,
+// dispatch to the gfx950 kernels on the caller's stream. See include/ss.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/ss.h"
+#include "ss_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+// Is the current device a gfx950? The answer is cached per device id.
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SS_ERR_HIP;
+  if (dev < kMaxDevices) {
+    const int c = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return SS_OK;
+    if (c == 2) return SS_ERR_DEVICE;
+  }
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, dev) != hipSuccess) return SS_ERR_HIP;
+  const bool ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? SS_OK : SS_ERR_DEVICE;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_size(int dtype) { return dtype == SS_DTYPE_BF16 ? 2 : 4; }
+
+// batch * seqlen * dim < 2^62 without overflow
+bool product_ok(int64_t a, int64_t b, int64_t c) {
+  const int64_t lim = int64_t(1) << 62;
+  if (a > 0 && b > lim / a) return false;
+  const int64_t ab = a * b;
+  if (ab > 0 && c > lim / ab) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss_abi_version(void) { return SS_ABI_VERSION; }
+
+const char* ss_status_string(int s) {
+  switch (s) {
+    case SS_OK: return "ok";
+    case SS_ERR_NULL_ARG: return "a required pointer argument is NULL";
+    case SS_ERR_BAD_SHAPE: return "a size argument is out of range";
+    case SS_ERR_BAD_DTYPE: return "unknown input dtype";
+    case SS_ERR_UNSUPPORTED_N: return "dstate exceeds the supported maximum of 16";
+    case SS_ERR_MISALIGNED: return "a pointer is not aligned to its element size";
+    case SS_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case SS_ERR_DEVICE: return "the current device is not a gfx950 GPU";
+    default: return "unknown status code";
+  }
+}
+
+int ss_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+           const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
+           float* last_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+           int in_dtype, void* stream) {
+  // with seqlen == 0 no token is read or written: the per-token arrays may be NULL
+  if (!A || (seqlen != 0 && (!u || !delta || !B || !C || !y))) return SS_ERR_NULL_ARG;
+  if (in_dtype != SS_DTYPE_F32 && in_dtype != SS_DTYPE_BF16) return SS_ERR_BAD_DTYPE;
+  if (batch < 1 || dim < 1 || dstate < 1 || seqlen < 0) return SS_ERR_BAD_SHAPE;
+  if (dstate > SS_MAX_DSTATE) return SS_ERR_UNSUPPORTED_N;
+  if (!product_ok(batch, seqlen, dim) || !product_ok(batch, seqlen, dstate) ||
+      !product_ok(batch, dim, dstate))
+    return SS_ERR_BAD_SHAPE;
+  if (batch * ((dim + 63) / 64) > 0x7fffffffLL) return SS_ERR_BAD_SHAPE;
+  const size_t es = elem_size(in_dtype);
+  if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
+      (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+      (delta_bias && !aligned(delta_bias, 4)) || !aligned(y, 4) ||
+      (last_state && !aligned(last_state, 4)))
+    return SS_ERR_MISALIGNED;
+  const int dv = check_device();
+  if (dv != SS_OK) return dv;
+
+  ss::FwdArgs a{u, delta, A, B, C, D, z, delta_bias, y, last_state,
+                batch, seqlen, dim, dstate, in_dtype, softplus_flag ? 1 : 0};
+  const hipError_t e = ss::fwd_seq(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+int ss_step(float* state, const void* u, const void* delta, const float* A, const void* B,
+            const void* C, const float* D, const void* z, const float* delta_bias,
+            int softplus_flag, float* y, int64_t batch, int64_t dim, int64_t dstate, int in_dtype,
+            void* stream) {
+  if (!state || !u || !delta || !A || !B || !C || !y) return SS_ERR_NULL_ARG;
+  if (in_dtype != SS_DTYPE_F32 && in_dtype != SS_DTYPE_BF16) return SS_ERR_BAD_DTYPE;
+  if (batch < 1 || dim < 1 || dstate < 1) return SS_ERR_BAD_SHAPE;
+  if (dstate > SS_MAX_DSTATE) return SS_ERR_UNSUPPORTED_N;
+  if (!product_ok(batch, dim, dstate)) return SS_ERR_BAD_SHAPE;
+  if ((batch * dim + 255) / 256 > 0x7fffffffLL) return SS_ERR_BAD_SHAPE;
+  const size_t es = elem_size(in_dtype);
+  if (!aligned(state, 4) || !aligned(u, es) || !aligned(delta, es) || !aligned(B, es) ||
+      !aligned(C, es) || (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+      (delta_bias && !aligned(delta_bias, 4)) || !aligned(y, 4))
+    return SS_ERR_MISALIGNED;
+  const int dv = check_device();
+  if (dv != SS_OK) return dv;
+
+  ss::StepArgs a{state, u, delta, A, B, C, D, z, delta_bias, y,
+                 batch, dim, dstate, in_dtype, softplus_flag ? 1 : 0};
+  const hipError_t e = ss::step(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+}  // extern "C"
