@@ -86,6 +86,23 @@ int ss_fwd(const void* u, const void* delta, const float* A, const void* B, cons
            float* last_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
            int in_dtype, void* stream);
 
+/* Kernel selection for ss_fwd_ex (tuning and testing; ss_fwd picks automatically). */
+typedef struct {
+  int kernel;    /* 0: automatic; 1: one lane per channel, sequential in t (any dstate);
+                    2: time-chunked (dstate == 16 only, else SS_ERR_UNSUPPORTED_N) */
+  int chunk_len; /* tokens per lane and tile for kernel 2: 0 (automatic), 4 or 8 */
+} ss_fwd_options;
+
+/*
+ * ss_fwd_ex -- ss_fwd with an explicit kernel choice. Same arguments, layouts, ownership
+ * and errors as ss_fwd; opt may be NULL (automatic). Every choice computes the same
+ * result up to fp32 rounding order. An out-of-range option returns SS_ERR_BAD_SHAPE.
+ */
+int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
+              const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
+              float* last_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+              int in_dtype, const ss_fwd_options* opt, void* stream);
+
 /*
  * ss_step -- one decode step: the same update for a single token, with the state
  * carried across calls and updated in place (streaming inference, O(1) per token:

@@ -11,7 +11,12 @@ _LIB_PATH = os.path.join(_HERE, "libss.so")
 _lib = None
 
 F32, BF16 = 0, 1
-EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_step")
+EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_step")
+
+
+class FwdOptions(ctypes.Structure):
+    """ss_fwd_options: kernel 0 automatic / 1 sequential / 2 time-chunked; chunk_len 0, 4, 8."""
+    _fields_ = [("kernel", ctypes.c_int), ("chunk_len", ctypes.c_int)]
 
 
 class SSError(RuntimeError):
@@ -39,6 +44,9 @@ def load_library():
     lib.ss_status_string.argtypes = [i32]
     lib.ss_fwd.restype = i32
     lib.ss_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.ss_fwd_ex.restype = i32
+    lib.ss_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32,
+                              ctypes.POINTER(FwdOptions), vp]
     lib.ss_step.restype = i32
     lib.ss_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, vp]
     _lib = lib
@@ -81,10 +89,11 @@ def _stream(device, stream):
 
 
 def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=None,
-        last_state=None, return_last_state=True, stream=None):
-    """Selective-scan forward (``ss_fwd``). u, delta, z: (batch, L, dim); B, C: (batch, L, N);
-    A: (dim, N) fp32; D, delta_bias: (dim,) fp32. Returns y (fp32) and, unless
-    return_last_state is False, the final state (batch, dim, N) fp32."""
+        last_state=None, return_last_state=True, stream=None, kernel=0, chunk_len=0):
+    """Selective-scan forward (``ss_fwd``; ``ss_fwd_ex`` when kernel/chunk_len are given).
+    u, delta, z: (batch, L, dim); B, C: (batch, L, N); A: (dim, N) fp32; D, delta_bias:
+    (dim,) fp32. Returns y (fp32) and, unless return_last_state is False, the final state
+    (batch, dim, N) fp32."""
     dev = u.device
     batch, L, dim = u.shape
     N = A.shape[1]
@@ -103,9 +112,14 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=Non
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _check(last_state, "last_state", dev, torch.float32, (batch, dim, N))
-    rc = load_library().ss_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                               _ptr(delta_bias), int(bool(softplus)), _ptr(y), _ptr(last_state),
-                               batch, L, dim, N, dt, _stream(dev, stream))
+    lib = load_library()
+    args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(softplus)), _ptr(y), _ptr(last_state), batch, L, dim, N, dt)
+    if kernel or chunk_len:
+        opt = FwdOptions(int(kernel), int(chunk_len))
+        rc = lib.ss_fwd_ex(*args, ctypes.byref(opt), _stream(dev, stream))
+    else:
+        rc = lib.ss_fwd(*args, _stream(dev, stream))
     if rc != 0:
         raise SSError(rc, "ss_fwd")
     return (y, last_state) if return_last_state else y

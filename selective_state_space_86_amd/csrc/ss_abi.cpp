@@ -12,20 +12,28 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_device_cus[kMaxDevices];
 
-// Is the current device a gfx950? The answer is cached per device id.
-int check_device() {
+// Is the current device a gfx950? The answer (and the CU count) is cached per device id.
+int check_device(int* cus) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SS_ERR_HIP;
   if (dev < kMaxDevices) {
-    const int c = g_device_ok[dev].load(std::memory_order_relaxed);
-    if (c == 1) return SS_OK;
+    const int c = g_device_ok[dev].load(std::memory_order_acquire);
+    if (c == 1) {
+      *cus = g_device_cus[dev].load(std::memory_order_relaxed);
+      return SS_OK;
+    }
     if (c == 2) return SS_ERR_DEVICE;
   }
   hipDeviceProp_t p;
   if (hipGetDeviceProperties(&p, dev) != hipSuccess) return SS_ERR_HIP;
   const bool ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
-  if (dev < kMaxDevices) g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  *cus = p.multiProcessorCount > 0 ? p.multiProcessorCount : 256;
+  if (dev < kMaxDevices) {
+    g_device_cus[dev].store(*cus, std::memory_order_relaxed);
+    g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_release);
+  }
   return ok ? SS_OK : SS_ERR_DEVICE;
 }
 
@@ -62,10 +70,10 @@ const char* ss_status_string(int s) {
   }
 }
 
-int ss_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-           const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
-           float* last_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-           int in_dtype, void* stream) {
+int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
+              const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
+              float* last_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+              int in_dtype, const ss_fwd_options* opt, void* stream) {
   // with seqlen == 0 no token is read or written: the per-token arrays may be NULL
   if (!A || (seqlen != 0 && (!u || !delta || !B || !C || !y))) return SS_ERR_NULL_ARG;
   if (in_dtype != SS_DTYPE_F32 && in_dtype != SS_DTYPE_BF16) return SS_ERR_BAD_DTYPE;
@@ -74,20 +82,39 @@ int ss_fwd(const void* u, const void* delta, const float* A, const void* B, cons
   if (!product_ok(batch, seqlen, dim) || !product_ok(batch, seqlen, dstate) ||
       !product_ok(batch, dim, dstate))
     return SS_ERR_BAD_SHAPE;
-  if (batch * ((dim + 63) / 64) > 0x7fffffffLL) return SS_ERR_BAD_SHAPE;
+  if (batch * ((dim + 15) / 16) > 0x7fffffffLL) return SS_ERR_BAD_SHAPE;
+  const int kernel = opt ? opt->kernel : 0;
+  const int chunk = opt ? opt->chunk_len : 0;
+  if (kernel < 0 || kernel > 2 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
+  if (kernel == 2 && dstate != 16) return SS_ERR_UNSUPPORTED_N;
   const size_t es = elem_size(in_dtype);
   if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
       (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
       (delta_bias && !aligned(delta_bias, 4)) || !aligned(y, 4) ||
       (last_state && !aligned(last_state, 4)))
     return SS_ERR_MISALIGNED;
-  const int dv = check_device();
+  int cus = 0;
+  const int dv = check_device(&cus);
   if (dv != SS_OK) return dv;
 
   ss::FwdArgs a{u, delta, A, B, C, D, z, delta_bias, y, last_state,
                 batch, seqlen, dim, dstate, in_dtype, softplus_flag ? 1 : 0};
-  const hipError_t e = ss::fwd_seq(a, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const bool chunked = kernel == 2 || (kernel == 0 && ss::fwd_chunked_supported(a));
+  if (chunked && seqlen > 0)
+    e = ss::fwd_chunked(a, chunk == 0 ? ss::fwd_chunked_pick(a, cus) : chunk, s);
+  else
+    e = ss::fwd_seq(a, s);
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+int ss_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+           const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
+           float* last_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+           int in_dtype, void* stream) {
+  return ss_fwd_ex(u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state, batch, seqlen,
+                   dim, dstate, in_dtype, nullptr, stream);
 }
 
 int ss_step(float* state, const void* u, const void* delta, const float* A, const void* B,
@@ -105,7 +132,8 @@ int ss_step(float* state, const void* u, const void* delta, const float* A, cons
       !aligned(C, es) || (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
       (delta_bias && !aligned(delta_bias, 4)) || !aligned(y, 4))
     return SS_ERR_MISALIGNED;
-  const int dv = check_device();
+  int cus = 0;
+  const int dv = check_device(&cus);
   if (dv != SS_OK) return dv;
 
   ss::StepArgs a{state, u, delta, A, B, C, D, z, delta_bias, y,

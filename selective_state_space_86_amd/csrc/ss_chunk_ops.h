@@ -1,0 +1,163 @@
+// ss_chunk_ops.h -- building blocks of the time-chunked selective-scan kernels (gfx950):
+// the hand-scheduled per-token update and fix-up for 16 states, buffer-resource loads,
+// and the per-lane tile loader. Included by ss_fwd_chunked.hip and ss_fwd_ring.hip.
+//
+// Lane layout shared by both kernels: a row of 16 lanes holds 16 consecutive channels at
+// one token, so B_t and C_t are row-uniform and lane n of the row holds B_t[n], C_t[n];
+// the update reads them through DPP row_newbcast:n folded into the consuming v_mul/v_fmac.
+#pragma once
+
+#include "ss_common.h"
+#include "ss_kernels.h"
+
+namespace ss {
+namespace chunk {
+
+#define SS_DPP_ROW(n) " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n"
+
+// One token of the local pass for all 16 states, software-pipelined so that
+//  - each exp result is consumed >= 2 instructions after it is produced, and
+//  - each VGPR read by a DPP instruction was written >= 2 instructions earlier
+// (the gfx950 transcendental-forwarding and DPP read-after-write wait states).
+#define SS_UPD(n, n2)                                                        \
+  "v_mul_f32_dpp %[bu], %[vb], %[du]" SS_DPP_ROW(n)                          \
+  "v_fma_f32 %[h" #n "], %[e" #n "], %[h" #n "], %[bu]\n"                    \
+  "v_mul_f32 %[x], %[dt], %[a" #n2 "]\n"                                     \
+  "v_exp_f32 %[e" #n2 "], %[x]\n"                                            \
+  "v_fmac_f32_dpp %[y], %[vc], %[h" #n "]" SS_DPP_ROW(n)
+
+#define SS_OPS16(P, r) \
+  [P##0] r(P[0]), [P##1] r(P[1]), [P##2] r(P[2]), [P##3] r(P[3]), [P##4] r(P[4]), [P##5] r(P[5]), \
+  [P##6] r(P[6]), [P##7] r(P[7]), [P##8] r(P[8]), [P##9] r(P[9]), [P##10] r(P[10]), [P##11] r(P[11]), \
+  [P##12] r(P[12]), [P##13] r(P[13]), [P##14] r(P[14]), [P##15] r(P[15])
+
+__device__ __forceinline__ void local_step(float (&h)[16], float (&e)[16], const float (&a)[16], float dt,
+                                           float du, float vb, float vc, float& y) {
+  float x, bu;
+  asm volatile(
+      "s_nop 0\n"
+      "v_mul_f32 %[x], %[dt], %[a0]\n"
+      "v_exp_f32 %[e0], %[x]\n"
+      "v_mul_f32 %[x], %[dt], %[a1]\n"
+      "v_exp_f32 %[e1], %[x]\n"
+      SS_UPD(0, 2) SS_UPD(1, 3) SS_UPD(2, 4) SS_UPD(3, 5) SS_UPD(4, 6) SS_UPD(5, 7)
+      SS_UPD(6, 8) SS_UPD(7, 9) SS_UPD(8, 10) SS_UPD(9, 11) SS_UPD(10, 12) SS_UPD(11, 13)
+      SS_UPD(12, 14) SS_UPD(13, 15)
+      "v_mul_f32_dpp %[bu], %[vb], %[du]" SS_DPP_ROW(14)
+      "v_fma_f32 %[h14], %[e14], %[h14], %[bu]\n"
+      "v_mul_f32_dpp %[bu], %[vb], %[du]" SS_DPP_ROW(15)
+      "v_fma_f32 %[h15], %[e15], %[h15], %[bu]\n"
+      "v_fmac_f32_dpp %[y], %[vc], %[h14]" SS_DPP_ROW(14)
+      "s_nop 0\n"
+      "v_fmac_f32_dpp %[y], %[vc], %[h15]" SS_DPP_ROW(15)
+      : SS_OPS16(h, "+v"), SS_OPS16(e, "=&v"), [y] "+v"(y), [x] "=&v"(x), [bu] "=&v"(bu)
+      : SS_OPS16(a, "v"), [dt] "v"(dt), [du] "v"(du), [vb] "v"(vb), [vc] "v"(vc));
+}
+
+#define SS_FIX_M(n) "v_mul_f32 %[q" #n "], %[q" #n "], %[e" #n "]\n"
+#define SS_FIX_F(n, Y) "v_fmac_f32_dpp %[" #Y "], %[vc], %[q" #n "]" SS_DPP_ROW(n)
+
+// Fix-up of one token: q[n] *= abar_t[n]; y += C_t[n] q[n] (C_t[n] via row_newbcast:n).
+// Each q is read by the DPP fmac >= 2 instructions after its multiply; even and odd states
+// accumulate into separate registers so consecutive fmacs do not wait on each other.
+__device__ __forceinline__ void fixup_step(float (&q)[16], const float (&e)[16], float vc, float& y) {
+  float y2 = 0.0f;
+  asm volatile(
+      SS_FIX_M(0) SS_FIX_M(1) SS_FIX_M(2) SS_FIX_F(0, y) SS_FIX_M(3) SS_FIX_F(1, y2) SS_FIX_M(4)
+      SS_FIX_F(2, y) SS_FIX_M(5) SS_FIX_F(3, y2) SS_FIX_M(6) SS_FIX_F(4, y) SS_FIX_M(7) SS_FIX_F(5, y2)
+      SS_FIX_M(8) SS_FIX_F(6, y) SS_FIX_M(9) SS_FIX_F(7, y2) SS_FIX_M(10) SS_FIX_F(8, y) SS_FIX_M(11)
+      SS_FIX_F(9, y2) SS_FIX_M(12) SS_FIX_F(10, y) SS_FIX_M(13) SS_FIX_F(11, y2) SS_FIX_M(14)
+      SS_FIX_F(12, y) SS_FIX_M(15) SS_FIX_F(13, y2) SS_FIX_F(14, y) SS_FIX_F(15, y2)
+      : SS_OPS16(q, "+v"), [y] "+v"(y), [y2] "+v"(y2)
+      : SS_OPS16(e, "v"), [vc] "v"(vc));
+  y += y2;
+}
+
+// Buffer resource (gfx9 V#) over [base, base + bytes): loads take an SGPR descriptor, a
+// per-lane 32-bit offset and an SGPR offset, so addressing costs no vector instructions.
+// Accesses past `bytes` read 0 / are dropped by the hardware range check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes > 0x7fffffffLL ? 0x7fffffff : static_cast<int32_t>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
+}
+// (the b32/b16 builtins move raw bits as unsigned integers: reinterpret, never convert)
+__device__ __forceinline__ float ldb(float*, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ float ldb(uint16_t*, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16);
+}
+
+// Map the linear workgroup id to a channel group so that neighbouring groups (which share
+// 128-byte lines of u, delta, z and y) land on the same XCD (workgroups are dealt to the 8
+// XCDs round-robin) and are dispatched close together.
+__device__ __forceinline__ int64_t group_of(int64_t bid, int64_t ngroups) {
+  if (ngroups % 8 != 0) return bid;
+  return (bid % 8) * (ngroups / 8) + bid / 8;
+}
+
+template <int TC>
+struct TileIn {
+  float raw[TC], uu[TC], zz[TC], vb[TC], vc[TC];
+};
+
+// ROWS chunks of TC tokens form one tile (16 for a workgroup tile, 4 for a wave-tile).
+template <typename T, bool GATE, int TC, int ROWS>
+struct TileLoader {
+  const FwdArgs& a;
+  int64_t b, c0, L, dim;
+  int k, i;
+  uint32_t tok_off, bc_off;  // lane byte offsets of token j = 0 of its chunk within a tile
+  uint32_t tok_row, bc_row;  // bytes per token of (.., dim) and (.., 16) rows
+
+  __device__ TileLoader(const FwdArgs& args, int64_t b_, int64_t c0_, int k_, int i_, int64_t cc)
+      : a(args), b(b_), c0(c0_), L(args.seqlen), dim(args.dim), k(k_), i(i_) {
+    tok_row = static_cast<uint32_t>(dim * sizeof(T));
+    bc_row = 16 * sizeof(T);
+    tok_off = static_cast<uint32_t>(k * TC) * tok_row + static_cast<uint32_t>((cc - c0) * sizeof(T));
+    bc_off = static_cast<uint32_t>(k * TC) * bc_row + static_cast<uint32_t>(i * sizeof(T));
+  }
+
+  // Request the inputs of the tile starting at t0. In a partial tile, tokens past the end
+  // re-read the last token (their step is forced to 0 later).
+  __device__ __forceinline__ void load(TileIn<TC>& x, int64_t t0) const {
+    const int64_t tok0 = (b * L + t0) * dim + c0;
+    const int64_t bc0 = (b * L + t0) * 16;
+    const int64_t tok_left = (a.batch * L * dim - tok0) * static_cast<int64_t>(sizeof(T));
+    const int64_t bc_left = (a.batch * L * 16 - bc0) * static_cast<int64_t>(sizeof(T));
+    const auto rd = rsrc(static_cast<const T*>(a.delta) + tok0, tok_left);
+    const auto ru = rsrc(static_cast<const T*>(a.u) + tok0, tok_left);
+    const auto rz = rsrc(GATE ? static_cast<const T*>(a.z) + tok0 : static_cast<const T*>(a.u), GATE ? tok_left : 0);
+    const auto rB = rsrc(static_cast<const T*>(a.B) + bc0, bc_left);
+    const auto rC = rsrc(static_cast<const T*>(a.C) + bc0, bc_left);
+    T* tag = nullptr;
+    if (t0 + ROWS * TC <= L) {
+#pragma unroll
+      for (int j = 0; j < TC; ++j) {
+        x.raw[j] = ldb(tag, rd, tok_off, j * tok_row);
+        x.uu[j] = ldb(tag, ru, tok_off, j * tok_row);
+        if (GATE) x.zz[j] = ldb(tag, rz, tok_off, j * tok_row);
+        x.vb[j] = ldb(tag, rB, bc_off, j * bc_row);
+        x.vc[j] = ldb(tag, rC, bc_off, j * bc_row);
+      }
+    } else {
+      const int last = static_cast<int>(L - 1 - t0);
+      const uint32_t col = tok_off - static_cast<uint32_t>(k * TC) * tok_row;
+#pragma unroll
+      for (int j = 0; j < TC; ++j) {
+        const uint32_t tt = static_cast<uint32_t>(min(k * TC + j, last));
+        const uint32_t to = tt * tok_row + col;
+        const uint32_t bo = tt * bc_row + static_cast<uint32_t>(i * sizeof(T));
+        x.raw[j] = ldb(tag, rd, to, 0);
+        x.uu[j] = ldb(tag, ru, to, 0);
+        if (GATE) x.zz[j] = ldb(tag, rz, to, 0);
+        x.vb[j] = ldb(tag, rB, bo, 0);
+        x.vc[j] = ldb(tag, rC, bo, 0);
+      }
+    }
+  }
+};
+
+
+}  // namespace chunk
+}  // namespace ss

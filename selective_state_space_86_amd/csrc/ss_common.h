@@ -24,22 +24,23 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// softplus(x) = log(1 + e^x), accurate to a few ulp in fp32 over the whole range.
-// For x > 15, e^-x < 3.1e-7 and softplus(x) = x + e^-x to within fp32 rounding of x.
-// Otherwise with e = e^x, log1p(e) is computed as log(1+e) * e / ((1+e) - 1), which
-// cancels the rounding of 1+e (the classic log1p identity); for tiny e the quotient
-// degenerates and log1p(e) = e is exact to fp32.
+// softplus(x) = max(x, 0) + log1p(t), t = e^-|x| in (0, 1].
+// log1p(t) is log(w) for w = fl(1 + t) plus the rounding error of w: with m = w - 1 (exact
+// for w in [1, 2]) and d = t - m (exact), log(1 + t) = log(w) + log(1 + d/w) ~ log(w) + d/w,
+// and 1/w ~ 1 - m to the accuracy this tiny correction needs. When t < 2^-24, w = 1, m = 0
+// and the result is t itself. Cost: 2 transcendentals and 8 simple VALU ops.
 __device__ __forceinline__ float softplus(float x) {
-  if (x > 15.0f) return x + fast_exp2(-x * kLog2e);
-  const float e = fast_exp2(x * kLog2e);
-  const float w = 1.0f + e;
+  const float t = fast_exp2(-__builtin_fabsf(x) * kLog2e);
+  const float w = 1.0f + t;
   const float m = w - 1.0f;
-  if (m == 0.0f) return e;
-  return fast_log2(w) * kLn2 * (e / m);
+  const float d = t - m;
+  const float corr = __builtin_fmaf(-d, m, d);
+  const float lp = __builtin_fmaf(fast_log2(w), kLn2, corr);
+  return __builtin_fmaxf(x, 0.0f) + lp;
 }
 
-// silu(z) = z * sigmoid(z) = z / (1 + e^-z); for z < -88 the denominator is inf and
-// the result is -0, the correct limit.
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + fast_exp2(-z * kLog2e)); }
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z), with the reciprocal on the transcendental unit.
+// For z < -88, e^-z = inf and the result is z * 0 = -0, the correct limit.
+__device__ __forceinline__ float silu(float z) { return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }
 
 }  // namespace ss

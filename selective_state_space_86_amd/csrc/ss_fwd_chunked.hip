@@ -1,0 +1,198 @@
+// ss_fwd_chunked.hip -- time-chunked selective-scan forward for dstate == 16 (gfx950).
+//
+// What it computes is the recurrence of "Mamba：选择性状态空间模型入门教程" (section
+// "Mamba 的关键创新：选择性机制"), discretised as in "架构变体：Mamba/SSM" (section
+// "离散化"); how it computes it follows the hardware-aware scan of "Mamba：选择性状态空间
+// 的线性时间序列建模" (section "第二个创新：硬件感知算法": a parallel associative scan,
+// fused so the expanded state stays on chip) and the block decomposition of "Mamba架构
+// 深度解析" (section "Mamba的创新": split the sequence into blocks, parallel inside a
+// block), laid out for 64-wide CDNA waves:
+//
+//  * A workgroup (4 waves, 16 rows of 16 lanes) owns 16 consecutive channels of one batch
+//    row. Lane i of a row is channel c0+i; the 16 rows are 16 consecutive time chunks of
+//    TC tokens, so a tile covers 16*TC tokens. Every lane keeps all 16 fp32 states of its
+//    channel in registers: softplus, the D term and the gate are paid once per 16 updates.
+//  * A row sits at one token at a time, so B_t and C_t are row-uniform: lane n of the row
+//    holds B_t[n] and C_t[n], and the update reads them through DPP row_newbcast:n folded
+//    into the v_mul / v_fmac that consume them (no LDS, no extra instruction).
+//  * Local pass: each lane scans its chunk from a zero state, keeping abar = exp(dt A) of
+//    every step in registers. The chunk aggregate (prod abar, end state) is the pair of the
+//    associative operator (a1, b1) o (a2, b2) = (a2 a1, a2 b1 + b2) ("架构变体" section
+//    "硬件感知算法": the update is associative, so it can be combined as a tree).
+//  * Combine: aggregates go to LDS; lane (chunk k, channel i) then owns state n = k and
+//    folds the 16 chunk aggregates of channel i in order, producing every chunk's carry-in
+//    and the carry into the next tile (kept in that lane's register across tiles).
+//  * Fix-up: y_t += sum_n C_t[n] (prod_{s<=t} abar_s[n]) carry[n], from the stored abar;
+//    then the gate, and one store per token. The (L x N) state never reaches memory.
+// Per state update the local pass issues 4 VALU ops and one v_exp_f32, the fix-up 2 VALU.
+//
+// Memory access: every lane has a fixed 32-bit byte offset into a tile (its chunk row and
+// channel); the tile origin and the token step within the chunk live in SGPR base pointers,
+// so the loads and stores need no per-access vector address arithmetic. The next tile's
+// inputs are requested right after the local pass, so the combine and the fix-up of the
+// current tile overlap their latency.
+#include "ss_chunk_ops.h"
+
+namespace ss {
+namespace {
+
+using namespace chunk;
+
+constexpr int kLdsChunkStride = 16 * 16 + 16;  // [chunk][n][lane], padded against bank conflicts
+
+// Register budget: TC = 4 must fit 3 workgroups (12 waves) per CU, TC = 8 two.
+template <typename T, bool GATE, int TC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TC <= 4 ? 3 : 2)))
+void fwd_chunked_kernel(FwdArgs a) {
+  // The prod-abar/carry array alternates between two buffers by tile, so a tile's
+  // aggregates never overwrite carries a slower wave may still be reading after the second
+  // barrier of the previous tile. The end states are read only between the two barriers of
+  // a tile, so one buffer suffices.
+  __shared__ float lds_a2[2][16 * kLdsChunkStride];  // chunk prod-abar, then the chunk carries
+  __shared__ float lds_h[16 * kLdsChunkStride];      // chunk end states
+
+  const int64_t ngd = (a.dim + 15) / 16;
+  const int64_t g = group_of(blockIdx.x, a.batch * ngd);
+  const int64_t b = g / ngd;
+  const int64_t c0 = (g % ngd) * 16;
+  const int tid = threadIdx.x;
+  const int i = tid & 15;  // channel within the group == the state index this lane owns in the combine
+  const int k = tid >> 4;  // time chunk within the tile (row of 16 lanes)
+  const int64_t c = c0 + i;
+  const bool cvalid = c < a.dim;
+  const int64_t cc = cvalid ? c : a.dim - 1;
+  const int64_t L = a.seqlen;
+  TileLoader<T, GATE, TC, 16> K(a, b, c0, k, i, cc);
+
+  float A2[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) A2[n] = a.A[cc * 16 + n] * kLog2e;
+  const float bias = a.delta_bias ? a.delta_bias[cc] : 0.0f;
+  const float Dd = a.D ? a.D[cc] : 0.0f;
+  float carry = 0.0f;  // state n = k of channel c0+i, carried across tiles
+  const uint32_t y_row = static_cast<uint32_t>(a.dim * 4);
+  const uint32_t y_off = static_cast<uint32_t>(k * TC) * y_row + static_cast<uint32_t>(i * 4);
+
+  TileIn<TC> cur;
+  K.load(cur, 0);
+  int buf = 0;
+  for (int64_t t0 = 0; t0 < L; t0 += 16 * TC, buf ^= 1) {
+    const bool full = t0 + 16 * TC <= L;
+    float* lds_a = lds_a2[buf];
+
+    // local pass from a zero state
+    float h[16], ex[TC][16], y[TC], gate[TC], vc[TC];
+#pragma unroll
+    for (int n = 0; n < 16; ++n) h[n] = 0.0f;
+    float dsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < TC; ++j) {
+      const float x = cur.raw[j] + bias;
+      float dt = a.softplus ? softplus(x) : x;
+      if (!full) dt = (t0 + k * TC + j < L) ? dt : 0.0f;  // a zero step is the identity
+      dsum += dt;
+      y[j] = Dd * cur.uu[j];
+      local_step(h, ex[j], A2, dt, dt * cur.uu[j], cur.vb[j], cur.vc[j], y[j]);
+      gate[j] = GATE ? silu(cur.zz[j]) : 1.0f;
+      vc[j] = cur.vc[j];
+    }
+
+    // request the next tile now: the combine and fix-up below hide its latency
+    if (t0 + 16 * TC < L) K.load(cur, t0 + 16 * TC);
+
+    // chunk aggregates (prod abar = exp(A * sum dt), end state) to LDS
+    {
+      float* la = lds_a + k * kLdsChunkStride + i;
+      float* lh = lds_h + k * kLdsChunkStride + i;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        float p;
+        if (TC <= 4) {  // product of the stored factors: TC-1 multiplies
+          p = ex[0][n];
+#pragma unroll
+          for (int j = 1; j < TC; ++j) p *= ex[j][n];
+        } else {        // one multiply and one exp
+          p = fast_exp2(A2[n] * dsum);
+        }
+        la[n * 16] = p;
+        lh[n * 16] = h[n];
+      }
+    }
+    __syncthreads();
+
+    // combine: this lane owns state n = k of channel i and folds the 16 chunks in order.
+    // Each lane reads exactly the LDS words it then overwrites with carries, so the carry
+    // array can alias the prod-abar array without another barrier.
+    {
+      float* sa = lds_a + k * 16 + i;
+      const float* sh = lds_h + k * 16 + i;
+      float av[16], hv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        av[j] = sa[j * kLdsChunkStride];
+        hv[j] = sh[j * kLdsChunkStride];
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        sa[j * kLdsChunkStride] = carry;  // carry into chunk j
+        carry = __builtin_fmaf(av[j], carry, hv[j]);
+      }
+    }
+    __syncthreads();
+    float q[16];  // this chunk's carry-in
+    {
+      const float* lc = lds_a + k * kLdsChunkStride + i;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) q[n] = lc[n * 16];
+    }
+
+    // fix-up with the carry-in, gate, store
+    const int64_t y0 = (b * L + t0) * a.dim + c0;
+    const auto ry = rsrc(a.y + y0, (a.batch * L * a.dim - y0) * 4);
+#pragma unroll
+    for (int j = 0; j < TC; ++j) {
+      fixup_step(q, ex[j], vc[j], y[j]);
+      const bool ok = full ? cvalid : (cvalid && t0 + k * TC + j < L);
+      if (ok) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[j] * gate[j]), ry, y_off, j * y_row, 0);
+    }
+  }
+  if (a.last_state && cvalid) a.last_state[(b * a.dim + c) * 16 + k] = carry;
+}
+
+template <typename T, bool GATE, int TC>
+hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
+  const int64_t ngroups = a.batch * ((a.dim + 15) / 16);
+  hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC>), dim3(static_cast<unsigned>(ngroups)), dim3(256), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int TC>
+hipError_t launch_chunked_g(const FwdArgs& a, hipStream_t s) {
+  return a.z ? launch_chunked<T, true, TC>(a, s) : launch_chunked<T, false, TC>(a, s);
+}
+
+}  // namespace
+
+bool fwd_chunked_supported(const FwdArgs& a) { return a.dstate == 16 && a.seqlen > 0; }
+
+// Chunk length: 8 halves the per-tile combine cost but needs ~2x the registers of 4
+// (2 resident workgroups per CU instead of 3). Pick the one whose workgroup count fills
+// the resident slots of every CU most evenly.
+int fwd_chunked_pick(const FwdArgs& a, int cus) {
+  const int64_t groups = a.batch * ((a.dim + 15) / 16);
+  auto eff = [&](int slots) {
+    const int64_t cap = static_cast<int64_t>(cus) * slots;
+    const int64_t rounds = (groups + cap - 1) / cap;
+    return static_cast<double>(groups) / static_cast<double>(rounds * cap);
+  };
+  return eff(3) > eff(2) + 1e-9 ? 4 : 8;
+}
+
+hipError_t fwd_chunked(const FwdArgs& a, int chunk_len, hipStream_t s) {
+  const bool bf = a.dtype == kBF16;
+  if (chunk_len == 4) return bf ? launch_chunked_g<uint16_t, 4>(a, s) : launch_chunked_g<float, 4>(a, s);
+  return bf ? launch_chunked_g<uint16_t, 8>(a, s) : launch_chunked_g<float, 8>(a, s);
+}
+
+}  // namespace ss

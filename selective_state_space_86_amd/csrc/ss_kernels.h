@@ -44,6 +44,9 @@ struct StepArgs {
 };
 
 hipError_t fwd_seq(const FwdArgs& a, hipStream_t s);
+bool fwd_chunked_supported(const FwdArgs& a);
+hipError_t fwd_chunked(const FwdArgs& a, int chunk_len, hipStream_t s);
+int fwd_chunked_pick(const FwdArgs& a, int cus);
 hipError_t step(const StepArgs& a, hipStream_t s);
 
 }  // namespace ss

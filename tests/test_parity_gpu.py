@@ -159,3 +159,36 @@ def test_mamba1_4b_full_size_sampled():
 
 def test_mamba3b_long_full_size_sampled():
     _check_sampled(inputs.WORKLOADS["mamba3b-long"], k=48)
+
+
+KERNELS = [(1, 0), (2, 4), (2, 8)]
+
+
+@pytest.mark.parametrize("kernel,chunk", KERNELS)
+@pytest.mark.parametrize("batch,L,dim,dt", [(3, 37, 100, "f32"), (2, 129, 70, "bf16"), (1, 1, 16, "f32"),
+                                            (2, 1000, 130, "f32"), (1, 777, 257, "bf16"),
+                                            (2, 128, 64, "f32"), (1, 300, 17, "f32")])
+def test_every_kernel_choice(kernel, chunk, batch, L, dim, dt):
+    """Every kernel and chunk length matches the oracle (the chunk split is free: the update
+    is associative), including ragged channel counts and partial last tiles."""
+    w = inputs.WORKLOADS["mamba130m"].replace(name=f"k{batch}x{L}x{dim}{dt}", batch=batch, seqlen=L, dim=dim,
+                                              dstate=16, dtype=dt)
+    x = inputs.make(w, seed=11, device=DEV)
+    _announce(f"kernel={kernel} chunk={chunk} {w.name}")
+    for gated in (False, True):
+        y, st = pu.gpu_fwd(x, gated, kernel=kernel, chunk_len=chunk)
+        torch.cuda.synchronize()
+        y_ref, st_ref = pu.oracle_full(x, gated)
+        tol = pu.tol_of(x)
+        assert pu.scaled_err(y.double().cpu().numpy(), y_ref) <= tol
+        assert pu.scaled_err(st.double().cpu().numpy(), st_ref) <= tol
+
+
+def test_chunk_lengths_agree_at_130m_shape():
+    x = inputs.make(inputs.WORKLOADS["mamba130m"], seed=2, device=DEV)
+    outs = [pu.gpu_fwd(x, False, kernel=kn, chunk_len=ch) for kn, ch in KERNELS]
+    torch.cuda.synchronize()
+    for y, st in outs[1:]:
+        ref_y, ref_st = outs[0]
+        assert ((y - ref_y).abs() / (1 + ref_y.abs())).max().item() <= 2e-5
+        assert ((st - ref_st).abs() / (1 + ref_st.abs())).max().item() <= 2e-5
