@@ -94,14 +94,19 @@ typedef struct {
 } ss_fwd_options;
 
 /*
- * ss_fwd_ex -- ss_fwd with an explicit kernel choice. Same arguments, layouts, ownership
- * and errors as ss_fwd; opt may be NULL (automatic). Every choice computes the same
- * result up to fp32 rounding order. An out-of-range option returns SS_ERR_BAD_SHAPE.
+ * ss_fwd_ex -- ss_fwd from a given initial state and with an explicit kernel choice.
+ * Same arguments, layouts, ownership and errors as ss_fwd, plus:
+ *   h0   (batch, dim, dstate) fp32 initial state, may be NULL (zero state, as ss_fwd).
+ *        With h0 = the last_state of a call over tokens [0, t0), a call over [t0, L)
+ *        continues that scan (chunked prefill; the update is associative, "架构变体：
+ *        Mamba/SSM" section "硬件感知算法"); with seqlen == 0, last_state = h0.
+ *   opt  kernel choice, may be NULL (automatic). Every choice computes the same result up
+ *        to fp32 rounding order. An out-of-range option returns SS_ERR_BAD_SHAPE.
  */
 int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
               const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
-              float* last_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-              int in_dtype, const ss_fwd_options* opt, void* stream);
+              float* last_state, const float* h0, int64_t batch, int64_t seqlen, int64_t dim,
+              int64_t dstate, int in_dtype, const ss_fwd_options* opt, void* stream);
 
 /*
  * ss_step -- one decode step: the same update for a single token, with the state

@@ -45,7 +45,7 @@ def load_library():
     lib.ss_fwd.restype = i32
     lib.ss_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, vp]
     lib.ss_fwd_ex.restype = i32
-    lib.ss_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32,
+    lib.ss_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i32,
                               ctypes.POINTER(FwdOptions), vp]
     lib.ss_step.restype = i32
     lib.ss_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, vp]
@@ -89,11 +89,11 @@ def _stream(device, stream):
 
 
 def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=None,
-        last_state=None, return_last_state=True, stream=None, kernel=0, chunk_len=0):
-    """Selective-scan forward (``ss_fwd``; ``ss_fwd_ex`` when kernel/chunk_len are given).
-    u, delta, z: (batch, L, dim); B, C: (batch, L, N); A: (dim, N) fp32; D, delta_bias:
-    (dim,) fp32. Returns y (fp32) and, unless return_last_state is False, the final state
-    (batch, dim, N) fp32."""
+        last_state=None, return_last_state=True, stream=None, kernel=0, chunk_len=0, h0=None):
+    """Selective-scan forward (``ss_fwd``; ``ss_fwd_ex`` when h0, kernel or chunk_len are
+    given). u, delta, z: (batch, L, dim); B, C: (batch, L, N); A: (dim, N) fp32; D,
+    delta_bias: (dim,) fp32; h0: (batch, dim, N) fp32 initial state or None. Returns y
+    (fp32) and, unless return_last_state is False, the final state (batch, dim, N) fp32."""
     dev = u.device
     batch, L, dim = u.shape
     N = A.shape[1]
@@ -106,6 +106,7 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=Non
     _check(A, "A", dev, torch.float32, (dim, N))
     _check(D, "D", dev, torch.float32, (dim,))
     _check(delta_bias, "delta_bias", dev, torch.float32, (dim,))
+    _check(h0, "h0", dev, torch.float32, (batch, dim, N))
     if y is None:
         y = torch.empty((batch, L, dim), dtype=torch.float32, device=dev)
     _check(y, "y", dev, torch.float32, (batch, L, dim))
@@ -113,13 +114,14 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=Non
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _check(last_state, "last_state", dev, torch.float32, (batch, dim, N))
     lib = load_library()
-    args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-            int(bool(softplus)), _ptr(y), _ptr(last_state), batch, L, dim, N, dt)
-    if kernel or chunk_len:
+    head = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(softplus)), _ptr(y), _ptr(last_state))
+    tail = (batch, L, dim, N, dt)
+    if kernel or chunk_len or h0 is not None:
         opt = FwdOptions(int(kernel), int(chunk_len))
-        rc = lib.ss_fwd_ex(*args, ctypes.byref(opt), _stream(dev, stream))
+        rc = lib.ss_fwd_ex(*head, _ptr(h0), *tail, ctypes.byref(opt), _stream(dev, stream))
     else:
-        rc = lib.ss_fwd(*args, _stream(dev, stream))
+        rc = lib.ss_fwd(*head, *tail, _stream(dev, stream))
     if rc != 0:
         raise SSError(rc, "ss_fwd")
     return (y, last_state) if return_last_state else y

@@ -72,8 +72,8 @@ const char* ss_status_string(int s) {
 
 int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
               const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
-              float* last_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
-              int in_dtype, const ss_fwd_options* opt, void* stream) {
+              float* last_state, const float* h0, int64_t batch, int64_t seqlen, int64_t dim,
+              int64_t dstate, int in_dtype, const ss_fwd_options* opt, void* stream) {
   // with seqlen == 0 no token is read or written: the per-token arrays may be NULL
   if (!A || (seqlen != 0 && (!u || !delta || !B || !C || !y))) return SS_ERR_NULL_ARG;
   if (in_dtype != SS_DTYPE_F32 && in_dtype != SS_DTYPE_BF16) return SS_ERR_BAD_DTYPE;
@@ -91,14 +91,14 @@ int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, c
   if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
       (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
       (delta_bias && !aligned(delta_bias, 4)) || !aligned(y, 4) ||
-      (last_state && !aligned(last_state, 4)))
+      (last_state && !aligned(last_state, 4)) || (h0 && !aligned(h0, 4)))
     return SS_ERR_MISALIGNED;
   int cus = 0;
   const int dv = check_device(&cus);
   if (dv != SS_OK) return dv;
 
   ss::FwdArgs a{u, delta, A, B, C, D, z, delta_bias, y, last_state,
-                batch, seqlen, dim, dstate, in_dtype, softplus_flag ? 1 : 0};
+                batch, seqlen, dim, dstate, in_dtype, softplus_flag ? 1 : 0, h0};
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   const bool chunked = kernel == 2 || (kernel == 0 && ss::fwd_chunked_supported(a));
@@ -113,8 +113,8 @@ int ss_fwd(const void* u, const void* delta, const float* A, const void* B, cons
            const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
            float* last_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
            int in_dtype, void* stream) {
-  return ss_fwd_ex(u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state, batch, seqlen,
-                   dim, dstate, in_dtype, nullptr, stream);
+  return ss_fwd_ex(u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state, nullptr, batch,
+                   seqlen, dim, dstate, in_dtype, nullptr, stream);
 }
 
 int ss_step(float* state, const void* u, const void* delta, const float* A, const void* B,

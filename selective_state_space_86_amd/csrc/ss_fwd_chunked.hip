@@ -41,7 +41,7 @@ using namespace chunk;
 constexpr int kLdsChunkStride = 16 * 16 + 16;  // [chunk][n][lane], padded against bank conflicts
 
 // Register budget: TC = 4 must fit 3 workgroups (12 waves) per CU, TC = 8 two.
-template <typename T, bool GATE, int TC>
+template <typename T, bool GATE, int TC, bool EARLY>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TC <= 4 ? 3 : 2)))
 void fwd_chunked_kernel(FwdArgs a) {
   // The prod-abar/carry array alternates between two buffers by tile, so a tile's
@@ -69,16 +69,19 @@ void fwd_chunked_kernel(FwdArgs a) {
   for (int n = 0; n < 16; ++n) A2[n] = a.A[cc * 16 + n] * kLog2e;
   const float bias = a.delta_bias ? a.delta_bias[cc] : 0.0f;
   const float Dd = a.D ? a.D[cc] : 0.0f;
-  float carry = 0.0f;  // state n = k of channel c0+i, carried across tiles
+  // state n = k of channel c0+i, carried across tiles; starts at h0 when one is given
+  float carry = a.h0 ? a.h0[(b * a.dim + cc) * 16 + k] : 0.0f;
   const uint32_t y_row = static_cast<uint32_t>(a.dim * 4);
   const uint32_t y_off = static_cast<uint32_t>(k * TC) * y_row + static_cast<uint32_t>(i * 4);
 
-  TileIn<TC> cur;
+  TileIn<TC> cur, nxt;
   K.load(cur, 0);
   int buf = 0;
   for (int64_t t0 = 0; t0 < L; t0 += 16 * TC, buf ^= 1) {
     const bool full = t0 + 16 * TC <= L;
     float* lds_a = lds_a2[buf];
+    // request the next tile first: the whole tile's work hides its latency
+    if (EARLY && t0 + 16 * TC < L) K.load(nxt, t0 + 16 * TC);
 
     // local pass from a zero state
     float h[16], ex[TC][16], y[TC], gate[TC], vc[TC];
@@ -97,8 +100,8 @@ void fwd_chunked_kernel(FwdArgs a) {
       vc[j] = cur.vc[j];
     }
 
-    // request the next tile now: the combine and fix-up below hide its latency
-    if (t0 + 16 * TC < L) K.load(cur, t0 + 16 * TC);
+    // otherwise request it now: the combine and fix-up below hide its latency
+    if (!EARLY && t0 + 16 * TC < L) K.load(nxt, t0 + 16 * TC);
 
     // chunk aggregates (prod abar = exp(A * sum dt), end state) to LDS
     {
@@ -155,6 +158,7 @@ void fwd_chunked_kernel(FwdArgs a) {
       const bool ok = full ? cvalid : (cvalid && t0 + k * TC + j < L);
       if (ok) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[j] * gate[j]), ry, y_off, j * y_row, 0);
     }
+    cur = nxt;
   }
   if (a.last_state && cvalid) a.last_state[(b * a.dim + c) * 16 + k] = carry;
 }
@@ -162,7 +166,7 @@ void fwd_chunked_kernel(FwdArgs a) {
 template <typename T, bool GATE, int TC>
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   const int64_t ngroups = a.batch * ((a.dim + 15) / 16);
-  hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC>), dim3(static_cast<unsigned>(ngroups)), dim3(256), 0,
+  hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, (TC <= 4 && !GATE)>), dim3(static_cast<unsigned>(ngroups)), dim3(256), 0,
                      s, a);
   return hipGetLastError();
 }

@@ -9,7 +9,8 @@
 // the same B_t and C_t (scalar loads) and u, delta, z, y are read/written as 64
 // consecutive elements. The expanded (L x N) state lives only in registers.
 // This kernel is the simple, always-applicable path (any dim, any dstate <= 16, ragged
-// channel tails); the tiled kernel covers the common shapes faster.
+// channel tails); the tiled kernel covers the common shapes faster. The state starts at
+// h0 when one is given, else at zero.
 #include "ss_common.h"
 #include "ss_kernels.h"
 
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(64) void fwd_seq_kernel(FwdArgs a) {
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
     A2[n] = (n < ns) ? a.A[dd * ns + n] * kLog2e : 0.0f;
-    h[n] = 0.0f;
+    h[n] = (n < ns && a.h0) ? a.h0[(b * a.dim + dd) * ns + n] : 0.0f;
   }
   const float bias = a.delta_bias ? a.delta_bias[dd] : 0.0f;
   const float Dd = a.D ? a.D[dd] : 0.0f;

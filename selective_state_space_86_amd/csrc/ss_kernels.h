@@ -24,6 +24,7 @@ struct FwdArgs {
   int64_t batch, seqlen, dim, dstate;
   int dtype;
   int softplus;
+  const float* h0;          // may be null: zero initial state
 };
 
 // Validated arguments of one ss_step call.

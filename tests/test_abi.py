@@ -101,17 +101,18 @@ def test_binding_rejects_mixed_dtypes():
 
 def fwd_ex_call(lib, kernel, chunk, **kw):
     a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, sp=1, y=FAKE,
-             st=None, batch=1, L=4, dim=8, N=16, dtype=0)
+             st=None, h0=None, batch=1, L=4, dim=8, N=16, dtype=0)
     a.update(kw)
     opt = _binding.FwdOptions(kernel, chunk)
     return lib.ss_fwd_ex(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
-                         a["y"], a["st"], a["batch"], a["L"], a["dim"], a["N"], a["dtype"],
+                         a["y"], a["st"], a["h0"], a["batch"], a["L"], a["dim"], a["N"], a["dtype"],
                          ctypes.byref(opt), None)
 
 
 @pytest.mark.parametrize("kernel,chunk,kw,code", [
     (3, 0, {}, 2), (-1, 0, {}, 2), (2, 5, {}, 2), (0, 16, {}, 2), (2, 0, dict(N=8), 4),
     (2, 4, dict(u=None), 1), (1, 0, dict(N=17), 4), (2, 8, dict(dtype=7), 3),
+    (0, 0, dict(h0=FAKE + 2), 5), (1, 0, dict(h0=FAKE + 1, L=0), 5),
 ])
 def test_fwd_ex_validation(lib, kernel, chunk, kw, code):
     assert fwd_ex_call(lib, kernel, chunk, **kw) == code

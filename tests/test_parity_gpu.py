@@ -192,3 +192,76 @@ def test_chunk_lengths_agree_at_130m_shape():
         ref_y, ref_st = outs[0]
         assert ((y - ref_y).abs() / (1 + ref_y.abs())).max().item() <= 2e-5
         assert ((st - ref_st).abs() / (1 + ref_st.abs())).max().item() <= 2e-5
+
+
+@pytest.mark.parametrize("kernel,chunk", KERNELS)
+@pytest.mark.parametrize("batch,L,dim,N,dt", [(2, 300, 70, 16, "f32"), (1, 129, 33, 16, "bf16"),
+                                              (3, 50, 40, 5, "f32")])
+def test_initial_state(kernel, chunk, batch, L, dim, N, dt):
+    """ss_fwd_ex with h0 matches the oracle started from the same state."""
+    if kernel == 2 and N != 16:
+        pytest.skip("the time-chunked kernel is for dstate 16")
+    w = inputs.WORKLOADS["mamba130m"].replace(name=f"h{batch}{L}{dim}{N}{dt}", batch=batch, seqlen=L, dim=dim,
+                                              dstate=N, dtype=dt)
+    x = inputs.make(w, seed=12, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    h0 = torch.randn((batch, dim, N), generator=g, device=DEV)
+    y, st = pu.gpu_fwd(x, True, kernel=kernel, chunk_len=chunk, h0=h0)
+    torch.cuda.synchronize()
+    n = {k: inputs.to_numpy(v) for k, v in x.items()}
+    import oracle
+    y_ref, st_ref = oracle.fwd(n["u"], n["delta"], n["A"], n["B"], n["C"], D=n["D"], z=n["z"],
+                               delta_bias=n["delta_bias"], h0=h0.double().cpu().numpy())
+    tol = pu.tol_of(x)
+    assert pu.scaled_err(y.double().cpu().numpy(), y_ref) <= tol
+    assert pu.scaled_err(st.double().cpu().numpy(), st_ref) <= tol
+
+
+def test_empty_sequence_returns_initial_state():
+    w = inputs.WORKLOADS["mamba130m"].replace(name="empty-h0", batch=2, seqlen=0, dim=80, dstate=16)
+    x = inputs.make(w, seed=5, device=DEV)
+    h0 = torch.randn((2, 80, 16), device=DEV)
+    _, st = pu.gpu_fwd(x, True, h0=h0)
+    torch.cuda.synchronize()
+    assert torch.equal(st, h0)
+
+
+def test_chunked_prefill_matches_one_pass():
+    """A forward over [0, t0) then one over [t0, L) from its final state equals one pass
+    (associativity of the update), up to fp32 rounding."""
+    w = inputs.WORKLOADS["mamba1.4b"].replace(name="prefill", batch=2, seqlen=3000, dim=256)
+    x = inputs.make(w, seed=13, device=DEV)
+    y, st = pu.gpu_fwd(x, True)
+    t0 = 1234
+    part = lambda sl: {k: (v[:, sl].contiguous() if k in ("u", "delta", "z", "B", "C") else v) for k, v in x.items()}
+    y1, s1 = pu.gpu_fwd(part(slice(0, t0)), True)
+    y2, s2 = pu.gpu_fwd(part(slice(t0, None)), True, h0=s1)
+    torch.cuda.synchronize()
+    yc = torch.cat([y1, y2], dim=1)
+    tol = pu.tol_of(x)
+    assert ((yc - y).abs() / (1 + y.abs())).max().item() <= tol
+    assert ((s2 - st).abs() / (1 + st.abs())).max().item() <= tol
+
+
+def test_prefill_then_decode_matches_one_pass():
+    """Prefill the first tokens with ss_fwd, continue token by token with ss_step from its
+    final state: the outputs equal one forward over all tokens."""
+    import selective_state_space_86_amd as ss
+    w = inputs.WORKLOADS["mamba130m"].replace(name="pre-dec", batch=3, seqlen=300, dim=192)
+    x = inputs.make(w, seed=14, device=DEV)
+    y, st = pu.gpu_fwd(x, True)
+    t0 = 200
+    pre = {k: (v[:, :t0].contiguous() if k in ("u", "delta", "z", "B", "C") else v) for k, v in x.items()}
+    _, state = pu.gpu_fwd(pre, True)
+    state = state.clone()
+    outs = []
+    for t in range(t0, w.seqlen):
+        outs.append(ss.step(state, x["u"][:, t].contiguous(), x["delta"][:, t].contiguous(), x["A"],
+                            x["B"][:, t].contiguous(), x["C"][:, t].contiguous(), D=x["D"],
+                            z=x["z"][:, t].contiguous(), delta_bias=x["delta_bias"]))
+    torch.cuda.synchronize()
+    yd = torch.stack(outs, dim=1)
+    yr = y[:, t0:]
+    assert ((yd - yr).abs() / (1 + yr.abs())).max().item() <= 1e-4
+    assert ((state - st).abs() / (1 + st.abs())).max().item() <= 1e-4
