@@ -50,10 +50,10 @@ def _bind(path):
     lib = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.ss_oracle_fwd.restype = i32
-    lib.ss_oracle_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+    lib.ss_oracle_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
                                   i64, i64, i64, i64, i32, vp, vp, i64, i32]
     lib.ss_oracle_step.restype = i32
-    lib.ss_oracle_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+    lib.ss_oracle_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp,
                                    i64, i64, i64, i32, i32]
     lib.ss_oracle_max_threads.restype = i32
     lib.ss_oracle_max_threads.argtypes = []
@@ -96,9 +96,10 @@ def _c(a, dtype=None):
 
 
 def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=None,
-        channels=None, nthreads=0, want_y=True, _lib=None):
+        channels=None, nthreads=0, want_y=True, zoh=False, _lib=None):
     """Forward scan. Shapes: u, delta, z (batch, L, dim); B, C (batch, L, N); A (dim, N);
     D, delta_bias (dim,); h0 (batch, dim, N) float64 or None.
+    zoh: input term (exp(dt A) - 1)/A * B instead of dt * B.
 
     channels: None for every channel, else an int array of shape (k, 2) of (b, d) pairs;
     then y is (k, L) and last_state is (k, N).
@@ -130,7 +131,8 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=No
         if nchan == 0:
             return y, st
     rc = (_lib or _load()).ss_oracle_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                               _ptr(delta_bias), int(bool(softplus)), _ptr(h0), _ptr(y), _ptr(st),
+                               _ptr(delta_bias), int(bool(softplus)), int(bool(zoh)), _ptr(h0),
+                               _ptr(y), _ptr(st),
                                batch, L, dim, N, dt, _ptr(cb), _ptr(cd), nchan, int(nthreads))
     if rc != 0:
         raise ValueError("ss_oracle_fwd rejected its arguments")
@@ -138,7 +140,7 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, h0=No
 
 
 def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, nthreads=0,
-         _lib=None):
+         zoh=False, _lib=None):
     """One decode step, state (batch, dim, N) float64 updated in place. u, delta, z are
     (batch, dim); B, C are (batch, N). Returns y (batch, dim) float64."""
     if state.dtype != np.float64 or not state.flags.c_contiguous:
@@ -152,7 +154,8 @@ def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tru
         raise ValueError("bad state, B or C shape")
     y = np.empty((batch, dim), np.float64)
     rc = (_lib or _load()).ss_oracle_step(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                                _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(y),
+                                _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
+                                int(bool(zoh)), _ptr(y),
                                 batch, dim, N, dt, int(nthreads))
     if rc != 0:
         raise ValueError("ss_oracle_step rejected its arguments")

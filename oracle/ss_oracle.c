@@ -11,7 +11,10 @@
  *   dt     = softplus(x) if softplus_flag else x
  *   for each state n:
  *     abar = exp(dt * A[d,n])                               (zero-order-hold decay)
- *     h[n] = abar * h[n] + (dt * B[b,t,n]) * u[b,t,d]
+ *     bbar = dt                       by default (first-order input term), or
+ *          = (exp(dt A[d,n]) - 1) / A[d,n]  with zoh set (exact zero-order hold; the
+ *            A -> 0 limit of that quotient is dt)
+ *     h[n] = abar * h[n] + (bbar * B[b,t,n]) * u[b,t,d]
  *   y[b,t,d] = (sum_n C[b,t,n] * h[n] + D[d] * u[b,t,d]) * silu(z[b,t,d])
  *   last_state[b,d,n] = h[n] after the last step
  *
@@ -28,13 +31,14 @@
  *  - "架构变体：Mamba/SSM" (aiqz.cc), section "离散化": zero-order hold with step Delta;
  *    section "Python 演示": state starts at zero.
  * Readings where the pages are silent or disagree (all in the design notes):
- *  - discretised input term is dt * B (not the exact ZOH (exp(dt A) - 1)/A * B);
+ *  - the default discretised input term is dt * B; the exact zero-order-hold term
+ *    (exp(dt A) - 1)/A * B of "架构变体：Mamba/SSM" section "离散化" is the zoh option;
  *  - y reads the post-update state; the D term is included; the SiLU gate multiplies
  *    the whole output including the D term; the bias is added before softplus;
  *  - A is a diagonal (dim, dstate) array; B and C carry no channel index.
  *
  * Arithmetic: every input is converted exactly to double (bf16 -> fp32 -> fp64 is
- * exact), all arithmetic is IEEE double with libm exp/log1p, compiled without fast
+ * exact), all arithmetic is IEEE double with libm exp/expm1/log1p, compiled without fast
  * math. Work is split over (b, d) channels with OpenMP; each channel runs the plain
  * sequential loop above, so the result does not depend on the thread count.
  */
@@ -75,8 +79,9 @@ static double silu(double z) {
    y_out[t * y_stride] receives y[b,t,d]. */
 static void scan_channel(const void* u, const void* delta, const float* A, const void* B,
                          const void* C, const float* D, const void* z, const float* bias,
-                         int softplus_flag, int64_t b, int64_t d, int64_t seqlen, int64_t dim,
-                         int64_t dstate, int dtype, double* h, double* y_out, int64_t y_stride) {
+                         int softplus_flag, int zoh, int64_t b, int64_t d, int64_t seqlen,
+                         int64_t dim, int64_t dstate, int dtype, double* h, double* y_out,
+                         int64_t y_stride) {
   const double bias_d = bias ? (double)bias[d] : 0.0;
   const double D_d = D ? (double)D[d] : 0.0;
   for (int64_t t = 0; t < seqlen; ++t) {
@@ -87,8 +92,10 @@ static void scan_channel(const void* u, const void* delta, const float* A, const
     const double uv = in_at(u, dtype, e);
     double acc = 0.0;
     for (int64_t n = 0; n < dstate; ++n) {
-      const double abar = exp(dt * (double)A[d * dstate + n]);
-      h[n] = abar * h[n] + (dt * in_at(B, dtype, bc + n)) * uv;
+      const double a_dn = (double)A[d * dstate + n];
+      const double abar = exp(dt * a_dn);
+      const double bbar = !zoh ? dt : (a_dn != 0.0 ? expm1(dt * a_dn) / a_dn : dt);
+      h[n] = abar * h[n] + (bbar * in_at(B, dtype, bc + n)) * uv;
       acc += in_at(C, dtype, bc + n) * h[n];
     }
     double yv = acc + D_d * uv;
@@ -99,6 +106,7 @@ static void scan_channel(const void* u, const void* delta, const float* A, const
 
 /*
  * Full forward over every (b, d), or over a listed subset of channels.
+ *   zoh         0: input term dt * B; 1: exact zero-order hold (exp(dt A) - 1)/A * B.
  *   h0          optional (batch, dim, dstate) initial state; NULL means zeros.
  *   nchan == 0  all channels: y is (batch, seqlen, dim), last_state is (batch, dim, dstate).
  *   nchan  > 0  only the channels (chan_b[i], chan_d[i]): y is (nchan, seqlen) and
@@ -107,8 +115,8 @@ static void scan_channel(const void* u, const void* delta, const float* A, const
  */
 int ss_oracle_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                   const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                  const double* h0, double* y, double* last_state, int64_t batch, int64_t seqlen,
-                  int64_t dim, int64_t dstate, int dtype, const int64_t* chan_b,
+                  int zoh, const double* h0, double* y, double* last_state, int64_t batch,
+                  int64_t seqlen, int64_t dim, int64_t dstate, int dtype, const int64_t* chan_b,
                   const int64_t* chan_d, int64_t nchan, int nthreads) {
   if (!u || !delta || !A || !B || !C) return -1;
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || nchan < 0) return -1;
@@ -136,8 +144,8 @@ int ss_oracle_fwd(const void* u, const void* delta, const float* A, const void* 
       if (nchan > 0) { yo = y + j * seqlen; ys = 1; }
       else { yo = y + b * seqlen * dim + d; ys = dim; }
     }
-    scan_channel(u, delta, A, B, C, D, z, delta_bias, softplus_flag, b, d, seqlen, dim, dstate,
-                 dtype, h, yo, ys);
+    scan_channel(u, delta, A, B, C, D, z, delta_bias, softplus_flag, zoh, b, d, seqlen, dim,
+                 dstate, dtype, h, yo, ys);
     if (last_state) {
       double* dst = nchan > 0 ? last_state + j * dstate : last_state + (b * dim + d) * dstate;
       for (int64_t n = 0; n < dstate; ++n) dst[n] = h[n];
@@ -154,8 +162,8 @@ int ss_oracle_fwd(const void* u, const void* delta, const float* A, const void* 
  */
 int ss_oracle_step(double* state, const void* u, const void* delta, const float* A, const void* B,
                    const void* C, const float* D, const void* z, const float* delta_bias,
-                   int softplus_flag, double* y, int64_t batch, int64_t dim, int64_t dstate,
-                   int dtype, int nthreads) {
+                   int softplus_flag, int zoh, double* y, int64_t batch, int64_t dim,
+                   int64_t dstate, int dtype, int nthreads) {
   if (!state || !u || !delta || !A || !B || !C) return -1;
   if (batch < 0 || dim < 0 || dstate < 1) return -1;
   if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
@@ -169,8 +177,8 @@ int ss_oracle_step(double* state, const void* u, const void* delta, const float*
     const int64_t b = j / dim, d = j % dim;
     /* a step is a length-1 sequence: (batch, 1, dim) and (batch, 1, dstate) index the
        same memory as (batch, dim) and (batch, dstate) */
-    scan_channel(u, delta, A, B, C, D, z, delta_bias, softplus_flag, b, d, 1, dim, dstate, dtype,
-                 state + j * dstate, y ? y + j : NULL, 1);
+    scan_channel(u, delta, A, B, C, D, z, delta_bias, softplus_flag, zoh, b, d, 1, dim, dstate,
+                 dtype, state + j * dstate, y ? y + j : NULL, 1);
   }
   return 0;
 }

@@ -19,15 +19,20 @@ MUTANTS = [
                              ("const double dt = softplus_flag ? softplus(x) : x;",
                               "const double dt = (softplus_flag ? softplus(x) : x) + bias_d;")]),
     ("no_softplus", [("const double dt = softplus_flag ? softplus(x) : x;", "const double dt = x;")]),
-    ("y_reads_old_state", [("      h[n] = abar * h[n] + (dt * in_at(B, dtype, bc + n)) * uv;\n"
+    ("y_reads_old_state", [("      h[n] = abar * h[n] + (bbar * in_at(B, dtype, bc + n)) * uv;\n"
                             "      acc += in_at(C, dtype, bc + n) * h[n];",
                             "      acc += in_at(C, dtype, bc + n) * h[n];\n"
-                            "      h[n] = abar * h[n] + (dt * in_at(B, dtype, bc + n)) * uv;")]),
+                            "      h[n] = abar * h[n] + (bbar * in_at(B, dtype, bc + n)) * uv;")]),
     ("A_transposed", [("(double)A[d * dstate + n]", "(double)A[n * dim + d]")]),
-    ("B_C_swapped", [("(dt * in_at(B, dtype, bc + n))", "(dt * in_at(C, dtype, bc + n))"),
+    ("B_C_swapped", [("(bbar * in_at(B, dtype, bc + n))", "(bbar * in_at(C, dtype, bc + n))"),
                      ("acc += in_at(C, dtype, bc + n) * h[n];", "acc += in_at(B, dtype, bc + n) * h[n];")]),
-    ("decay_sign", [("exp(dt * (double)A[d * dstate + n])", "exp(-dt * (double)A[d * dstate + n])")]),
-    ("input_term_without_dt", [("(dt * in_at(B, dtype, bc + n)) * uv", "in_at(B, dtype, bc + n) * uv")]),
+    ("decay_sign", [("const double abar = exp(dt * a_dn);", "const double abar = exp(-dt * a_dn);")]),
+    ("input_term_without_dt", [("const double bbar = !zoh ? dt :", "const double bbar = !zoh ? 1.0 :")]),
+    ("zoh_not_divided_by_A", [("expm1(dt * a_dn) / a_dn : dt", "expm1(dt * a_dn) : dt")]),
+    ("zoh_zero_A_limit", [("expm1(dt * a_dn) / a_dn : dt", "expm1(dt * a_dn) / a_dn : 0.0")]),
+    ("zoh_ignored", [("const double bbar = !zoh ? dt :", "const double bbar = 1 ? dt :")]),
+    ("zoh_sign", [("expm1(dt * a_dn) / a_dn : dt", "-expm1(dt * a_dn) / a_dn : dt")]),
+    ("zoh_divides_by_dt_A", [("expm1(dt * a_dn) / a_dn : dt", "expm1(dt * a_dn) / (dt * a_dn) : dt")]),
     ("gate_skips_D_term", [("    double yv = acc + D_d * uv;\n    if (z) yv *= silu(in_at(z, dtype, e));",
                             "    double yv = acc;\n    if (z) yv *= silu(in_at(z, dtype, e));\n    yv += D_d * uv;")]),
     ("gate_is_sigmoid", [("if (z >= 0.0) return z / (1.0 + exp(-z));", "if (z >= 0.0) return 1.0 / (1.0 + exp(-z));"),
@@ -53,6 +58,10 @@ def pin_suite(lib):
         ("huge_step", lambda: pins.test_huge_step_resets_state(lib)),
         ("page5", lambda: pins.test_page5_worked_example(lib)),
         ("step", lambda: pins.test_step_by_step_matches_forward(lib)),
+        ("zoh_continuous", lambda: pins.test_zoh_matches_continuous_solution(lib)),
+        ("zoh_half_steps", lambda: pins.test_zoh_half_steps_compose(lib)),
+        ("zoh_brute", lambda: pins.test_zoh_brute_force_unrolled_sum(lib, True)),
+        ("zoh_step", lambda: pins.test_zoh_step_by_step_matches_forward(lib)),
     ]
     for name, fn in checks:
         try:

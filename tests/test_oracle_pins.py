@@ -7,7 +7,10 @@
 - constant inputs follow the geometric series;
 - tiny cases equal the fully unrolled double sum;
 - the page-5 demo values (exact decimals, tests/golden);
-- splitting the sequence, stepping token by token, causality and linearity in u.
+- splitting the sequence, stepping token by token, causality and linearity in u;
+- the exact zero-order-hold option: the exact solution of h' = A h + B u for inputs held
+  constant over each step (page "架构变体：Mamba/SSM", section "离散化"), so it matches
+  the continuous-time solution for any step sizes and two half steps equal one step.
 Reference numbers here come from numpy/scipy formulas written independently of the
 oracle's loop (convolution, closed forms, explicit sums), never from the oracle itself.
 """
@@ -63,9 +66,18 @@ def step_sizes(c, softplus=True):
     return softplus_ref(x) if softplus else x
 
 
-def brute_force(c, softplus=True):
+def zoh_coef(dt, A):
+    """(exp(dt A) - 1) / A, with its A -> 0 limit dt (numpy expm1; broadcasts)."""
+    A = np.asarray(A, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.expm1(dt * A) / A
+    return np.where(A == 0.0, dt, q)
+
+
+def brute_force(c, softplus=True, zoh=False):
     """Unrolled closed form: y_t = sum_{s<=t} sum_n C_t[n] exp(A[d,n] sum_{r=s+1..t} dt_r)
-    dt_s B_s[n] u_s + D u_t, times silu(z_t); also the final state."""
+    bbar_s[n] B_s[n] u_s + D u_t, times silu(z_t); also the final state. bbar_s = dt_s, or
+    the exact zero-order-hold (exp(dt_s A) - 1)/A with zoh."""
     u, B, C, A = f64(c["u"]), f64(c["B"]), f64(c["C"]), f64(c["A"])
     dt = step_sizes(c, softplus)
     batch, L, dim = u.shape
@@ -79,7 +91,8 @@ def brute_force(c, softplus=True):
                 tot = 0.0
                 for s in range(t + 1):
                     decay = np.exp(A[d] * (cum[t + 1] - cum[s + 1]))  # sum_{r=s+1..t} dt_r
-                    tot += np.sum(C[b, t] * decay * dt[b, s, d] * B[b, s] * u[b, s, d])
+                    coef = zoh_coef(dt[b, s, d], A[d]) if zoh else dt[b, s, d]
+                    tot += np.sum(C[b, t] * decay * coef * B[b, s] * u[b, s, d])
                 if c["D"] is not None:
                     tot += f64(c["D"])[d] * u[b, t, d]
                 if c["z"] is not None:
@@ -87,7 +100,8 @@ def brute_force(c, softplus=True):
                 y[b, t, d] = tot
             for s in range(L):
                 decay = np.exp(A[d] * (cum[L] - cum[s + 1]))
-                last[b, d] += decay * dt[b, s, d] * B[b, s] * u[b, s, d]
+                coef = zoh_coef(dt[b, s, d], A[d]) if zoh else dt[b, s, d]
+                last[b, d] += decay * coef * B[b, s] * u[b, s, d]
     return y, last
 
 
@@ -333,3 +347,76 @@ def test_rejects_bad_arguments(oracle_lib):
         oracle_lib.fwd(**dict(c, A=c["A"][:, :3]))
     with pytest.raises(ValueError):
         oracle_lib.fwd(**c, channels=np.array([[5, 0]]))
+
+
+# ---- exact zero-order hold (zoh=True) ----------------------------------------------------
+# Page "架构变体：Mamba/SSM", section "离散化": the continuous system h' = A h + B u is
+# discretised by holding the input constant over each step of length dt. The resulting
+# update is the exact solution of the ODE for piecewise-constant input, which gives pins
+# that hold for any sequence of step sizes.
+
+
+def test_zoh_matches_continuous_solution(oracle_lib):
+    """Constant u and B, arbitrary positive steps: after steps dt_1..dt_t the state is the
+    ODE solution e^{A S} h0 + (e^{A S} - 1)/A B u at S = dt_1 + .. + dt_t, however S was cut
+    into steps (A = 0 integrates: h0 + S B u; a positive A grows)."""
+    rng = np.random.default_rng(21)
+    batch, L, dim, N = 2, 60, 3, 5
+    f = np.float32
+    u = np.repeat(rng.standard_normal((batch, 1, dim)), L, axis=1).astype(f)
+    B = np.repeat(rng.standard_normal((batch, 1, N)), L, axis=1).astype(f)
+    C = rng.standard_normal((batch, L, N)).astype(f)
+    delta = rng.uniform(0.001, 0.4, (batch, L, dim)).astype(f)  # the steps (softplus off)
+    A = (-rng.uniform(0.2, 3.0, (dim, N))).astype(f)
+    A[1, 2] = 0.0
+    A[2, 4] = 0.05
+    h0 = rng.standard_normal((batch, dim, N))
+    y, last = oracle_lib.fwd(u, delta, A, B, C, softplus=False, h0=h0, zoh=True)
+    S = np.cumsum(f64(delta), axis=1)
+    Af = f64(A)
+    for b in range(batch):
+        for d in range(dim):
+            St = S[b, :, d][:, None]
+            h = np.exp(Af[d] * St) * h0[b, d] + zoh_coef(St, Af[d]) * f64(B[b, 0]) * f64(u[b, 0, d])
+            assert_close(y[b, :, d], np.sum(f64(C[b]) * h, axis=1), 1e-12, f"zoh y b={b} d={d}")
+            assert_close(last[b, d], h[-1], 1e-12, f"zoh state b={b} d={d}")
+
+
+def test_zoh_half_steps_compose(oracle_lib):
+    """Holding an input for dt equals holding it for dt/2 twice: repeating every token with
+    half the step gives the same states, and every second output equals the original's
+    (time-varying u, B, C; halving a float is exact)."""
+    rng = np.random.default_rng(22)
+    c = rand_case(rng, L=30, bias=False, gated=False, with_D=False)
+    c["delta"] = rng.uniform(0.01, 0.6, c["delta"].shape).astype(np.float32)
+    y, last = oracle_lib.fwd(**c, softplus=False, zoh=True)
+    c2 = dict(c)
+    for k in ("u", "B", "C"):
+        c2[k] = np.repeat(c[k], 2, axis=1)
+    c2["delta"] = np.repeat(c["delta"] * np.float32(0.5), 2, axis=1)
+    y2, last2 = oracle_lib.fwd(**c2, softplus=False, zoh=True)
+    assert_close(y2[:, 1::2], y, 1e-12, "half-step outputs")
+    assert_close(last2, last, 1e-12, "half-step state")
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_zoh_brute_force_unrolled_sum(oracle_lib, gated):
+    rng = np.random.default_rng(23)
+    c = rand_case(rng, gated=gated)
+    c["A"][0, 1] = 0.0  # the A -> 0 limit of the input term
+    y, last = oracle_lib.fwd(**c, softplus=True, zoh=True)
+    y_ref, last_ref = brute_force(c, softplus=True, zoh=True)
+    assert_close(y, y_ref, 1e-12, "y")
+    assert_close(last, last_ref, 1e-12, "last_state")
+
+
+def test_zoh_step_by_step_matches_forward(oracle_lib):
+    rng = np.random.default_rng(24)
+    c = rand_case(rng, L=20)
+    y, last = oracle_lib.fwd(**c, zoh=True)
+    st = np.zeros((2, 3, 5))
+    for t in range(20):
+        yt = oracle_lib.step(st, c["u"][:, t], c["delta"][:, t], c["A"], c["B"][:, t], c["C"][:, t],
+                             D=c["D"], z=c["z"][:, t], delta_bias=c["delta_bias"], zoh=True)
+        assert np.array_equal(yt, y[:, t])
+    assert np.array_equal(st, last)
