@@ -5,7 +5,8 @@
  *
  *   dt        = softplus(delta[b,t,d] + delta_bias[d])   (or without softplus)
  *   abar      = exp(dt * A[d,n])
- *   h[n]      = abar * h[n] + (dt * B[b,t,n]) * u[b,t,d]
+ *   h[n]      = abar * h[n] + (dt * B[b,t,n]) * u[b,t,d]      (ss_discretization: or
+ *               the exact zero-order-hold coefficient in place of dt)
  *   y[b,t,d]  = (sum_n C[b,t,n] * h[n] + D[d] * u[b,t,d]) * silu(z[b,t,d])
  *
  * Sources: "Mamba：选择性状态空间的线性时间序列建模" (wiki note on arXiv 2312.00752),
@@ -39,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 1
+#define SS_ABI_VERSION 2
 #define SS_MAX_DSTATE 16
 
 typedef enum {
@@ -57,6 +58,15 @@ typedef enum {
   SS_DTYPE_F32 = 0,  /* IEEE binary32 */
   SS_DTYPE_BF16 = 1  /* bfloat16: the upper 16 bits of a binary32 */
 } ss_dtype;
+
+/* Discretised input term bbar in h = abar h + (bbar B) u. ss_fwd and ss_step use the
+ * first; the _ex entry points take either. Both hold the decay abar = exp(dt A). */
+typedef enum {
+  SS_DISC_DT = 0, /* bbar = dt (the simplified input term) */
+  SS_DISC_ZOH = 1 /* bbar = (exp(dt A) - 1) / A, the exact zero-order hold of the
+                     continuous input ("架构变体：Mamba/SSM", section "离散化"); its
+                     A -> 0 limit dt is used where A == 0 */
+} ss_discretization;
 
 /* SS_ABI_VERSION of the built library. */
 int ss_abi_version(void);
@@ -86,22 +96,25 @@ int ss_fwd(const void* u, const void* delta, const float* A, const void* B, cons
            float* last_state, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
            int in_dtype, void* stream);
 
-/* Kernel selection for ss_fwd_ex (tuning and testing; ss_fwd picks automatically). */
+/* Options of ss_fwd_ex. A zero-initialised struct (or a NULL pointer) means ss_fwd's
+ * behaviour. kernel and chunk_len are for tuning and testing. */
 typedef struct {
-  int kernel;    /* 0: automatic; 1: one lane per channel, sequential in t (any dstate);
-                    2: time-chunked (dstate == 16 only, else SS_ERR_UNSUPPORTED_N) */
-  int chunk_len; /* tokens per lane and tile for kernel 2: 0 (automatic), 4 or 8 */
+  int kernel;         /* 0: automatic; 1: one lane per channel, sequential in t (any dstate);
+                         2: time-chunked (dstate == 16 only, else SS_ERR_UNSUPPORTED_N) */
+  int chunk_len;      /* tokens per lane and tile for kernel 2: 0 (automatic), 4 or 8 */
+  int discretization; /* an ss_discretization value */
 } ss_fwd_options;
 
 /*
- * ss_fwd_ex -- ss_fwd from a given initial state and with an explicit kernel choice.
+ * ss_fwd_ex -- ss_fwd from a given initial state, with a choice of input term and kernel.
  * Same arguments, layouts, ownership and errors as ss_fwd, plus:
  *   h0   (batch, dim, dstate) fp32 initial state, may be NULL (zero state, as ss_fwd).
  *        With h0 = the last_state of a call over tokens [0, t0), a call over [t0, L)
  *        continues that scan (chunked prefill; the update is associative, "架构变体：
  *        Mamba/SSM" section "硬件感知算法"); with seqlen == 0, last_state = h0.
- *   opt  kernel choice, may be NULL (automatic). Every choice computes the same result up
- *        to fp32 rounding order. An out-of-range option returns SS_ERR_BAD_SHAPE.
+ *   opt  options, may be NULL (automatic kernel, bbar = dt). Every kernel choice computes
+ *        the same result up to fp32 rounding order. An out-of-range option returns
+ *        SS_ERR_BAD_SHAPE.
  */
 int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
               const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
@@ -125,6 +138,16 @@ int ss_step(float* state, const void* u, const void* delta, const float* A, cons
             const void* C, const float* D, const void* z, const float* delta_bias,
             int softplus_flag, float* y, int64_t batch, int64_t dim, int64_t dstate, int in_dtype,
             void* stream);
+
+/*
+ * ss_step_ex -- ss_step with a choice of input term: discretization is an
+ * ss_discretization value (anything else returns SS_ERR_BAD_SHAPE). A decode stream must
+ * use the discretization of the ss_fwd_ex prefill whose last_state it continues.
+ */
+int ss_step_ex(float* state, const void* u, const void* delta, const float* A, const void* B,
+               const void* C, const float* D, const void* z, const float* delta_bias,
+               int softplus_flag, float* y, int64_t batch, int64_t dim, int64_t dstate,
+               int in_dtype, int discretization, void* stream);
 
 #ifdef __cplusplus
 }

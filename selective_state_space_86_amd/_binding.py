@@ -11,12 +11,16 @@ _LIB_PATH = os.path.join(_HERE, "libss.so")
 _lib = None
 
 F32, BF16 = 0, 1
-EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_step")
+DISC_DT, DISC_ZOH = 0, 1
+ABI_VERSION = 2
+EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_step", "ss_step_ex")
 
 
 class FwdOptions(ctypes.Structure):
-    """ss_fwd_options: kernel 0 automatic / 1 sequential / 2 time-chunked; chunk_len 0, 4, 8."""
-    _fields_ = [("kernel", ctypes.c_int), ("chunk_len", ctypes.c_int)]
+    """ss_fwd_options: kernel 0 automatic / 1 sequential / 2 time-chunked; chunk_len 0, 4, 8;
+    discretization 0 (input term dt*B) / 1 (exact zero-order hold)."""
+    _fields_ = [("kernel", ctypes.c_int), ("chunk_len", ctypes.c_int),
+                ("discretization", ctypes.c_int)]
 
 
 class SSError(RuntimeError):
@@ -49,6 +53,11 @@ def load_library():
                               ctypes.POINTER(FwdOptions), vp]
     lib.ss_step.restype = i32
     lib.ss_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, vp]
+    lib.ss_step_ex.restype = i32
+    lib.ss_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, i32, vp]
+    if lib.ss_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{_LIB_PATH} has ABI version {lib.ss_abi_version()}, this binding "
+                           f"needs {ABI_VERSION}: rebuild it")
     _lib = lib
     return lib
 
@@ -89,11 +98,13 @@ def _stream(device, stream):
 
 
 def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=None,
-        last_state=None, return_last_state=True, stream=None, kernel=0, chunk_len=0, h0=None):
-    """Selective-scan forward (``ss_fwd``; ``ss_fwd_ex`` when h0, kernel or chunk_len are
-    given). u, delta, z: (batch, L, dim); B, C: (batch, L, N); A: (dim, N) fp32; D,
-    delta_bias: (dim,) fp32; h0: (batch, dim, N) fp32 initial state or None. Returns y
-    (fp32) and, unless return_last_state is False, the final state (batch, dim, N) fp32."""
+        last_state=None, return_last_state=True, stream=None, kernel=0, chunk_len=0, h0=None,
+        zoh=False):
+    """Selective-scan forward (``ss_fwd``; ``ss_fwd_ex`` when h0, kernel, chunk_len or zoh
+    are given). u, delta, z: (batch, L, dim); B, C: (batch, L, N); A: (dim, N) fp32; D,
+    delta_bias: (dim,) fp32; h0: (batch, dim, N) fp32 initial state or None; zoh: exact
+    zero-order-hold input term. Returns y (fp32) and, unless return_last_state is False,
+    the final state (batch, dim, N) fp32."""
     dev = u.device
     batch, L, dim = u.shape
     N = A.shape[1]
@@ -117,8 +128,8 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=Non
     head = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
             int(bool(softplus)), _ptr(y), _ptr(last_state))
     tail = (batch, L, dim, N, dt)
-    if kernel or chunk_len or h0 is not None:
-        opt = FwdOptions(int(kernel), int(chunk_len))
+    if kernel or chunk_len or h0 is not None or zoh:
+        opt = FwdOptions(int(kernel), int(chunk_len), DISC_ZOH if zoh else DISC_DT)
         rc = lib.ss_fwd_ex(*head, _ptr(h0), *tail, ctypes.byref(opt), _stream(dev, stream))
     else:
         rc = lib.ss_fwd(*head, *tail, _stream(dev, stream))
@@ -128,9 +139,9 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=Non
 
 
 def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=None,
-         stream=None):
-    """One decode step (``ss_step``); state (batch, dim, N) fp32 is updated in place.
-    u, delta, z: (batch, dim); B, C: (batch, N). Returns y (batch, dim) fp32."""
+         stream=None, zoh=False):
+    """One decode step (``ss_step``; ``ss_step_ex`` with zoh); state (batch, dim, N) fp32 is
+    updated in place. u, delta, z: (batch, dim); B, C: (batch, N). Returns y (batch, dim)."""
     dev = state.device
     batch, dim, N = state.shape
     dt = _in_dtype(u, delta, B, C, z)
@@ -146,9 +157,13 @@ def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tru
     if y is None:
         y = torch.empty((batch, dim), dtype=torch.float32, device=dev)
     _check(y, "y", dev, torch.float32, (batch, dim))
-    rc = load_library().ss_step(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                                _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(y),
-                                batch, dim, N, dt, _stream(dev, stream))
+    args = (_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), int(bool(softplus)), _ptr(y), batch, dim, N, dt)
+    lib = load_library()
+    if zoh:
+        rc = lib.ss_step_ex(*args, DISC_ZOH, _stream(dev, stream))
+    else:
+        rc = lib.ss_step(*args, _stream(dev, stream))
     if rc != 0:
         raise SSError(rc, "ss_step")
     return y

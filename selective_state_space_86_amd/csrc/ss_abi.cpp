@@ -85,7 +85,9 @@ int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, c
   if (batch * ((dim + 15) / 16) > 0x7fffffffLL) return SS_ERR_BAD_SHAPE;
   const int kernel = opt ? opt->kernel : 0;
   const int chunk = opt ? opt->chunk_len : 0;
+  const int disc = opt ? opt->discretization : SS_DISC_DT;
   if (kernel < 0 || kernel > 2 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
+  if (disc != SS_DISC_DT && disc != SS_DISC_ZOH) return SS_ERR_BAD_SHAPE;
   if (kernel == 2 && dstate != 16) return SS_ERR_UNSUPPORTED_N;
   const size_t es = elem_size(in_dtype);
   if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
@@ -98,7 +100,8 @@ int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, c
   if (dv != SS_OK) return dv;
 
   ss::FwdArgs a{u, delta, A, B, C, D, z, delta_bias, y, last_state,
-                batch, seqlen, dim, dstate, in_dtype, softplus_flag ? 1 : 0, h0};
+                batch, seqlen, dim, dstate, in_dtype, softplus_flag ? 1 : 0, h0,
+                disc == SS_DISC_ZOH ? 1 : 0};
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   const bool chunked = kernel == 2 || (kernel == 0 && ss::fwd_chunked_supported(a));
@@ -117,13 +120,14 @@ int ss_fwd(const void* u, const void* delta, const float* A, const void* B, cons
                    seqlen, dim, dstate, in_dtype, nullptr, stream);
 }
 
-int ss_step(float* state, const void* u, const void* delta, const float* A, const void* B,
-            const void* C, const float* D, const void* z, const float* delta_bias,
-            int softplus_flag, float* y, int64_t batch, int64_t dim, int64_t dstate, int in_dtype,
-            void* stream) {
+int ss_step_ex(float* state, const void* u, const void* delta, const float* A, const void* B,
+               const void* C, const float* D, const void* z, const float* delta_bias,
+               int softplus_flag, float* y, int64_t batch, int64_t dim, int64_t dstate,
+               int in_dtype, int discretization, void* stream) {
   if (!state || !u || !delta || !A || !B || !C || !y) return SS_ERR_NULL_ARG;
   if (in_dtype != SS_DTYPE_F32 && in_dtype != SS_DTYPE_BF16) return SS_ERR_BAD_DTYPE;
   if (batch < 1 || dim < 1 || dstate < 1) return SS_ERR_BAD_SHAPE;
+  if (discretization != SS_DISC_DT && discretization != SS_DISC_ZOH) return SS_ERR_BAD_SHAPE;
   if (dstate > SS_MAX_DSTATE) return SS_ERR_UNSUPPORTED_N;
   if (!product_ok(batch, dim, dstate)) return SS_ERR_BAD_SHAPE;
   if ((batch * dim + 255) / 256 > 0x7fffffffLL) return SS_ERR_BAD_SHAPE;
@@ -137,9 +141,18 @@ int ss_step(float* state, const void* u, const void* delta, const float* A, cons
   if (dv != SS_OK) return dv;
 
   ss::StepArgs a{state, u, delta, A, B, C, D, z, delta_bias, y,
-                 batch, dim, dstate, in_dtype, softplus_flag ? 1 : 0};
+                 batch, dim, dstate, in_dtype, softplus_flag ? 1 : 0,
+                 discretization == SS_DISC_ZOH ? 1 : 0};
   const hipError_t e = ss::step(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+int ss_step(float* state, const void* u, const void* delta, const float* A, const void* B,
+            const void* C, const float* D, const void* z, const float* delta_bias,
+            int softplus_flag, float* y, int64_t batch, int64_t dim, int64_t dstate, int in_dtype,
+            void* stream) {
+  return ss_step_ex(state, u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, batch, dim, dstate,
+                    in_dtype, SS_DISC_DT, stream);
 }
 
 }  // extern "C"

@@ -1,8 +1,8 @@
-// ss_chunk_ops.h -- building blocks of the time-chunked selective-scan kernels (gfx950):
+// ss_chunk_ops.h -- building blocks of the time-chunked selective-scan kernel (gfx950):
 // the hand-scheduled per-token update and fix-up for 16 states, buffer-resource loads,
-// and the per-lane tile loader. Included by ss_fwd_chunked.hip and ss_fwd_ring.hip.
+// and the per-lane tile loader.
 //
-// Lane layout shared by both kernels: a row of 16 lanes holds 16 consecutive channels at
+// Lane layout: a row of 16 lanes holds 16 consecutive channels at
 // one token, so B_t and C_t are row-uniform and lane n of the row holds B_t[n], C_t[n];
 // the update reads them through DPP row_newbcast:n folded into the consuming v_mul/v_fmac.
 #pragma once
@@ -52,6 +52,48 @@ __device__ __forceinline__ void local_step(float (&h)[16], float (&e)[16], const
       "v_fmac_f32_dpp %[y], %[vc], %[h15]" SS_DPP_ROW(15)
       : SS_OPS16(h, "+v"), SS_OPS16(e, "=&v"), [y] "+v"(y), [x] "=&v"(x), [bu] "=&v"(bu)
       : SS_OPS16(a, "v"), [dt] "v"(dt), [du] "v"(du), [vb] "v"(vb), [vc] "v"(vc));
+}
+
+// State update of one token from precomputed input terms bbu[n] = bbar[n] * u:
+// h[n] = abar[n] h[n] + bbu[n] B_t[n]; y += C_t[n] h[n] (B_t, C_t by row_newbcast:n).
+// Pipelined like local_step: each h is read by its DPP fmac >= 2 instructions after the
+// fma that wrote it.
+#define SS_UPDB(n, n1)                                                        \
+  "v_mul_f32_dpp %[t], %[vb], %[bb" #n1 "]" SS_DPP_ROW(n1)                    \
+  "v_fma_f32 %[h" #n1 "], %[e" #n1 "], %[h" #n1 "], %[t]\n"                  \
+  "v_fmac_f32_dpp %[y], %[vc], %[h" #n "]" SS_DPP_ROW(n)
+
+__device__ __forceinline__ void update_from_terms(float (&h)[16], const float (&e)[16],
+                                                  const float (&bb)[16], float vb, float vc, float& y) {
+  float t;
+  asm volatile(
+      "s_nop 1\n"
+      "v_mul_f32_dpp %[t], %[vb], %[bb0]" SS_DPP_ROW(0)
+      "v_fma_f32 %[h0], %[e0], %[h0], %[t]\n"
+      SS_UPDB(0, 1) SS_UPDB(1, 2) SS_UPDB(2, 3) SS_UPDB(3, 4) SS_UPDB(4, 5) SS_UPDB(5, 6)
+      SS_UPDB(6, 7) SS_UPDB(7, 8) SS_UPDB(8, 9) SS_UPDB(9, 10) SS_UPDB(10, 11) SS_UPDB(11, 12)
+      SS_UPDB(12, 13) SS_UPDB(13, 14) SS_UPDB(14, 15)
+      "s_nop 1\n"
+      "v_fmac_f32_dpp %[y], %[vc], %[h15]" SS_DPP_ROW(15)
+      : SS_OPS16(h, "+v"), [y] "+v"(y), [t] "=&v"(t)
+      : SS_OPS16(e, "v"), SS_OPS16(bb, "v"), [vb] "v"(vb), [vc] "v"(vc));
+}
+
+// One token of the local pass with the exact zero-order-hold input term bbar = (abar - 1)/A
+// (zoh_coef): the decays and input terms of the 16 states first (compiler-scheduled), then
+// the pipelined update. Computing them in two phases keeps the live temporaries to one
+// array of 16; interleaving everything per state made the compiler spill.
+__device__ __forceinline__ void local_step_zoh(float (&h)[16], float (&e)[16], const float (&a)[16],
+                                               const float (&ia)[16], float dt, float uu, float vb,
+                                               float vc, float& y) {
+  float bb[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    const float x2 = dt * a[n];
+    e[n] = fast_exp2(x2);
+    bb[n] = zoh_coef(dt, x2 * kLn2, e[n], ia[n]) * uu;
+  }
+  update_from_terms(h, e, bb, vb, vc, y);
 }
 
 #define SS_FIX_M(n) "v_mul_f32 %[q" #n "], %[q" #n "], %[e" #n "]\n"

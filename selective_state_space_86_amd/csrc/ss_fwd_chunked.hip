@@ -25,6 +25,8 @@
 //  * Fix-up: y_t += sum_n C_t[n] (prod_{s<=t} abar_s[n]) carry[n], from the stored abar;
 //    then the gate, and one store per token. The (L x N) state never reaches memory.
 // Per state update the local pass issues 4 VALU ops and one v_exp_f32, the fix-up 2 VALU.
+// With the exact zero-order-hold input term (ZOH) the local pass also evaluates
+// (abar - 1)/A per update (zoh_coef); the combine and the fix-up do not change.
 //
 // Memory access: every lane has a fixed 32-bit byte offset into a tile (its chunk row and
 // channel); the tile origin and the token step within the chunk live in SGPR base pointers,
@@ -40,9 +42,10 @@ using namespace chunk;
 
 constexpr int kLdsChunkStride = 16 * 16 + 16;  // [chunk][n][lane], padded against bank conflicts
 
-// Register budget: TC = 4 must fit 3 workgroups (12 waves) per CU, TC = 8 two.
-template <typename T, bool GATE, int TC, bool EARLY>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TC <= 4 ? 3 : 2)))
+// Register budget: TC = 4 must fit 3 workgroups (12 waves) per CU, TC = 8 two; the
+// zero-order-hold variant holds 16 more values (1/A) and runs two per CU.
+template <typename T, bool GATE, int TC, bool EARLY, bool ZOH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TC <= 4 && !ZOH ? 3 : 2)))
 void fwd_chunked_kernel(FwdArgs a) {
   // The prod-abar/carry array alternates between two buffers by tile, so a tile's
   // aggregates never overwrite carries a slower wave may still be reading after the second
@@ -64,9 +67,12 @@ void fwd_chunked_kernel(FwdArgs a) {
   const int64_t L = a.seqlen;
   TileLoader<T, GATE, TC, 16> K(a, b, c0, k, i, cc);
 
-  float A2[16];
+  float A2[16], iA[16];
 #pragma unroll
-  for (int n = 0; n < 16; ++n) A2[n] = a.A[cc * 16 + n] * kLog2e;
+  for (int n = 0; n < 16; ++n) {
+    A2[n] = a.A[cc * 16 + n] * kLog2e;
+    if (ZOH) iA[n] = 1.0f / a.A[cc * 16 + n];
+  }
   const float bias = a.delta_bias ? a.delta_bias[cc] : 0.0f;
   const float Dd = a.D ? a.D[cc] : 0.0f;
   // state n = k of channel c0+i, carried across tiles; starts at h0 when one is given
@@ -95,7 +101,10 @@ void fwd_chunked_kernel(FwdArgs a) {
       if (!full) dt = (t0 + k * TC + j < L) ? dt : 0.0f;  // a zero step is the identity
       dsum += dt;
       y[j] = Dd * cur.uu[j];
-      local_step(h, ex[j], A2, dt, dt * cur.uu[j], cur.vb[j], cur.vc[j], y[j]);
+      if (ZOH)
+        local_step_zoh(h, ex[j], A2, iA, dt, cur.uu[j], cur.vb[j], cur.vc[j], y[j]);
+      else
+        local_step(h, ex[j], A2, dt, dt * cur.uu[j], cur.vb[j], cur.vc[j], y[j]);
       gate[j] = GATE ? silu(cur.zz[j]) : 1.0f;
       vc[j] = cur.vc[j];
     }
@@ -165,9 +174,12 @@ void fwd_chunked_kernel(FwdArgs a) {
 
 template <typename T, bool GATE, int TC>
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
-  const int64_t ngroups = a.batch * ((a.dim + 15) / 16);
-  hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, (TC <= 4 && !GATE)>), dim3(static_cast<unsigned>(ngroups)), dim3(256), 0,
-                     s, a);
+  const dim3 grid(static_cast<unsigned>(a.batch * ((a.dim + 15) / 16)));
+  constexpr bool early = TC <= 4 && !GATE;
+  if (a.zoh)
+    hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -184,6 +196,7 @@ bool fwd_chunked_supported(const FwdArgs& a) { return a.dstate == 16 && a.seqlen
 // (2 resident workgroups per CU instead of 3). Pick the one whose workgroup count fills
 // the resident slots of every CU most evenly.
 int fwd_chunked_pick(const FwdArgs& a, int cus) {
+  if (a.zoh) return 4;  // the zero-order-hold variant spills registers at 8
   const int64_t groups = a.batch * ((a.dim + 15) / 16);
   auto eff = [&](int slots) {
     const int64_t cap = static_cast<int64_t>(cus) * slots;

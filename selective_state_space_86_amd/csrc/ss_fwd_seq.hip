@@ -3,8 +3,9 @@
 //
 // The recurrence of "Mamba：选择性状态空间模型入门教程" (section "Mamba 的关键创新：
 // 选择性机制") per channel, discretised as in "架构变体：Mamba/SSM" (section "离散化"):
-//   dt = softplus(delta + bias); abar = exp(dt A[d,n]); h = abar h + (dt B_t[n]) u;
-//   y = (C_t . h + D u) silu(z).
+//   dt = softplus(delta + bias); abar = exp(dt A[d,n]); h = abar h + (bbar B_t[n]) u;
+//   y = (C_t . h + D u) silu(z),
+// with bbar = dt, or the exact zero-order hold (abar - 1)/A[d,n] when ZOH is set.
 // A wave covers 64 consecutive channels of one batch row, so every lane of the wave reads
 // the same B_t and C_t (scalar loads) and u, delta, z, y are read/written as 64
 // consecutive elements. The expanded (L x N) state lives only in registers.
@@ -16,7 +17,7 @@
 
 namespace ss {
 
-template <int NS, typename T, bool GATE>
+template <int NS, typename T, bool GATE, bool ZOH>
 __global__ __launch_bounds__(64) void fwd_seq_kernel(FwdArgs a) {
   const int64_t nblk_d = (a.dim + 63) / 64;
   const int64_t b = blockIdx.x / nblk_d;
@@ -30,10 +31,11 @@ __global__ __launch_bounds__(64) void fwd_seq_kernel(FwdArgs a) {
   const T* __restrict__ Bm = static_cast<const T*>(a.B);
   const T* __restrict__ Cm = static_cast<const T*>(a.C);
 
-  float A2[16], h[16];
+  float A2[16], h[16], iA[16];
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
     A2[n] = (n < ns) ? a.A[dd * ns + n] * kLog2e : 0.0f;
+    if (ZOH) iA[n] = (n < ns) ? 1.0f / a.A[dd * ns + n] : 0.0f;
     h[n] = (n < ns && a.h0) ? a.h0[(b * a.dim + dd) * ns + n] : 0.0f;
   }
   const float bias = a.delta_bias ? a.delta_bias[dd] : 0.0f;
@@ -50,8 +52,10 @@ __global__ __launch_bounds__(64) void fwd_seq_kernel(FwdArgs a) {
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
       if (n < ns) {
-        const float ab = fast_exp2(dt * A2[n]);
-        h[n] = __builtin_fmaf(ab, h[n], du * load_elem(Bm, r + n));
+        const float x2 = dt * A2[n];
+        const float ab = fast_exp2(x2);
+        const float bu = ZOH ? zoh_coef(dt, x2 * kLn2, ab, iA[n]) * uv : du;
+        h[n] = __builtin_fmaf(ab, h[n], bu * load_elem(Bm, r + n));
         acc = __builtin_fmaf(load_elem(Cm, r + n), h[n], acc);
       }
     }
@@ -69,8 +73,12 @@ __global__ __launch_bounds__(64) void fwd_seq_kernel(FwdArgs a) {
 template <int NS, typename T, bool GATE>
 static hipError_t launch_seq(const FwdArgs& a, hipStream_t s) {
   const int64_t nblk = a.batch * ((a.dim + 63) / 64);
-  hipLaunchKernelGGL((fwd_seq_kernel<NS, T, GATE>), dim3(static_cast<unsigned>(nblk)), dim3(64), 0,
-                     s, a);
+  if (a.zoh)
+    hipLaunchKernelGGL((fwd_seq_kernel<NS, T, GATE, true>), dim3(static_cast<unsigned>(nblk)), dim3(64),
+                       0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_seq_kernel<NS, T, GATE, false>), dim3(static_cast<unsigned>(nblk)), dim3(64),
+                       0, s, a);
   return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@ struct FwdArgs {
   int dtype;
   int softplus;
   const float* h0;          // may be null: zero initial state
+  int zoh;                  // input term: 0 dt*B, 1 exact zero-order hold (e^{dt A} - 1)/A * B
 };
 
 // Validated arguments of one ss_step call.
@@ -42,6 +43,7 @@ struct StepArgs {
   int64_t batch, dim, dstate;
   int dtype;
   int softplus;
+  int zoh;                  // as FwdArgs::zoh
 };
 
 hipError_t fwd_seq(const FwdArgs& a, hipStream_t s);

@@ -1,4 +1,5 @@
 // ss_step.hip -- one decode step of the selective scan, state carried in place.
+// (Input term dt*B, or the exact zero-order hold (abar - 1)/A * B when StepArgs::zoh is set.)
 //
 // Recurrent inference with a fixed-size state and constant work per token
 // ("Mamba：选择性状态空间模型入门教程", table "Mamba vs Transformer vs RNN", and the step
@@ -15,7 +16,7 @@
 
 namespace ss {
 
-template <int NS, typename T, bool GATE, bool UNIFORM_ROW, bool VEC>
+template <int NS, typename T, bool GATE, bool UNIFORM_ROW, bool VEC, bool ZOH>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t total = a.batch * a.dim;
@@ -48,8 +49,11 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
     if (n < ns) {
-      const float ab = fast_exp2(dt * (a.A[d * ns + n] * kLog2e));
-      h[n] = __builtin_fmaf(ab, h[n], du * load_elem(Bm, n));
+      const float an = a.A[d * ns + n];
+      const float x2 = dt * (an * kLog2e);
+      const float ab = fast_exp2(x2);
+      const float bu = ZOH ? zoh_coef(dt, x2 * kLn2, ab, 1.0f / an) * uv : du;
+      h[n] = __builtin_fmaf(ab, h[n], bu * load_elem(Bm, n));
       acc = __builtin_fmaf(load_elem(Cm, n), h[n], acc);
     }
   }
@@ -72,7 +76,10 @@ template <int NS, typename T, bool GATE, bool UNI, bool VEC>
 static hipError_t launch_step(const StepArgs& a, hipStream_t s) {
   const int64_t total = a.batch * a.dim;
   const unsigned grid = static_cast<unsigned>((total + 255) / 256);
-  hipLaunchKernelGGL((step_kernel<NS, T, GATE, UNI, VEC>), dim3(grid), dim3(256), 0, s, a);
+  if (a.zoh)
+    hipLaunchKernelGGL((step_kernel<NS, T, GATE, UNI, VEC, true>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((step_kernel<NS, T, GATE, UNI, VEC, false>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

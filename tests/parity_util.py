@@ -29,11 +29,12 @@ def gpu_fwd(x, gated=True, use_D=True, use_bias=True, softplus=True, **kw):
                   softplus=softplus, **kw)
 
 
-def oracle_full(x, gated=True, use_D=True, use_bias=True, softplus=True):
+def oracle_full(x, gated=True, use_D=True, use_bias=True, softplus=True, zoh=False, h0=None):
     n = {k: inputs.to_numpy(v) for k, v in x.items()}
     return oracle.fwd(n["u"], n["delta"], n["A"], n["B"], n["C"], D=n["D"] if use_D else None,
                       z=n["z"] if gated else None,
-                      delta_bias=n["delta_bias"] if use_bias else None, softplus=softplus)
+                      delta_bias=n["delta_bias"] if use_bias else None, softplus=softplus,
+                      zoh=zoh, h0=None if h0 is None else h0.double().cpu().numpy())
 
 
 def sample_channels(batch, dim, k, seed=0):
@@ -50,7 +51,7 @@ def sample_channels(batch, dim, k, seed=0):
 
 
 def oracle_channels(x, chans, gated=True, use_D=True, use_bias=True, softplus=True,
-                    time_major=False):
+                    time_major=False, zoh=False):
     """Oracle y (k, L) and final state (k, N) for the listed (b, d) channels, computed from
     only those channels' inputs (gathered on the device, copied to the host)."""
     ys, sts = [], []
@@ -73,7 +74,8 @@ def oracle_channels(x, chans, gated=True, use_D=True, use_bias=True, softplus=Tr
         n = {k: inputs.to_numpy(v) for k, v in n.items()}
         y, st = oracle.fwd(n["u"], n["delta"], n["A"], n["B"], n["C"], D=n["D"] if use_D else None,
                            z=n["z"] if gated else None,
-                           delta_bias=n["delta_bias"] if use_bias else None, softplus=softplus)
+                           delta_bias=n["delta_bias"] if use_bias else None, softplus=softplus,
+                           zoh=zoh)
         ys.append(y[0].T)  # (k_b, L)
         sts.append(st[0])
         order += [(int(b), int(d)) for d in ds]

@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss_abi_version() == 1
+    assert lib.ss_abi_version() == _binding.ABI_VERSION == 2
     for s in range(0, 8):
         assert lib.ss_status_string(s)
     assert b"unknown" in lib.ss_status_string(99)
@@ -99,11 +99,11 @@ def test_binding_rejects_mixed_dtypes():
         _binding._in_dtype(torch.zeros(1), torch.zeros(1, dtype=torch.bfloat16))
 
 
-def fwd_ex_call(lib, kernel, chunk, **kw):
+def fwd_ex_call(lib, kernel, chunk, disc=0, **kw):
     a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, sp=1, y=FAKE,
              st=None, h0=None, batch=1, L=4, dim=8, N=16, dtype=0)
     a.update(kw)
-    opt = _binding.FwdOptions(kernel, chunk)
+    opt = _binding.FwdOptions(kernel, chunk, disc)
     return lib.ss_fwd_ex(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
                          a["y"], a["st"], a["h0"], a["batch"], a["L"], a["dim"], a["N"], a["dtype"],
                          ctypes.byref(opt), None)
@@ -116,3 +116,26 @@ def fwd_ex_call(lib, kernel, chunk, **kw):
 ])
 def test_fwd_ex_validation(lib, kernel, chunk, kw, code):
     assert fwd_ex_call(lib, kernel, chunk, **kw) == code
+
+
+@pytest.mark.parametrize("disc,kw,code", [
+    (2, {}, 2), (-1, {}, 2), (1, dict(u=None), 1), (1, dict(N=17), 4), (1, dict(dtype=3), 3),
+])
+def test_fwd_ex_discretization_validation(lib, disc, kw, code):
+    assert fwd_ex_call(lib, 0, 0, disc=disc, **kw) == code
+
+
+def step_ex_call(lib, disc, **kw):
+    a = dict(st=FAKE, u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, sp=1,
+             y=FAKE, batch=1, dim=8, N=4, dtype=0)
+    a.update(kw)
+    return lib.ss_step_ex(a["st"], a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                          a["bias"], a["sp"], a["y"], a["batch"], a["dim"], a["N"], a["dtype"], disc, None)
+
+
+@pytest.mark.parametrize("disc,kw,code", [
+    (2, {}, 2), (-3, {}, 2), (1, dict(st=None), 1), (1, dict(N=0), 2), (0, dict(dtype=9), 3),
+    (1, dict(y=FAKE + 2), 5),
+])
+def test_step_ex_validation(lib, disc, kw, code):
+    assert step_ex_call(lib, disc, **kw) == code
