@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the selective-scan (S6) forward and decode step.
+"""fp64 CPU oracle for the selective-scan (S6) forward, decode step and backward.
 
 TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
 leg of ``bench.py`` may import this package. It never imports or calls the GPU library,
@@ -55,6 +55,10 @@ def _bind(path):
     lib.ss_oracle_step.restype = i32
     lib.ss_oracle_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp,
                                    i64, i64, i64, i32, i32]
+    lib.ss_oracle_bwd.restype = i32
+    lib.ss_oracle_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                  vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  i64, i64, i64, i64, i32, vp, vp, i64, i32]
     lib.ss_oracle_max_threads.restype = i32
     lib.ss_oracle_max_threads.argtypes = []
     return lib
@@ -162,6 +166,58 @@ def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tru
     return y
 
 
+def bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True, h0=None,
+        dlast=None, channels=None, nthreads=0, _lib=None):
+    """Backward of ``fwd`` (input term dt*B) for dL/dy = dy (batch, L, dim) float32 and
+    dL/dlast_state = dlast (batch, dim, N) float32 or None.
+
+    Returns a dict of float64 arrays: du, ddelta, dz (batch, L, dim) [dz only with z];
+    dA (dim, N); dD, ddelta_bias (dim,); dh0 (batch, dim, N); dB, dC (batch, L, N).
+    With channels ((k, 2) array of (b, d)): du, ddelta, dz are (k, L); dA, dh0 (k, N) and
+    dD, ddelta_bias (k,) are each channel's own terms; dB, dC sum the listed channels.
+    """
+    u, delta, B, C, z = _c(u), _c(delta), _c(B), _c(C), _c(z)
+    A, D, delta_bias = _c(A, np.float32), _c(D, np.float32), _c(delta_bias, np.float32)
+    dy, dlast = _c(dy, np.float32), _c(dlast, np.float32)
+    dt = _dtype_of(u, delta, B, C, z)
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    if delta.shape != u.shape or (z is not None and z.shape != u.shape) or dy.shape != u.shape:
+        raise ValueError("u, delta, z and dy must share a shape")
+    if B.shape != (batch, L, N) or C.shape != (batch, L, N) or A.shape != (dim, N):
+        raise ValueError("bad B, C or A shape")
+    if h0 is not None:
+        h0 = _c(h0, np.float64)
+        if h0.shape != (batch, dim, N):
+            raise ValueError("bad h0 shape")
+    if dlast is not None and dlast.shape != (batch, dim, N):
+        raise ValueError("bad dlast shape")
+    f = np.float64
+    if channels is None:
+        nchan, cb, cd = 0, None, None
+        tok, per_ch, rows = (batch, L, dim), (dim,), (batch, dim)
+    else:
+        ch = np.ascontiguousarray(np.asarray(channels, dtype=np.int64).reshape(-1, 2))
+        nchan = ch.shape[0]
+        cb, cd = np.ascontiguousarray(ch[:, 0]), np.ascontiguousarray(ch[:, 1])
+        tok, per_ch, rows = (nchan, L), (nchan,), (nchan,)
+    out = dict(du=np.zeros(tok, f), ddelta=np.zeros(tok, f),
+               dz=np.zeros(tok, f) if z is not None else None,
+               dA=np.zeros(per_ch + (N,), f), dD=np.zeros(per_ch, f), ddelta_bias=np.zeros(per_ch, f),
+               dh0=np.zeros(rows + (N,), f), dB=np.zeros((batch, L, N), f), dC=np.zeros((batch, L, N), f))
+    if channels is not None and nchan == 0:
+        return out
+    rc = (_lib or _load()).ss_oracle_bwd(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        int(bool(softplus)), _ptr(h0), _ptr(dy), _ptr(dlast), _ptr(out["du"]), _ptr(out["ddelta"]),
+        _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+        _ptr(out["ddelta_bias"]), _ptr(out["dh0"]), batch, L, dim, N, dt, _ptr(cb), _ptr(cd), nchan,
+        int(nthreads))
+    if rc != 0:
+        raise ValueError("ss_oracle_bwd rejected its arguments")
+    return out
+
+
 class Library:
     """The oracle API bound to another build of the same C source (used by the tests that
     plant mistakes in a copy of the oracle and check that the pins catch them)."""
@@ -174,3 +230,6 @@ class Library:
 
     def step(self, *a, **k):
         return step(*a, _lib=self._h, **k)
+
+    def bwd(self, *a, **k):
+        return bwd(*a, _lib=self._h, **k)

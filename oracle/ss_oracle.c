@@ -37,6 +37,8 @@
  *    the whole output including the D term; the bias is added before softplus;
  *  - A is a diagonal (dim, dstate) array; B and C carry no channel index.
  *
+ * The backward (ss_oracle_bwd, below) is the chain rule of the same loop, run in reverse.
+ *
  * Arithmetic: every input is converted exactly to double (bf16 -> fp32 -> fp64 is
  * exact), all arithmetic is IEEE double with libm exp/expm1/log1p, compiled without fast
  * math. Work is split over (b, d) channels with OpenMP; each channel runs the plain
@@ -181,6 +183,198 @@ int ss_oracle_step(double* state, const void* u, const void* delta, const float*
                  dtype, state + j * dstate, y ? y + j : NULL, 1);
   }
   return 0;
+}
+
+/* ----------------------------------------------------------------------------------------
+ * Backward: the reverse-mode derivative of the forward above (input term dt * B), written
+ * out by the chain rule for one channel. With lam_t[n] = dL/dh_t[n] and
+ * mu_t[n] = abar_t[n] lam_t[n] (what token t passes back to h_{t-1}):
+ *   s_t = sum_n C_t[n] h_t[n] + D u_t,  g_t = silu(z_t) (1 without z),  ds_t = dy_t g_t
+ *   dz_t = dy_t s_t silu'(z_t),  dD += ds_t u_t,  du_t = ds_t D + sum_n lam_t[n] dt_t B_t[n]
+ *   lam_t[n] = ds_t C_t[n] + mu_{t+1}[n]                   (mu_L = dL/dlast_state)
+ *   dC_t[n] += ds_t h_t[n];  dB_t[n] += lam_t[n] dt_t u_t
+ *   ddt_t = sum_n lam_t[n] (B_t[n] u_t + A[n] abar_t[n] h_{t-1}[n])
+ *   dA[n] += lam_t[n] abar_t[n] h_{t-1}[n] dt_t
+ *   ddelta_t = ddt_t sigmoid(x_t) with softplus (its derivative), ddt_t without; dbias += it
+ *   dh0 = mu_0
+ * The backward of the pages' method ("Mamba：选择性状态空间的线性时间序列建模", section
+ * "第二个创新：硬件感知算法") recomputes the states instead of storing them; this
+ * reference simply keeps every state of the channel it is differentiating.
+ */
+
+static double sigmoid(double x) {
+  if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+  double e = exp(x);
+  return e / (1.0 + e);
+}
+
+/* d silu(z) / dz = sigmoid(z) (1 + z (1 - sigmoid(z))) */
+static double dsilu(double z) {
+  double s = sigmoid(z);
+  return s * (1.0 + z * (1.0 - s));
+}
+
+/* One channel (b, d). hs: (seqlen + 1) * dstate scratch, mu: dstate scratch. du, dd, dz
+   receive element t at index t * stride; dA_ch, dD_ch, dbias_ch are accumulated (+=),
+   dh0_ch written; dB and dC ((batch, seqlen, dstate)) are accumulated. */
+static void grad_channel(const void* u, const void* delta, const float* A, const void* B,
+                         const void* C, const float* D, const void* z, const float* bias,
+                         int softplus_flag, const double* h0_ch, const float* dy,
+                         const float* dlast_ch, int64_t b, int64_t d, int64_t seqlen, int64_t dim,
+                         int64_t dstate, int dtype, double* hs, double* mu, double* du, double* dd,
+                         double* dz, int64_t stride, double* dA_ch, double* dD_ch, double* dbias_ch,
+                         double* dh0_ch, double* dB, double* dC) {
+  const double bias_d = bias ? (double)bias[d] : 0.0;
+  const double D_d = D ? (double)D[d] : 0.0;
+  /* forward, keeping every state: hs[(t + 1) * dstate + n] = h_t[n], hs[n] = h_{-1}[n] */
+  for (int64_t n = 0; n < dstate; ++n) hs[n] = h0_ch ? h0_ch[n] : 0.0;
+  for (int64_t t = 0; t < seqlen; ++t) {
+    const int64_t e = (b * seqlen + t) * dim + d;
+    const int64_t bc = (b * seqlen + t) * dstate;
+    const double x = in_at(delta, dtype, e) + bias_d;
+    const double dt = softplus_flag ? softplus(x) : x;
+    const double uv = in_at(u, dtype, e);
+    const double* hp = hs + t * dstate;
+    double* ht = hs + (t + 1) * dstate;
+    for (int64_t n = 0; n < dstate; ++n) {
+      const double abar = exp(dt * (double)A[d * dstate + n]);
+      ht[n] = abar * hp[n] + (dt * in_at(B, dtype, bc + n)) * uv;
+    }
+  }
+  /* reverse */
+  for (int64_t n = 0; n < dstate; ++n) mu[n] = dlast_ch ? (double)dlast_ch[n] : 0.0;
+  for (int64_t t = seqlen - 1; t >= 0; --t) {
+    const int64_t e = (b * seqlen + t) * dim + d;
+    const int64_t bc = (b * seqlen + t) * dstate;
+    const double x = in_at(delta, dtype, e) + bias_d;
+    const double dt = softplus_flag ? softplus(x) : x;
+    const double uv = in_at(u, dtype, e);
+    const double* hp = hs + t * dstate;
+    const double* ht = hs + (t + 1) * dstate;
+    double acc = 0.0;
+    for (int64_t n = 0; n < dstate; ++n) acc += in_at(C, dtype, bc + n) * ht[n];
+    const double st = acc + D_d * uv;
+    const double dyv = (double)dy[e];
+    double ds = dyv;
+    if (z) {
+      const double zv = in_at(z, dtype, e);
+      ds = dyv * silu(zv);
+      dz[t * stride] = dyv * st * dsilu(zv);
+    }
+    *dD_ch += ds * uv;
+    double du_t = ds * D_d;
+    double ddt = 0.0;
+    for (int64_t n = 0; n < dstate; ++n) {
+      const double a_dn = (double)A[d * dstate + n];
+      const double abar = exp(dt * a_dn);
+      const double Bv = in_at(B, dtype, bc + n);
+      const double lam = ds * in_at(C, dtype, bc + n) + mu[n];
+      dC[bc + n] += ds * ht[n];
+      dB[bc + n] += lam * dt * uv;
+      du_t += lam * dt * Bv;
+      const double g_abar = lam * hp[n]; /* dL/dabar_t[n] */
+      ddt += lam * Bv * uv + g_abar * abar * a_dn;
+      dA_ch[n] += g_abar * abar * dt;
+      mu[n] = abar * lam;
+    }
+    du[t * stride] = du_t;
+    const double dx = softplus_flag ? ddt * sigmoid(x) : ddt;
+    dd[t * stride] = dx;
+    *dbias_ch += dx;
+  }
+  if (dh0_ch)
+    for (int64_t n = 0; n < dstate; ++n) dh0_ch[n] = mu[n];
+}
+
+/*
+ * Backward of ss_oracle_fwd (input term dt * B) for the loss L with dL/dy = dy and
+ * dL/dlast_state = dlast (NULL: 0). dy and dlast are fp32; h0 is fp64 (NULL: zeros).
+ *   nchan == 0: du, ddelta, dz (batch, seqlen, dim); dA (dim, dstate); dD, dbias (dim);
+ *               dh0 (batch, dim, dstate); dB, dC (batch, seqlen, dstate).
+ *   nchan  > 0: only the listed (b, d) channels: du, ddelta, dz (nchan, seqlen);
+ *               dA (nchan, dstate), dD, dbias (nchan) and dh0 (nchan, dstate) are that
+ *               channel's own terms; dB, dC (batch, seqlen, dstate) sum the listed channels.
+ * dz is required when z is given (else ignored), dh0 may be NULL; every other output is
+ * required. Sums over channels go through per-thread buffers (static schedule) added in
+ * thread order, so a result depends on the thread count only through rounding.
+ * Returns 0, or -1 on a bad argument or allocation failure.
+ */
+int ss_oracle_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                  const double* h0, const float* dy, const float* dlast, double* du,
+                  double* ddelta, double* dA, double* dB, double* dC, double* dD, double* dz,
+                  double* dbias, double* dh0, int64_t batch, int64_t seqlen, int64_t dim,
+                  int64_t dstate, int dtype, const int64_t* chan_b, const int64_t* chan_d,
+                  int64_t nchan, int nthreads) {
+  if (!u || !delta || !A || !B || !C || !dy) return -1;
+  if (!du || !ddelta || !dA || !dB || !dC || !dD || !dbias || (z && !dz)) return -1;
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || nchan < 0) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (nchan > 0 && (!chan_b || !chan_d)) return -1;
+  const int64_t bln = batch * seqlen * dstate;
+  const int64_t njobs = nchan > 0 ? nchan : dim;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  const int nth = omp_get_max_threads();
+#else
+  (void)nthreads;
+  const int nth = 1;
+#endif
+  double** part = (double**)calloc((size_t)nth, sizeof(double*));
+  if (!part) return -1;
+  int bad = 0;
+#pragma omp parallel reduction(| : bad)
+  {
+#ifdef _OPENMP
+    const int tid = omp_get_thread_num();
+#else
+    const int tid = 0;
+#endif
+    double* acc = (double*)calloc((size_t)(2 * bln + (seqlen + 2) * dstate + 1), sizeof(double));
+    part[tid] = acc;
+    if (!acc) bad = 1;
+#pragma omp for schedule(static)
+    for (int64_t j = 0; j < njobs; ++j) {
+      if (!acc) continue;
+      double* hs = acc + 2 * bln;
+      double* mu = hs + (seqlen + 1) * dstate;
+      const int64_t b_lo = nchan > 0 ? chan_b[j] : 0;
+      const int64_t b_hi = nchan > 0 ? chan_b[j] + 1 : batch;
+      const int64_t d = nchan > 0 ? chan_d[j] : j;
+      if (b_lo < 0 || b_hi > batch || d < 0 || d >= dim) { bad = 1; continue; }
+      double* dA_ch = nchan > 0 ? dA + j * dstate : dA + d * dstate;
+      double* dD_ch = nchan > 0 ? dD + j : dD + d;
+      double* dbias_ch = nchan > 0 ? dbias + j : dbias + d;
+      for (int64_t n = 0; n < dstate; ++n) dA_ch[n] = 0.0;
+      *dD_ch = 0.0;
+      *dbias_ch = 0.0;
+      for (int64_t b = b_lo; b < b_hi; ++b) {
+        const int64_t o = nchan > 0 ? j * seqlen : b * seqlen * dim + d;
+        const int64_t stride = nchan > 0 ? 1 : dim;
+        double* dh0_ch = !dh0 ? NULL : (nchan > 0 ? dh0 + j * dstate : dh0 + (b * dim + d) * dstate);
+        grad_channel(u, delta, A, B, C, D, z, delta_bias, softplus_flag,
+                     h0 ? h0 + (b * dim + d) * dstate : NULL, dy,
+                     dlast ? dlast + (b * dim + d) * dstate : NULL, b, d, seqlen, dim, dstate, dtype,
+                     hs, mu, du + o, ddelta + o, z ? dz + o : NULL, stride, dA_ch, dD_ch, dbias_ch,
+                     dh0_ch, acc, acc + bln);
+      }
+    }
+  }
+  if (!bad) {
+    for (int64_t i = 0; i < bln; ++i) {
+      double sb = 0.0, sc = 0.0;
+      for (int k = 0; k < nth; ++k) {
+        if (!part[k]) continue;
+        sb += part[k][i];
+        sc += part[k][bln + i];
+      }
+      dB[i] = sb;
+      dC[i] = sc;
+    }
+  }
+  for (int k = 0; k < nth; ++k) free(part[k]);
+  free(part);
+  return bad ? -1 : 0;
 }
 
 int ss_oracle_max_threads(void) {

@@ -1,5 +1,5 @@
 """Plant plausible mistakes in a copy of the oracle's C source (on the CPU) and check
-that the pins in test_oracle_pins.py catch every one of them."""
+that the pins in test_oracle_pins.py and test_oracle_bwd_pins.py catch every one."""
 import os
 import shutil
 
@@ -7,11 +7,13 @@ import numpy as np
 import pytest
 
 import oracle
+from tests import test_oracle_bwd_pins as bpins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ss_oracle.c")
 
-# (name, [(original text, planted text), ...]) -- each original must occur in the source
+# (name, [(original text, planted text), ...]) -- each original must occur in the source;
+# its first occurrence is replaced
 MUTANTS = [
     ("drop_D_term", [("double yv = acc + D_d * uv;", "double yv = acc;")]),
     ("bias_after_softplus", [("const double x = in_at(delta, dtype, e) + bias_d;",
@@ -41,6 +43,19 @@ MUTANTS = [
     ("bf16_decode_shift", [("<< 16;", "<< 15;")]),
     ("state_not_carried_in_step", [("state + j * dstate, y ? y + j : NULL, 1);",
                                     "state + 0 * dstate, y ? y + j : NULL, 1);")]),
+    # backward
+    ("bwd_carry_without_decay", [("mu[n] = abar * lam;", "mu[n] = lam;")]),
+    ("bwd_ddt_drops_decay_term", [("ddt += lam * Bv * uv + g_abar * abar * a_dn;", "ddt += lam * Bv * uv;")]),
+    ("bwd_no_softplus_derivative", [("const double dx = softplus_flag ? ddt * sigmoid(x) : ddt;",
+                                     "const double dx = ddt;")]),
+    ("bwd_dB_without_dt", [("dB[bc + n] += lam * dt * uv;", "dB[bc + n] += lam * uv;")]),
+    ("bwd_dC_from_previous_state", [("dC[bc + n] += ds * ht[n];", "dC[bc + n] += ds * hp[n];")]),
+    ("bwd_dsilu_is_sigmoid", [("return s * (1.0 + z * (1.0 - s));", "return s;")]),
+    ("bwd_dA_without_dt", [("dA_ch[n] += g_abar * abar * dt;", "dA_ch[n] += g_abar * abar;")]),
+    ("bwd_dlast_ignored", [("mu[n] = dlast_ch ? (double)dlast_ch[n] : 0.0;", "mu[n] = 0.0;")]),
+    ("bwd_du_without_D", [("double du_t = ds * D_d;", "double du_t = 0.0;")]),
+    ("bwd_decay_grad_uses_current_state", [("const double g_abar = lam * hp[n];", "const double g_abar = lam * ht[n];")]),
+    ("bwd_gate_not_applied", [("      ds = dyv * silu(zv);\n", "      ds = dyv;\n")]),
 ]
 
 
@@ -62,6 +77,12 @@ def pin_suite(lib):
         ("zoh_half_steps", lambda: pins.test_zoh_half_steps_compose(lib)),
         ("zoh_brute", lambda: pins.test_zoh_brute_force_unrolled_sum(lib, True)),
         ("zoh_step", lambda: pins.test_zoh_step_by_step_matches_forward(lib)),
+        ("bwd_fd", lambda: bpins.test_backward_matches_finite_differences(lib, True)),
+        ("bwd_fd_no_softplus", lambda: bpins.test_backward_matches_finite_differences(lib, False)),
+        ("bwd_adjoint_u", lambda: bpins.test_adjoint_identity_for_linear_arguments(lib, "u")),
+        ("bwd_adjoint_h0", lambda: bpins.test_adjoint_identity_for_linear_arguments(lib, "h0")),
+        ("bwd_lti", lambda: bpins.test_lti_du_is_correlation_with_kernel(lib)),
+        ("bwd_zero_step", lambda: bpins.test_zero_step_closed_forms(lib)),
     ]
     for name, fn in checks:
         try:
@@ -82,8 +103,10 @@ def test_unmodified_copy_passes(tmp_path):
 def test_planted_mistake_is_caught(tmp_path, name, edits):
     text = open(SRC).read()
     for old, new in edits:
-        assert text.count(old) == 1, f"mutation anchor not found once: {old!r}"
-        text = text.replace(old, new)
+        # the forward loop comes first in the file; the backward repeats a few of its lines
+        # for its own recomputation, and a forward mistake is planted in the forward only
+        assert text.count(old) >= 1, f"mutation anchor not found: {old!r}"
+        text = text.replace(old, new, 1)
     src = tmp_path / "ss_oracle_mutant.c"
     src.write_text(text)
     lib = oracle.Library(oracle.compile_source(str(src), str(tmp_path / "mutant.so")))
