@@ -34,13 +34,14 @@
 #ifndef SS_H_
 #define SS_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 2
+#define SS_ABI_VERSION 3
 #define SS_MAX_DSTATE 16
 
 typedef enum {
@@ -51,7 +52,8 @@ typedef enum {
   SS_ERR_UNSUPPORTED_N = 4, /* dstate > SS_MAX_DSTATE */
   SS_ERR_MISALIGNED = 5,    /* a pointer is not aligned to its element size */
   SS_ERR_HIP = 6,           /* a HIP runtime call or kernel launch failed */
-  SS_ERR_DEVICE = 7         /* the current device is not a gfx950 GPU */
+  SS_ERR_DEVICE = 7,        /* the current device is not a gfx950 GPU */
+  SS_ERR_WORKSPACE = 8      /* workspace NULL or smaller than ss_bwd_workspace_size() */
 } ss_status;
 
 typedef enum {
@@ -148,6 +150,47 @@ int ss_step_ex(float* state, const void* u, const void* delta, const float* A, c
                const void* C, const float* D, const void* z, const float* delta_bias,
                int softplus_flag, float* y, int64_t batch, int64_t dim, int64_t dstate,
                int in_dtype, int discretization, void* stream);
+
+/*
+ * ss_bwd_workspace_size -- bytes of device workspace ss_bwd needs for these sizes
+ * (about 4/(16*2) * 16 bytes per (b, t, d) of tile-start states plus 8 bytes per
+ * (b, t, n) per group of 16 channels of partial sums; see ss_bwd).
+ */
+size_t ss_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+
+/*
+ * ss_bwd -- backward of ss_fwd_ex with the default input term (bbar = dt): the gradients
+ * of a loss L given dL/dy and, optionally, dL/d(last_state), by the chain rule of the
+ * recurrence run in reverse time. The expanded (batch, L, dim, N) state is never stored:
+ * the states are recomputed tile by tile from checkpoints kept in the workspace, as the
+ * pages prescribe for the backward ("Mamba：选择性状态空间的线性时间序列建模", section
+ * "第二个创新：硬件感知算法": recomputation instead of storing intermediate states).
+ *
+ *   u, delta, A, B, C, D, z, delta_bias, softplus_flag, h0
+ *                 the forward's inputs, as in ss_fwd_ex (h0 may be NULL: zero state).
+ *   dy            (batch, seqlen, dim) fp32: dL/dy.
+ *   dlast_state   (batch, dim, dstate) fp32, may be NULL (zero): dL/d(last_state).
+ * Outputs (fp32, written, never accumulated into):
+ *   du, ddelta    (batch, seqlen, dim); ddelta is dL/d(delta) (before the bias).
+ *   dz            (batch, seqlen, dim); required when z is given, ignored otherwise.
+ *   dA            (dim, dstate).
+ *   dB, dC        (batch, seqlen, dstate).
+ *   dD, ddelta_bias (dim), may be NULL (not computed). With D or delta_bias NULL they are
+ *                 the gradients at D = 0 / bias = 0.
+ *   dh0           (batch, dim, dstate), may be NULL: dL/dh0 (of the zero state if h0 is NULL).
+ *   workspace     device memory of at least ss_bwd_workspace_size() bytes, 4-byte
+ *                 aligned, owned by the caller; its contents on entry do not matter and
+ *                 are undefined on return.
+ * seqlen == 0 is allowed (the per-token arrays may then be NULL): dh0 = dlast_state and
+ * dA, dD, ddelta_bias are zero. Sums over channels, tokens and batch rows have a fixed
+ * order, so the result is deterministic. Errors as ss_fwd, plus SS_ERR_WORKSPACE.
+ */
+int ss_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+           const float* D, const void* z, const float* delta_bias, int softplus_flag,
+           const float* h0, const float* dy, const float* dlast_state, float* du, float* ddelta,
+           float* dA, float* dB, float* dC, float* dD, float* dz, float* ddelta_bias, float* dh0,
+           void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim,
+           int64_t dstate, int in_dtype, void* stream);
 
 #ifdef __cplusplus
 }

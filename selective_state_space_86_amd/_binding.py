@@ -12,8 +12,9 @@ _lib = None
 
 F32, BF16 = 0, 1
 DISC_DT, DISC_ZOH = 0, 1
-ABI_VERSION = 2
-EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_step", "ss_step_ex")
+ABI_VERSION = 3
+EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_step", "ss_step_ex",
+           "ss_bwd_workspace_size", "ss_bwd")
 
 
 class FwdOptions(ctypes.Structure):
@@ -55,6 +56,12 @@ def load_library():
     lib.ss_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, vp]
     lib.ss_step_ex.restype = i32
     lib.ss_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, i32, vp]
+    lib.ss_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ss_bwd_workspace_size.argtypes = [i64, i64, i64, i64]
+    lib.ss_bwd.restype = i32
+    lib.ss_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                           vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                           i64, i64, i64, i64, i32, vp]
     if lib.ss_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{_LIB_PATH} has ABI version {lib.ss_abi_version()}, this binding "
                            f"needs {ABI_VERSION}: rebuild it")
@@ -167,3 +174,66 @@ def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tru
     if rc != 0:
         raise SSError(rc, "ss_step")
     return y
+
+
+def bwd_workspace_size(batch, seqlen, dim, dstate) -> int:
+    return int(load_library().ss_bwd_workspace_size(batch, seqlen, dim, dstate))
+
+
+def bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True, h0=None,
+        dlast=None, stream=None, workspace=None, out=None):
+    """Backward of ``fwd`` (``ss_bwd``; input term dt*B) for dL/dy = dy (batch, L, dim)
+    fp32 and dL/dlast_state = dlast (batch, dim, N) fp32 or None.
+
+    Returns a dict of fp32 device tensors: du, ddelta, dz (batch, L, dim) [dz None without
+    z]; dA (dim, N); dB, dC (batch, L, N); dD, ddelta_bias (dim,) [None when D / delta_bias
+    is None]; dh0 (batch, dim, N). ``workspace``: a uint8 device tensor of at least
+    bwd_workspace_size() bytes, allocated here when None. ``out``: a dict like the returned
+    one whose tensors are written instead of new ones (reuse across calls)."""
+    dev = u.device
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    dt = _in_dtype(u, delta, B, C, z)
+    _check(u, "u", dev)
+    _check(delta, "delta", dev, shape=u.shape)
+    _check(z, "z", dev, shape=u.shape)
+    _check(B, "B", dev, shape=(batch, L, N))
+    _check(C, "C", dev, shape=(batch, L, N))
+    _check(A, "A", dev, torch.float32, (dim, N))
+    _check(D, "D", dev, torch.float32, (dim,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (dim,))
+    _check(h0, "h0", dev, torch.float32, (batch, dim, N))
+    _check(dy, "dy", dev, torch.float32, (batch, L, dim))
+    _check(dlast, "dlast", dev, torch.float32, (batch, dim, N))
+    f = dict(dtype=torch.float32, device=dev)
+    if out is not None:
+        shapes = dict(du=(batch, L, dim), ddelta=(batch, L, dim), dz=(batch, L, dim), dA=(dim, N),
+                      dB=(batch, L, N), dC=(batch, L, N), dD=(dim,), ddelta_bias=(dim,),
+                      dh0=(batch, dim, N))
+        for k, shape in shapes.items():
+            _check(out.get(k), k, dev, torch.float32, shape)
+        for k in ("du", "ddelta", "dA", "dB", "dC") + (("dz",) if z is not None else ()):
+            if out.get(k) is None:
+                raise ValueError(f"out[{k!r}] is required")
+    else:
+        out = dict(du=torch.empty((batch, L, dim), **f), ddelta=torch.empty((batch, L, dim), **f),
+                   dz=torch.empty((batch, L, dim), **f) if z is not None else None,
+                   dA=torch.empty((dim, N), **f), dB=torch.empty((batch, L, N), **f),
+                   dC=torch.empty((batch, L, N), **f),
+                   dD=torch.empty((dim,), **f) if D is not None else None,
+                   ddelta_bias=torch.empty((dim,), **f) if delta_bias is not None else None,
+                   dh0=torch.empty((batch, dim, N), **f))
+    lib = load_library()
+    need = int(lib.ss_bwd_workspace_size(batch, L, dim, N))
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", dev, torch.uint8)
+    rc = lib.ss_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                    _ptr(delta_bias), int(bool(softplus)), _ptr(h0), _ptr(dy), _ptr(dlast),
+                    _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                    _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]),
+                    _ptr(out["dh0"]), _ptr(workspace), workspace.numel(), batch, L, dim, N, dt,
+                    _stream(dev, stream))
+    if rc != 0:
+        raise SSError(rc, "ss_bwd")
+    return out

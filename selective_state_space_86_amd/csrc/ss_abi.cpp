@@ -66,6 +66,7 @@ const char* ss_status_string(int s) {
     case SS_ERR_MISALIGNED: return "a pointer is not aligned to its element size";
     case SS_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case SS_ERR_DEVICE: return "the current device is not a gfx950 GPU";
+    case SS_ERR_WORKSPACE: return "the workspace is NULL or smaller than ss_bwd_workspace_size()";
     default: return "unknown status code";
   }
 }
@@ -153,6 +154,58 @@ int ss_step(float* state, const void* u, const void* delta, const float* A, cons
             void* stream) {
   return ss_step_ex(state, u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, batch, dim, dstate,
                     in_dtype, SS_DISC_DT, stream);
+}
+
+size_t ss_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
+  if (batch < 1 || dim < 1 || dstate < 1 || seqlen < 0 || dstate > SS_MAX_DSTATE) return 0;
+  if (!product_ok(batch, seqlen, dim) || !product_ok(batch, seqlen, 16 * dstate)) return 0;
+  return ss::bwd_workspace_bytes(batch, seqlen, dim, dstate);
+}
+
+int ss_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+           const float* D, const void* z, const float* delta_bias, int softplus_flag,
+           const float* h0, const float* dy, const float* dlast_state, float* du, float* ddelta,
+           float* dA, float* dB, float* dC, float* dD, float* dz, float* ddelta_bias, float* dh0,
+           void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim,
+           int64_t dstate, int in_dtype, void* stream) {
+  if (!A || !dA) return SS_ERR_NULL_ARG;
+  if (seqlen != 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta || !dB || !dC || (z && !dz)))
+    return SS_ERR_NULL_ARG;
+  if (in_dtype != SS_DTYPE_F32 && in_dtype != SS_DTYPE_BF16) return SS_ERR_BAD_DTYPE;
+  if (batch < 1 || dim < 1 || dstate < 1 || seqlen < 0) return SS_ERR_BAD_SHAPE;
+  if (dstate > SS_MAX_DSTATE) return SS_ERR_UNSUPPORTED_N;
+  if (!product_ok(batch, seqlen, dim) || !product_ok(batch, seqlen, 16 * dstate) ||
+      !product_ok(batch, dim, dstate))
+    return SS_ERR_BAD_SHAPE;
+  const int64_t ngroups = (dim + 15) / 16;
+  if (batch * ngroups > 0x7fffffffLL) return SS_ERR_BAD_SHAPE;
+  if (batch * seqlen * dstate + dim * (dstate + 2) > 0x7fffffffLL * 256LL) return SS_ERR_BAD_SHAPE;
+  const size_t es = elem_size(in_dtype);
+  if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
+      (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+      (delta_bias && !aligned(delta_bias, 4)) || (h0 && !aligned(h0, 4)) || !aligned(dy, 4) ||
+      (dlast_state && !aligned(dlast_state, 4)) || !aligned(du, 4) || !aligned(ddelta, 4) ||
+      !aligned(dA, 4) || !aligned(dB, 4) || !aligned(dC, 4) || (dD && !aligned(dD, 4)) ||
+      (dz && !aligned(dz, 4)) || (ddelta_bias && !aligned(ddelta_bias, 4)) || (dh0 && !aligned(dh0, 4)) ||
+      !aligned(workspace, 4))
+    return SS_ERR_MISALIGNED;
+  const size_t need = ss::bwd_workspace_bytes(batch, seqlen, dim, dstate);
+  if (!workspace || workspace_bytes < need) return SS_ERR_WORKSPACE;
+  int cus = 0;
+  const int dv = check_device(&cus);
+  if (dv != SS_OK) return dv;
+
+  const int64_t ntiles = seqlen > 0 ? (seqlen + ss::bwd_tile_tokens() - 1) / ss::bwd_tile_tokens() : 0;
+  float* ws = static_cast<float*>(workspace);
+  float* ckpt = ws;
+  float* part_bc = ckpt + batch * ntiles * ngroups * 16 * 16;
+  float* part_ch = part_bc + 2 * batch * ngroups * seqlen * dstate;
+  ss::BwdArgs a{u, delta, A, B, C, D, z, delta_bias, h0, dy, dlast_state,
+                du, ddelta, z ? dz : nullptr, dh0, dA, dB, dC, dD, ddelta_bias,
+                ckpt, part_bc, part_ch, batch, seqlen, dim, dstate, ngroups, ntiles,
+                in_dtype, softplus_flag ? 1 : 0};
+  const hipError_t e = ss::bwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
 }  // extern "C"

@@ -46,10 +46,49 @@ struct StepArgs {
   int zoh;                  // as FwdArgs::zoh
 };
 
+// Validated arguments of one ss_bwd call. Workspace regions (fp32): ckpt
+// (batch, ntiles, ngroups*16, 16), part_bc (2, batch, ngroups, seqlen, dstate),
+// part_ch (batch, ngroups*16, 18).
+struct BwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;           // may be null
+  const void* z;            // may be null
+  const float* delta_bias;  // may be null
+  const float* h0;          // may be null
+  const float* dy;
+  const float* dlast;       // may be null
+  float* du;
+  float* ddelta;
+  float* dz;                // required iff z
+  float* dh0;               // may be null
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;                // may be null
+  float* dbias;             // may be null
+  float* ckpt;
+  float* part_bc;
+  float* part_ch;
+  int64_t batch, seqlen, dim, dstate;
+  int64_t ngroups;          // channel groups of 16 per batch row
+  int64_t ntiles;           // tiles of bwd_tile_tokens() tokens
+  int dtype;
+  int softplus;
+};
+
+constexpr int kBwdChunk = 2;  // tokens per lane and chunk in the backward kernels
+
 hipError_t fwd_seq(const FwdArgs& a, hipStream_t s);
 bool fwd_chunked_supported(const FwdArgs& a);
 hipError_t fwd_chunked(const FwdArgs& a, int chunk_len, hipStream_t s);
 int fwd_chunked_pick(const FwdArgs& a, int cus);
 hipError_t step(const StepArgs& a, hipStream_t s);
+int64_t bwd_tile_tokens();
+size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
+hipError_t bwd(const BwdArgs& a, hipStream_t s);
 
 }  // namespace ss

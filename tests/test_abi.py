@@ -36,8 +36,8 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss_abi_version() == _binding.ABI_VERSION == 2
-    for s in range(0, 8):
+    assert lib.ss_abi_version() == _binding.ABI_VERSION == 3
+    for s in range(0, 9):
         assert lib.ss_status_string(s)
     assert b"unknown" in lib.ss_status_string(99)
 
@@ -139,3 +139,46 @@ def step_ex_call(lib, disc, **kw):
 ])
 def test_step_ex_validation(lib, disc, kw, code):
     assert step_ex_call(lib, disc, **kw) == code
+
+
+def bwd_call(lib, ws_bytes=None, **kw):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, sp=1, h0=None,
+             dy=FAKE, dlast=None, du=FAKE, dd=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dz=None,
+             dbias=None, dh0=None, ws=FAKE, batch=2, L=40, dim=20, N=16, dtype=0)
+    a.update(kw)
+    need = lib.ss_bwd_workspace_size(a["batch"], max(a["L"], 0), a["dim"], max(min(a["N"], 16), 1))
+    return lib.ss_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
+                      a["h0"], a["dy"], a["dlast"], a["du"], a["dd"], a["dA"], a["dB"], a["dC"], a["dD"],
+                      a["dz"], a["dbias"], a["dh0"], a["ws"], need if ws_bytes is None else ws_bytes,
+                      a["batch"], a["L"], a["dim"], a["N"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("arg", ["u", "delta", "A", "B", "C", "dy", "du", "dd", "dA", "dB", "dC"])
+def test_bwd_null_required_pointer(lib, arg):
+    assert bwd_call(lib, **{arg: None}) == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(z=FAKE), 1), (dict(batch=0), 2), (dict(L=-1), 2), (dict(N=17), 4), (dict(dtype=4), 3),
+    (dict(dy=FAKE + 2), 5), (dict(ws=FAKE + 1), 5), (dict(dz=FAKE + 2, z=FAKE), 5),
+    (dict(u=FAKE + 1, dtype=1), 5), (dict(ws=None), 8),
+])
+def test_bwd_validation(lib, kw, code):
+    assert bwd_call(lib, **kw) == code
+
+
+def test_bwd_workspace_too_small(lib):
+    need = lib.ss_bwd_workspace_size(2, 40, 20, 16)
+    assert need > 0
+    assert bwd_call(lib, ws_bytes=need - 4) == 8
+
+
+def test_bwd_workspace_size_formula(lib):
+    """Tile-start states (tiles of 32 tokens, channel groups of 16, 16 states), dB/dC partial
+    sums per channel group, and dA/dD/dbias partial sums per batch row."""
+    batch, L, dim, N = 3, 100, 40, 5
+    groups, tiles = 3, 4
+    floats = batch * tiles * groups * 16 * 16 + 2 * batch * groups * L * N + batch * groups * 16 * 18
+    assert lib.ss_bwd_workspace_size(batch, L, dim, N) == 4 * floats
+    assert lib.ss_bwd_workspace_size(0, L, dim, N) == 0
+    assert lib.ss_bwd_workspace_size(batch, L, dim, 17) == 0
