@@ -25,6 +25,7 @@ _lib = None
 
 F32 = 0
 BF16 = 1
+F64 = 2
 
 
 CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-std=c11", "-Wall",
@@ -59,6 +60,8 @@ def _bind(path):
     lib.ss_oracle_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                   vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   i64, i64, i64, i64, i32, vp, vp, i64, i32]
+    lib.ss_oracle_conv_silu.restype = i32
+    lib.ss_oracle_conv_silu.argtypes = [vp, vp, vp, vp, i64, vp, i64, i64, i64, i32, i32]
     lib.ss_oracle_max_threads.restype = i32
     lib.ss_oracle_max_threads.argtypes = []
     return lib
@@ -83,7 +86,10 @@ def _dtype_of(*arrays) -> int:
         return F32
     if kinds == {np.dtype(np.uint16)}:
         return BF16
-    raise TypeError(f"u, delta, z, B, C must all be float32 or all uint16 (bf16 bits), got {kinds}")
+    if kinds == {np.dtype(np.float64)}:
+        return F64
+    raise TypeError(f"u, delta, z, B, C must all be float32, all uint16 (bf16 bits) or all "
+                    f"float64, got {kinds}")
 
 
 def _ptr(a):
@@ -218,6 +224,48 @@ def bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True, h
     return out
 
 
+def conv_silu(x, conv_w, conv_b=None, conv_state=None, nthreads=0, _lib=None):
+    """The prologue u = silu(causal depthwise conv1d(x) + conv_b): x (batch, L, dim) float32,
+    uint16 (bf16 bits) or float64; conv_w (dim, K) float32; conv_b (dim,) float32 or None;
+    conv_state (batch, dim, K-1) float32 or None (the K-1 inputs before t = 0, oldest
+    first; zeros when None). Returns u (batch, L, dim) float64."""
+    x = _c(x)
+    conv_w, conv_b, conv_state = _c(conv_w, np.float32), _c(conv_b, np.float32), _c(conv_state, np.float32)
+    dt = _dtype_of(x)
+    batch, L, dim = x.shape
+    K = conv_w.shape[1]
+    if conv_w.shape != (dim, K) or (conv_b is not None and conv_b.shape != (dim,)):
+        raise ValueError("bad conv_w or conv_b shape")
+    if conv_state is not None and conv_state.shape != (batch, dim, K - 1):
+        raise ValueError("bad conv_state shape")
+    u = np.empty((batch, L, dim), np.float64)
+    rc = (_lib or _load()).ss_oracle_conv_silu(_ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), K,
+                                              _ptr(u), batch, L, dim, dt, int(nthreads))
+    if rc != 0:
+        raise ValueError("ss_oracle_conv_silu rejected its arguments")
+    return u
+
+
+def _widen(a):
+    """float32 / bf16-bit arrays to float64, exactly."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def fwd_conv(x, conv_w, delta, A, B, C, conv_b=None, conv_state=None, D=None, z=None,
+             delta_bias=None, softplus=True, h0=None, channels=None, nthreads=0, zoh=False, _lib=None):
+    """Forward with the conv prologue: u = conv_silu(x, ...) in fp64, then the scan of
+    ``fwd`` on that u (delta, B, C, z widened exactly to fp64). Returns (y, last_state, u)."""
+    u = conv_silu(x, conv_w, conv_b, conv_state, nthreads=nthreads, _lib=_lib)
+    y, st = fwd(u, _widen(_c(delta)), A, _widen(_c(B)), _widen(_c(C)), D=D, z=_widen(_c(z)),
+                delta_bias=delta_bias, softplus=softplus, h0=h0, channels=channels,
+                nthreads=nthreads, zoh=zoh, _lib=_lib)
+    return y, st, u
+
+
 class Library:
     """The oracle API bound to another build of the same C source (used by the tests that
     plant mistakes in a copy of the oracle and check that the pins catch them)."""
@@ -233,3 +281,9 @@ class Library:
 
     def bwd(self, *a, **k):
         return bwd(*a, _lib=self._h, **k)
+
+    def conv_silu(self, *a, **k):
+        return conv_silu(*a, _lib=self._h, **k)
+
+    def fwd_conv(self, *a, **k):
+        return fwd_conv(*a, _lib=self._h, **k)

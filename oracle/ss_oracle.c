@@ -38,6 +38,7 @@
  *  - A is a diagonal (dim, dstate) array; B and C carry no channel index.
  *
  * The backward (ss_oracle_bwd, below) is the chain rule of the same loop, run in reverse.
+ * ss_oracle_conv_silu is the causal-convolution + SiLU prologue that produces u from x.
  *
  * Arithmetic: every input is converted exactly to double (bf16 -> fp32 -> fp64 is
  * exact), all arithmetic is IEEE double with libm exp/expm1/log1p, compiled without fast
@@ -52,12 +53,19 @@
 #include <omp.h>
 #endif
 
-/* element types of u, delta, z, B and C */
+/* element types of u, delta, z, B and C (fp64 lets a caller feed values that are not
+   representable in fp32, e.g. the output of the conv prologue below) */
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_F64 2
+
+static int dtype_ok(int dtype) {
+  return dtype == ORACLE_F32 || dtype == ORACLE_BF16 || dtype == ORACLE_F64;
+}
 
 static double in_at(const void* p, int dtype, int64_t i) {
   if (dtype == ORACLE_F32) return (double)((const float*)p)[i];
+  if (dtype == ORACLE_F64) return ((const double*)p)[i];
   uint32_t w = (uint32_t)((const uint16_t*)p)[i] << 16; /* bf16 is the top half of an fp32 */
   float f;
   memcpy(&f, &w, sizeof f);
@@ -122,7 +130,7 @@ int ss_oracle_fwd(const void* u, const void* delta, const float* A, const void* 
                   const int64_t* chan_d, int64_t nchan, int nthreads) {
   if (!u || !delta || !A || !B || !C) return -1;
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || nchan < 0) return -1;
-  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (!dtype_ok(dtype)) return -1;
   if (nchan > 0 && (!chan_b || !chan_d)) return -1;
   const int64_t njobs = nchan > 0 ? nchan : batch * dim;
   int bad = 0;
@@ -168,7 +176,7 @@ int ss_oracle_step(double* state, const void* u, const void* delta, const float*
                    int64_t dstate, int dtype, int nthreads) {
   if (!state || !u || !delta || !A || !B || !C) return -1;
   if (batch < 0 || dim < 0 || dstate < 1) return -1;
-  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (!dtype_ok(dtype)) return -1;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -309,7 +317,7 @@ int ss_oracle_bwd(const void* u, const void* delta, const float* A, const void* 
   if (!u || !delta || !A || !B || !C || !dy) return -1;
   if (!du || !ddelta || !dA || !dB || !dC || !dD || !dbias || (z && !dz)) return -1;
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || nchan < 0) return -1;
-  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (!dtype_ok(dtype)) return -1;
   if (nchan > 0 && (!chan_b || !chan_d)) return -1;
   const int64_t bln = batch * seqlen * dstate;
   const int64_t njobs = nchan > 0 ? nchan : dim;
@@ -375,6 +383,47 @@ int ss_oracle_bwd(const void* u, const void* delta, const float* A, const void* 
   for (int k = 0; k < nth; ++k) free(part[k]);
   free(part);
   return bad ? -1 : 0;
+}
+
+/* ----------------------------------------------------------------------------------------
+ * Prologue: causal depthwise convolution over time, then SiLU, per channel
+ * ("Mamba：选择性状态空间的线性时间序列建模", section "架构：极简设计": in the SSM branch
+ * of the block the input passes a short causal convolution and a SiLU before the scan;
+ * "Mamba：选择性状态空间模型入门教程", section "Mamba 的关键创新：选择性机制", uses the
+ * same order).
+ *   pre[b,t,d] = conv_b[d] + sum_{m=0}^{K-1} conv_w[d,m] * x[b, t-(K-1)+m, d]
+ *   u[b,t,d]   = silu(pre[b,t,d])
+ * x before t = 0 is conv_state[b,d,j] for t-(K-1)+m = j-(K-1) (the K-1 inputs preceding
+ * the sequence, oldest first), or 0 when conv_state is NULL. conv_b may be NULL (0).
+ * x is u_dtype (f32 / bf16 / f64); conv_w, conv_b and conv_state are fp32; u is fp64
+ * (batch, seqlen, dim). Returns 0, or -1 on a bad argument.
+ */
+int ss_oracle_conv_silu(const void* x, const float* conv_w, const float* conv_b,
+                        const float* conv_state, int64_t kconv, double* u, int64_t batch,
+                        int64_t seqlen, int64_t dim, int dtype, int nthreads) {
+  if (!x || !conv_w || !u || kconv < 1 || batch < 0 || seqlen < 0 || dim < 0) return -1;
+  if (!dtype_ok(dtype)) return -1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < batch * dim; ++j) {
+    const int64_t b = j / dim, d = j % dim;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      double pre = conv_b ? (double)conv_b[d] : 0.0;
+      for (int64_t m = 0; m < kconv; ++m) {
+        const int64_t tau = t - (kconv - 1) + m;
+        double xv;
+        if (tau >= 0) xv = in_at(x, dtype, (b * seqlen + tau) * dim + d);
+        else xv = conv_state ? (double)conv_state[(b * dim + d) * (kconv - 1) + (kconv - 1) + tau] : 0.0;
+        pre += (double)conv_w[d * kconv + m] * xv;
+      }
+      u[(b * seqlen + t) * dim + d] = silu(pre);
+    }
+  }
+  return 0;
 }
 
 int ss_oracle_max_threads(void) {

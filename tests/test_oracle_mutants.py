@@ -8,6 +8,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_bwd_pins as bpins
+from tests import test_oracle_conv_pins as cpins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ss_oracle.c")
@@ -56,6 +57,16 @@ MUTANTS = [
     ("bwd_du_without_D", [("double du_t = ds * D_d;", "double du_t = 0.0;")]),
     ("bwd_decay_grad_uses_current_state", [("const double g_abar = lam * hp[n];", "const double g_abar = lam * ht[n];")]),
     ("bwd_gate_not_applied", [("      ds = dyv * silu(zv);\n", "      ds = dyv;\n")]),
+    # conv prologue
+    ("conv_filter_not_flipped", [("pre += (double)conv_w[d * kconv + m] * xv;",
+                                  "pre += (double)conv_w[d * kconv + (kconv - 1 - m)] * xv;")]),
+    ("conv_no_bias", [("double pre = conv_b ? (double)conv_b[d] : 0.0;", "double pre = 0.0;")]),
+    ("conv_no_silu", [("u[(b * seqlen + t) * dim + d] = silu(pre);", "u[(b * seqlen + t) * dim + d] = pre;")]),
+    ("conv_state_ignored", [("else xv = conv_state ? (double)conv_state[(b * dim + d) * (kconv - 1) + (kconv - 1) + tau] : 0.0;",
+                             "else xv = 0.0;")]),
+    ("conv_state_reversed", [("(double)conv_state[(b * dim + d) * (kconv - 1) + (kconv - 1) + tau]",
+                              "(double)conv_state[(b * dim + d) * (kconv - 1) - 1 - tau]")]),
+    ("conv_acausal", [("const int64_t tau = t - (kconv - 1) + m;", "const int64_t tau = t + m;")]),
 ]
 
 
@@ -83,6 +94,9 @@ def pin_suite(lib):
         ("bwd_adjoint_h0", lambda: bpins.test_adjoint_identity_for_linear_arguments(lib, "h0")),
         ("bwd_lti", lambda: bpins.test_lti_du_is_correlation_with_kernel(lib)),
         ("bwd_zero_step", lambda: bpins.test_zero_step_closed_forms(lib)),
+        ("conv_numpy", lambda: cpins.test_conv_matches_numpy_convolve(lib, 4, True, True)),
+        ("conv_impulse", lambda: cpins.test_impulse_response(lib)),
+        ("conv_split", lambda: cpins.test_split_continues_with_conv_state(lib)),
     ]
     for name, fn in checks:
         try:
