@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 3
+#define SS_ABI_VERSION 4
 #define SS_MAX_DSTATE 16
 
 typedef enum {
@@ -122,6 +122,27 @@ int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, c
               const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
               float* last_state, const float* h0, int64_t batch, int64_t seqlen, int64_t dim,
               int64_t dstate, int in_dtype, const ss_fwd_options* opt, void* stream);
+
+/*
+ * ss_fwd_conv -- ss_fwd_ex with the block's prologue fused into the scan: the scan's input
+ * u is computed from x as silu(causal depthwise conv1d(x) + conv_b), the short causal
+ * convolution and SiLU that precede the SSM in the Mamba block ("Mamba：选择性状态空间的
+ * 线性时间序列建模", section "架构：极简设计"):
+ *   u[b,t,d] = silu(conv_b[d] + sum_{m=0}^{kconv-1} conv_w[d,m] * x[b, t-(kconv-1)+m, d])
+ * and y = (C h + D u) silu(z) uses that u. u never has to be written unless asked for.
+ *   x             (batch, seqlen, dim)       in_dtype, in place of ss_fwd's u.
+ *   conv_w        (dim, kconv) fp32; kconv in 1..4 (else SS_ERR_BAD_SHAPE).
+ *   conv_b        (dim) fp32, may be NULL (zero).
+ *   conv_state    (batch, dim, kconv - 1) fp32, may be NULL (zeros): the kconv - 1 inputs x
+ *                 before t = 0, oldest first (the last inputs of a previous call continue it).
+ *   u_out         (batch, seqlen, dim) fp32, may be NULL: receives u (for a backward pass).
+ * Everything else (delta .. h0, opt, errors) as in ss_fwd_ex.
+ */
+int ss_fwd_conv(const void* x, const float* conv_w, const float* conv_b, const float* conv_state,
+                int64_t kconv, const void* delta, const float* A, const void* B, const void* C,
+                const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
+                float* last_state, const float* h0, float* u_out, int64_t batch, int64_t seqlen,
+                int64_t dim, int64_t dstate, int in_dtype, const ss_fwd_options* opt, void* stream);
 
 /*
  * ss_step -- one decode step: the same update for a single token, with the state

@@ -2,9 +2,11 @@
 
 Every step of the scan runs in the HIP kernels of ``libss.so``; this package only
 marshals torch device tensors into the C ABI declared in ``include/ss.h``
-(``ss_fwd``, ``ss_step``, ``ss_bwd``). The library is loaded on first use and a missing or
+(``ss_fwd``, ``ss_fwd_conv``, ``ss_step``, ``ss_bwd``). The library is loaded on first use and a missing or
 unloadable build raises: there is no fallback path.
 """
-from ._binding import SSError, bwd, bwd_workspace_size, fwd, lib_path, load_library, step  # noqa: F401
+from ._binding import (SSError, bwd, bwd_workspace_size, fwd, fwd_conv, lib_path,  # noqa: F401
+                       load_library, step)
 
-__all__ = ["fwd", "step", "bwd", "bwd_workspace_size", "SSError", "load_library", "lib_path"]
+__all__ = ["fwd", "fwd_conv", "step", "bwd", "bwd_workspace_size", "SSError", "load_library",
+           "lib_path"]

@@ -12,9 +12,9 @@ _lib = None
 
 F32, BF16 = 0, 1
 DISC_DT, DISC_ZOH = 0, 1
-ABI_VERSION = 3
-EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_step", "ss_step_ex",
-           "ss_bwd_workspace_size", "ss_bwd")
+ABI_VERSION = 4
+EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_fwd_conv", "ss_step",
+           "ss_step_ex", "ss_bwd_workspace_size", "ss_bwd")
 
 
 class FwdOptions(ctypes.Structure):
@@ -52,6 +52,9 @@ def load_library():
     lib.ss_fwd_ex.restype = i32
     lib.ss_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i32,
                               ctypes.POINTER(FwdOptions), vp]
+    lib.ss_fwd_conv.restype = i32
+    lib.ss_fwd_conv.argtypes = [vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                                i64, i64, i64, i64, i32, ctypes.POINTER(FwdOptions), vp]
     lib.ss_step.restype = i32
     lib.ss_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, vp]
     lib.ss_step_ex.restype = i32
@@ -143,6 +146,55 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=Non
     if rc != 0:
         raise SSError(rc, "ss_fwd")
     return (y, last_state) if return_last_state else y
+
+
+def fwd_conv(x, conv_w, delta, A, B, C, conv_b=None, conv_state=None, D=None, z=None,
+             delta_bias=None, softplus=True, y=None, last_state=None, h0=None, u_out=None,
+             stream=None, kernel=0, chunk_len=0, zoh=False):
+    """Forward with the fused prologue (``ss_fwd_conv``): u = silu(causal depthwise
+    conv1d(x) + conv_b), then the scan of ``fwd`` on it. x: (batch, L, dim); conv_w
+    (dim, K) fp32, K <= 4; conv_b (dim,) fp32 or None; conv_state (batch, dim, K-1) fp32 or
+    None (the K-1 inputs before the sequence, oldest first). u_out: None, True (allocate),
+    or an fp32 (batch, L, dim) tensor that receives u. Returns (y, last_state) or, with
+    u_out, (y, last_state, u)."""
+    dev = x.device
+    batch, L, dim = x.shape
+    N = A.shape[1]
+    K = conv_w.shape[1] if conv_w.dim() == 2 else 0
+    dt = _in_dtype(x, delta, B, C, z)
+    _check(x, "x", dev)
+    _check(conv_w, "conv_w", dev, torch.float32, (dim, K))
+    _check(conv_b, "conv_b", dev, torch.float32, (dim,))
+    _check(conv_state, "conv_state", dev, torch.float32, (batch, dim, K - 1))
+    _check(delta, "delta", dev, shape=x.shape)
+    _check(z, "z", dev, shape=x.shape)
+    _check(B, "B", dev, shape=(batch, L, N))
+    _check(C, "C", dev, shape=(batch, L, N))
+    _check(A, "A", dev, torch.float32, (dim, N))
+    _check(D, "D", dev, torch.float32, (dim,))
+    _check(delta_bias, "delta_bias", dev, torch.float32, (dim,))
+    _check(h0, "h0", dev, torch.float32, (batch, dim, N))
+    f = dict(dtype=torch.float32, device=dev)
+    if y is None:
+        y = torch.empty((batch, L, dim), **f)
+    _check(y, "y", dev, torch.float32, (batch, L, dim))
+    if last_state is None:
+        last_state = torch.empty((batch, dim, N), **f)
+    _check(last_state, "last_state", dev, torch.float32, (batch, dim, N))
+    want_u = u_out is not None and u_out is not False
+    if u_out is True:
+        u_out = torch.empty((batch, L, dim), **f)
+    if not want_u:
+        u_out = None
+    _check(u_out, "u_out", dev, torch.float32, (batch, L, dim))
+    opt = FwdOptions(int(kernel), int(chunk_len), DISC_ZOH if zoh else DISC_DT)
+    rc = load_library().ss_fwd_conv(_ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), K, _ptr(delta),
+                                    _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                    int(bool(softplus)), _ptr(y), _ptr(last_state), _ptr(h0), _ptr(u_out),
+                                    batch, L, dim, N, dt, ctypes.byref(opt), _stream(dev, stream))
+    if rc != 0:
+        raise SSError(rc, "ss_fwd_conv")
+    return (y, last_state, u_out) if want_u else (y, last_state)
 
 
 def step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=None,

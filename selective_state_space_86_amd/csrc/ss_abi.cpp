@@ -52,6 +52,64 @@ bool product_ok(int64_t a, int64_t b, int64_t c) {
 
 }  // namespace
 
+namespace {
+
+struct ConvArgs {
+  int64_t kconv;
+  const float* conv_w;
+  const float* conv_b;
+  const float* conv_state;
+  float* u_out;
+};
+
+int fwd_common(const void* u, const void* delta, const float* A, const void* B, const void* C,
+               const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
+               float* last_state, const float* h0, int64_t batch, int64_t seqlen, int64_t dim,
+               int64_t dstate, int in_dtype, const ss_fwd_options* opt, const ConvArgs& cv,
+               void* stream) {
+  // with seqlen == 0 no token is read or written: the per-token arrays may be NULL
+  if (!A || (seqlen != 0 && (!u || !delta || !B || !C || !y))) return SS_ERR_NULL_ARG;
+  if (in_dtype != SS_DTYPE_F32 && in_dtype != SS_DTYPE_BF16) return SS_ERR_BAD_DTYPE;
+  if (batch < 1 || dim < 1 || dstate < 1 || seqlen < 0) return SS_ERR_BAD_SHAPE;
+  if (dstate > SS_MAX_DSTATE) return SS_ERR_UNSUPPORTED_N;
+  if (!product_ok(batch, seqlen, dim) || !product_ok(batch, seqlen, dstate) ||
+      !product_ok(batch, dim, dstate))
+    return SS_ERR_BAD_SHAPE;
+  if (batch * ((dim + 15) / 16) > 0x7fffffffLL) return SS_ERR_BAD_SHAPE;
+  const int kernel = opt ? opt->kernel : 0;
+  const int chunk = opt ? opt->chunk_len : 0;
+  const int disc = opt ? opt->discretization : SS_DISC_DT;
+  if (kernel < 0 || kernel > 2 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
+  if (disc != SS_DISC_DT && disc != SS_DISC_ZOH) return SS_ERR_BAD_SHAPE;
+  if (kernel == 2 && dstate != 16) return SS_ERR_UNSUPPORTED_N;
+  const size_t es = elem_size(in_dtype);
+  if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
+      (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+      (delta_bias && !aligned(delta_bias, 4)) || !aligned(y, 4) ||
+      (last_state && !aligned(last_state, 4)) || (h0 && !aligned(h0, 4)) || !aligned(cv.conv_w, 4) ||
+      (cv.conv_b && !aligned(cv.conv_b, 4)) || (cv.conv_state && !aligned(cv.conv_state, 4)) ||
+      (cv.u_out && !aligned(cv.u_out, 4)))
+    return SS_ERR_MISALIGNED;
+  int cus = 0;
+  const int dv = check_device(&cus);
+  if (dv != SS_OK) return dv;
+
+  ss::FwdArgs a{u, delta, A, B, C, D, z, delta_bias, y, last_state,
+                batch, seqlen, dim, dstate, in_dtype, softplus_flag ? 1 : 0, h0,
+                disc == SS_DISC_ZOH ? 1 : 0, static_cast<int>(cv.kconv), cv.conv_w, cv.conv_b,
+                cv.conv_state, cv.u_out};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const bool chunked = kernel == 2 || (kernel == 0 && ss::fwd_chunked_supported(a));
+  if (chunked && seqlen > 0)
+    e = ss::fwd_chunked(a, chunk == 0 ? ss::fwd_chunked_pick(a, cus) : chunk, s);
+  else
+    e = ss::fwd_seq(a, s);
+  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 int ss_abi_version(void) { return SS_ABI_VERSION; }
@@ -75,42 +133,19 @@ int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, c
               const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
               float* last_state, const float* h0, int64_t batch, int64_t seqlen, int64_t dim,
               int64_t dstate, int in_dtype, const ss_fwd_options* opt, void* stream) {
-  // with seqlen == 0 no token is read or written: the per-token arrays may be NULL
-  if (!A || (seqlen != 0 && (!u || !delta || !B || !C || !y))) return SS_ERR_NULL_ARG;
-  if (in_dtype != SS_DTYPE_F32 && in_dtype != SS_DTYPE_BF16) return SS_ERR_BAD_DTYPE;
-  if (batch < 1 || dim < 1 || dstate < 1 || seqlen < 0) return SS_ERR_BAD_SHAPE;
-  if (dstate > SS_MAX_DSTATE) return SS_ERR_UNSUPPORTED_N;
-  if (!product_ok(batch, seqlen, dim) || !product_ok(batch, seqlen, dstate) ||
-      !product_ok(batch, dim, dstate))
-    return SS_ERR_BAD_SHAPE;
-  if (batch * ((dim + 15) / 16) > 0x7fffffffLL) return SS_ERR_BAD_SHAPE;
-  const int kernel = opt ? opt->kernel : 0;
-  const int chunk = opt ? opt->chunk_len : 0;
-  const int disc = opt ? opt->discretization : SS_DISC_DT;
-  if (kernel < 0 || kernel > 2 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
-  if (disc != SS_DISC_DT && disc != SS_DISC_ZOH) return SS_ERR_BAD_SHAPE;
-  if (kernel == 2 && dstate != 16) return SS_ERR_UNSUPPORTED_N;
-  const size_t es = elem_size(in_dtype);
-  if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
-      (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
-      (delta_bias && !aligned(delta_bias, 4)) || !aligned(y, 4) ||
-      (last_state && !aligned(last_state, 4)) || (h0 && !aligned(h0, 4)))
-    return SS_ERR_MISALIGNED;
-  int cus = 0;
-  const int dv = check_device(&cus);
-  if (dv != SS_OK) return dv;
+  return fwd_common(u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state, h0, batch, seqlen,
+                    dim, dstate, in_dtype, opt, ConvArgs{0, nullptr, nullptr, nullptr, nullptr}, stream);
+}
 
-  ss::FwdArgs a{u, delta, A, B, C, D, z, delta_bias, y, last_state,
-                batch, seqlen, dim, dstate, in_dtype, softplus_flag ? 1 : 0, h0,
-                disc == SS_DISC_ZOH ? 1 : 0};
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  const bool chunked = kernel == 2 || (kernel == 0 && ss::fwd_chunked_supported(a));
-  if (chunked && seqlen > 0)
-    e = ss::fwd_chunked(a, chunk == 0 ? ss::fwd_chunked_pick(a, cus) : chunk, s);
-  else
-    e = ss::fwd_seq(a, s);
-  return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+int ss_fwd_conv(const void* x, const float* conv_w, const float* conv_b, const float* conv_state,
+                int64_t kconv, const void* delta, const float* A, const void* B, const void* C,
+                const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
+                float* last_state, const float* h0, float* u_out, int64_t batch, int64_t seqlen,
+                int64_t dim, int64_t dstate, int in_dtype, const ss_fwd_options* opt, void* stream) {
+  if (!conv_w) return SS_ERR_NULL_ARG;
+  if (kconv < 1 || kconv > 4) return SS_ERR_BAD_SHAPE;
+  return fwd_common(x, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state, h0, batch, seqlen,
+                    dim, dstate, in_dtype, opt, ConvArgs{kconv, conv_w, conv_b, conv_state, u_out}, stream);
 }
 
 int ss_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,

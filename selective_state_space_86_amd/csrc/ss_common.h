@@ -55,4 +55,37 @@ __device__ __forceinline__ float zoh_coef(float dt, float x, float ab, float inv
 // For z < -88, e^-z = inf and the result is z * 0 = -0, the correct limit.
 __device__ __forceinline__ float silu(float z) { return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e)); }
 
+// Causal depthwise convolution + SiLU of the conv prologue for token t of one channel:
+// silu(cb + w4[0] x_{t-3} + w4[1] x_{t-2} + w4[2] x_{t-1} + w4[3] x_t), the taps of a
+// shorter filter right-aligned in w4 (zeros in front).
+__device__ __forceinline__ float conv4_silu(const float (&w4)[4], float cb, float xm3, float xm2, float xm1,
+                                            float x0) {
+  float p = __builtin_fmaf(w4[0], xm3, cb);
+  p = __builtin_fmaf(w4[1], xm2, p);
+  p = __builtin_fmaf(w4[2], xm1, p);
+  p = __builtin_fmaf(w4[3], x0, p);
+  return silu(p);
+}
+
+// The four right-aligned taps of channel d's filter (kconv <= 4 taps) and its bias.
+__device__ __forceinline__ void conv_taps(const float* conv_w, const float* conv_b, int kconv, int64_t d,
+                                          float (&w4)[4], float& cb) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int tap = m - (4 - kconv);
+    w4[m] = tap >= 0 ? conv_w[d * kconv + tap] : 0.0f;
+  }
+  cb = conv_b ? conv_b[d] : 0.0f;
+}
+
+// Input x at token tau of channel (b, d) for the conv window: the sequence for tau >= 0,
+// the conv state (the kconv - 1 inputs before the sequence, oldest first) or 0 before it.
+template <typename T>
+__device__ __forceinline__ float conv_input(const T* x, const float* conv_state, int kconv, int64_t b,
+                                            int64_t d, int64_t tau, int64_t seqlen, int64_t dim) {
+  if (tau >= 0) return load_elem(x, (b * seqlen + tau) * dim + d);
+  const int64_t j = (kconv - 1) + tau;
+  return (conv_state && j >= 0) ? conv_state[(b * dim + d) * (kconv - 1) + j] : 0.0f;
+}
+
 }  // namespace ss

@@ -26,7 +26,9 @@
 //    then the gate, and one store per token. The (L x N) state never reaches memory.
 // Per state update the local pass issues 4 VALU ops and one v_exp_f32, the fix-up 2 VALU.
 // With the exact zero-order-hold input term (ZOH) the local pass also evaluates
-// (abar - 1)/A per update (zoh_coef); the combine and the fix-up do not change.
+// (abar - 1)/A per update (zoh_coef); the combine and the fix-up do not change. With the
+// conv prologue (CONV) the u operand is x and each lane first forms
+// u_t = silu(conv_b + conv_w * x_{t-3..t}) from its chunk's inputs and the 3 before them.
 //
 // Memory access: every lane has a fixed 32-bit byte offset into a tile (its chunk row and
 // channel); the tile origin and the token step within the chunk live in SGPR base pointers,
@@ -44,7 +46,7 @@ constexpr int kLdsChunkStride = 16 * 16 + 16;  // [chunk][n][lane], padded again
 
 // Register budget: TC = 4 must fit 3 workgroups (12 waves) per CU, TC = 8 two; the
 // zero-order-hold variant holds 16 more values (1/A) and runs two per CU.
-template <typename T, bool GATE, int TC, bool EARLY, bool ZOH>
+template <typename T, bool GATE, int TC, bool EARLY, bool ZOH, bool CONV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TC <= 4 && !ZOH ? 3 : 2)))
 void fwd_chunked_kernel(FwdArgs a) {
   // The prod-abar/carry array alternates between two buffers by tile, so a tile's
@@ -75,6 +77,8 @@ void fwd_chunked_kernel(FwdArgs a) {
   }
   const float bias = a.delta_bias ? a.delta_bias[cc] : 0.0f;
   const float Dd = a.D ? a.D[cc] : 0.0f;
+  float w4[4], cb = 0.0f;
+  if (CONV) conv_taps(a.conv_w, a.conv_b, a.kconv, cc, w4, cb);
   // state n = k of channel c0+i, carried across tiles; starts at h0 when one is given
   float carry = a.h0 ? a.h0[(b * a.dim + cc) * 16 + k] : 0.0f;
   const uint32_t y_row = static_cast<uint32_t>(a.dim * 4);
@@ -94,6 +98,23 @@ void fwd_chunked_kernel(FwdArgs a) {
 #pragma unroll
     for (int n = 0; n < 16; ++n) h[n] = 0.0f;
     float dsum = 0.0f;
+    if (CONV) {  // u = silu(conv(x)) over the window [3 inputs before the chunk, x_0 .. x_{TC-1}]
+      // (the 3 earlier inputs are the end of the previous chunk: cache hits, loaded here
+      // rather than prefetched to keep registers for the 16 states)
+      float win[TC + 3];
+#pragma unroll
+      for (int m = 0; m < 3; ++m)
+        win[m] = conv_input(static_cast<const T*>(a.u), a.conv_state, a.kconv, b, cc,
+                            min(t0 + k * TC - 3 + m, L - 1), L, a.dim);
+#pragma unroll
+      for (int j = 0; j < TC; ++j) win[j + 3] = cur.uu[j];
+#pragma unroll
+      for (int j = 0; j < TC; ++j) {
+        cur.uu[j] = conv4_silu(w4, cb, win[j], win[j + 1], win[j + 2], win[j + 3]);
+        const bool ok = full ? cvalid : (cvalid && t0 + k * TC + j < L);
+        if (a.u_out && ok) a.u_out[(b * L + t0 + k * TC + j) * a.dim + c] = cur.uu[j];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
       const float x = cur.raw[j] + bias;
@@ -172,14 +193,22 @@ void fwd_chunked_kernel(FwdArgs a) {
   if (a.last_state && cvalid) a.last_state[(b * a.dim + c) * 16 + k] = carry;
 }
 
-template <typename T, bool GATE, int TC>
-hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
+template <typename T, bool GATE, int TC, bool ZOH>
+void launch_chunked_c(const FwdArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.batch * ((a.dim + 15) / 16)));
   constexpr bool early = TC <= 4 && !GATE;
-  if (a.zoh)
-    hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, true>), grid, dim3(256), 0, s, a);
+  if (a.kconv > 0)
+    hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, ZOH, true>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, ZOH, false>), grid, dim3(256), 0, s, a);
+}
+
+template <typename T, bool GATE, int TC>
+hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
+  if (a.zoh)
+    launch_chunked_c<T, GATE, TC, true>(a, s);
+  else
+    launch_chunked_c<T, GATE, TC, false>(a, s);
   return hipGetLastError();
 }
 

@@ -11,13 +11,14 @@
 // consecutive elements. The expanded (L x N) state lives only in registers.
 // This kernel is the simple, always-applicable path (any dim, any dstate <= 16, ragged
 // channel tails); the tiled kernel covers the common shapes faster. The state starts at
-// h0 when one is given, else at zero.
+// h0 when one is given, else at zero. With the conv prologue (CONV) u_t is
+// silu(conv_b + conv_w * x) over a sliding window of the last 4 inputs kept in registers.
 #include "ss_common.h"
 #include "ss_kernels.h"
 
 namespace ss {
 
-template <int NS, typename T, bool GATE, bool ZOH>
+template <int NS, typename T, bool GATE, bool ZOH, bool CONV>
 __global__ __launch_bounds__(64) void fwd_seq_kernel(FwdArgs a) {
   const int64_t nblk_d = (a.dim + 63) / 64;
   const int64_t b = blockIdx.x / nblk_d;
@@ -40,13 +41,28 @@ __global__ __launch_bounds__(64) void fwd_seq_kernel(FwdArgs a) {
   }
   const float bias = a.delta_bias ? a.delta_bias[dd] : 0.0f;
   const float Dd = a.D ? a.D[dd] : 0.0f;
+  float w4[4], cb = 0.0f, xw0 = 0.0f, xw1 = 0.0f, xw2 = 0.0f;  // conv taps and window
+  if (CONV) {
+    conv_taps(a.conv_w, a.conv_b, a.kconv, dd, w4, cb);
+    xw0 = conv_input(u, a.conv_state, a.kconv, b, dd, -3, a.seqlen, a.dim);
+    xw1 = conv_input(u, a.conv_state, a.kconv, b, dd, -2, a.seqlen, a.dim);
+    xw2 = conv_input(u, a.conv_state, a.kconv, b, dd, -1, a.seqlen, a.dim);
+  }
 
   for (int64_t t = 0; t < a.seqlen; ++t) {
     const int64_t e = (b * a.seqlen + t) * a.dim + dd;
     const int64_t r = (b * a.seqlen + t) * ns;
     const float x = load_elem(dl, e) + bias;
     const float dt = a.softplus ? softplus(x) : x;
-    const float uv = load_elem(u, e);
+    float uv = load_elem(u, e);
+    if (CONV) {
+      const float xt = uv;
+      uv = conv4_silu(w4, cb, xw0, xw1, xw2, xt);
+      xw0 = xw1;
+      xw1 = xw2;
+      xw2 = xt;
+      if (a.u_out && active) a.u_out[e] = uv;
+    }
     const float du = dt * uv;
     float acc = 0.0f;
 #pragma unroll
@@ -70,15 +86,21 @@ __global__ __launch_bounds__(64) void fwd_seq_kernel(FwdArgs a) {
   }
 }
 
+template <int NS, typename T, bool GATE, bool ZOH>
+static void launch_seq_c(const FwdArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.batch * ((a.dim + 63) / 64)));
+  if (a.kconv > 0)
+    hipLaunchKernelGGL((fwd_seq_kernel<NS, T, GATE, ZOH, true>), grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_seq_kernel<NS, T, GATE, ZOH, false>), grid, dim3(64), 0, s, a);
+}
+
 template <int NS, typename T, bool GATE>
 static hipError_t launch_seq(const FwdArgs& a, hipStream_t s) {
-  const int64_t nblk = a.batch * ((a.dim + 63) / 64);
   if (a.zoh)
-    hipLaunchKernelGGL((fwd_seq_kernel<NS, T, GATE, true>), dim3(static_cast<unsigned>(nblk)), dim3(64),
-                       0, s, a);
+    launch_seq_c<NS, T, GATE, true>(a, s);
   else
-    hipLaunchKernelGGL((fwd_seq_kernel<NS, T, GATE, false>), dim3(static_cast<unsigned>(nblk)), dim3(64),
-                       0, s, a);
+    launch_seq_c<NS, T, GATE, false>(a, s);
   return hipGetLastError();
 }
 

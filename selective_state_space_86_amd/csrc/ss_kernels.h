@@ -26,6 +26,12 @@ struct FwdArgs {
   int softplus;
   const float* h0;          // may be null: zero initial state
   int zoh;                  // input term: 0 dt*B, 1 exact zero-order hold (e^{dt A} - 1)/A * B
+  // conv prologue (kconv > 0): u is x, and the scan uses silu(conv_b + conv_w * x) instead
+  int kconv;                // 0 (no prologue) or 1..4 taps
+  const float* conv_w;      // (dim, kconv)
+  const float* conv_b;      // (dim), may be null
+  const float* conv_state;  // (batch, dim, kconv - 1) inputs before t = 0, may be null
+  float* u_out;             // (batch, seqlen, dim) the prologue output, may be null
 };
 
 // Validated arguments of one ss_step call.

@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss_abi_version() == _binding.ABI_VERSION == 3
+    assert lib.ss_abi_version() == _binding.ABI_VERSION == 4
     for s in range(0, 9):
         assert lib.ss_status_string(s)
     assert b"unknown" in lib.ss_status_string(99)
@@ -182,3 +182,21 @@ def test_bwd_workspace_size_formula(lib):
     assert lib.ss_bwd_workspace_size(batch, L, dim, N) == 4 * floats
     assert lib.ss_bwd_workspace_size(0, L, dim, N) == 0
     assert lib.ss_bwd_workspace_size(batch, L, dim, 17) == 0
+
+
+def conv_call(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, cb=None, cs=None, K=4, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None,
+             bias=None, sp=1, y=FAKE, st=None, h0=None, uo=None, batch=1, L=8, dim=16, N=16, dtype=0)
+    a.update(kw)
+    opt = _binding.FwdOptions(0, 0, 0)
+    return lib.ss_fwd_conv(a["x"], a["w"], a["cb"], a["cs"], a["K"], a["delta"], a["A"], a["B"], a["C"],
+                           a["D"], a["z"], a["bias"], a["sp"], a["y"], a["st"], a["h0"], a["uo"], a["batch"],
+                           a["L"], a["dim"], a["N"], a["dtype"], ctypes.byref(opt), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=None), 1), (dict(x=None), 1), (dict(K=0), 2), (dict(K=5), 2), (dict(w=FAKE + 2), 5),
+    (dict(cs=FAKE + 1), 5), (dict(uo=FAKE + 2), 5), (dict(cb=FAKE + 3), 5), (dict(N=17), 4),
+])
+def test_fwd_conv_validation(lib, kw, code):
+    assert conv_call(lib, **kw) == code
