@@ -102,7 +102,10 @@ int ss_fwd(const void* u, const void* delta, const float* A, const void* B, cons
  * behaviour. kernel and chunk_len are for tuning and testing. */
 typedef struct {
   int kernel;         /* 0: automatic; 1: one lane per channel, sequential in t (any dstate);
-                         2: time-chunked (dstate == 16 only, else SS_ERR_UNSUPPORTED_N) */
+                         2: time-chunked (dstate == 16 only, else SS_ERR_UNSUPPORTED_N);
+                         3: one lane per (channel, state), sequential in t (default input
+                            term, no conv prologue, else SS_ERR_BAD_SHAPE); automatic picks
+                            2 for dstate == 16, else 3 when it applies, else 1 */
   int chunk_len;      /* tokens per lane and tile for kernel 2: 0 (automatic), 4 or 8 */
   int discretization; /* an ss_discretization value */
 } ss_fwd_options;

@@ -79,7 +79,7 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
   const int kernel = opt ? opt->kernel : 0;
   const int chunk = opt ? opt->chunk_len : 0;
   const int disc = opt ? opt->discretization : SS_DISC_DT;
-  if (kernel < 0 || kernel > 2 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
+  if (kernel < 0 || kernel > 3 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
   if (disc != SS_DISC_DT && disc != SS_DISC_ZOH) return SS_ERR_BAD_SHAPE;
   if (kernel == 2 && dstate != 16) return SS_ERR_UNSUPPORTED_N;
   const size_t es = elem_size(in_dtype);
@@ -100,9 +100,16 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
                 cv.conv_state, cv.u_out};
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (kernel == 3 && seqlen > 0) {
+    if (!ss::fwd_state_supported(a)) return SS_ERR_BAD_SHAPE;
+    const hipError_t es = ss::fwd_state(a, s);
+    return es == hipSuccess ? SS_OK : SS_ERR_HIP;
+  }
   const bool chunked = kernel == 2 || (kernel == 0 && ss::fwd_chunked_supported(a));
   if (chunked && seqlen > 0)
     e = ss::fwd_chunked(a, chunk == 0 ? ss::fwd_chunked_pick(a, cus) : chunk, s);
+  else if (kernel == 0 && ss::fwd_state_supported(a))
+    e = ss::fwd_state(a, s);  // dstate != 16
   else
     e = ss::fwd_seq(a, s);
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;

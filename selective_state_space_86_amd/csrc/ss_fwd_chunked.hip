@@ -222,17 +222,15 @@ hipError_t launch_chunked_g(const FwdArgs& a, hipStream_t s) {
 bool fwd_chunked_supported(const FwdArgs& a) { return a.dstate == 16 && a.seqlen > 0; }
 
 // Chunk length: 8 halves the per-tile combine cost but needs ~2x the registers of 4
-// (2 resident workgroups per CU instead of 3). Pick the one whose workgroup count fills
-// the resident slots of every CU most evenly.
+// (2 resident workgroups per CU instead of 3). Measured on the 130M (768 groups), 1.4B
+// (1024) and 3B-long (320) shapes, 4 is faster whenever the groups fill more than two
+// slots per CU (the extra resident wave per SIMD hides more latency; a partly filled last
+// round costs less than that, since CUs with fewer workgroups run each one faster), and 8
+// when every group fits at two per CU.
 int fwd_chunked_pick(const FwdArgs& a, int cus) {
   if (a.zoh) return 4;  // the zero-order-hold variant spills registers at 8
   const int64_t groups = a.batch * ((a.dim + 15) / 16);
-  auto eff = [&](int slots) {
-    const int64_t cap = static_cast<int64_t>(cus) * slots;
-    const int64_t rounds = (groups + cap - 1) / cap;
-    return static_cast<double>(groups) / static_cast<double>(rounds * cap);
-  };
-  return eff(3) > eff(2) + 1e-9 ? 4 : 8;
+  return groups <= 2 * static_cast<int64_t>(cus) ? 8 : 4;
 }
 
 hipError_t fwd_chunked(const FwdArgs& a, int chunk_len, hipStream_t s) {

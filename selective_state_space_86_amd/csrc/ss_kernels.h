@@ -89,6 +89,8 @@ struct BwdArgs {
 constexpr int kBwdChunk = 2;  // tokens per lane and chunk in the backward kernels
 
 hipError_t fwd_seq(const FwdArgs& a, hipStream_t s);
+bool fwd_state_supported(const FwdArgs& a);
+hipError_t fwd_state(const FwdArgs& a, hipStream_t s);
 bool fwd_chunked_supported(const FwdArgs& a);
 hipError_t fwd_chunked(const FwdArgs& a, int chunk_len, hipStream_t s);
 int fwd_chunked_pick(const FwdArgs& a, int cus);

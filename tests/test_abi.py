@@ -110,7 +110,7 @@ def fwd_ex_call(lib, kernel, chunk, disc=0, **kw):
 
 
 @pytest.mark.parametrize("kernel,chunk,kw,code", [
-    (3, 0, {}, 2), (-1, 0, {}, 2), (2, 5, {}, 2), (0, 16, {}, 2), (2, 0, dict(N=8), 4),
+    (4, 0, {}, 2), (-1, 0, {}, 2), (3, 0, dict(N=17), 4), (2, 5, {}, 2), (0, 16, {}, 2), (2, 0, dict(N=8), 4),
     (2, 4, dict(u=None), 1), (1, 0, dict(N=17), 4), (2, 8, dict(dtype=7), 3),
     (0, 0, dict(h0=FAKE + 2), 5), (1, 0, dict(h0=FAKE + 1, L=0), 5),
 ])

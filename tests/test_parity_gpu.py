@@ -161,7 +161,7 @@ def test_mamba3b_long_full_size_sampled():
     _check_sampled(inputs.WORKLOADS["mamba3b-long"], k=48)
 
 
-KERNELS = [(1, 0), (2, 4), (2, 8)]
+KERNELS = [(1, 0), (2, 4), (2, 8), (3, 0)]
 
 
 @pytest.mark.parametrize("kernel,chunk", KERNELS)
@@ -265,3 +265,20 @@ def test_prefill_then_decode_matches_one_pass():
     yr = y[:, t0:]
     assert ((yd - yr).abs() / (1 + yr.abs())).max().item() <= 1e-4
     assert ((state - st).abs() / (1 + st.abs())).max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("batch,L,dim,N,dt", [(2, 37, 40, 1, "f32"), (1, 100, 33, 4, "bf16"),
+                                              (3, 17, 20, 5, "f32"), (1, 300, 70, 12, "f32"),
+                                              (2, 16, 16, 16, "bf16"), (1, 1, 3, 16, "f32")])
+def test_state_parallel_kernel_any_dstate(batch, L, dim, N, dt):
+    """The one-lane-per-(channel, state) kernel pads dstate < 16 with zero states."""
+    w = inputs.WORKLOADS["mamba130m"].replace(name=f"s{batch}x{L}x{dim}x{N}{dt}", batch=batch, seqlen=L,
+                                              dim=dim, dstate=N, dtype=dt)
+    x = inputs.make(w, seed=19, device=DEV)
+    for gated in (False, True):
+        y, st = pu.gpu_fwd(x, gated, kernel=3)
+        torch.cuda.synchronize()
+        y_ref, st_ref = pu.oracle_full(x, gated)
+        tol = pu.tol_of(x)
+        assert pu.scaled_err(y.double().cpu().numpy(), y_ref) <= tol
+        assert pu.scaled_err(st.double().cpu().numpy(), st_ref) <= tol
