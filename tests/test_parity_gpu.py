@@ -282,3 +282,10 @@ def test_state_parallel_kernel_any_dstate(batch, L, dim, N, dt):
         tol = pu.tol_of(x)
         assert pu.scaled_err(y.double().cpu().numpy(), y_ref) <= tol
         assert pu.scaled_err(st.double().cpu().numpy(), st_ref) <= tol
+
+
+def test_longest_sweep_point_sampled():
+    """The longest sequence of the L sweep: 3B-layer channels, L = 2^20 (5.4e9 elements,
+    beyond 2^32 bytes per input tensor), sampled channels against the oracle, every token."""
+    w = inputs.WORKLOADS["mamba3b-long"].replace(name="mamba3b-L1M", seqlen=1 << 20)
+    _check_sampled(w, k=12, seed=7)
