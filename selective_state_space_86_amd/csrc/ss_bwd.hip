@@ -34,8 +34,7 @@
 // and A = 0, which keeps those states at zero and their adjoint at zero.
 #include <utility>
 
-#include "ss_common.h"
-#include "ss_kernels.h"
+#include "ss_chunk_ops.h"
 
 namespace ss {
 namespace {
@@ -73,6 +72,296 @@ __device__ __forceinline__ float chunk_em1(float x2) {
   return __builtin_fabsf(x) < 0.0625f ? x * p : fast_exp2(x2) - 1.0f;
 }
 
+// ---- hand-scheduled per-token blocks of the backward (16 states of one token) ----------
+// Conventions as the forward's local_step: B_t[n] and C_t[n] are read from lane n of the
+// row by DPP row_newbcast:n folded into the consuming instruction; every VGPR a DPP
+// instruction reads is written >= 2 instructions earlier (or before the block, which
+// starts with s_nop 1); every exp result is consumed >= 2 instructions later.
+
+// Forward local pass of one token: e[n] = 2^(dt a2[n]); h[n] = e[n] h[n] + dtu B[n].
+#define BW_L(n, n2)                                                           \
+  "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(n)                           \
+  "v_fma_f32 %[h" #n "], %[e" #n "], %[h" #n "], %[t]\n"                      \
+  "v_mul_f32 %[x], %[dt], %[a" #n2 "]\n"                                      \
+  "v_exp_f32 %[e" #n2 "], %[x]\n"
+#define BW_L_END(n)                                                           \
+  "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(n)                           \
+  "v_fma_f32 %[h" #n "], %[e" #n "], %[h" #n "], %[t]\n"
+
+__device__ __forceinline__ void bwd_local(float (&h)[16], float (&e)[16], const float (&a)[16], float dt,
+                                          float dtu, float vb) {
+  float x, t;
+  asm volatile(
+      "s_nop 1\n"
+      "v_mul_f32 %[x], %[dt], %[a0]\n"
+      "v_exp_f32 %[e0], %[x]\n"
+      "v_mul_f32 %[x], %[dt], %[a1]\n"
+      "v_exp_f32 %[e1], %[x]\n"
+      BW_L(0, 2) BW_L(1, 3) BW_L(2, 4) BW_L(3, 5) BW_L(4, 6) BW_L(5, 7) BW_L(6, 8) BW_L(7, 9)
+      BW_L(8, 10) BW_L(9, 11) BW_L(10, 12) BW_L(11, 13) BW_L(12, 14) BW_L(13, 15)
+      BW_L_END(14) BW_L_END(15)
+      : SS_OPS16(h, "+v"), SS_OPS16(e, "=&v"), [x] "=&v"(x), [t] "=&v"(t)
+      : SS_OPS16(a, "v"), [dt] "v"(dt), [dtu] "v"(dtu), [vb] "v"(vb));
+}
+#undef BW_L
+#undef BW_L_END
+
+// True forward step of one token from the previous states P: H[n] = e[n] P[n] + dtu B[n];
+// s += C[n] H[n] (the DPP fmac of state n runs after state n+1's fma).
+#define BW_T(n, np)                                                           \
+  "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(n)                           \
+  "v_fma_f32 %[H" #n "], %[e" #n "], %[P" #n "], %[t]\n"                      \
+  "v_fmac_f32_dpp %[s], %[vc], %[H" #np "]" SS_DPP_ROW(np)
+
+__device__ __forceinline__ void bwd_true(const float (&P)[16], float (&H)[16], const float (&e)[16],
+                                         float dtu, float vb, float vc, float& s) {
+  float t;
+  asm volatile(
+      "s_nop 1\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(0)
+      "v_fma_f32 %[H0], %[e0], %[P0], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(1)
+      "v_fma_f32 %[H1], %[e1], %[P1], %[t]\n"
+      BW_T(2, 0) BW_T(3, 1) BW_T(4, 2) BW_T(5, 3) BW_T(6, 4) BW_T(7, 5) BW_T(8, 6) BW_T(9, 7)
+      BW_T(10, 8) BW_T(11, 9) BW_T(12, 10) BW_T(13, 11) BW_T(14, 12) BW_T(15, 13)
+      "v_fmac_f32_dpp %[s], %[vc], %[H14]" SS_DPP_ROW(14)
+      "s_nop 1\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H15]" SS_DPP_ROW(15)
+      : SS_OPS16(H, "=&v"), [s] "+v"(s), [t] "=&v"(t)
+      : SS_OPS16(P, "v"), SS_OPS16(e, "v"), [dtu] "v"(dtu), [vb] "v"(vb), [vc] "v"(vc));
+}
+#undef BW_T
+
+// Reverse local step of one token: m[n] = e[n] (m[n] + ds C[n]).
+#define BW_R(n)                                                               \
+  "v_fmac_f32_dpp %[m" #n "], %[vc], %[ds]" SS_DPP_ROW(n)                     \
+  "v_mul_f32 %[m" #n "], %[e" #n "], %[m" #n "]\n"
+
+__device__ __forceinline__ void bwd_rlocal(float (&m)[16], const float (&e)[16], float ds, float vc) {
+  asm volatile(
+      "s_nop 1\n"
+      BW_R(0) BW_R(1) BW_R(2) BW_R(3) BW_R(4) BW_R(5) BW_R(6) BW_R(7)
+      BW_R(8) BW_R(9) BW_R(10) BW_R(11) BW_R(12) BW_R(13) BW_R(14) BW_R(15)
+      : SS_OPS16(m, "+v")
+      : SS_OPS16(e, "v"), [ds] "v"(ds), [vc] "v"(vc));
+}
+#undef BW_R
+
+// True reverse step of one token and its gradient terms (lam = m + ds C[n] in m[n]):
+//   g = lam (H[n] - dtu B[n])  (= lam abar h_prev);  dA[n] += dt g;  ga += A2[n] g;
+//   sb += B[n] lam;  LDS[ad + 64 n] = lam dtu (dB term);  LDS[ad + RC + 64 n] = ds H[n] (dC);
+//   m[n] = e[n] lam (the adjoint passed to the previous token).
+// The LDS data registers rotate over three temporaries.
+__device__ __forceinline__ void bwd_grad(float (&m)[16], float (&dA)[16], const float (&H)[16],
+                                         const float (&e)[16], const float (&a)[16], float dt, float dtu,
+                                         float ds, float vb, float vc, float& ga, float& sb, uint32_t ad) {
+  float t0, t1, t2, u0, u1, u2;
+  asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f32_dpp %[m0], %[vc], %[ds]" SS_DPP_ROW(0)
+      "v_mul_f32_dpp %[t0], %[vb], %[dtu]" SS_DPP_ROW(0)
+      "v_sub_f32 %[t0], %[H0], %[t0]\n"
+      "v_mul_f32 %[t0], %[m0], %[t0]\n"
+      "v_fmac_f32 %[dA0], %[dt], %[t0]\n"
+      "v_fmac_f32 %[ga], %[a0], %[t0]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m0]" SS_DPP_ROW(0)
+      "v_mul_f32 %[t0], %[m0], %[dtu]\n"
+      "v_mul_f32 %[u0], %[ds], %[H0]\n"
+      "ds_write_b32 %[ad], %[t0] offset:0\n"
+      "ds_write_b32 %[ad], %[u0] offset:4352\n"
+      "v_mul_f32 %[m0], %[e0], %[m0]\n"
+      "v_fmac_f32_dpp %[m1], %[vc], %[ds]" SS_DPP_ROW(1)
+      "v_mul_f32_dpp %[t1], %[vb], %[dtu]" SS_DPP_ROW(1)
+      "v_sub_f32 %[t1], %[H1], %[t1]\n"
+      "v_mul_f32 %[t1], %[m1], %[t1]\n"
+      "v_fmac_f32 %[dA1], %[dt], %[t1]\n"
+      "v_fmac_f32 %[ga], %[a1], %[t1]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m1]" SS_DPP_ROW(1)
+      "v_mul_f32 %[t1], %[m1], %[dtu]\n"
+      "v_mul_f32 %[u1], %[ds], %[H1]\n"
+      "ds_write_b32 %[ad], %[t1] offset:64\n"
+      "ds_write_b32 %[ad], %[u1] offset:4416\n"
+      "v_mul_f32 %[m1], %[e1], %[m1]\n"
+      "v_fmac_f32_dpp %[m2], %[vc], %[ds]" SS_DPP_ROW(2)
+      "v_mul_f32_dpp %[t2], %[vb], %[dtu]" SS_DPP_ROW(2)
+      "v_sub_f32 %[t2], %[H2], %[t2]\n"
+      "v_mul_f32 %[t2], %[m2], %[t2]\n"
+      "v_fmac_f32 %[dA2], %[dt], %[t2]\n"
+      "v_fmac_f32 %[ga], %[a2], %[t2]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m2]" SS_DPP_ROW(2)
+      "v_mul_f32 %[t2], %[m2], %[dtu]\n"
+      "v_mul_f32 %[u2], %[ds], %[H2]\n"
+      "ds_write_b32 %[ad], %[t2] offset:128\n"
+      "ds_write_b32 %[ad], %[u2] offset:4480\n"
+      "v_mul_f32 %[m2], %[e2], %[m2]\n"
+      "v_fmac_f32_dpp %[m3], %[vc], %[ds]" SS_DPP_ROW(3)
+      "v_mul_f32_dpp %[t0], %[vb], %[dtu]" SS_DPP_ROW(3)
+      "v_sub_f32 %[t0], %[H3], %[t0]\n"
+      "v_mul_f32 %[t0], %[m3], %[t0]\n"
+      "v_fmac_f32 %[dA3], %[dt], %[t0]\n"
+      "v_fmac_f32 %[ga], %[a3], %[t0]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m3]" SS_DPP_ROW(3)
+      "v_mul_f32 %[t0], %[m3], %[dtu]\n"
+      "v_mul_f32 %[u0], %[ds], %[H3]\n"
+      "ds_write_b32 %[ad], %[t0] offset:192\n"
+      "ds_write_b32 %[ad], %[u0] offset:4544\n"
+      "v_mul_f32 %[m3], %[e3], %[m3]\n"
+      "v_fmac_f32_dpp %[m4], %[vc], %[ds]" SS_DPP_ROW(4)
+      "v_mul_f32_dpp %[t1], %[vb], %[dtu]" SS_DPP_ROW(4)
+      "v_sub_f32 %[t1], %[H4], %[t1]\n"
+      "v_mul_f32 %[t1], %[m4], %[t1]\n"
+      "v_fmac_f32 %[dA4], %[dt], %[t1]\n"
+      "v_fmac_f32 %[ga], %[a4], %[t1]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m4]" SS_DPP_ROW(4)
+      "v_mul_f32 %[t1], %[m4], %[dtu]\n"
+      "v_mul_f32 %[u1], %[ds], %[H4]\n"
+      "ds_write_b32 %[ad], %[t1] offset:256\n"
+      "ds_write_b32 %[ad], %[u1] offset:4608\n"
+      "v_mul_f32 %[m4], %[e4], %[m4]\n"
+      "v_fmac_f32_dpp %[m5], %[vc], %[ds]" SS_DPP_ROW(5)
+      "v_mul_f32_dpp %[t2], %[vb], %[dtu]" SS_DPP_ROW(5)
+      "v_sub_f32 %[t2], %[H5], %[t2]\n"
+      "v_mul_f32 %[t2], %[m5], %[t2]\n"
+      "v_fmac_f32 %[dA5], %[dt], %[t2]\n"
+      "v_fmac_f32 %[ga], %[a5], %[t2]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m5]" SS_DPP_ROW(5)
+      "v_mul_f32 %[t2], %[m5], %[dtu]\n"
+      "v_mul_f32 %[u2], %[ds], %[H5]\n"
+      "ds_write_b32 %[ad], %[t2] offset:320\n"
+      "ds_write_b32 %[ad], %[u2] offset:4672\n"
+      "v_mul_f32 %[m5], %[e5], %[m5]\n"
+      "v_fmac_f32_dpp %[m6], %[vc], %[ds]" SS_DPP_ROW(6)
+      "v_mul_f32_dpp %[t0], %[vb], %[dtu]" SS_DPP_ROW(6)
+      "v_sub_f32 %[t0], %[H6], %[t0]\n"
+      "v_mul_f32 %[t0], %[m6], %[t0]\n"
+      "v_fmac_f32 %[dA6], %[dt], %[t0]\n"
+      "v_fmac_f32 %[ga], %[a6], %[t0]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m6]" SS_DPP_ROW(6)
+      "v_mul_f32 %[t0], %[m6], %[dtu]\n"
+      "v_mul_f32 %[u0], %[ds], %[H6]\n"
+      "ds_write_b32 %[ad], %[t0] offset:384\n"
+      "ds_write_b32 %[ad], %[u0] offset:4736\n"
+      "v_mul_f32 %[m6], %[e6], %[m6]\n"
+      "v_fmac_f32_dpp %[m7], %[vc], %[ds]" SS_DPP_ROW(7)
+      "v_mul_f32_dpp %[t1], %[vb], %[dtu]" SS_DPP_ROW(7)
+      "v_sub_f32 %[t1], %[H7], %[t1]\n"
+      "v_mul_f32 %[t1], %[m7], %[t1]\n"
+      "v_fmac_f32 %[dA7], %[dt], %[t1]\n"
+      "v_fmac_f32 %[ga], %[a7], %[t1]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m7]" SS_DPP_ROW(7)
+      "v_mul_f32 %[t1], %[m7], %[dtu]\n"
+      "v_mul_f32 %[u1], %[ds], %[H7]\n"
+      "ds_write_b32 %[ad], %[t1] offset:448\n"
+      "ds_write_b32 %[ad], %[u1] offset:4800\n"
+      "v_mul_f32 %[m7], %[e7], %[m7]\n"
+      "v_fmac_f32_dpp %[m8], %[vc], %[ds]" SS_DPP_ROW(8)
+      "v_mul_f32_dpp %[t2], %[vb], %[dtu]" SS_DPP_ROW(8)
+      "v_sub_f32 %[t2], %[H8], %[t2]\n"
+      "v_mul_f32 %[t2], %[m8], %[t2]\n"
+      "v_fmac_f32 %[dA8], %[dt], %[t2]\n"
+      "v_fmac_f32 %[ga], %[a8], %[t2]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m8]" SS_DPP_ROW(8)
+      "v_mul_f32 %[t2], %[m8], %[dtu]\n"
+      "v_mul_f32 %[u2], %[ds], %[H8]\n"
+      "ds_write_b32 %[ad], %[t2] offset:512\n"
+      "ds_write_b32 %[ad], %[u2] offset:4864\n"
+      "v_mul_f32 %[m8], %[e8], %[m8]\n"
+      "v_fmac_f32_dpp %[m9], %[vc], %[ds]" SS_DPP_ROW(9)
+      "v_mul_f32_dpp %[t0], %[vb], %[dtu]" SS_DPP_ROW(9)
+      "v_sub_f32 %[t0], %[H9], %[t0]\n"
+      "v_mul_f32 %[t0], %[m9], %[t0]\n"
+      "v_fmac_f32 %[dA9], %[dt], %[t0]\n"
+      "v_fmac_f32 %[ga], %[a9], %[t0]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m9]" SS_DPP_ROW(9)
+      "v_mul_f32 %[t0], %[m9], %[dtu]\n"
+      "v_mul_f32 %[u0], %[ds], %[H9]\n"
+      "ds_write_b32 %[ad], %[t0] offset:576\n"
+      "ds_write_b32 %[ad], %[u0] offset:4928\n"
+      "v_mul_f32 %[m9], %[e9], %[m9]\n"
+      "v_fmac_f32_dpp %[m10], %[vc], %[ds]" SS_DPP_ROW(10)
+      "v_mul_f32_dpp %[t1], %[vb], %[dtu]" SS_DPP_ROW(10)
+      "v_sub_f32 %[t1], %[H10], %[t1]\n"
+      "v_mul_f32 %[t1], %[m10], %[t1]\n"
+      "v_fmac_f32 %[dA10], %[dt], %[t1]\n"
+      "v_fmac_f32 %[ga], %[a10], %[t1]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m10]" SS_DPP_ROW(10)
+      "v_mul_f32 %[t1], %[m10], %[dtu]\n"
+      "v_mul_f32 %[u1], %[ds], %[H10]\n"
+      "ds_write_b32 %[ad], %[t1] offset:640\n"
+      "ds_write_b32 %[ad], %[u1] offset:4992\n"
+      "v_mul_f32 %[m10], %[e10], %[m10]\n"
+      "v_fmac_f32_dpp %[m11], %[vc], %[ds]" SS_DPP_ROW(11)
+      "v_mul_f32_dpp %[t2], %[vb], %[dtu]" SS_DPP_ROW(11)
+      "v_sub_f32 %[t2], %[H11], %[t2]\n"
+      "v_mul_f32 %[t2], %[m11], %[t2]\n"
+      "v_fmac_f32 %[dA11], %[dt], %[t2]\n"
+      "v_fmac_f32 %[ga], %[a11], %[t2]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m11]" SS_DPP_ROW(11)
+      "v_mul_f32 %[t2], %[m11], %[dtu]\n"
+      "v_mul_f32 %[u2], %[ds], %[H11]\n"
+      "ds_write_b32 %[ad], %[t2] offset:704\n"
+      "ds_write_b32 %[ad], %[u2] offset:5056\n"
+      "v_mul_f32 %[m11], %[e11], %[m11]\n"
+      "v_fmac_f32_dpp %[m12], %[vc], %[ds]" SS_DPP_ROW(12)
+      "v_mul_f32_dpp %[t0], %[vb], %[dtu]" SS_DPP_ROW(12)
+      "v_sub_f32 %[t0], %[H12], %[t0]\n"
+      "v_mul_f32 %[t0], %[m12], %[t0]\n"
+      "v_fmac_f32 %[dA12], %[dt], %[t0]\n"
+      "v_fmac_f32 %[ga], %[a12], %[t0]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m12]" SS_DPP_ROW(12)
+      "v_mul_f32 %[t0], %[m12], %[dtu]\n"
+      "v_mul_f32 %[u0], %[ds], %[H12]\n"
+      "ds_write_b32 %[ad], %[t0] offset:768\n"
+      "ds_write_b32 %[ad], %[u0] offset:5120\n"
+      "v_mul_f32 %[m12], %[e12], %[m12]\n"
+      "v_fmac_f32_dpp %[m13], %[vc], %[ds]" SS_DPP_ROW(13)
+      "v_mul_f32_dpp %[t1], %[vb], %[dtu]" SS_DPP_ROW(13)
+      "v_sub_f32 %[t1], %[H13], %[t1]\n"
+      "v_mul_f32 %[t1], %[m13], %[t1]\n"
+      "v_fmac_f32 %[dA13], %[dt], %[t1]\n"
+      "v_fmac_f32 %[ga], %[a13], %[t1]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m13]" SS_DPP_ROW(13)
+      "v_mul_f32 %[t1], %[m13], %[dtu]\n"
+      "v_mul_f32 %[u1], %[ds], %[H13]\n"
+      "ds_write_b32 %[ad], %[t1] offset:832\n"
+      "ds_write_b32 %[ad], %[u1] offset:5184\n"
+      "v_mul_f32 %[m13], %[e13], %[m13]\n"
+      "v_fmac_f32_dpp %[m14], %[vc], %[ds]" SS_DPP_ROW(14)
+      "v_mul_f32_dpp %[t2], %[vb], %[dtu]" SS_DPP_ROW(14)
+      "v_sub_f32 %[t2], %[H14], %[t2]\n"
+      "v_mul_f32 %[t2], %[m14], %[t2]\n"
+      "v_fmac_f32 %[dA14], %[dt], %[t2]\n"
+      "v_fmac_f32 %[ga], %[a14], %[t2]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m14]" SS_DPP_ROW(14)
+      "v_mul_f32 %[t2], %[m14], %[dtu]\n"
+      "v_mul_f32 %[u2], %[ds], %[H14]\n"
+      "ds_write_b32 %[ad], %[t2] offset:896\n"
+      "ds_write_b32 %[ad], %[u2] offset:5248\n"
+      "v_mul_f32 %[m14], %[e14], %[m14]\n"
+      "v_fmac_f32_dpp %[m15], %[vc], %[ds]" SS_DPP_ROW(15)
+      "v_mul_f32_dpp %[t0], %[vb], %[dtu]" SS_DPP_ROW(15)
+      "v_sub_f32 %[t0], %[H15], %[t0]\n"
+      "v_mul_f32 %[t0], %[m15], %[t0]\n"
+      "v_fmac_f32 %[dA15], %[dt], %[t0]\n"
+      "v_fmac_f32 %[ga], %[a15], %[t0]\n"
+      "v_fmac_f32_dpp %[sb], %[vb], %[m15]" SS_DPP_ROW(15)
+      "v_mul_f32 %[t0], %[m15], %[dtu]\n"
+      "v_mul_f32 %[u0], %[ds], %[H15]\n"
+      "ds_write_b32 %[ad], %[t0] offset:960\n"
+      "ds_write_b32 %[ad], %[u0] offset:5312\n"
+      "v_mul_f32 %[m15], %[e15], %[m15]\n"
+      : SS_OPS16(m, "+v"), SS_OPS16(dA, "+v"), [ga] "+v"(ga), [sb] "+v"(sb), [t0] "=&v"(t0), [t1] "=&v"(t1),
+        [t2] "=&v"(t2), [u0] "=&v"(u0), [u1] "=&v"(u1), [u2] "=&v"(u2)
+      : SS_OPS16(H, "v"), SS_OPS16(e, "v"), SS_OPS16(a, "v"), [dt] "v"(dt), [dtu] "v"(dtu), [ds] "v"(ds),
+        [vb] "v"(vb), [vc] "v"(vc), [ad] "v"(ad)
+      : "memory");
+}
+
+// LDS byte address of a __shared__ float (for the ds_write instructions of bwd_grad).
+__device__ __forceinline__ uint32_t lds_addr(float* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) float*)(p)));
+}
+
 template <typename T>
 __device__ __forceinline__ float ld(const void* p, int64_t i) {
   return load_elem(static_cast<const T*>(p), i);
@@ -97,41 +386,67 @@ __device__ __forceinline__ Lane lane_of(const BwdArgs& a) {
   return l;
 }
 
-// Forward scan from h0 (or zero), storing the state at the start of every tile:
-// ckpt[((b * ntiles + tile) * dimp + c) * 16 + n].
-template <typename T, int TC>
+// Forward scan from h0 (or zero), storing the state at the start of every tile of the
+// reverse kernel (bwd_tile_tokens() = 32 tokens): ckpt[((b * ntiles + tile) * dimp + c) * 16
+// + n]. It runs its own, longer chunks (CTC tokens, tiles of 16 * CTC tokens) with the
+// hand-scheduled local step; the folding lane writes a checkpoint whenever the state it
+// carries reaches a multiple of 32 tokens. The inputs of the next tile are requested before
+// the current one is computed.
+template <typename T, int CTC>
 __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
+  static_assert(CTC * 4 == 32 || CTC * 8 == 32 || CTC * 16 == 32, "checkpoints every 32 tokens");
+  constexpr int kPer = 32 / CTC;  // chunks per checkpoint interval
   __shared__ float lds_p[16 * kS];
   __shared__ float lds_h[16 * kS];
   const Lane l = lane_of(a);
   const int64_t L = a.seqlen, N = a.dstate, dimp = a.ngroups * 16;
-  constexpr int TT = 16 * TC;
+  constexpr int TT = 16 * CTC;
   float A2[16];
 #pragma unroll
   for (int n = 0; n < 16; ++n) A2[n] = n < N ? a.A[l.cc * N + n] * kLog2e : 0.0f;
   const float bias = a.delta_bias ? a.delta_bias[l.cc] : 0.0f;
   float carry = (a.h0 && l.k < N) ? a.h0[(l.b * a.dim + l.cc) * N + l.k] : 0.0f;
-  for (int64_t tile = 0; tile < a.ntiles; ++tile) {
-    const int64_t t0 = tile * TT;
-    a.ckpt[((l.b * a.ntiles + tile) * dimp + l.c) * 16 + l.k] = carry;
-    if (tile == a.ntiles - 1) break;  // the state after the last tile is not needed
-    float h[16], dsum = 0.0f;
+
+  // lane (k, i): tokens t0 + k*CTC + j of channel cc and B_t[i]; fixed 32-bit byte offsets
+  const uint32_t tok_row = static_cast<uint32_t>(a.dim * sizeof(T));
+  const uint32_t bc_row = static_cast<uint32_t>(N * sizeof(T));
+  const uint32_t col = static_cast<uint32_t>((l.cc - l.c0) * sizeof(T));
+  const uint32_t bcol = l.i < N ? static_cast<uint32_t>(l.i * sizeof(T)) : 0x7fffffffu;
+  T* tag = nullptr;
+  struct In {
+    float x[CTC], u[CTC], b[CTC];
+  };
+  auto fetch = [&](In& r, int64_t t0) {
+    const int64_t e0 = (l.b * L + t0) * a.dim + l.c0;
+    const int64_t bc0 = (l.b * L + t0) * N;
+    const int64_t left = (a.batch * L * a.dim - e0) * static_cast<int64_t>(sizeof(T));
+    const int64_t bleft = (a.batch * L * N - bc0) * static_cast<int64_t>(sizeof(T));
+    const auto rd = chunk::rsrc(static_cast<const T*>(a.delta) + e0, left);
+    const auto ru = chunk::rsrc(static_cast<const T*>(a.u) + e0, left);
+    const auto rb = chunk::rsrc(static_cast<const T*>(a.B) + bc0, bleft);
+    const int last = static_cast<int>(min(L - 1 - t0, static_cast<int64_t>(TT - 1)));
+#pragma unroll
+    for (int j = 0; j < CTC; ++j) {
+      const uint32_t tt = static_cast<uint32_t>(min(l.k * CTC + j, last));  // past the end: last token
+      r.x[j] = chunk::ldb(tag, rd, tt * tok_row + col, 0);
+      r.u[j] = chunk::ldb(tag, ru, tt * tok_row + col, 0);
+      r.b[j] = chunk::ldb(tag, rb, bcol == 0x7fffffffu ? bcol : tt * bc_row + bcol, 0);
+    }
+  };
+  In cur, nxt;
+  if (a.ntiles > 0) fetch(cur, 0);
+  for (int64_t t0 = 0; t0 < L; t0 += TT) {
+    if (t0 + TT < L) fetch(nxt, t0 + TT);
+    float h[16], e[16], dsum = 0.0f;
 #pragma unroll
     for (int n = 0; n < 16; ++n) h[n] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < TC; ++j) {
-      const int64_t t = t0 + l.k * TC + j;  // full tile: every t < L
-      const int64_t e = (l.b * L + t) * a.dim + l.cc;
-      const float x = ld<T>(a.delta, e) + bias;
-      const float dt = a.softplus ? softplus(x) : x;
-      const float dtu = dt * ld<T>(a.u, e);
-      const float vb = l.i < N ? ld<T>(a.B, (l.b * L + t) * N + l.i) : 0.0f;
+    for (int j = 0; j < CTC; ++j) {
+      const float x = cur.x[j] + bias;
+      float dt = a.softplus ? softplus(x) : x;
+      dt = (t0 + l.k * CTC + j < L) ? dt : 0.0f;  // a zero step is the identity
       dsum += dt;
-      unroll16([&](auto nc) {
-        constexpr int n = decltype(nc)::value;
-        const float ab = fast_exp2(dt * A2[n]);
-        h[n] = __builtin_fmaf(ab, h[n], dtu * row_bcast<n>(vb));
-      });
+      bwd_local(h, e, A2, dt, dt * cur.u[j], cur.b[j]);
     }
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
@@ -139,22 +454,30 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
       lds_h[l.k * kS + n * 16 + l.i] = h[n];
     }
     __syncthreads();
-    // lane (k, i) owns state n = k of channel i: fold the 16 chunks in order
+    // lane (k, i) owns state n = k of channel i: fold the 16 chunks in order, writing the
+    // state at every multiple of 32 tokens that starts a reverse-kernel tile
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
+      if (jj % kPer == 0) {
+        const int64_t tile = (t0 + jj * CTC) / 32;
+        if (tile < a.ntiles) a.ckpt[((l.b * a.ntiles + tile) * dimp + l.c) * 16 + l.k] = carry;
+      }
       const int o = jj * kS + l.k * 16 + l.i;
       carry = __builtin_fmaf(lds_p[o], carry, carry + lds_h[o]);
     }
     __syncthreads();
+    cur = nxt;
   }
 }
 
 template <typename T, bool GATE, int TC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_chunked_kernel(BwdArgs a) {
-  __shared__ float lds_p[16 * kS];       // chunk prod-abar, then chunk carries
-  __shared__ float lds_v[16 * kS];       // chunk end values (state, then adjoint)
-  __shared__ float lds_r[4][2][4 * kS];  // per wave: dB and dC terms [row][n][lane]
+  // [0]: chunk decays - 1, [1]: chunk end states then forward carries; after the carries
+  // are read, the same 8704 floats hold the per-wave dB/dC reduction blocks
+  // [wave][dB or dC][row][n][lane] (4 x 2 x 4 x kS floats)
+  __shared__ __attribute__((aligned(16))) float lds_eh[2][16 * kS];
+  __shared__ float lds_m[16 * kS];  // chunk adjoint aggregates, then reverse carries
   const Lane l = lane_of(a);
   const int64_t L = a.seqlen, N = a.dstate, dimp = a.ngroups * 16;
   constexpr int TT = 16 * TC;
@@ -172,8 +495,30 @@ void bwd_chunked_kernel(BwdArgs a) {
   for (int n = 0; n < 16; ++n) dAacc[n] = 0.0f;
   float dDacc = 0.0f, dbacc = 0.0f;
 
+  // raw inputs of a tile's chunk for this lane (tokens past the end re-read the last one);
+  // the tile processed next (the earlier one) is requested before this one is computed
+  struct Raw {
+    float x[TC], u[TC], z[TC], dy[TC], b[TC], c[TC];
+  };
+  auto fetch = [&](Raw& r, int64_t t0) {
+#pragma unroll
+    for (int j = 0; j < TC; ++j) {
+      const int64_t t = t0 + l.k * TC + j;
+      const int64_t tt = t < L ? t : L - 1;
+      const int64_t e = (l.b * L + tt) * a.dim + l.cc;
+      r.x[j] = ld<T>(a.delta, e);
+      r.u[j] = ld<T>(a.u, e);
+      r.z[j] = GATE ? ld<T>(a.z, e) : 0.0f;
+      r.dy[j] = a.dy[e];
+      r.b[j] = l.i < N ? ld<T>(a.B, (l.b * L + tt) * N + l.i) : 0.0f;
+      r.c[j] = l.i < N ? ld<T>(a.C, (l.b * L + tt) * N + l.i) : 0.0f;
+    }
+  };
+  Raw cur, nxt;
+  if (a.ntiles > 0) fetch(cur, (a.ntiles - 1) * TT);
   for (int64_t tile = a.ntiles - 1; tile >= 0; --tile) {
     const int64_t t0 = tile * TT;
+    if (tile > 0) fetch(nxt, t0 - TT);
     // per-token inputs of this lane's chunk (tokens past the end: zero step, zero dy)
     float dt[TC], dtu[TC], uu[TC], ds[TC], sg[TC], vb[TC], vc[TC], dyv[TC], dsl[TC];
     bool ok[TC];
@@ -182,25 +527,23 @@ void bwd_chunked_kernel(BwdArgs a) {
       const int64_t t = t0 + l.k * TC + j;
       const bool tv = t < L;
       ok[j] = tv && l.cvalid;
-      const int64_t tt = tv ? t : L - 1;
-      const int64_t e = (l.b * L + tt) * a.dim + l.cc;
-      const float x = ld<T>(a.delta, e) + bias;
+      const float x = cur.x[j] + bias;
       dt[j] = tv ? (a.softplus ? softplus(x) : x) : 0.0f;
       sg[j] = a.softplus ? sigmoid(x) : 1.0f;
-      uu[j] = ld<T>(a.u, e);
+      uu[j] = cur.u[j];
       dtu[j] = dt[j] * uu[j];
-      dyv[j] = ok[j] ? a.dy[e] : 0.0f;
+      dyv[j] = ok[j] ? cur.dy[j] : 0.0f;
       float g = 1.0f;
       dsl[j] = 0.0f;
       if (GATE) {
-        const float zv = ld<T>(a.z, e);
+        const float zv = cur.z[j];
         const float s = fast_rcp(1.0f + fast_exp2(-zv * kLog2e));
         g = zv * s;
         dsl[j] = s * __builtin_fmaf(zv, 1.0f - s, 1.0f);
       }
       ds[j] = dyv[j] * g;
-      vb[j] = l.i < N ? ld<T>(a.B, (l.b * L + tt) * N + l.i) : 0.0f;
-      vc[j] = l.i < N ? ld<T>(a.C, (l.b * L + tt) * N + l.i) : 0.0f;
+      vb[j] = cur.b[j];
+      vc[j] = cur.c[j];
     }
 
     // forward local pass from a zero state: decays and chunk aggregates
@@ -210,99 +553,72 @@ void bwd_chunked_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
       dsum += dt[j];
-      unroll16([&](auto nc) {
-        constexpr int n = decltype(nc)::value;
-        ex[j][n] = fast_exp2(dt[j] * A2[n]);
-        h[n] = __builtin_fmaf(ex[j][n], h[n], dtu[j] * row_bcast<n>(vb[j]));
-      });
+      bwd_local(h, ex[j], A2, dt[j], dtu[j], vb[j]);
     }
-    __syncthreads();  // the previous tile's readers of lds_p / lds_v are done
+    // reverse local pass from a zero adjoint (it needs only the decays): the chunk
+    // aggregate mu_loc, so both folds share one pair of barriers
+    float mu[16];
+#pragma unroll
+    for (int n = 0; n < 16; ++n) mu[n] = 0.0f;
+#pragma unroll
+    for (int j = TC - 1; j >= 0; --j) bwd_rlocal(mu, ex[j], ds[j], vc[j]);
+
+    __syncthreads();  // the previous tile is done with every LDS array
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
-      lds_p[l.k * kS + n * 16 + l.i] = chunk_em1(A2[n] * dsum);  // chunk decay - 1
-      lds_v[l.k * kS + n * 16 + l.i] = h[n];
+      lds_eh[0][l.k * kS + n * 16 + l.i] = chunk_em1(A2[n] * dsum);  // chunk decay - 1
+      lds_eh[1][l.k * kS + n * 16 + l.i] = h[n];
+      lds_m[l.k * kS + n * 16 + l.i] = mu[n];
     }
     __syncthreads();
-    {  // forward fold from the checkpoint; each lane overwrites exactly what it read
+    {  // lane (k, i) owns state n = k of channel i: the forward fold from the checkpoint,
+       // then the reverse fold from the adjoint of the later tile; each lane overwrites
+       // exactly the words it read
       float carry = a.ckpt[((l.b * a.ntiles + tile) * dimp + l.c) * 16 + l.k];
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const int o = jj * kS + l.k * 16 + l.i;
-        const float pm = lds_p[o], hv = lds_v[o];
-        lds_p[o] = carry;
-        lds_v[o] = pm;  // keep the chunk decay for the reverse fold
+        const float pm = lds_eh[0][o], hv = lds_eh[1][o];
+        lds_eh[1][o] = carry;  // state entering chunk jj
         carry = __builtin_fmaf(pm, carry, carry + hv);
+      }
+#pragma unroll
+      for (int jj = 15; jj >= 0; --jj) {
+        const int o = jj * kS + l.k * 16 + l.i;
+        const float pm = lds_eh[0][o], mv = lds_m[o];
+        lds_m[o] = rcarry;  // adjoint entering chunk jj from its end
+        rcarry = __builtin_fmaf(pm, rcarry, rcarry + mv);
       }
     }
     __syncthreads();
     float q[16];
 #pragma unroll
-    for (int n = 0; n < 16; ++n) q[n] = lds_p[l.k * kS + n * 16 + l.i];
+    for (int n = 0; n < 16; ++n) {
+      q[n] = lds_eh[1][l.k * kS + n * 16 + l.i];
+      mu[n] = lds_m[l.k * kS + n * 16 + l.i];
+    }
+    __syncthreads();  // every lane has its carries: lds_eh is free for the reductions
 
     // true states of the chunk, the pre-gate output s and dz
     float H[TC][16];
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
       float s = Dd * uu[j];
-      unroll16([&](auto nc) {
-        constexpr int n = decltype(nc)::value;
-        q[n] = __builtin_fmaf(ex[j][n], q[n], dtu[j] * row_bcast<n>(vb[j]));
-        H[j][n] = q[n];
-        s = __builtin_fmaf(row_bcast<n>(vc[j]), q[n], s);
-      });
+      bwd_true(j == 0 ? q : H[j > 0 ? j - 1 : 0], H[j], ex[j], dtu[j], vb[j], vc[j], s);
       if (GATE && ok[j]) {
         const int64_t e = (l.b * L + t0 + l.k * TC + j) * a.dim + l.c;
         a.dz[e] = dyv[j] * s * dsl[j];
       }
     }
 
-    // reverse local pass from a zero adjoint: the chunk aggregate mu_loc
-    float mu[16];
-#pragma unroll
-    for (int n = 0; n < 16; ++n) mu[n] = 0.0f;
-#pragma unroll
-    for (int j = TC - 1; j >= 0; --j) {
-      unroll16([&](auto nc) {
-        constexpr int n = decltype(nc)::value;
-        mu[n] = ex[j][n] * __builtin_fmaf(ds[j], row_bcast<n>(vc[j]), mu[n]);
-      });
-    }
-    __syncthreads();  // every lane has read its forward carry-in
-#pragma unroll
-    for (int n = 0; n < 16; ++n) lds_p[l.k * kS + n * 16 + l.i] = mu[n];
-    __syncthreads();
-    {  // reverse fold, from the last chunk to the first (lds_v still holds the chunk decays)
-#pragma unroll
-      for (int jj = 15; jj >= 0; --jj) {
-        const int o = jj * kS + l.k * 16 + l.i;
-        const float pm = lds_v[o], mv = lds_p[o];
-        lds_p[o] = rcarry;  // adjoint entering chunk jj from its end
-        rcarry = __builtin_fmaf(pm, rcarry, rcarry + mv);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int n = 0; n < 16; ++n) mu[n] = lds_p[l.k * kS + n * 16 + l.i];
-
     // true reverse recurrence and the gradient terms, token by token from the chunk end
-    float* rB = &lds_r[w][0][rw * kS];
-    float* rC = &lds_r[w][1][rw * kS];
+    float* rB = &lds_eh[0][0] + w * (2 * 4 * kS) + rw * kS;  // this row's dB block; dC 4*kS on
+    const float* rC = rB + 4 * kS;
+    const uint32_t rad = lds_addr(rB + l.i);
 #pragma unroll
     for (int j = TC - 1; j >= 0; --j) {
       float sb = 0.0f, ga = 0.0f;
-      unroll16([&](auto nc) {
-        constexpr int n = decltype(nc)::value;
-        const float cn = row_bcast<n>(vc[j]);
-        const float bn = row_bcast<n>(vb[j]);
-        const float lam = __builtin_fmaf(ds[j], cn, mu[n]);
-        const float g = lam * (H[j][n] - dtu[j] * bn);  // lam * abar_t h_{t-1}
-        dAacc[n] = __builtin_fmaf(dt[j], g, dAacc[n]);
-        ga = __builtin_fmaf(A2[n], g, ga);
-        sb = __builtin_fmaf(lam, bn, sb);
-        rB[n * 16 + l.i] = lam * dtu[j];
-        rC[n * 16 + l.i] = ds[j] * H[j][n];
-        mu[n] = ex[j][n] * lam;
-      });
+      bwd_grad(mu, dAacc, H[j], ex[j], A2, dt[j], dtu[j], ds[j], vb[j], vc[j], ga, sb, rad);
       const int64_t t = t0 + l.k * TC + j;
       if (ok[j]) {
         const int64_t e = (l.b * L + t) * a.dim + l.c;
@@ -318,10 +634,15 @@ void bwd_chunked_kernel(BwdArgs a) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       float sB = 0.0f, sC = 0.0f;
+      {
+        const float4* qb = reinterpret_cast<const float4*>(rB + l.i * 16);
+        const float4* qc = reinterpret_cast<const float4*>(rC + l.i * 16);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        sB += rB[l.i * 16 + m];
-        sC += rC[l.i * 16 + m];
+        for (int m = 0; m < 4; ++m) {
+          const float4 vb4 = qb[m], vc4 = qc[m];
+          sB += (vb4.x + vb4.y) + (vb4.z + vb4.w);
+          sC += (vc4.x + vc4.y) + (vc4.z + vc4.w);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_wave_barrier();
@@ -332,26 +653,27 @@ void bwd_chunked_kernel(BwdArgs a) {
         a.part_bc[a.batch * a.ngroups * L * N + o] = sC;
       }
     }
+    cur = nxt;
   }
   if (a.dh0 && l.cvalid && l.k < N) a.dh0[(l.b * a.dim + l.c) * N + l.k] = rcarry;
 
   // dA, dD and dbias of this workgroup: sum the 16 rows
   __syncthreads();
 #pragma unroll
-  for (int n = 0; n < 16; ++n) lds_p[l.k * kS + n * 16 + l.i] = dAacc[n];
-  lds_v[l.k * 16 + l.i] = dDacc;
-  lds_v[256 + l.k * 16 + l.i] = dbacc;
+  for (int n = 0; n < 16; ++n) lds_eh[0][l.k * kS + n * 16 + l.i] = dAacc[n];
+  lds_m[l.k * 16 + l.i] = dDacc;
+  lds_m[256 + l.k * 16 + l.i] = dbacc;
   __syncthreads();
   {
     float s = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) s += lds_p[kk * kS + l.k * 16 + l.i];
+    for (int kk = 0; kk < 16; ++kk) s += lds_eh[0][kk * kS + l.k * 16 + l.i];
     float* pc = a.part_ch + (l.b * dimp + l.c) * 18;
     if (l.k < N) pc[l.k] = s;
     if (l.k == 0 || l.k == 1) {
       float t = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) t += lds_v[l.k * 256 + kk * 16 + l.i];
+      for (int kk = 0; kk < 16; ++kk) t += lds_m[l.k * 256 + kk * 16 + l.i];
       pc[16 + l.k] = t;
     }
   }
@@ -389,7 +711,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
 template <typename T, int TC>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.batch * a.ngroups));
-  hipLaunchKernelGGL((bwd_ckpt_kernel<T, TC>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_ckpt_kernel<T, 8>), grid, dim3(256), 0, s, a);
   if (a.z)
     hipLaunchKernelGGL((bwd_chunked_kernel<T, true, TC>), grid, dim3(256), 0, s, a);
   else
