@@ -436,6 +436,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   In cur, nxt;
   if (a.ntiles > 0) fetch(cur, 0);
   for (int64_t t0 = 0; t0 < L; t0 += TT) {
+    progress_priority(t0, L);
     if (t0 + TT < L) fetch(nxt, t0 + TT);
     float h[16], e[16], dsum = 0.0f;
 #pragma unroll
@@ -517,6 +518,7 @@ void bwd_chunked_kernel(BwdArgs a) {
   Raw cur, nxt;
   if (a.ntiles > 0) fetch(cur, (a.ntiles - 1) * TT);
   for (int64_t tile = a.ntiles - 1; tile >= 0; --tile) {
+    progress_priority(a.ntiles - 1 - tile, a.ntiles);
     const int64_t t0 = tile * TT;
     if (tile > 0) fetch(nxt, t0 - TT);
     // per-token inputs of this lane's chunk (tokens past the end: zero step, zero dy)

@@ -122,6 +122,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
   const int32_t n = bytes > 0x7fffffffLL ? 0x7fffffff : static_cast<int32_t>(bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
 }
+// A per-lane byte offset beyond every range rsrc() creates (those are clamped to 2^31 - 1):
+// a buffer store at it is dropped by the range check, a load returns 0.
+constexpr uint32_t kDropOffset = 0x80000000u;
 // (the b32/b16 builtins move raw bits as unsigned integers: reinterpret, never convert)
 __device__ __forceinline__ float ldb(float*, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));

@@ -88,6 +88,7 @@ void fwd_chunked_kernel(FwdArgs a) {
   K.load(cur, 0);
   int buf = 0;
   for (int64_t t0 = 0; t0 < L; t0 += 16 * TC, buf ^= 1) {
+    progress_priority(t0, L);
     const bool full = t0 + 16 * TC <= L;
     float* lds_a = lds_a2[buf];
     // request the next tile first: the whole tile's work hides its latency
@@ -108,11 +109,14 @@ void fwd_chunked_kernel(FwdArgs a) {
                             min(t0 + k * TC - 3 + m, L - 1), L, a.dim);
 #pragma unroll
       for (int j = 0; j < TC; ++j) win[j + 3] = cur.uu[j];
+      // u_out has y's layout; a null u_out gets an empty range, so every store is dropped
+      const int64_t u0 = (b * L + t0) * a.dim + c0;
+      const auto ru = rsrc(a.u_out ? a.u_out + u0 : a.y, a.u_out ? (a.batch * L * a.dim - u0) * 4 : 0);
 #pragma unroll
       for (int j = 0; j < TC; ++j) {
         cur.uu[j] = conv4_silu(w4, cb, win[j], win[j + 1], win[j + 2], win[j + 3]);
         const bool ok = full ? cvalid : (cvalid && t0 + k * TC + j < L);
-        if (a.u_out && ok) a.u_out[(b * L + t0 + k * TC + j) * a.dim + c] = cur.uu[j];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cur.uu[j]), ru, ok ? y_off : kDropOffset, j * y_row, 0);
       }
     }
 #pragma unroll
@@ -179,14 +183,16 @@ void fwd_chunked_kernel(FwdArgs a) {
       for (int n = 0; n < 16; ++n) q[n] = lc[n * 16];
     }
 
-    // fix-up with the carry-in, gate, store
+    // fix-up with the carry-in, gate, store (unconditionally: a masked lane's store goes to an
+    // offset past the buffer range and is dropped, so the compiler sees a fixed number of
+    // outstanding stores and never waits for them when the prefetched loads are consumed)
     const int64_t y0 = (b * L + t0) * a.dim + c0;
     const auto ry = rsrc(a.y + y0, (a.batch * L * a.dim - y0) * 4);
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
       fixup_step(q, ex[j], vc[j], y[j]);
       const bool ok = full ? cvalid : (cvalid && t0 + k * TC + j < L);
-      if (ok) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[j] * gate[j]), ry, y_off, j * y_row, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[j] * gate[j]), ry, ok ? y_off : kDropOffset, j * y_row, 0);
     }
     cur = nxt;
   }

@@ -145,6 +145,7 @@ __global__ __launch_bounds__(256) void fwd_state_kernel(FwdArgs a) {
   __syncthreads();
   int buf = 0;
   for (int64_t t0 = 0; t0 < L; t0 += 16, buf ^= 1) {
+    progress_priority(t0, L);
     const bool more = t0 + 16 < L;
     if (more) load(nxt, t0 + 16);
     // per-token work for token t0 + n (a zero step past the end is the identity)
