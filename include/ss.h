@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 4
+#define SS_ABI_VERSION 5
 #define SS_MAX_DSTATE 16
 
 typedef enum {
@@ -108,6 +108,10 @@ typedef struct {
                             2 for dstate == 16, else 3 when it applies, else 1 */
   int chunk_len;      /* tokens per lane and tile for kernel 2: 0 (automatic), 4 or 8 */
   int discretization; /* an ss_discretization value */
+  int chunk_rows;     /* time chunks per workgroup tile for kernel 2: 0 (automatic), 16 or 12;
+                         12 needs chunk_len 0 or 4 (else SS_ERR_BAD_SHAPE) and is chosen
+                         automatically when channel groups of 16 per CU fill 4 slots of 3-wave
+                         workgroups better than 3 slots of 4-wave ones */
 } ss_fwd_options;
 
 /*

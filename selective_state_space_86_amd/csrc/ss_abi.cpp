@@ -79,7 +79,9 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
   const int kernel = opt ? opt->kernel : 0;
   const int chunk = opt ? opt->chunk_len : 0;
   const int disc = opt ? opt->discretization : SS_DISC_DT;
+  const int rows = opt ? opt->chunk_rows : 0;
   if (kernel < 0 || kernel > 3 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
+  if (!(rows == 0 || rows == 16 || rows == 12) || (rows == 12 && chunk == 8)) return SS_ERR_BAD_SHAPE;
   if (disc != SS_DISC_DT && disc != SS_DISC_ZOH) return SS_ERR_BAD_SHAPE;
   if (kernel == 2 && dstate != 16) return SS_ERR_UNSUPPORTED_N;
   const size_t es = elem_size(in_dtype);
@@ -106,9 +108,17 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
     return es == hipSuccess ? SS_OK : SS_ERR_HIP;
   }
   const bool chunked = kernel == 2 || (kernel == 0 && ss::fwd_chunked_supported(a));
-  if (chunked && seqlen > 0)
-    e = ss::fwd_chunked(a, chunk == 0 ? ss::fwd_chunked_pick(a, cus) : chunk, s);
-  else if (kernel == 0 && ss::fwd_state_supported(a))
+  if (chunked && seqlen > 0) {
+    // explicit choices override the automatic plan; 12 rows exist only with 4-token chunks
+    ss::ChunkPlan plan = ss::fwd_chunked_pick(a, cus);
+    if (chunk != 0) plan.chunk_len = chunk;
+    if (rows != 0) plan.rows = rows;
+    if (plan.rows == 12 && plan.chunk_len != 4) {
+      if (rows == 12) plan.chunk_len = 4;  // rows asked for, chunk length automatic
+      else plan.rows = 16;                 // chunk length 8 asked for, rows automatic
+    }
+    e = ss::fwd_chunked(a, plan, s);
+  } else if (kernel == 0 && ss::fwd_state_supported(a))
     e = ss::fwd_state(a, s);  // dstate != 16
   else
     e = ss::fwd_seq(a, s);

@@ -44,17 +44,21 @@ using namespace chunk;
 
 constexpr int kLdsChunkStride = 16 * 16 + 16;  // [chunk][n][lane], padded against bank conflicts
 
-// Register budget: TC = 4 must fit 3 workgroups (12 waves) per CU, TC = 8 two; the
-// zero-order-hold variant holds 16 more values (1/A) and runs two per CU.
-template <typename T, bool GATE, int TC, bool EARLY, bool ZOH, bool CONV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TC <= 4 && !ZOH ? 3 : 2)))
+// R rows (time chunks) per workgroup: 16 (4 waves) or 12 (3 waves; four such workgroups fit
+// a CU where three of 16 do, for shapes with between 3 and 4 channel groups per CU).
+// Register budget: TC = 4 must fit 3 waves per SIMD, TC = 8 two; the zero-order-hold
+// variant holds 16 more values (1/A) and runs at two.
+template <typename T, bool GATE, int TC, bool EARLY, bool ZOH, bool CONV, int R>
+__global__ __launch_bounds__(R * 16) __attribute__((amdgpu_waves_per_eu(TC <= 4 && !ZOH ? 3 : 2)))
 void fwd_chunked_kernel(FwdArgs a) {
+  static_assert(R == 16 || R == 12, "16 or 12 chunks per tile");
+  constexpr int NOWN = (16 + R - 1) / R;  // states each lane folds: n = k, k + R (when < 16)
   // The prod-abar/carry array alternates between two buffers by tile, so a tile's
   // aggregates never overwrite carries a slower wave may still be reading after the second
   // barrier of the previous tile. The end states are read only between the two barriers of
   // a tile, so one buffer suffices.
-  __shared__ float lds_a2[2][16 * kLdsChunkStride];  // chunk prod-abar, then the chunk carries
-  __shared__ float lds_h[16 * kLdsChunkStride];      // chunk end states
+  __shared__ float lds_a2[2][R * kLdsChunkStride];  // chunk prod-abar, then the chunk carries
+  __shared__ float lds_h[R * kLdsChunkStride];      // chunk end states
 
   const int64_t ngd = (a.dim + 15) / 16;
   const int64_t g = group_of(blockIdx.x, a.batch * ngd);
@@ -67,7 +71,7 @@ void fwd_chunked_kernel(FwdArgs a) {
   const bool cvalid = c < a.dim;
   const int64_t cc = cvalid ? c : a.dim - 1;
   const int64_t L = a.seqlen;
-  TileLoader<T, GATE, TC, 16> K(a, b, c0, k, i, cc);
+  TileLoader<T, GATE, TC, R> K(a, b, c0, k, i, cc);
 
   float A2[16], iA[16];
 #pragma unroll
@@ -79,20 +83,25 @@ void fwd_chunked_kernel(FwdArgs a) {
   const float Dd = a.D ? a.D[cc] : 0.0f;
   float w4[4], cb = 0.0f;
   if (CONV) conv_taps(a.conv_w, a.conv_b, a.kconv, cc, w4, cb);
-  // state n = k of channel c0+i, carried across tiles; starts at h0 when one is given
-  float carry = a.h0 ? a.h0[(b * a.dim + cc) * 16 + k] : 0.0f;
+  // states n = k (+ R) of channel c0+i, carried across tiles; start at h0 when one is given
+  float carry[NOWN];
+#pragma unroll
+  for (int m = 0; m < NOWN; ++m) {
+    const int n = k + m * R;
+    carry[m] = (a.h0 && n < 16) ? a.h0[(b * a.dim + cc) * 16 + n] : 0.0f;
+  }
   const uint32_t y_row = static_cast<uint32_t>(a.dim * 4);
   const uint32_t y_off = static_cast<uint32_t>(k * TC) * y_row + static_cast<uint32_t>(i * 4);
 
   TileIn<TC> cur, nxt;
   K.load(cur, 0);
   int buf = 0;
-  for (int64_t t0 = 0; t0 < L; t0 += 16 * TC, buf ^= 1) {
+  for (int64_t t0 = 0; t0 < L; t0 += R * TC, buf ^= 1) {
     progress_priority(t0, L);
-    const bool full = t0 + 16 * TC <= L;
+    const bool full = t0 + R * TC <= L;
     float* lds_a = lds_a2[buf];
     // request the next tile first: the whole tile's work hides its latency
-    if (EARLY && t0 + 16 * TC < L) K.load(nxt, t0 + 16 * TC);
+    if (EARLY && t0 + R * TC < L) K.load(nxt, t0 + R * TC);
 
     // local pass from a zero state
     float h[16], ex[TC][16], y[TC], gate[TC], vc[TC];
@@ -135,7 +144,7 @@ void fwd_chunked_kernel(FwdArgs a) {
     }
 
     // otherwise request it now: the combine and fix-up below hide its latency
-    if (!EARLY && t0 + 16 * TC < L) K.load(nxt, t0 + 16 * TC);
+    if (!EARLY && t0 + R * TC < L) K.load(nxt, t0 + R * TC);
 
     // chunk aggregates (prod abar = exp(A * sum dt), end state) to LDS
     {
@@ -157,22 +166,26 @@ void fwd_chunked_kernel(FwdArgs a) {
     }
     __syncthreads();
 
-    // combine: this lane owns state n = k of channel i and folds the 16 chunks in order.
-    // Each lane reads exactly the LDS words it then overwrites with carries, so the carry
-    // array can alias the prod-abar array without another barrier.
-    {
-      float* sa = lds_a + k * 16 + i;
-      const float* sh = lds_h + k * 16 + i;
-      float av[16], hv[16];
+    // combine: this lane owns state n = k (and k + R) of channel i and folds the R chunks in
+    // order. Each lane reads exactly the LDS words it then overwrites with carries, so the
+    // carry array can alias the prod-abar array without another barrier.
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        av[j] = sa[j * kLdsChunkStride];
-        hv[j] = sh[j * kLdsChunkStride];
-      }
+    for (int m = 0; m < NOWN; ++m) {
+      const int n = k + m * R;
+      if (m == 0 || n < 16) {
+        float* sa = lds_a + n * 16 + i;
+        const float* sh = lds_h + n * 16 + i;
+        float av[R], hv[R];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        sa[j * kLdsChunkStride] = carry;  // carry into chunk j
-        carry = __builtin_fmaf(av[j], carry, hv[j]);
+        for (int j = 0; j < R; ++j) {
+          av[j] = sa[j * kLdsChunkStride];
+          hv[j] = sh[j * kLdsChunkStride];
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          sa[j * kLdsChunkStride] = carry[m];  // carry into chunk j
+          carry[m] = __builtin_fmaf(av[j], carry[m], hv[j]);
+        }
       }
     }
     __syncthreads();
@@ -196,53 +209,73 @@ void fwd_chunked_kernel(FwdArgs a) {
     }
     cur = nxt;
   }
-  if (a.last_state && cvalid) a.last_state[(b * a.dim + c) * 16 + k] = carry;
+  if (a.last_state && cvalid) {
+#pragma unroll
+    for (int m = 0; m < NOWN; ++m) {
+      const int n = k + m * R;
+      if (n < 16) a.last_state[(b * a.dim + c) * 16 + n] = carry[m];
+    }
+  }
 }
 
-template <typename T, bool GATE, int TC, bool ZOH>
+template <typename T, bool GATE, int TC, bool ZOH, int R>
 void launch_chunked_c(const FwdArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.batch * ((a.dim + 15) / 16)));
   constexpr bool early = TC <= 4 && !GATE;
   if (a.kconv > 0)
-    hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, ZOH, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, ZOH, true, R>), grid, dim3(R * 16), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, ZOH, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, ZOH, false, R>), grid, dim3(R * 16), 0, s, a);
 }
 
-template <typename T, bool GATE, int TC>
+template <typename T, bool GATE, int TC, int R>
 hipError_t launch_chunked(const FwdArgs& a, hipStream_t s) {
   if (a.zoh)
-    launch_chunked_c<T, GATE, TC, true>(a, s);
+    launch_chunked_c<T, GATE, TC, true, R>(a, s);
   else
-    launch_chunked_c<T, GATE, TC, false>(a, s);
+    launch_chunked_c<T, GATE, TC, false, R>(a, s);
   return hipGetLastError();
 }
 
-template <typename T, int TC>
+template <typename T, int TC, int R>
 hipError_t launch_chunked_g(const FwdArgs& a, hipStream_t s) {
-  return a.z ? launch_chunked<T, true, TC>(a, s) : launch_chunked<T, false, TC>(a, s);
+  return a.z ? launch_chunked<T, true, TC, R>(a, s) : launch_chunked<T, false, TC, R>(a, s);
+}
+
+template <typename T>
+hipError_t launch_chunked_t(const FwdArgs& a, ChunkPlan p, hipStream_t s) {
+  if (p.rows == 12) return launch_chunked_g<T, 4, 12>(a, s);
+  return p.chunk_len == 4 ? launch_chunked_g<T, 4, 16>(a, s) : launch_chunked_g<T, 8, 16>(a, s);
 }
 
 }  // namespace
 
 bool fwd_chunked_supported(const FwdArgs& a) { return a.dstate == 16 && a.seqlen > 0; }
 
-// Chunk length: 8 halves the per-tile combine cost but needs ~2x the registers of 4
-// (2 resident workgroups per CU instead of 3). Measured on the 130M (768 groups), 1.4B
-// (1024) and 3B-long (320) shapes, 4 is faster whenever the groups fill more than two
-// slots per CU (the extra resident wave per SIMD hides more latency; a partly filled last
-// round costs less than that, since CUs with fewer workgroups run each one faster), and 8
-// when every group fits at two per CU.
-int fwd_chunked_pick(const FwdArgs& a, int cus) {
-  if (a.zoh) return 4;  // the zero-order-hold variant spills registers at 8
+// Tile shape. Chunk length 8 halves the per-tile combine cost but needs ~2x the registers
+// of 4 (2 resident workgroups of 16 rows per CU instead of 3); 12 rows (3 waves) let four
+// workgroups share a CU where three of 16 rows do. The channel groups of 16 are dealt to
+// the resident slots in rounds, and a partly filled last round runs at low occupancy, so
+// the plan maximises the filled fraction of the slots:
+//  - at most 2 groups per CU (the 3B long-context shape: 320 groups): length 8, 16 rows;
+//  - otherwise length 4 with 16 rows (3 slots per CU) unless 12 rows (4 slots) fill the
+//    rounds better by more than 5% (1024 groups, the 1.4B shape: 1 full round of 4 against
+//    2/3 of a second round of 3; 768 groups, the 130M shape: 16 rows, one full round).
+// The zero-order-hold variant runs at two waves per SIMD either way and keeps 16 rows.
+ChunkPlan fwd_chunked_pick(const FwdArgs& a, int cus) {
   const int64_t groups = a.batch * ((a.dim + 15) / 16);
-  return groups <= 2 * static_cast<int64_t>(cus) ? 8 : 4;
+  if (a.zoh) return {4, 16};  // the zero-order-hold variant spills registers at 8
+  if (groups <= 2 * static_cast<int64_t>(cus)) return {8, 16};
+  auto filled = [&](int64_t slots_per_cu) {
+    const int64_t slots = slots_per_cu * cus;
+    const int64_t rounds = (groups + slots - 1) / slots;
+    return static_cast<double>(groups) / static_cast<double>(rounds * slots);
+  };
+  return filled(4) > filled(3) + 0.05 ? ChunkPlan{4, 12} : ChunkPlan{4, 16};
 }
 
-hipError_t fwd_chunked(const FwdArgs& a, int chunk_len, hipStream_t s) {
-  const bool bf = a.dtype == kBF16;
-  if (chunk_len == 4) return bf ? launch_chunked_g<uint16_t, 4>(a, s) : launch_chunked_g<float, 4>(a, s);
-  return bf ? launch_chunked_g<uint16_t, 8>(a, s) : launch_chunked_g<float, 8>(a, s);
+hipError_t fwd_chunked(const FwdArgs& a, ChunkPlan plan, hipStream_t s) {
+  return a.dtype == kBF16 ? launch_chunked_t<uint16_t>(a, plan, s) : launch_chunked_t<float>(a, plan, s);
 }
 
 }  // namespace ss

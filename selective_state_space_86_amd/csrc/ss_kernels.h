@@ -92,8 +92,14 @@ hipError_t fwd_seq(const FwdArgs& a, hipStream_t s);
 bool fwd_state_supported(const FwdArgs& a);
 hipError_t fwd_state(const FwdArgs& a, hipStream_t s);
 bool fwd_chunked_supported(const FwdArgs& a);
-hipError_t fwd_chunked(const FwdArgs& a, int chunk_len, hipStream_t s);
-int fwd_chunked_pick(const FwdArgs& a, int cus);
+// Tile shape of the time-chunked forward: chunk_len tokens per lane (4 or 8) and rows time
+// chunks per workgroup (16, or 12 with chunk_len 4).
+struct ChunkPlan {
+  int chunk_len;
+  int rows;
+};
+hipError_t fwd_chunked(const FwdArgs& a, ChunkPlan plan, hipStream_t s);
+ChunkPlan fwd_chunked_pick(const FwdArgs& a, int cus);
 hipError_t step(const StepArgs& a, hipStream_t s);
 int64_t bwd_tile_tokens();
 size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);

@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss_abi_version() == _binding.ABI_VERSION == 4
+    assert lib.ss_abi_version() == _binding.ABI_VERSION == 5
     for s in range(0, 9):
         assert lib.ss_status_string(s)
     assert b"unknown" in lib.ss_status_string(99)
@@ -99,11 +99,11 @@ def test_binding_rejects_mixed_dtypes():
         _binding._in_dtype(torch.zeros(1), torch.zeros(1, dtype=torch.bfloat16))
 
 
-def fwd_ex_call(lib, kernel, chunk, disc=0, **kw):
+def fwd_ex_call(lib, kernel, chunk, disc=0, rows=0, **kw):
     a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, sp=1, y=FAKE,
              st=None, h0=None, batch=1, L=4, dim=8, N=16, dtype=0)
     a.update(kw)
-    opt = _binding.FwdOptions(kernel, chunk, disc)
+    opt = _binding.FwdOptions(kernel, chunk, disc, rows)
     return lib.ss_fwd_ex(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
                          a["y"], a["st"], a["h0"], a["batch"], a["L"], a["dim"], a["N"], a["dtype"],
                          ctypes.byref(opt), None)
@@ -123,6 +123,16 @@ def test_fwd_ex_validation(lib, kernel, chunk, kw, code):
 ])
 def test_fwd_ex_discretization_validation(lib, disc, kw, code):
     assert fwd_ex_call(lib, 0, 0, disc=disc, **kw) == code
+
+
+@pytest.mark.parametrize("chunk,rows,kw,code", [
+    (0, 8, {}, 2), (0, 15, {}, 2), (0, -12, {}, 2), (8, 12, {}, 2), (4, 32, {}, 2),
+    (4, 12, dict(u=None), 1), (0, 12, dict(dtype=5), 3), (0, 16, dict(y=FAKE + 1), 5),
+])
+def test_fwd_ex_chunk_rows_validation(lib, chunk, rows, kw, code):
+    """chunk_rows is 0, 16 or 12, and 12 only with chunk length 0 or 4; errors are reported
+    before any device work (no GPU is needed to reach them)."""
+    assert fwd_ex_call(lib, 2, chunk, rows=rows, **kw) == code
 
 
 def step_ex_call(lib, disc, **kw):
@@ -188,7 +198,7 @@ def conv_call(lib, **kw):
     a = dict(x=FAKE, w=FAKE, cb=None, cs=None, K=4, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None,
              bias=None, sp=1, y=FAKE, st=None, h0=None, uo=None, batch=1, L=8, dim=16, N=16, dtype=0)
     a.update(kw)
-    opt = _binding.FwdOptions(0, 0, 0)
+    opt = _binding.FwdOptions(0, 0, 0, 0)
     return lib.ss_fwd_conv(a["x"], a["w"], a["cb"], a["cs"], a["K"], a["delta"], a["A"], a["B"], a["C"],
                            a["D"], a["z"], a["bias"], a["sp"], a["y"], a["st"], a["h0"], a["uo"], a["batch"],
                            a["L"], a["dim"], a["N"], a["dtype"], ctypes.byref(opt), None)

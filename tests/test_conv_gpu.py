@@ -14,7 +14,7 @@ from tests import parity_util as pu
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-KERNELS = [(1, 0), (2, 4), (2, 8)]
+KERNELS = [(1, 0, 0), (2, 4, 16), (2, 8, 16), (2, 4, 12)]  # (kernel, chunk_len, chunk_rows)
 
 
 def _announce(msg):
@@ -51,12 +51,12 @@ def check(x, got, ref, what):
         assert err <= tol, f"{what}: {name} max scaled error {err:.3e} > {tol}"
 
 
-@pytest.mark.parametrize("kernel,chunk", KERNELS)
+@pytest.mark.parametrize("kernel,chunk,rows", KERNELS)
 @pytest.mark.parametrize("batch,L,dim,N,dt,K", [(2, 37, 40, 16, "f32", 4), (1, 129, 33, 16, "bf16", 4),
                                                 (2, 300, 70, 16, "f32", 3), (3, 64, 20, 5, "f32", 4),
                                                 (1, 777, 130, 16, "bf16", 2), (2, 50, 16, 16, "f32", 1),
                                                 (1, 2, 24, 16, "f32", 4)])
-def test_conv_every_kernel_choice(kernel, chunk, batch, L, dim, N, dt, K):
+def test_conv_every_kernel_choice(kernel, chunk, rows, batch, L, dim, N, dt, K):
     if kernel == 2 and N != 16:
         pytest.skip("the time-chunked kernel is for dstate 16")
     w = inputs.WORKLOADS["mamba130m"].replace(name=f"c{batch}x{L}x{dim}x{N}{dt}k{K}", batch=batch, seqlen=L,
@@ -65,7 +65,7 @@ def test_conv_every_kernel_choice(kernel, chunk, batch, L, dim, N, dt, K):
     _announce(f"kernel={kernel} chunk={chunk} {w.name}")
     for gated, bias, state in ((True, True, True), (False, False, False)):
         cw, cb, cs = conv_params(batch, dim, K, 82, bias, state)
-        got = gpu_conv(x, cw, cb, cs, gated, kernel=kernel, chunk_len=chunk)
+        got = gpu_conv(x, cw, cb, cs, gated, kernel=kernel, chunk_len=chunk, chunk_rows=rows)
         torch.cuda.synchronize()
         check(x, got, oracle_conv(x, cw, cb, cs, gated), f"{w.name} gated={gated}")
 

@@ -161,22 +161,22 @@ def test_mamba3b_long_full_size_sampled():
     _check_sampled(inputs.WORKLOADS["mamba3b-long"], k=48)
 
 
-KERNELS = [(1, 0), (2, 4), (2, 8), (3, 0)]
+KERNELS = [(1, 0, 0), (2, 4, 16), (2, 8, 16), (2, 4, 12), (3, 0, 0)]  # (kernel, chunk_len, chunk_rows)
 
 
-@pytest.mark.parametrize("kernel,chunk", KERNELS)
+@pytest.mark.parametrize("kernel,chunk,rows", KERNELS)
 @pytest.mark.parametrize("batch,L,dim,dt", [(3, 37, 100, "f32"), (2, 129, 70, "bf16"), (1, 1, 16, "f32"),
                                             (2, 1000, 130, "f32"), (1, 777, 257, "bf16"),
                                             (2, 128, 64, "f32"), (1, 300, 17, "f32")])
-def test_every_kernel_choice(kernel, chunk, batch, L, dim, dt):
+def test_every_kernel_choice(kernel, chunk, rows, batch, L, dim, dt):
     """Every kernel and chunk length matches the oracle (the chunk split is free: the update
     is associative), including ragged channel counts and partial last tiles."""
     w = inputs.WORKLOADS["mamba130m"].replace(name=f"k{batch}x{L}x{dim}{dt}", batch=batch, seqlen=L, dim=dim,
                                               dstate=16, dtype=dt)
     x = inputs.make(w, seed=11, device=DEV)
-    _announce(f"kernel={kernel} chunk={chunk} {w.name}")
+    _announce(f"kernel={kernel} chunk={chunk} rows={rows} {w.name}")
     for gated in (False, True):
-        y, st = pu.gpu_fwd(x, gated, kernel=kernel, chunk_len=chunk)
+        y, st = pu.gpu_fwd(x, gated, kernel=kernel, chunk_len=chunk, chunk_rows=rows)
         torch.cuda.synchronize()
         y_ref, st_ref = pu.oracle_full(x, gated)
         tol = pu.tol_of(x)
@@ -186,7 +186,7 @@ def test_every_kernel_choice(kernel, chunk, batch, L, dim, dt):
 
 def test_chunk_lengths_agree_at_130m_shape():
     x = inputs.make(inputs.WORKLOADS["mamba130m"], seed=2, device=DEV)
-    outs = [pu.gpu_fwd(x, False, kernel=kn, chunk_len=ch) for kn, ch in KERNELS]
+    outs = [pu.gpu_fwd(x, False, kernel=kn, chunk_len=ch, chunk_rows=r) for kn, ch, r in KERNELS]
     torch.cuda.synchronize()
     for y, st in outs[1:]:
         ref_y, ref_st = outs[0]
@@ -194,10 +194,10 @@ def test_chunk_lengths_agree_at_130m_shape():
         assert ((st - ref_st).abs() / (1 + ref_st.abs())).max().item() <= 2e-5
 
 
-@pytest.mark.parametrize("kernel,chunk", KERNELS)
+@pytest.mark.parametrize("kernel,chunk,rows", KERNELS)
 @pytest.mark.parametrize("batch,L,dim,N,dt", [(2, 300, 70, 16, "f32"), (1, 129, 33, 16, "bf16"),
                                               (3, 50, 40, 5, "f32")])
-def test_initial_state(kernel, chunk, batch, L, dim, N, dt):
+def test_initial_state(kernel, chunk, rows, batch, L, dim, N, dt):
     """ss_fwd_ex with h0 matches the oracle started from the same state."""
     if kernel == 2 and N != 16:
         pytest.skip("the time-chunked kernel is for dstate 16")
@@ -207,7 +207,7 @@ def test_initial_state(kernel, chunk, batch, L, dim, N, dt):
     g = torch.Generator(device=DEV)
     g.manual_seed(5)
     h0 = torch.randn((batch, dim, N), generator=g, device=DEV)
-    y, st = pu.gpu_fwd(x, True, kernel=kernel, chunk_len=chunk, h0=h0)
+    y, st = pu.gpu_fwd(x, True, kernel=kernel, chunk_len=chunk, chunk_rows=rows, h0=h0)
     torch.cuda.synchronize()
     n = {k: inputs.to_numpy(v) for k, v in x.items()}
     import oracle

@@ -17,7 +17,7 @@ from tests import parity_util as pu
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-KERNELS = [(1, 0), (2, 4), (2, 8)]
+KERNELS = [(1, 0, 0), (2, 4, 16), (2, 8, 16), (2, 4, 12)]  # (kernel, chunk_len, chunk_rows)
 
 
 def _announce(msg):
@@ -33,11 +33,11 @@ def _check(x, y, st, gated=True, h0=None, softplus=True, what=""):
     assert es <= tol, f"{what}: state max scaled error {es:.3e} > {tol}"
 
 
-@pytest.mark.parametrize("kernel,chunk", KERNELS)
+@pytest.mark.parametrize("kernel,chunk,rows", KERNELS)
 @pytest.mark.parametrize("batch,L,dim,N,dt", [(3, 37, 100, 16, "f32"), (2, 129, 70, 16, "bf16"),
                                               (2, 1000, 130, 16, "f32"), (1, 300, 17, 16, "f32"),
                                               (2, 64, 40, 7, "f32")])
-def test_zoh_every_kernel_choice(kernel, chunk, batch, L, dim, N, dt):
+def test_zoh_every_kernel_choice(kernel, chunk, rows, batch, L, dim, N, dt):
     if kernel == 2 and N != 16:
         pytest.skip("the time-chunked kernel is for dstate 16")
     w = inputs.WORKLOADS["mamba130m"].replace(name=f"z{batch}x{L}x{dim}x{N}{dt}", batch=batch, seqlen=L,
@@ -45,7 +45,7 @@ def test_zoh_every_kernel_choice(kernel, chunk, batch, L, dim, N, dt):
     x = inputs.make(w, seed=31, device=DEV)
     _announce(f"kernel={kernel} chunk={chunk} {w.name}")
     for gated in (False, True):
-        y, st = pu.gpu_fwd(x, gated, kernel=kernel, chunk_len=chunk, zoh=True)
+        y, st = pu.gpu_fwd(x, gated, kernel=kernel, chunk_len=chunk, chunk_rows=rows, zoh=True)
         torch.cuda.synchronize()
         _check(x, y, st, gated, what=f"{w.name} gated={gated}")
 
@@ -71,21 +71,21 @@ def _wide_range_inputs(batch, L, dim, seed):
     return dict(u=u, delta=delta, z=z, B=B, C=C, A=A.contiguous(), D=D, delta_bias=bias)
 
 
-@pytest.mark.parametrize("kernel,chunk", KERNELS)
-def test_zoh_step_sizes_across_the_series_switch(kernel, chunk):
+@pytest.mark.parametrize("kernel,chunk,rows", KERNELS)
+def test_zoh_step_sizes_across_the_series_switch(kernel, chunk, rows):
     x = _wide_range_inputs(2, 400, 96, seed=32)
     _announce(f"wide-range dt*A kernel={kernel} chunk={chunk}")
-    y, st = pu.gpu_fwd(x, True, kernel=kernel, chunk_len=chunk, zoh=True)
+    y, st = pu.gpu_fwd(x, True, kernel=kernel, chunk_len=chunk, chunk_rows=rows, zoh=True)
     torch.cuda.synchronize()
     _check(x, y, st, True, what="wide range")
 
 
-@pytest.mark.parametrize("kernel,chunk", KERNELS)
-def test_zoh_initial_state(kernel, chunk):
+@pytest.mark.parametrize("kernel,chunk,rows", KERNELS)
+def test_zoh_initial_state(kernel, chunk, rows):
     w = inputs.WORKLOADS["mamba1.4b"].replace(name="zh0", batch=2, seqlen=333, dim=80)
     x = inputs.make(w, seed=33, device=DEV)
     h0 = torch.randn((2, 80, 16), device=DEV)
-    y, st = pu.gpu_fwd(x, True, kernel=kernel, chunk_len=chunk, zoh=True, h0=h0)
+    y, st = pu.gpu_fwd(x, True, kernel=kernel, chunk_len=chunk, chunk_rows=rows, zoh=True, h0=h0)
     torch.cuda.synchronize()
     _check(x, y, st, True, h0=h0, what="zoh from h0")
 
