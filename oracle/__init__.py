@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the selective-scan (S6) forward, decode step and backward.
+"""fp64 CPU oracle for the selective-scan (S6) forward, decode step, backward, conv prologue
+and input projections.
 
 TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
 leg of ``bench.py`` may import this package. It never imports or calls the GPU library,
@@ -62,6 +63,8 @@ def _bind(path):
                                   i64, i64, i64, i64, i32, vp, vp, i64, i32]
     lib.ss_oracle_conv_silu.restype = i32
     lib.ss_oracle_conv_silu.argtypes = [vp, vp, vp, vp, i64, vp, i64, i64, i64, i32, i32]
+    lib.ss_oracle_proj.restype = i32
+    lib.ss_oracle_proj.argtypes = [vp, vp, vp, i32, i32, i64, i64, i64, i64, i64, vp, vp, vp, i32]
     lib.ss_oracle_max_threads.restype = i32
     lib.ss_oracle_max_threads.argtypes = []
     return lib
@@ -266,6 +269,30 @@ def fwd_conv(x, conv_w, delta, A, B, C, conv_b=None, conv_state=None, D=None, z=
     return y, st, u
 
 
+def proj(u, W_x, W_dt, rank, dstate, conv_w=None, conv_b=None, conv_state=None, nthreads=0, _lib=None):
+    """Projections of the token inputs: xp = W_x u_t, delta_raw = W_dt xp[:rank],
+    B = xp[rank:rank+N], C = xp[rank+N:rank+2N] (see ss_oracle_proj). u (batch, L, dim) is
+    float32, uint16 (bf16 bits) or float64; with conv_w it is x, and u = conv_silu(x, ...)
+    first (fp64). W_x (rank + 2N, dim) and W_dt (dim, rank): float32 or uint16 (bf16 bits).
+    Returns (delta_raw, B, C) as float64."""
+    lib = _lib or _load()
+    if conv_w is not None:
+        u = conv_silu(u, conv_w, conv_b, conv_state, nthreads=nthreads, _lib=lib)
+    u, W_x, W_dt = _c(u), _c(W_x), _c(W_dt)
+    batch, L, dim = u.shape
+    if W_x.shape != (rank + 2 * dstate, dim) or W_dt.shape != (dim, rank):
+        raise ValueError("bad W_x or W_dt shape")
+    wdt = _dtype_of(W_x, W_dt)
+    delta_raw = np.empty((batch, L, dim), np.float64)
+    B = np.empty((batch, L, dstate), np.float64)
+    C = np.empty((batch, L, dstate), np.float64)
+    rc = lib.ss_oracle_proj(_ptr(u), _ptr(W_x), _ptr(W_dt), _dtype_of(u), wdt, batch, L, dim, dstate, rank,
+                            _ptr(delta_raw), _ptr(B), _ptr(C), int(nthreads))
+    if rc != 0:
+        raise ValueError("ss_oracle_proj rejected its arguments")
+    return delta_raw, B, C
+
+
 class Library:
     """The oracle API bound to another build of the same C source (used by the tests that
     plant mistakes in a copy of the oracle and check that the pins catch them)."""
@@ -287,3 +314,6 @@ class Library:
 
     def fwd_conv(self, *a, **k):
         return fwd_conv(*a, _lib=self._h, **k)
+
+    def proj(self, *a, **k):
+        return proj(*a, _lib=self._h, **k)

@@ -426,6 +426,63 @@ int ss_oracle_conv_silu(const void* x, const float* conv_w, const float* conv_b,
   return 0;
 }
 
+/* ----------------------------------------------------------------------------------------
+ * Input-dependent projections: B_t, C_t and the step come from linear maps of the token's
+ * input vector u_t ("Mamba：选择性状态空间模型入门教程", section "Mamba 的关键创新：选择性
+ * 机制": B, C and the step are linear functions of x_t; "Mamba：选择性状态空间的线性时间
+ * 序列建模", table "算法对比（核心直觉）", row S6: s_B(x_t), s_C(x_t) have shape (B, L, N)
+ * and the step is tau(Delta + s_Delta(x_t)), the bias added afterwards by the scan). The
+ * pages give no rank for the step map; it is taken as the low-rank product W_dt W_x[0:rank]
+ * (rank = dim expresses any full map):
+ *   xp[o]             = sum_d W_x[o, d] * u[b,t,d]          o < rank + 2 dstate
+ *   delta_raw[b,t,d]  = sum_r W_dt[d, r] * xp[r]             r < rank
+ *   B[b,t,n]          = xp[rank + n]
+ *   C[b,t,n]          = xp[rank + dstate + n]
+ * u is u_dtype (f32 / bf16 / f64, (batch, seqlen, dim)); W_x (rank + 2 dstate, dim) and
+ * W_dt (dim, rank) are w_dtype (f32 / bf16); outputs fp64. Sums run in index order in
+ * double. Returns 0, or -1 on a bad argument.
+ */
+int ss_oracle_proj(const void* u, const void* W_x, const void* W_dt, int u_dtype, int w_dtype,
+                   int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t rank,
+                   double* delta_raw, double* B, double* C, int nthreads) {
+  if (!u || !W_x || !W_dt || !delta_raw || !B || !C) return -1;
+  if (batch < 0 || seqlen < 0 || dim < 1 || dstate < 1 || rank < 1) return -1;
+  if (!dtype_ok(u_dtype) || (w_dtype != ORACLE_F32 && w_dtype != ORACLE_BF16)) return -1;
+  const int64_t nx = rank + 2 * dstate;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int bad = 0;
+#pragma omp parallel reduction(| : bad)
+  {
+    double* xp = (double*)malloc((size_t)nx * sizeof(double));
+    if (!xp) bad = 1;
+#pragma omp for schedule(static)
+    for (int64_t bt = 0; bt < batch * seqlen; ++bt) {
+      if (!xp) continue;
+      const int64_t ub = bt * dim;
+      for (int64_t o = 0; o < nx; ++o) {
+        double acc = 0.0;
+        for (int64_t d = 0; d < dim; ++d) acc += in_at(W_x, w_dtype, o * dim + d) * in_at(u, u_dtype, ub + d);
+        xp[o] = acc;
+      }
+      for (int64_t d = 0; d < dim; ++d) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < rank; ++r) acc += in_at(W_dt, w_dtype, d * rank + r) * xp[r];
+        delta_raw[ub + d] = acc;
+      }
+      for (int64_t n = 0; n < dstate; ++n) {
+        B[bt * dstate + n] = xp[rank + n];
+        C[bt * dstate + n] = xp[rank + dstate + n];
+      }
+    }
+    free(xp);
+  }
+  return bad ? -1 : 0;
+}
+
 int ss_oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

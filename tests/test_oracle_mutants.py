@@ -1,5 +1,6 @@
 """Plant plausible mistakes in a copy of the oracle's C source (on the CPU) and check
-that the pins in test_oracle_pins.py and test_oracle_bwd_pins.py catch every one."""
+that the pins in test_oracle_pins.py, test_oracle_bwd_pins.py, test_oracle_conv_pins.py and
+test_oracle_proj_pins.py catch every one."""
 import os
 import shutil
 
@@ -10,6 +11,7 @@ import oracle
 from tests import test_oracle_bwd_pins as bpins
 from tests import test_oracle_conv_pins as cpins
 from tests import test_oracle_pins as pins
+from tests import test_oracle_proj_pins as ppins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ss_oracle.c")
 
@@ -67,6 +69,14 @@ MUTANTS = [
     ("conv_state_reversed", [("(double)conv_state[(b * dim + d) * (kconv - 1) + (kconv - 1) + tau]",
                               "(double)conv_state[(b * dim + d) * (kconv - 1) - 1 - tau]")]),
     ("conv_acausal", [("const int64_t tau = t - (kconv - 1) + m;", "const int64_t tau = t + m;")]),
+    # input projections
+    ("proj_B_C_swapped", [("B[bt * dstate + n] = xp[rank + n];", "B[bt * dstate + n] = xp[rank + dstate + n];"),
+                          ("C[bt * dstate + n] = xp[rank + dstate + n];", "C[bt * dstate + n] = xp[rank + n];")]),
+    ("proj_Wx_transposed", [("in_at(W_x, w_dtype, o * dim + d)", "in_at(W_x, w_dtype, d * nx + o)")]),
+    ("proj_Wdt_transposed", [("in_at(W_dt, w_dtype, d * rank + r)", "in_at(W_dt, w_dtype, r * dim + d)")]),
+    ("proj_B_off_by_one", [("B[bt * dstate + n] = xp[rank + n];", "B[bt * dstate + n] = xp[rank - 1 + n];")]),
+    ("proj_step_from_inputs", [("acc += in_at(W_dt, w_dtype, d * rank + r) * xp[r];",
+                                "acc += in_at(W_dt, w_dtype, d * rank + r) * in_at(u, u_dtype, ub + r);")]),
 ]
 
 
@@ -97,6 +107,9 @@ def pin_suite(lib):
         ("conv_numpy", lambda: cpins.test_conv_matches_numpy_convolve(lib, 4, True, True)),
         ("conv_impulse", lambda: cpins.test_impulse_response(lib)),
         ("conv_split", lambda: cpins.test_split_continues_with_conv_state(lib)),
+        ("proj_numpy", lambda: ppins.test_matches_numpy_product_other_association(lib)),
+        ("proj_selection", lambda: ppins.test_selection_matrices_are_exact(lib)),
+        ("proj_rank1", lambda: ppins.test_rank_one_closed_form(lib)),
     ]
     for name, fn in checks:
         try:
