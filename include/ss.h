@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 5
+#define SS_ABI_VERSION 6
 #define SS_MAX_DSTATE 16
 
 typedef enum {
@@ -219,6 +219,35 @@ int ss_bwd(const void* u, const void* delta, const float* A, const void* B, cons
            float* dA, float* dB, float* dC, float* dD, float* dz, float* ddelta_bias, float* dh0,
            void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t dim,
            int64_t dstate, int in_dtype, void* stream);
+
+/*
+ * ss_proj -- the input projections that give the scan its step, B and C: linear maps of
+ * each token's input vector ("Mamba：选择性状态空间模型入门教程", section "Mamba 的关键创新：
+ * 选择性机制": B, C and the step are linear functions of x_t; "Mamba：选择性状态空间的线性
+ * 时间序列建模", table "算法对比（核心直觉）", row S6: s_B(x_t), s_C(x_t) of shape (B, L, N),
+ * step tau(Delta + s_Delta(x_t))). The step map is low-rank, W_dt W_x[0:rank] (rank = dim
+ * expresses any full map). For every token t (b, t flattened):
+ *   xp_t          = W_x u_t                       rank + 2*dstate outputs
+ *   delta_raw_t   = W_dt xp_t[0 : rank]           dim outputs (ss_fwd adds delta_bias, softplus)
+ *   B_t           = xp_t[rank : rank + dstate]
+ *   C_t           = xp_t[rank + dstate : rank + 2*dstate]
+ *
+ *   u          (batch, seqlen, dim)          in_dtype, device, read
+ *   W_x        (rank + 2*dstate, dim)        in_dtype, device, read (out x in, row-major)
+ *   W_dt       (dim, rank)                   in_dtype, device, read
+ *   delta_raw  (batch, seqlen, dim)          in_dtype, device, written
+ *   B, C       (batch, seqlen, dstate)       in_dtype, device, written
+ * The products run on the matrix cores with fp32 accumulation; bf16 outputs are rounded to
+ * nearest even. Requirements: dim % 8 == 0 and dim <= 2^20; rank % 8 == 0 and
+ * 8 <= rank <= 256; 1 <= dstate <= 16; u, W_x, W_dt, delta_raw 16-byte aligned, B and C
+ * element aligned. seqlen == 0 writes nothing (the token arrays may then be NULL).
+ * Errors: SS_ERR_NULL_ARG, SS_ERR_BAD_DTYPE, SS_ERR_BAD_SHAPE (sizes, the divisibility
+ * above), SS_ERR_UNSUPPORTED_N (dstate > 16), SS_ERR_MISALIGNED, SS_ERR_DEVICE, SS_ERR_HIP.
+ * Nothing is allocated; the work is enqueued on stream.
+ */
+int ss_proj(const void* u, const void* W_x, const void* W_dt, void* delta_raw, void* B, void* C,
+            int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t rank, int in_dtype,
+            void* stream);
 
 #ifdef __cplusplus
 }

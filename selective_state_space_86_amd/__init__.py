@@ -2,11 +2,11 @@
 
 Every step of the scan runs in the HIP kernels of ``libss.so``; this package only
 marshals torch device tensors into the C ABI declared in ``include/ss.h``
-(``ss_fwd``, ``ss_fwd_conv``, ``ss_step``, ``ss_bwd``). The library is loaded on first use and a missing or
+(``ss_fwd``, ``ss_fwd_conv``, ``ss_step``, ``ss_bwd``, ``ss_proj``). The library is loaded on first use and a missing or
 unloadable build raises: there is no fallback path.
 """
 from ._binding import (SSError, bwd, bwd_workspace_size, fwd, fwd_conv, lib_path,  # noqa: F401
-                       load_library, step)
+                       load_library, proj, step)
 
-__all__ = ["fwd", "fwd_conv", "step", "bwd", "bwd_workspace_size", "SSError", "load_library",
+__all__ = ["fwd", "fwd_conv", "step", "bwd", "bwd_workspace_size", "proj", "SSError", "load_library",
            "lib_path"]

@@ -12,9 +12,9 @@ _lib = None
 
 F32, BF16 = 0, 1
 DISC_DT, DISC_ZOH = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_fwd_conv", "ss_step",
-           "ss_step_ex", "ss_bwd_workspace_size", "ss_bwd")
+           "ss_step_ex", "ss_bwd_workspace_size", "ss_bwd", "ss_proj")
 
 
 class FwdOptions(ctypes.Structure):
@@ -66,6 +66,8 @@ def load_library():
     lib.ss_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                            vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                            i64, i64, i64, i64, i32, vp]
+    lib.ss_proj.restype = i32
+    lib.ss_proj.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     if lib.ss_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{_LIB_PATH} has ABI version {lib.ss_abi_version()}, this binding "
                            f"needs {ABI_VERSION}: rebuild it")
@@ -290,3 +292,32 @@ def bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True, h
     if rc != 0:
         raise SSError(rc, "ss_bwd")
     return out
+
+
+def proj(u, W_x, W_dt, rank, delta_raw=None, B=None, C=None, stream=None):
+    """Input projections (``ss_proj``): for every token, xp = W_x u_t, delta_raw = W_dt
+    xp[:rank], B = xp[rank:rank+N], C = xp[rank+N:]. u: (batch, L, dim); W_x: (rank + 2N,
+    dim); W_dt: (dim, rank); all float32 or all bfloat16. Returns (delta_raw, B, C) in the
+    same dtype, ready for ``fwd``."""
+    dev = u.device
+    batch, L, dim = u.shape
+    N = (W_x.shape[0] - rank) // 2
+    dt = _in_dtype(u, W_x, W_dt)
+    tdt = u.dtype
+    _check(u, "u", dev)
+    _check(W_x, "W_x", dev, tdt, (rank + 2 * N, dim))
+    _check(W_dt, "W_dt", dev, tdt, (dim, rank))
+    if delta_raw is None:
+        delta_raw = torch.empty((batch, L, dim), dtype=tdt, device=dev)
+    if B is None:
+        B = torch.empty((batch, L, N), dtype=tdt, device=dev)
+    if C is None:
+        C = torch.empty((batch, L, N), dtype=tdt, device=dev)
+    _check(delta_raw, "delta_raw", dev, tdt, (batch, L, dim))
+    _check(B, "B", dev, tdt, (batch, L, N))
+    _check(C, "C", dev, tdt, (batch, L, N))
+    rc = load_library().ss_proj(_ptr(u), _ptr(W_x), _ptr(W_dt), _ptr(delta_raw), _ptr(B), _ptr(C),
+                                batch, L, dim, N, int(rank), dt, _stream(dev, stream))
+    if rc != 0:
+        raise SSError(rc, "ss_proj")
+    return delta_raw, B, C

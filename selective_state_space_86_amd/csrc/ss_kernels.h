@@ -88,6 +88,18 @@ struct BwdArgs {
 
 constexpr int kBwdChunk = 2;  // tokens per lane and chunk in the backward kernels
 
+// Validated arguments of one ss_proj call (all token arrays and weights in one dtype).
+struct ProjArgs {
+  const void* u;            // (tokens, dim)
+  const void* W_x;          // (rank + 2 dstate, dim)
+  const void* W_dt;         // (dim, rank)
+  void* delta_raw;          // (tokens, dim)
+  void* B;                  // (tokens, dstate)
+  void* C;                  // (tokens, dstate)
+  int64_t tokens, dim, dstate, rank;
+  int dtype;
+};
+
 hipError_t fwd_seq(const FwdArgs& a, hipStream_t s);
 bool fwd_state_supported(const FwdArgs& a);
 hipError_t fwd_state(const FwdArgs& a, hipStream_t s);
@@ -100,6 +112,8 @@ struct ChunkPlan {
 };
 hipError_t fwd_chunked(const FwdArgs& a, ChunkPlan plan, hipStream_t s);
 ChunkPlan fwd_chunked_pick(const FwdArgs& a, int cus);
+hipError_t proj(const ProjArgs& a, int cus, hipStream_t s);
+int proj_step_tiles(int64_t rank);
 hipError_t step(const StepArgs& a, hipStream_t s);
 int64_t bwd_tile_tokens();
 size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);

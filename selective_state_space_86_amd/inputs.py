@@ -132,6 +132,29 @@ def make(w: Workload, seed: int = 0, device="cpu", time_major: bool = False) -> 
     return out
 
 
+def proj_rank(dim: int) -> int:
+    """Rank of the step projection in the projection workloads: dim / 32 rounded up to a
+    multiple of 8 (1536 -> 48, 4096 -> 128, 5120 -> 160)."""
+    return max(8, -(-dim // 256) * 8)
+
+
+def make_proj(w: Workload, rank: int, seed: int = 0, device="cpu") -> dict:
+    """Inputs of the projections for workload ``w``: u (batch, seqlen, dim) ~ N(0, 1),
+    W_x (rank + 2 dstate, dim) ~ N(0, 1/dim) and W_dt (dim, rank) ~ N(0, 1/rank), so every
+    output is O(1); all in w.dtype (bf16: fp32 draws rounded to nearest even)."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(_seed(w.name + "/proj", seed))
+    f32 = dict(dtype=torch.float32, device=dev, generator=g)
+    d, n = w.dim, w.dstate
+    out = dict(u=torch.randn((w.batch, w.seqlen, d), **f32),
+               W_x=torch.randn((rank + 2 * n, d), **f32) / math.sqrt(d),
+               W_dt=torch.randn((d, rank), **f32) / math.sqrt(rank))
+    if w.dtype == "bf16":
+        out = {k: v.to(torch.bfloat16) for k, v in out.items()}
+    return out
+
+
 def to_numpy(t):
     """A host numpy view of a tensor for the oracle: float32 stays float32, bfloat16
     becomes uint16 bit patterns. None stays None."""

@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss_abi_version() == _binding.ABI_VERSION == 5
+    assert lib.ss_abi_version() == _binding.ABI_VERSION == 6
     for s in range(0, 9):
         assert lib.ss_status_string(s)
     assert b"unknown" in lib.ss_status_string(99)
@@ -210,3 +210,29 @@ def conv_call(lib, **kw):
 ])
 def test_fwd_conv_validation(lib, kw, code):
     assert conv_call(lib, **kw) == code
+
+
+def proj_call(lib, **kw):
+    a = dict(u=FAKE, wx=FAKE, wdt=FAKE, dr=FAKE, B=FAKE, C=FAKE, batch=1, L=4, dim=64, N=16, rank=16, dtype=0)
+    a.update(kw)
+    return lib.ss_proj(a["u"], a["wx"], a["wdt"], a["dr"], a["B"], a["C"], a["batch"], a["L"], a["dim"], a["N"],
+                       a["rank"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(u=None), 1), (dict(wx=None), 1), (dict(wdt=None), 1), (dict(B=None), 1), (dict(dr=None), 1),
+    (dict(dtype=2), 3), (dict(batch=0), 2), (dict(L=-1), 2), (dict(dim=60), 2), (dict(dim=0), 2),
+    (dict(rank=12), 2), (dict(rank=0), 2), (dict(rank=264), 2), (dict(N=0), 2), (dict(N=17), 4),
+    (dict(u=FAKE + 8), 5), (dict(wx=FAKE + 4), 5), (dict(wdt=FAKE + 8), 5), (dict(dr=FAKE + 4), 5),
+    (dict(B=FAKE + 2), 5), (dict(C=FAKE + 1, dtype=1), 5),
+])
+def test_proj_validation(lib, kw, code):
+    """ss_proj rejects bad arguments with their codes before any device work."""
+    assert proj_call(lib, **kw) == code
+
+
+def test_proj_empty_sequence_needs_no_token_arrays(lib):
+    """With seqlen 0 the token arrays may be NULL: every argument check passes, and the device
+    query answers (SS_OK on a gfx950; SS_ERR_HIP without a GPU, SS_ERR_DEVICE on another)."""
+    rc = proj_call(lib, u=None, dr=None, B=None, C=None, L=0)
+    assert rc in (0, 6, 7)
