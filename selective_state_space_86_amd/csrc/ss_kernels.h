@@ -113,7 +113,7 @@ struct ChunkPlan {
 hipError_t fwd_chunked(const FwdArgs& a, ChunkPlan plan, hipStream_t s);
 ChunkPlan fwd_chunked_pick(const FwdArgs& a, int cus);
 hipError_t proj(const ProjArgs& a, int cus, hipStream_t s);
-int proj_step_tiles(int64_t rank);
+int proj_step_tiles(int64_t rank, int dtype);
 hipError_t step(const StepArgs& a, hipStream_t s);
 int64_t bwd_tile_tokens();
 size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);

@@ -52,8 +52,6 @@ struct Elem<uint16_t> {
   static constexpr int kCh = 8;
 };
 
-constexpr int kUnits = 4;       // 16-byte units per W_x row and phase-1 LDS chunk (one MFMA K block)
-constexpr int kGroup = 32;      // channels per phase-2 group: two 16-channel output tiles
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs)
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
@@ -63,14 +61,12 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 }
 __device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
 
-// one K block of phase 1: a = 16 bytes of W_x, b = 16 bytes of the inputs
-__device__ __forceinline__ f32x4 mfma_block(float*, const u32x4& a, const u32x4& b, f32x4 acc) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), acc, 0, 0, 0);
-  return acc;
+// Phase-1 MFMA step e of a K block (a = 16 bytes of W_x, b = 16 bytes of the inputs): fp32
+// takes 4 steps of K = 4 (element e of each), bf16 one step of K = 32.
+__device__ __forceinline__ f32x4 mfma_step(float*, const u32x4& a, const u32x4& b, int e, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), acc, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_block(uint16_t*, const u32x4& a, const u32x4& b, f32x4 acc) {
+__device__ __forceinline__ f32x4 mfma_step(uint16_t*, const u32x4& a, const u32x4& b, int, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
                                                  0, 0, 0);
 }
@@ -88,10 +84,17 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
   constexpr int ROWS = T1 * 16;               // W_x rows staged per chunk (zeros where absent)
   constexpr int CH = Elem<T>::kCh;
   constexpr int ES = static_cast<int>(sizeof(T));
+  constexpr int KU = ES == 4 ? 1 : 2;         // MFMA K blocks per phase-1 chunk
+  constexpr int CU = 4 * KU;                  // 16-byte units per W_x row and chunk
+  constexpr int KB = CU * CH;                 // channels per chunk (16 fp32, 64 bf16)
+  constexpr int GC = ES == 4 ? 32 : 64;       // channels per phase-2 group
+  constexpr int TG = GC / 16;                 // output tiles per group
   constexpr int RPU = RT * 16 / CH;           // 16-byte units per staged W_dt row (RT*16 ranks)
-  constexpr int P1 = ROWS * (kUnits + 1);     // padded rows (one spare unit against bank conflicts)
-  constexpr int P2 = kGroup * (RPU + 1);
+  constexpr int P1 = ROWS * (CU + 1);         // padded rows (one spare unit against bank conflicts)
+  constexpr int P2 = GC * (RPU + 1);
   constexpr int HALF = P1 > P2 ? P1 : P2;
+  constexpr int KSTEP = ES == 4 ? 4 : 1;      // MFMA steps per K block
+  constexpr int PD = ES == 4 ? 3 : 2;         // chunks (phase 1) / groups (phase 2) in flight
   __shared__ u32x4 lds[2 * HALF];
   T* tag = nullptr;
 
@@ -108,10 +111,12 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
   for (int s = 0; s < S; ++s) xrow[s] = static_cast<uint32_t>((w * 16 * S + s * 16 + li) * row_bytes);
 
   // ---- phase 1: xp^T = W_x X^T ------------------------------------------------------------
+  // Chunk c of W_x is requested PD + 1 iterations before it is used and staged in LDS one
+  // iteration before; the inputs of chunk c are requested PD iterations before. The loop is
+  // unrolled by PD so every register slot is static.
   const auto rwx = rsrc(a.W_x, (rank + 2 * N) * row_bytes);
-  constexpr int EPL = (ROWS * kUnits + 255) / 256;  // staged units per lane and chunk
-  // source row of staged row r (-1: zero row)
-  auto wx_row = [&](int r) -> int64_t {
+  constexpr int EPL = (ROWS * CU + 255) / 256;  // staged units per lane and chunk
+  auto wx_row = [&](int r) -> int64_t {         // source row of staged row r (-1: zero row)
     const int c = r >> 4, i = r & 15;
     if (c < RT) return 16 * c + i < rank ? 16 * c + i : -1;
     if (i >= N) return -1;
@@ -121,9 +126,9 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
 #pragma unroll
     for (int m = 0; m < EPL; ++m) {
       const int e = tid + 256 * m;
-      const int r = e / kUnits, un = e % kUnits;
+      const int r = e / CU, un = e % CU;
       const int64_t kk = k0 + un * CH;
-      const int64_t sr = e < ROWS * kUnits ? wx_row(r) : -1;
+      const int64_t sr = e < ROWS * CU ? wx_row(r) : -1;
       const uint32_t off = (sr >= 0 && kk < dim) ? static_cast<uint32_t>((sr * dim + kk) * ES) : kDropOffset;
       v[m] = __builtin_amdgcn_raw_buffer_load_b128(rwx, off, 0, 0);
     }
@@ -132,15 +137,18 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
 #pragma unroll
     for (int m = 0; m < EPL; ++m) {
       const int e = tid + 256 * m;
-      if (e < ROWS * kUnits) lds[buf * HALF + (e / kUnits) * (kUnits + 1) + e % kUnits] = v[m];
+      if (e < ROWS * CU) lds[buf * HALF + (e / CU) * (CU + 1) + e % CU] = v[m];
     }
   };
-  auto load_x = [&](u32x4 (&x)[S], int64_t k0) {
-    const int64_t kk = k0 + lq * CH;
+  auto load_x = [&](u32x4 (&x)[S][KU], int64_t k0) {
 #pragma unroll
-    for (int s = 0; s < S; ++s)
-      x[s] = __builtin_amdgcn_raw_buffer_load_b128(ru, kk < dim ? xrow[s] + static_cast<uint32_t>(kk * ES) : kDropOffset,
-                                                   0, 0);
+    for (int kb = 0; kb < KU; ++kb) {
+      const int64_t kk = k0 + (4 * kb + lq) * CH;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        x[s][kb] = __builtin_amdgcn_raw_buffer_load_b128(
+            ru, kk < dim ? xrow[s] + static_cast<uint32_t>(kk * ES) : kDropOffset, 0, 0);
+    }
   };
 
   f32x4 acc[S][T1];
@@ -149,37 +157,44 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
 #pragma unroll
     for (int c = 0; c < T1; ++c) acc[s][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  constexpr int KB = kUnits * CH;  // channels per chunk
   const int64_t nchunks = (dim + KB - 1) / KB;
+  u32x4 wq[PD][EPL], xq[PD][S][KU];
   {
-    u32x4 wv[EPL];
-    load_wx(wv, 0);
-    store_wx(wv, 0);
+    u32x4 w0[EPL];
+    load_wx(w0, 0);
+    store_wx(w0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < PD; ++j) {
+    if (j + 1 < nchunks) load_wx(wq[(j + 1) % PD], (j + 1) * KB);
+    if (j < nchunks) load_x(xq[j], j * KB);
   }
   __syncthreads();
-  u32x4 xc[S], xn[S];
-  load_x(xc, 0);
-  for (int64_t ci = 0; ci < nchunks; ++ci) {
-    const int buf = static_cast<int>(ci & 1);
-    const bool more = ci + 1 < nchunks;
-    u32x4 wv[EPL];
-    if (more) {
-      load_wx(wv, (ci + 1) * KB);
-      load_x(xn, (ci + 1) * KB);
-    }
-    const u32x4* lb = lds + buf * HALF;
+  for (int64_t base = 0; base < nchunks; base += PD) {
 #pragma unroll
-    for (int c = 0; c < T1; ++c) {
-      const u32x4 av = lb[(c * 16 + li) * (kUnits + 1) + lq];
+    for (int j = 0; j < PD; ++j) {
+      const int64_t ci = base + j;
+      if (ci < nchunks) {
+        const u32x4* lb = lds + static_cast<int>(ci & 1) * HALF;
 #pragma unroll
-      for (int s = 0; s < S; ++s) acc[s][c] = mfma_block(tag, av, xc[s], acc[s][c]);
-    }
-    if (more) {
-      store_wx(wv, buf ^ 1);
+        for (int kb = 0; kb < KU; ++kb) {
+          u32x4 av[T1];
 #pragma unroll
-      for (int s = 0; s < S; ++s) xc[s] = xn[s];
+          for (int c = 0; c < T1; ++c) av[c] = lb[(c * 16 + li) * (CU + 1) + 4 * kb + lq];
+          // consecutive MFMAs go to different tiles, so none waits on the one before
+#pragma unroll
+          for (int e = 0; e < KSTEP; ++e)
+#pragma unroll
+            for (int c = 0; c < T1; ++c)
+#pragma unroll
+              for (int s = 0; s < S; ++s) acc[s][c] = mfma_step(tag, av[c], xq[j][s][kb], e, acc[s][c]);
+        }
+        if (ci + 1 < nchunks) store_wx(wq[(j + 1) % PD], static_cast<int>((ci + 1) & 1));
+        if (ci + 1 + PD < nchunks) load_wx(wq[(j + 1) % PD], (ci + 1 + PD) * KB);
+        if (ci + PD < nchunks) load_x(xq[j], (ci + PD) * KB);
+        __syncthreads();
+      }
     }
-    __syncthreads();
   }
 
   // ---- B and C ----------------------------------------------------------------------------
@@ -203,9 +218,9 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
   // ---- phase 2: delta_raw = xp[:, :rank] W_dt^T --------------------------------------------
   // The intermediate as phase-2 A operands: fp32 uses acc directly; bf16 packs tiles 2s, 2s+1
   // into 8 bf16 values, as a hi part and a lo (remainder) part.
-  constexpr int NS = (sizeof(T) == 4) ? RT : RT / 2;  // bf16 steps (RT is even for bf16)
-  i16x8 ahi[S][NS > 0 ? NS : 1], alo[S][NS > 0 ? NS : 1];
-  if constexpr (sizeof(T) == 2) {
+  constexpr int NS = (ES == 4) ? RT : RT / 2;  // bf16 steps (RT is even for bf16)
+  i16x8 ahi[S][NS], alo[S][NS];
+  if constexpr (ES == 2) {
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
@@ -220,15 +235,15 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
   }
 
   const auto rdt = rsrc(a.W_dt, dim * rank * ES);
-  constexpr int GPL = (kGroup * RPU + 255) / 256;  // staged W_dt units per lane and group
+  constexpr int GPL = (GC * RPU + 255) / 256;  // staged W_dt units per lane and group
   auto load_dt = [&](u32x4 (&v)[GPL], int64_t d0) {
 #pragma unroll
     for (int m = 0; m < GPL; ++m) {
       const int e = tid + 256 * m;
       const int r = e / RPU, un = e % RPU;  // channel row within the group, unit along rank
       const int64_t d = d0 + r, rk = static_cast<int64_t>(un) * CH;
-      const uint32_t off = (e < kGroup * RPU && d < dim && rk < rank) ? static_cast<uint32_t>((d * rank + rk) * ES)
-                                                                       : kDropOffset;
+      const uint32_t off = (e < GC * RPU && d < dim && rk < rank) ? static_cast<uint32_t>((d * rank + rk) * ES)
+                                                                   : kDropOffset;
       v[m] = __builtin_amdgcn_raw_buffer_load_b128(rdt, off, 0, 0);
     }
   };
@@ -236,72 +251,93 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
 #pragma unroll
     for (int m = 0; m < GPL; ++m) {
       const int e = tid + 256 * m;
-      if (e < kGroup * RPU) lds[buf * HALF + (e / RPU) * (RPU + 1) + e % RPU] = v[m];
+      if (e < GC * RPU) lds[buf * HALF + (e / RPU) * (RPU + 1) + e % RPU] = v[m];
     }
   };
 
   const auto rd = rsrc(static_cast<T*>(a.delta_raw) + wg_tok0 * dim, (M - wg_tok0) * row_bytes);
-  const int64_t ngroups = (dim + kGroup - 1) / kGroup;
+  const int64_t ngroups = (dim + GC - 1) / GC;
+  u32x4 dq[PD][GPL];
   {
-    u32x4 dv[GPL];
-    load_dt(dv, 0);
-    store_dt(dv, 0);
+    u32x4 d0v[GPL];
+    load_dt(d0v, 0);
+    store_dt(d0v, 0);
   }
+#pragma unroll
+  for (int j = 0; j < PD; ++j)
+    if (j + 1 < ngroups) load_dt(dq[(j + 1) % PD], (j + 1) * GC);
   __syncthreads();
-  for (int64_t g = 0; g < ngroups; ++g) {
-    const int buf = static_cast<int>(g & 1);
-    const bool more = g + 1 < ngroups;
-    u32x4 dv[GPL];
-    if (more) load_dt(dv, (g + 1) * kGroup);
-    const u32x4* lb = lds + buf * HALF;
-    f32x4 o[S][2];
+  for (int64_t base = 0; base < ngroups; base += PD) {
 #pragma unroll
-    for (int s = 0; s < S; ++s) o[s][0] = o[s][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < PD; ++j) {
+      const int64_t g = base + j;
+      if (g < ngroups) {
+        const u32x4* lb = lds + static_cast<int>(g & 1) * HALF;
+        f32x4 o[S][TG];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const u32x4* row = lb + (16 * t + li) * (RPU + 1);
-      if constexpr (sizeof(T) == 4) {
+        for (int s = 0; s < S; ++s)
 #pragma unroll
-        for (int c = 0; c < RT; ++c) {
-          const u32x4 bv = row[4 * c + lq];  // ranks 16c + 4lq .. +3
+          for (int t = 0; t < TG; ++t) o[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (ES == 4) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
+          for (int c = 0; c < RT; ++c) {
+            u32x4 bv[TG];
 #pragma unroll
-            for (int s = 0; s < S; ++s)
-              o[s][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(acc[s][c][r], __uint_as_float(bv[r]), o[s][t], 0, 0, 0);
-        }
-      } else {
-        const u32x2* row2 = reinterpret_cast<const u32x2*>(row);
+            for (int t = 0; t < TG; ++t) bv[t] = lb[(16 * t + li) * (RPU + 1) + 4 * c + lq];  // ranks 16c + 4lq ..
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          // ranks 16(2st) + 4lq .. +3 and 16(2st+1) + 4lq .. +3, 4 bf16 each
-          const u32x2 lo8 = row2[(32 * st + 4 * lq) / 4];
-          const u32x2 hi8 = row2[(32 * st + 16 + 4 * lq) / 4];
-          const u32x4 bv = {lo8[0], lo8[1], hi8[0], hi8[1]};
-          const bf16x8 b8 = __builtin_bit_cast(bf16x8, bv);
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int s = 0; s < S; ++s) {
-            o[s][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ahi[s][st]), b8, o[s][t], 0, 0, 0);
-            o[s][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo[s][st]), b8, o[s][t], 0, 0, 0);
+              for (int t = 0; t < TG; ++t)
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+                  o[s][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(acc[s][c][r], __uint_as_float(bv[t][r]), o[s][t],
+                                                                 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            bf16x8 b8[TG];
+#pragma unroll
+            for (int t = 0; t < TG; ++t) {
+              // ranks 16(2st) + 4lq .. +3 and 16(2st+1) + 4lq .. +3, 4 bf16 each
+              const u32x2* row2 = reinterpret_cast<const u32x2*>(lb + (16 * t + li) * (RPU + 1));
+              const u32x2 lo8 = row2[8 * st + lq];
+              const u32x2 hi8 = row2[8 * st + 4 + lq];
+              const u32x4 bv = {lo8[0], lo8[1], hi8[0], hi8[1]};
+              b8[t] = __builtin_bit_cast(bf16x8, bv);
+            }
+#pragma unroll
+            for (int t = 0; t < TG; ++t)
+#pragma unroll
+              for (int s = 0; s < S; ++s)
+                o[s][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ahi[s][st]), b8[t], o[s][t],
+                                                                  0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < TG; ++t)
+#pragma unroll
+              for (int s = 0; s < S; ++s)
+                o[s][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo[s][st]), b8[t], o[s][t],
+                                                                  0, 0, 0);
           }
         }
+        // lane (channel li, q) holds tokens 4q .. 4q+3 of each strip for channel g*GC + 16t + li
+#pragma unroll
+        for (int t = 0; t < TG; ++t) {
+          const int64_t d = g * GC + 16 * t + li;
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int64_t tok = w * 16 * S + s * 16 + 4 * lq + r;
+              const uint32_t off = d < dim ? static_cast<uint32_t>(tok * row_bytes + d * ES) : kDropOffset;
+              store_elem(tag, rd, off, o[s][t][r]);
+            }
+        }
+        if (g + 1 < ngroups) store_dt(dq[(j + 1) % PD], static_cast<int>((g + 1) & 1));
+        if (g + 1 + PD < ngroups) load_dt(dq[(j + 1) % PD], (g + 1 + PD) * GC);
+        __syncthreads();
       }
     }
-    // lane (channel li, q) holds tokens 4q .. 4q+3 of each strip for channel d0 + 16t + li
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t d = g * kGroup + 16 * t + li;
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t tok = w * 16 * S + s * 16 + 4 * lq + r;
-          const uint32_t off = d < dim ? static_cast<uint32_t>(tok * row_bytes + d * ES) : kDropOffset;
-          store_elem(tag, rd, off, o[s][t][r]);
-        }
-    }
-    if (more) store_dt(dv, buf ^ 1);
-    __syncthreads();
   }
 }
 
@@ -315,6 +351,9 @@ hipError_t launch_proj(const ProjArgs& a, hipStream_t s) {
 
 template <typename T>
 hipError_t proj_t(const ProjArgs& a, int rt, int strips, hipStream_t s) {
+  if constexpr (sizeof(T) == 4) {  // fp32 also has 3 step tiles (rank 48: 1536 / 32)
+    if (rt == 3) return strips == 2 ? launch_proj<T, 3, 2>(a, s) : launch_proj<T, 3, 1>(a, s);
+  }
   if (strips == 2) {
     switch (rt) {
       case 2: return launch_proj<T, 2, 2>(a, s);
@@ -337,9 +376,11 @@ hipError_t proj_t(const ProjArgs& a, int rt, int strips, hipStream_t s) {
 
 }  // namespace
 
-// Step tiles: the instantiated even count covering rank (rank <= 256 by the host check).
-int proj_step_tiles(int64_t rank) {
+// Step tiles: the smallest instantiated count covering rank (rank <= 256 by the host check);
+// bf16 needs an even count (one MFMA step covers two tiles), fp32 also has 3.
+int proj_step_tiles(int64_t rank, int dtype) {
   const int need = static_cast<int>((rank + 15) / 16);
+  if (dtype != kBF16 && need == 3) return 3;
   for (int rt : {2, 4, 6, 8, 10, 12, 16})
     if (rt >= need) return rt;
   return 16;
@@ -348,7 +389,7 @@ int proj_step_tiles(int64_t rank) {
 // Two strips per wave (128 tokens per workgroup) halve the W_x and W_dt reads per token and
 // are used when that still leaves at least two workgroups per CU and the accumulators fit.
 hipError_t proj(const ProjArgs& a, int cus, hipStream_t s) {
-  const int rt = proj_step_tiles(a.rank);
+  const int rt = proj_step_tiles(a.rank, a.dtype);
   const int max_rt = a.dtype == kBF16 ? 6 : 10;  // the bf16 hi/lo operands need more registers
   const int strips = (rt <= max_rt && (a.tokens + 127) / 128 >= 2 * static_cast<int64_t>(cus)) ? 2 : 1;
   return a.dtype == kBF16 ? proj_t<uint16_t>(a, rt, strips, s) : proj_t<float>(a, rt, strips, s);

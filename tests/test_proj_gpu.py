@@ -81,7 +81,8 @@ def test_proj_matches_oracle(batch, L, dim, N, rank, dt):
 
 @pytest.mark.parametrize("rank", [8, 40, 72, 104, 136, 168, 200, 256])
 def test_proj_every_step_tile_count(rank):
-    """rank -> 2, 4, 6, 8, 10, 12 or 16 step tiles of 16 (zero-padded beyond rank)."""
+    """rank -> 2, 3 (fp32; bf16 rounds up to 4), 4, 6, 8, 10, 12 or 16 step tiles of 16
+    (zero-padded beyond rank)."""
     run_case(1, 48, 72, 16, rank, "f32", seed=102)
     run_case(1, 48, 72, 16, rank, "bf16", seed=103)
 
