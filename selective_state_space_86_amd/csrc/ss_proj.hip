@@ -23,7 +23,8 @@
 //    transpose of the intermediate (fp32: K index 4q of step (c, r) is rank 16c + 4q + r;
 //    bf16: one step covers tiles 2s and 2s+1, and the fp32 intermediate enters as a hi and a
 //    lo bf16 part, two MFMAs, so its rounding stays near 2^-17 relative).
-//  * B and C leave from tiles RT and RT + 1; delta_raw from the phase-2 accumulators. bf16
+//  * B and C leave from tiles RT and RT + 1; delta_raw from the phase-2 accumulators (bf16
+//    through a wave-private LDS block, so that every store is 16 bytes of a full row). bf16
 //    outputs are rounded to nearest even.
 // Shapes the host side guarantees: dim % 8 == 0, rank % 8 == 0, rank <= 16 RT, dstate <= 16,
 // 16-byte aligned u, W_x, W_dt and delta_raw.
@@ -96,6 +97,10 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
   constexpr int KSTEP = ES == 4 ? 4 : 1;      // MFMA steps per K block
   constexpr int PD = ES == 4 ? 3 : 2;         // chunks (phase 1) / groups (phase 2) in flight
   __shared__ u32x4 lds[2 * HALF];
+  // bf16 output tiles pass through a wave-private block so each lane stores 16 bytes of a
+  // 128-byte row (direct stores would write 32-byte pieces, twice the HBM write traffic)
+  constexpr int SROW = GC + 8;                // bf16 per staged row (16-byte pad)
+  __shared__ __attribute__((aligned(16))) uint16_t stage[ES == 2 ? 4 * S * 16 * SROW : 1];
   T* tag = nullptr;
 
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
@@ -321,17 +326,46 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
           }
         }
         // lane (channel li, q) holds tokens 4q .. 4q+3 of each strip for channel g*GC + 16t + li
+        if constexpr (ES == 4) {
 #pragma unroll
-        for (int t = 0; t < TG; ++t) {
-          const int64_t d = g * GC + 16 * t + li;
+          for (int t = 0; t < TG; ++t) {
+            const int64_t d = g * GC + 16 * t + li;
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int64_t tok = w * 16 * S + s * 16 + 4 * lq + r;
+                const uint32_t off = d < dim ? static_cast<uint32_t>(tok * row_bytes + d * ES) : kDropOffset;
+                store_elem(tag, rd, off, o[s][t][r]);
+              }
+          }
+        } else {
+          uint16_t* st = stage + w * (S * 16 * SROW);
 #pragma unroll
           for (int s = 0; s < S; ++s)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int64_t tok = w * 16 * S + s * 16 + 4 * lq + r;
-              const uint32_t off = d < dim ? static_cast<uint32_t>(tok * row_bytes + d * ES) : kDropOffset;
-              store_elem(tag, rd, off, o[s][t][r]);
+            for (int t = 0; t < TG; ++t)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                st[(s * 16 + 4 * lq + r) * SROW + 16 * t + li] = static_cast<uint16_t>(bf16_bits(o[s][t][r]));
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+          // 16 tokens x 128 bytes per strip = 128 pieces of 16 bytes: pieces l and l + 64
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int piece = l + 64 * h, tok = piece >> 3, col = (piece & 7) * 8;
+              const u32x4 v = *reinterpret_cast<const u32x4*>(st + (s * 16 + tok) * SROW + col);
+              const int64_t d = g * GC + col;
+              const int64_t tk = w * 16 * S + s * 16 + tok;
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  v, rd, d < dim ? static_cast<uint32_t>(tk * row_bytes + d * ES) : kDropOffset, 0, 0);
             }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         }
         if (g + 1 < ngroups) store_dt(dq[(j + 1) % PD], static_cast<int>((g + 1) & 1));
         if (g + 1 + PD < ngroups) load_dt(dq[(j + 1) % PD], (g + 1 + PD) * GC);
