@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 6
+#define SS_ABI_VERSION 7
 #define SS_MAX_DSTATE 16
 
 typedef enum {
@@ -248,6 +248,27 @@ int ss_bwd(const void* u, const void* delta, const float* A, const void* B, cons
 int ss_proj(const void* u, const void* W_x, const void* W_dt, void* delta_raw, void* B, void* C,
             int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t rank, int in_dtype,
             void* stream);
+
+/*
+ * ss_proj_conv -- ss_proj with the block's prologue fused into the input loads: the
+ * projections take u = silu(causal depthwise conv1d(x) + conv_b) ("Mamba：选择性状态空间的
+ * 线性时间序列建模", section "架构：极简设计"), formed per token in fp32 and never written, so
+ * x -> ss_proj_conv -> ss_fwd_conv runs the block's SSM path from its input without u in
+ * memory:
+ *   u[b,t,d] = silu(conv_b[d] + sum_{m=0}^{kconv-1} conv_w[d,m] * x[b, t-(kconv-1)+m, d])
+ *   x             (batch, seqlen, dim)       in_dtype, in place of ss_proj's u (16-byte aligned).
+ *   conv_w        (dim, kconv) fp32; kconv in 1..4 (else SS_ERR_BAD_SHAPE; NULL: SS_ERR_NULL_ARG).
+ *   conv_b        (dim) fp32, may be NULL (zero).
+ *   conv_state    (batch, dim, kconv - 1) fp32, may be NULL (zeros): the kconv - 1 inputs x
+ *                 before t = 0, oldest first.
+ * With bf16 x the fp32 u enters the matrix cores as a bf16 hi part and a bf16 remainder, so
+ * the products see u to about 2^-17 relative. Everything else (W_x .. C, requirements,
+ * errors) as in ss_proj.
+ */
+int ss_proj_conv(const void* x, const float* conv_w, const float* conv_b, const float* conv_state,
+                 int64_t kconv, const void* W_x, const void* W_dt, void* delta_raw, void* B, void* C,
+                 int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t rank, int in_dtype,
+                 void* stream);
 
 #ifdef __cplusplus
 }

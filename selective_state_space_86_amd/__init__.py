@@ -6,7 +6,7 @@ marshals torch device tensors into the C ABI declared in ``include/ss.h``
 unloadable build raises: there is no fallback path.
 """
 from ._binding import (SSError, bwd, bwd_workspace_size, fwd, fwd_conv, lib_path,  # noqa: F401
-                       load_library, proj, step)
+                       load_library, proj, proj_conv, step)
 
-__all__ = ["fwd", "fwd_conv", "step", "bwd", "bwd_workspace_size", "proj", "SSError", "load_library",
-           "lib_path"]
+__all__ = ["fwd", "fwd_conv", "step", "bwd", "bwd_workspace_size", "proj", "proj_conv", "SSError",
+           "load_library", "lib_path"]

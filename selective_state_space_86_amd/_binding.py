@@ -12,9 +12,9 @@ _lib = None
 
 F32, BF16 = 0, 1
 DISC_DT, DISC_ZOH = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_fwd_conv", "ss_step",
-           "ss_step_ex", "ss_bwd_workspace_size", "ss_bwd", "ss_proj")
+           "ss_step_ex", "ss_bwd_workspace_size", "ss_bwd", "ss_proj", "ss_proj_conv")
 
 
 class FwdOptions(ctypes.Structure):
@@ -68,6 +68,8 @@ def load_library():
                            i64, i64, i64, i64, i32, vp]
     lib.ss_proj.restype = i32
     lib.ss_proj.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    lib.ss_proj_conv.restype = i32
+    lib.ss_proj_conv.argtypes = [vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     if lib.ss_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{_LIB_PATH} has ABI version {lib.ss_abi_version()}, this binding "
                            f"needs {ABI_VERSION}: rebuild it")
@@ -294,15 +296,10 @@ def bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True, h
     return out
 
 
-def proj(u, W_x, W_dt, rank, delta_raw=None, B=None, C=None, stream=None):
-    """Input projections (``ss_proj``): for every token, xp = W_x u_t, delta_raw = W_dt
-    xp[:rank], B = xp[rank:rank+N], C = xp[rank+N:]. u: (batch, L, dim); W_x: (rank + 2N,
-    dim); W_dt: (dim, rank); all float32 or all bfloat16. Returns (delta_raw, B, C) in the
-    same dtype, ready for ``fwd``."""
+def _proj_outputs(u, W_x, W_dt, rank, delta_raw, B, C):
     dev = u.device
     batch, L, dim = u.shape
     N = (W_x.shape[0] - rank) // 2
-    dt = _in_dtype(u, W_x, W_dt)
     tdt = u.dtype
     _check(u, "u", dev)
     _check(W_x, "W_x", dev, tdt, (rank + 2 * N, dim))
@@ -316,8 +313,41 @@ def proj(u, W_x, W_dt, rank, delta_raw=None, B=None, C=None, stream=None):
     _check(delta_raw, "delta_raw", dev, tdt, (batch, L, dim))
     _check(B, "B", dev, tdt, (batch, L, N))
     _check(C, "C", dev, tdt, (batch, L, N))
+    return N, delta_raw, B, C
+
+
+def proj(u, W_x, W_dt, rank, delta_raw=None, B=None, C=None, stream=None):
+    """Input projections (``ss_proj``): for every token, xp = W_x u_t, delta_raw = W_dt
+    xp[:rank], B = xp[rank:rank+N], C = xp[rank+N:]. u: (batch, L, dim); W_x: (rank + 2N,
+    dim); W_dt: (dim, rank); all float32 or all bfloat16. Returns (delta_raw, B, C) in the
+    same dtype, ready for ``fwd``."""
+    dt = _in_dtype(u, W_x, W_dt)
+    batch, L, dim = u.shape
+    N, delta_raw, B, C = _proj_outputs(u, W_x, W_dt, rank, delta_raw, B, C)
     rc = load_library().ss_proj(_ptr(u), _ptr(W_x), _ptr(W_dt), _ptr(delta_raw), _ptr(B), _ptr(C),
-                                batch, L, dim, N, int(rank), dt, _stream(dev, stream))
+                                batch, L, dim, N, int(rank), dt, _stream(u.device, stream))
     if rc != 0:
         raise SSError(rc, "ss_proj")
+    return delta_raw, B, C
+
+
+def proj_conv(x, conv_w, W_x, W_dt, rank, conv_b=None, conv_state=None, delta_raw=None, B=None, C=None,
+              stream=None):
+    """Input projections with the fused prologue (``ss_proj_conv``): ``proj`` of u =
+    silu(causal depthwise conv1d(x) + conv_b), u formed on the fly and never stored. x:
+    (batch, L, dim) like ``proj``'s u; conv_w (dim, K) fp32, K <= 4; conv_b (dim,) fp32 or
+    None; conv_state (batch, dim, K-1) fp32 or None. Returns (delta_raw, B, C)."""
+    dev = x.device
+    dt = _in_dtype(x, W_x, W_dt)
+    batch, L, dim = x.shape
+    K = conv_w.shape[1] if conv_w.dim() == 2 else 0
+    _check(conv_w, "conv_w", dev, torch.float32, (dim, K))
+    _check(conv_b, "conv_b", dev, torch.float32, (dim,))
+    _check(conv_state, "conv_state", dev, torch.float32, (batch, dim, K - 1))
+    N, delta_raw, B, C = _proj_outputs(x, W_x, W_dt, rank, delta_raw, B, C)
+    rc = load_library().ss_proj_conv(_ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), K, _ptr(W_x),
+                                     _ptr(W_dt), _ptr(delta_raw), _ptr(B), _ptr(C), batch, L, dim, N, int(rank),
+                                     dt, _stream(dev, stream))
+    if rc != 0:
+        raise SSError(rc, "ss_proj_conv")
     return delta_raw, B, C

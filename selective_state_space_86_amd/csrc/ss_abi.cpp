@@ -208,27 +208,51 @@ int ss_step(float* state, const void* u, const void* delta, const float* A, cons
                     in_dtype, SS_DISC_DT, stream);
 }
 
-int ss_proj(const void* u, const void* W_x, const void* W_dt, void* delta_raw, void* B, void* C,
-            int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t rank, int in_dtype,
-            void* stream) {
+namespace {
+
+int proj_common(const void* u, const void* W_x, const void* W_dt, void* delta_raw, void* B, void* C,
+                int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t rank, int in_dtype,
+                int64_t kconv, const float* conv_w, const float* conv_b, const float* conv_state,
+                void* stream) {
   if (!W_x || !W_dt || (seqlen != 0 && (!u || !delta_raw || !B || !C))) return SS_ERR_NULL_ARG;
   if (in_dtype != SS_DTYPE_F32 && in_dtype != SS_DTYPE_BF16) return SS_ERR_BAD_DTYPE;
   if (batch < 1 || seqlen < 0 || dim < 8 || dstate < 1 || dim % 8 != 0 || dim > (1 << 20)) return SS_ERR_BAD_SHAPE;
   if (rank < 8 || rank > 256 || rank % 8 != 0) return SS_ERR_BAD_SHAPE;
   if (dstate > SS_MAX_DSTATE) return SS_ERR_UNSUPPORTED_N;
   if (!product_ok(batch, seqlen, dim) || !product_ok(batch, seqlen, dstate)) return SS_ERR_BAD_SHAPE;
-  if ((batch * seqlen + 63) / 64 > 0x7fffffffLL) return SS_ERR_BAD_SHAPE;
+  if ((batch * seqlen + 31) / 32 > 0x7fffffffLL) return SS_ERR_BAD_SHAPE;
   const size_t es = elem_size(in_dtype);
   if (!aligned(u, 16) || !aligned(W_x, 16) || !aligned(W_dt, 16) || !aligned(delta_raw, 16) ||
-      !aligned(B, es) || !aligned(C, es))
+      !aligned(B, es) || !aligned(C, es) || !aligned(conv_w, 4) || (conv_b && !aligned(conv_b, 4)) ||
+      (conv_state && !aligned(conv_state, 4)))
     return SS_ERR_MISALIGNED;
   int cus = 0;
   const int dv = check_device(&cus);
   if (dv != SS_OK) return dv;
   if (seqlen == 0) return SS_OK;
-  const ss::ProjArgs a{u, W_x, W_dt, delta_raw, B, C, batch * seqlen, dim, dstate, rank, in_dtype};
+  const ss::ProjArgs a{u,      W_x,   W_dt,     delta_raw, B,      C,      batch * seqlen, dim, dstate, rank,
+                       in_dtype, seqlen, static_cast<int>(kconv), conv_w, conv_b, conv_state};
   const hipError_t e = ss::proj(a, cus, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+}  // namespace
+
+int ss_proj(const void* u, const void* W_x, const void* W_dt, void* delta_raw, void* B, void* C,
+            int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t rank, int in_dtype,
+            void* stream) {
+  return proj_common(u, W_x, W_dt, delta_raw, B, C, batch, seqlen, dim, dstate, rank, in_dtype, 0, nullptr,
+                     nullptr, nullptr, stream);
+}
+
+int ss_proj_conv(const void* x, const float* conv_w, const float* conv_b, const float* conv_state,
+                 int64_t kconv, const void* W_x, const void* W_dt, void* delta_raw, void* B, void* C,
+                 int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t rank, int in_dtype,
+                 void* stream) {
+  if (!conv_w) return SS_ERR_NULL_ARG;
+  if (kconv < 1 || kconv > 4) return SS_ERR_BAD_SHAPE;
+  return proj_common(x, W_x, W_dt, delta_raw, B, C, batch, seqlen, dim, dstate, rank, in_dtype, kconv, conv_w,
+                     conv_b, conv_state, stream);
 }
 
 size_t ss_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {

@@ -98,6 +98,11 @@ struct ProjArgs {
   void* C;                  // (tokens, dstate)
   int64_t tokens, dim, dstate, rank;
   int dtype;
+  int64_t seqlen;           // tokens per sequence (the convolution restarts at each)
+  int kconv;                // 0: u is given; 1..4: u = silu(conv(x) + conv_b) with kconv taps
+  const float* conv_w;      // (dim, kconv)
+  const float* conv_b;      // (dim,) or null
+  const float* conv_state;  // (tokens / seqlen, dim, kconv - 1) or null (zeros)
 };
 
 hipError_t fwd_seq(const FwdArgs& a, hipStream_t s);

@@ -6,28 +6,35 @@
 // map taken low-rank: for every token t,
 //   xp_t = W_x u_t (rank + 2N outputs), delta_raw_t = W_dt xp_t[0:rank],
 //   B_t = xp_t[rank : rank+N], C_t = xp_t[rank+N : rank+2N].
-// Both products are dense contractions, so they run on MFMA: v_mfma_f32_16x16x4_f32 for fp32
-// operands, v_mfma_f32_16x16x32_bf16 for bf16, fp32 accumulation either way.
+// Optionally u_t is formed on the fly from the block input x as silu(conv_b + sum of the causal
+// depthwise conv taps over x_{t-K+1..t}) (the short convolution and SiLU in front of the SSM,
+// "Mamba：选择性状态空间的线性时间序列建模", section "架构：极简设计"), so u never goes
+// through HBM. Both products are dense contractions and run on MFMA:
+// v_mfma_f32_16x16x4_f32 for fp32 operands, v_mfma_f32_16x16x32_bf16 for bf16, fp32
+// accumulation either way.
 //
-// A workgroup is 4 waves; a wave owns S strips of 16 consecutive tokens.
-//  * Phase 1 computes xp transposed, D = W_x X^T, in T1 = RT + 2 output tiles of 16 rows
-//    (RT tiles for the step part, rows >= rank zero; one tile for B, one for C). The A operand
-//    (W_x, shared by all waves) goes through LDS in chunks of 4 16-byte units per row; the B
-//    operand (a strip's inputs) is loaded straight from HBM, 16 bytes per lane. Lane (i, q)
-//    of a 16-byte unit holds channels k0 + (4h + q) * CH .. + CH - 1 (CH = 4 fp32 / 8 bf16),
-//    and both operands use that same channel-to-K map, so the contraction covers every
-//    channel once whatever order the MFMA steps take.
-//  * The phase-1 accumulators are laid out exactly as the A operand of phase 2: lane
-//    (token i, q) holds xp[i][16c + 4q + r] in register r of tile c. Phase 2 computes
-//    delta_raw = xp[:, :rank] W_dt^T per 32-channel group with W_dt staged in LDS and no
-//    transpose of the intermediate (fp32: K index 4q of step (c, r) is rank 16c + 4q + r;
-//    bf16: one step covers tiles 2s and 2s+1, and the fp32 intermediate enters as a hi and a
-//    lo bf16 part, two MFMAs, so its rounding stays near 2^-17 relative).
-//  * B and C leave from tiles RT and RT + 1; delta_raw from the phase-2 accumulators (bf16
-//    through a wave-private LDS block, so that every store is 16 bytes of a full row). bf16
-//    outputs are rounded to nearest even.
+// A workgroup is 4 waves and owns TOK = 16 S consecutive tokens (S strips of 16).
+//  * Phase 1 (xp^T = W_x X^T) is split over K: wave w takes a quarter of the channel blocks
+//    and computes all T1 = RT + 2 output tiles (RT for the step part, rows >= rank zero; one
+//    for B, one for C) for all S strips, so each fragment it loads feeds T1 or S MFMAs and
+//    nothing is shared in the main loop. Both operands come straight from global memory, 16
+//    bytes per lane (lane (i, q) holds channels k0 + q CH .. + CH - 1 of token or row i), with
+//    a few stages in flight. With the convolution, the window x_{t-1..t-3} of lane i is
+//    taken from lanes i-1..i-3 of the same 16-lane row (DPP row rotates; the previous strip,
+//    or a halo load for the first one, supplies the rows' first lanes), and a token whose
+//    window crosses the start of its sequence takes the conv state (or zeros) there. A bf16
+//    convolution output enters the MFMA as a hi and a lo bf16 part, so it keeps ~2^-17
+//    relative precision.
+//  * The four partial sums of every (strip, tile) are added in a fixed order through LDS,
+//    two (strip, tile) units per wave per round; B and C leave from there, the step part goes
+//    to an LDS copy of xp (fp32, or bf16 hi and lo parts).
+//  * Phase 2 computes delta_raw^T = W_dt xp^T: wave w takes every fourth group of 16 TG
+//    channels, with the W_dt fragments (the A operand) from global memory one group ahead
+//    and the xp fragments (the B operand) from the LDS copy. The A rows of a group are
+//    permuted so that each lane ends up with consecutive channels of one token: every store
+//    is 16 bytes of a row.
 // Shapes the host side guarantees: dim % 8 == 0, rank % 8 == 0, rank <= 16 RT, dstate <= 16,
-// 16-byte aligned u, W_x, W_dt and delta_raw.
+// 16-byte aligned u, W_x, W_dt and delta_raw, element-aligned B and C, 1 <= kconv <= 4.
 #include "ss_chunk_ops.h"
 
 namespace ss {
@@ -38,21 +45,8 @@ using chunk::rsrc;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-template <typename T>
-struct Elem;
-template <>
-struct Elem<float> {
-  static constexpr int kCh = 4;  // elements per 16-byte unit
-};
-template <>
-struct Elem<uint16_t> {
-  static constexpr int kCh = 8;
-};
-
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs)
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
@@ -62,8 +56,8 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 }
 __device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Phase-1 MFMA step e of a K block (a = 16 bytes of W_x, b = 16 bytes of the inputs): fp32
-// takes 4 steps of K = 4 (element e of each), bf16 one step of K = 32.
+// MFMA step e of a 16-byte K block: fp32 takes 4 steps of K = 4 (element e of each operand),
+// bf16 one step of K = 32.
 __device__ __forceinline__ f32x4 mfma_step(float*, const u32x4& a, const u32x4& b, int e, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), acc, 0, 0, 0);
 }
@@ -72,89 +66,97 @@ __device__ __forceinline__ f32x4 mfma_step(uint16_t*, const u32x4& a, const u32x
                                                  0, 0, 0);
 }
 
-__device__ __forceinline__ void store_elem(float*, __amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
-}
-__device__ __forceinline__ void store_elem(uint16_t*, __amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bf16_bits(v)), r, off, 0, 0);
+// Lane i of each 16-lane row receives lane (i - J) mod 16 of the same row.
+template <int J>
+__device__ __forceinline__ u32x4 row_ror(const u32x4& v) {
+  u32x4 r;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    r[d] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v[d]), 0x120 + J, 0xf, 0xf, false));
+  return r;
 }
 
-template <typename T, int RT, int S>
+// the CH channel values of a 16-byte piece as floats
+__device__ __forceinline__ void unpack(float*, const u32x4& v, float (&f)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[e]);
+}
+__device__ __forceinline__ void unpack(uint16_t*, const u32x4& v, float (&f)[8]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    f[2 * d] = __uint_as_float(v[d] << 16);
+    f[2 * d + 1] = __uint_as_float(v[d] & 0xffff0000u);
+  }
+}
+
+// stage depth: fragments of a few stages in flight, within a register budget
+constexpr int stage_depth(int stage_regs) { return stage_regs <= 40 ? 4 : (stage_regs <= 64 ? 3 : 2); }
+
+template <typename T, int RT, int S, bool CONV>
 __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
-  constexpr int T1 = RT + 2;                  // phase-1 output tiles
-  constexpr int ROWS = T1 * 16;               // W_x rows staged per chunk (zeros where absent)
-  constexpr int CH = Elem<T>::kCh;
   constexpr int ES = static_cast<int>(sizeof(T));
-  constexpr int KU = ES == 4 ? 1 : 2;         // MFMA K blocks per phase-1 chunk
-  constexpr int CU = 4 * KU;                  // 16-byte units per W_x row and chunk
-  constexpr int KB = CU * CH;                 // channels per chunk (16 fp32, 64 bf16)
-  constexpr int GC = ES == 4 ? 32 : 64;       // channels per phase-2 group
-  constexpr int TG = GC / 16;                 // output tiles per group
-  constexpr int RPU = RT * 16 / CH;           // 16-byte units per staged W_dt row (RT*16 ranks)
-  constexpr int P1 = ROWS * (CU + 1);         // padded rows (one spare unit against bank conflicts)
-  constexpr int P2 = GC * (RPU + 1);
-  constexpr int HALF = P1 > P2 ? P1 : P2;
-  constexpr int KSTEP = ES == 4 ? 4 : 1;      // MFMA steps per K block
-  constexpr int PD = ES == 4 ? 3 : 2;         // chunks (phase 1) / groups (phase 2) in flight
-  __shared__ u32x4 lds[2 * HALF];
-  // bf16 output tiles pass through a wave-private block so each lane stores 16 bytes of a
-  // 128-byte row (direct stores would write 32-byte pieces, twice the HBM write traffic)
-  constexpr int SROW = GC + 8;                // bf16 per staged row (16-byte pad)
-  __shared__ __attribute__((aligned(16))) uint16_t stage[ES == 2 ? 4 * S * 16 * SROW : 1];
+  constexpr bool BF = ES == 2;
+  constexpr int T1 = RT + 2;            // phase-1 output tiles
+  constexpr int CH = 16 / ES;           // channels per lane and stage
+  constexpr int KBW = 4 * CH;           // channels per stage (16 fp32, 32 bf16)
+  constexpr int KSTEP = BF ? 1 : 4;     // MFMA steps per 16-byte K block
+  constexpr int TOK = 16 * S;
+  constexpr int PD = CONV ? 2 : stage_depth(4 * (T1 + S));
+  constexpr int RC = 8 / S;             // tiles per reduction round (8 units, 2 per wave)
+  constexpr int NR = (T1 + RC - 1) / RC;
+  constexpr int NS = BF ? RT / 2 : RT;  // phase-2 K steps (32 ranks bf16, 16 ranks fp32)
+  constexpr int TG = BF ? (NS <= 5 ? 4 : 2) : (NS <= 6 ? 2 : 1);  // phase-2 tiles per group
+  constexpr int GC = 16 * TG;           // channels per phase-2 group
+  constexpr int XS = BF ? 16 * RT + 8 : 16 * RT + 4;  // xp copy row stride (elements; odd 16-byte units)
   T* tag = nullptr;
+
+  __shared__ f32x4 part[2][4][8][64];                   // partial tiles, double-buffered by round
+  __shared__ __attribute__((aligned(16))) T xph[TOK * XS];               // xp (fp32) or its hi part
+  __shared__ __attribute__((aligned(16))) uint16_t xpl[BF ? TOK * XS : 8];  // bf16 lo part
+  __shared__ __attribute__((aligned(16))) float cwl[CONV ? 4 * 2 * 5 * KBW : 4];  // conv taps per wave
 
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int li = l & 15, lq = l >> 4;
   const int64_t M = a.tokens, dim = a.dim, N = a.dstate, rank = a.rank;
-  const int64_t wg_tok0 = static_cast<int64_t>(blockIdx.x) * (64 * S);
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * TOK;
   const int64_t row_bytes = dim * ES;
 
-  // inputs of this workgroup's tokens; tokens past M read 0 (range check)
-  const auto ru = rsrc(static_cast<const T*>(a.u) + wg_tok0 * dim, (M - wg_tok0) * row_bytes);
-  uint32_t xrow[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) xrow[s] = static_cast<uint32_t>((w * 16 * S + s * 16 + li) * row_bytes);
+  // ---- phase 1 -------------------------------------------------------------------------------
+  const int64_t nkb = (dim + KBW - 1) / KBW;
+  const int64_t kb_lo = nkb * w / 4, kb_hi = nkb * (w + 1) / 4;
 
-  // ---- phase 1: xp^T = W_x X^T ------------------------------------------------------------
-  // Chunk c of W_x is requested PD + 1 iterations before it is used and staged in LDS one
-  // iteration before; the inputs of chunk c are requested PD iterations before. The loop is
-  // unrolled by PD so every register slot is static.
+  // this workgroup's input rows (and, with the convolution, the 16 before them)
+  const int hb = (CONV && tok0 >= 16) ? 16 : 0;
+  const int64_t rows_here = (M - tok0 + hb) < (TOK + hb) ? (M - tok0 + hb) : (TOK + hb);
+  const auto rx = rsrc(static_cast<const T*>(a.u) + (tok0 - hb) * dim, rows_here * row_bytes);
+  uint32_t xoff[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) xoff[s] = static_cast<uint32_t>((hb + 16 * s + li) * row_bytes);
+  const uint32_t hoff = hb ? static_cast<uint32_t>(li * row_bytes) : kDropOffset;
+
   const auto rwx = rsrc(a.W_x, (rank + 2 * N) * row_bytes);
-  constexpr int EPL = (ROWS * CU + 255) / 256;  // staged units per lane and chunk
-  auto wx_row = [&](int r) -> int64_t {         // source row of staged row r (-1: zero row)
-    const int c = r >> 4, i = r & 15;
-    if (c < RT) return 16 * c + i < rank ? 16 * c + i : -1;
-    if (i >= N) return -1;
-    return c == RT ? rank + i : rank + N + i;
-  };
-  auto load_wx = [&](u32x4 (&v)[EPL], int64_t k0) {
+  uint32_t woff[T1];  // byte offset of row li of each tile (kDropOffset: a zero row)
 #pragma unroll
-    for (int m = 0; m < EPL; ++m) {
-      const int e = tid + 256 * m;
-      const int r = e / CU, un = e % CU;
-      const int64_t kk = k0 + un * CH;
-      const int64_t sr = e < ROWS * CU ? wx_row(r) : -1;
-      const uint32_t off = (sr >= 0 && kk < dim) ? static_cast<uint32_t>((sr * dim + kk) * ES) : kDropOffset;
-      v[m] = __builtin_amdgcn_raw_buffer_load_b128(rwx, off, 0, 0);
+  for (int c = 0; c < T1; ++c) {
+    int64_t r = -1;
+    if (c < RT) r = 16 * c + li < rank ? 16 * c + li : -1;
+    else if (li < N) r = (c == RT ? rank : rank + N) + li;
+    woff[c] = r >= 0 ? static_cast<uint32_t>(r * row_bytes) : kDropOffset;
+  }
+
+  // convolution: taps right-aligned to 4 (zeros in front for kconv < 4) and the bias
+  const int K = a.kconv;
+  const auto rcw = rsrc(a.conv_w, CONV ? dim * K * 4 : 0);
+  const auto rcb = rsrc(a.conv_b, (CONV && a.conv_b) ? dim * 4 : 0);
+  const auto rcs = rsrc(a.conv_state, (CONV && a.conv_state) ? (M / a.seqlen) * dim * (K - 1) * 4 : 0);
+  int pc[S];  // min(position in the sequence, 3) of this lane's token in each strip
+  if constexpr (CONV) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int64_t p = (tok0 + 16 * s + li) % a.seqlen;
+      pc[s] = p < 3 ? static_cast<int>(p) : 3;
     }
-  };
-  auto store_wx = [&](const u32x4 (&v)[EPL], int buf) {
-#pragma unroll
-    for (int m = 0; m < EPL; ++m) {
-      const int e = tid + 256 * m;
-      if (e < ROWS * CU) lds[buf * HALF + (e / CU) * (CU + 1) + e % CU] = v[m];
-    }
-  };
-  auto load_x = [&](u32x4 (&x)[S][KU], int64_t k0) {
-#pragma unroll
-    for (int kb = 0; kb < KU; ++kb) {
-      const int64_t kk = k0 + (4 * kb + lq) * CH;
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-        x[s][kb] = __builtin_amdgcn_raw_buffer_load_b128(
-            ru, kk < dim ? xrow[s] + static_cast<uint32_t>(kk * ES) : kDropOffset, 0, 0);
-    }
-  };
+  }
 
   f32x4 acc[S][T1];
 #pragma unroll
@@ -162,249 +164,360 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
 #pragma unroll
     for (int c = 0; c < T1; ++c) acc[s][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int64_t nchunks = (dim + KB - 1) / KB;
-  u32x4 wq[PD][EPL], xq[PD][S][KU];
-  {
-    u32x4 w0[EPL];
-    load_wx(w0, 0);
-    store_wx(w0, 0);
-  }
+  u32x4 wq[PD][T1], xq[PD][S], hq[PD];
+  float cq[PD][5];
+  // (issued for every slot, also past the wave's last block, where every offset is dropped:
+  // loads under a branch would make the compiler wait for all of them before each stage)
+  auto load_stage = [&](int j, int64_t kb) {
+    const int64_t kk = kb * KBW + lq * CH;
+    const bool in = kb < kb_hi && kk < dim;
+    const uint32_t ko = static_cast<uint32_t>(kk * ES);
 #pragma unroll
-  for (int j = 0; j < PD; ++j) {
-    if (j + 1 < nchunks) load_wx(wq[(j + 1) % PD], (j + 1) * KB);
-    if (j < nchunks) load_x(xq[j], j * KB);
-  }
-  __syncthreads();
-  for (int64_t base = 0; base < nchunks; base += PD) {
+    for (int c = 0; c < T1; ++c)
+      wq[j][c] = __builtin_amdgcn_raw_buffer_load_b128(rwx, (in && woff[c] != kDropOffset) ? woff[c] + ko : kDropOffset,
+                                                       0, 0);
 #pragma unroll
-    for (int j = 0; j < PD; ++j) {
-      const int64_t ci = base + j;
-      if (ci < nchunks) {
-        const u32x4* lb = lds + static_cast<int>(ci & 1) * HALF;
+    for (int s = 0; s < S; ++s)
+      xq[j][s] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? xoff[s] + ko : kDropOffset, 0, 0);
+    if constexpr (CONV) {
+      hq[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (in && hb) ? hoff + ko : kDropOffset, 0, 0);
+      // lane l < KBW: the taps and bias of channel kb*KBW + l
+      const int64_t ch = kb * KBW + l;
+      const bool cin = kb < kb_hi && l < KBW && ch < dim;
 #pragma unroll
-        for (int kb = 0; kb < KU; ++kb) {
-          u32x4 av[T1];
+      for (int m = 0; m < 4; ++m) {
+        const int t = m - (4 - K);
+        const uint32_t off = (cin && t >= 0) ? static_cast<uint32_t>((ch * K + t) * 4) : kDropOffset;
+        cq[j][m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rcw, off, 0, 0));
+      }
+      cq[j][4] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rcb, (cin && a.conv_b) ? static_cast<uint32_t>(ch * 4) : kDropOffset, 0, 0));
+    }
+  };
+
+  auto compute_stage = [&](int j, int64_t kb) {
+    if constexpr (!CONV) {
 #pragma unroll
-          for (int c = 0; c < T1; ++c) av[c] = lb[(c * 16 + li) * (CU + 1) + 4 * kb + lq];
-          // consecutive MFMAs go to different tiles, so none waits on the one before
+      for (int e = 0; e < KSTEP; ++e)
+#pragma unroll
+        for (int c = 0; c < T1; ++c)
+#pragma unroll
+          for (int s = 0; s < S; ++s) acc[s][c] = mfma_step(tag, wq[j][c], xq[j][s], e, acc[s][c]);
+    } else {
+      // the stage's taps through a wave-private LDS slot, read back per lane's channels
+      float* cs = cwl + (w * 2 + static_cast<int>(kb & 1)) * (5 * KBW);
+      if (l < KBW) {
+#pragma unroll
+        for (int m = 0; m < 5; ++m) cs[m * KBW + l] = cq[j][m];
+      }
+      // (LDS executes a wave's operations in order; the fences only keep the compiler from
+      // moving the accesses across the other lanes' writes)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float wv[5][CH];
+#pragma unroll
+      for (int m = 0; m < 5; ++m)
+#pragma unroll
+        for (int v = 0; v < CH / 4; ++v) {
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(cs + m * KBW + lq * CH + 4 * v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wv[m][4 * v + e] = t4[e];
+        }
+      const int64_t ch0 = kb * KBW + lq * CH;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const u32x4 cur = xq[j][s];
+        const u32x4 prev = s == 0 ? hq[j] : xq[j][s - 1];
+        // window position m holds x_{t-3+m}; the value lane i needs from x_{t-J} sits in lane
+        // i - J of this strip or, for i < J, in lane 16 + i - J of the previous one: select
+        // at the source lane, then rotate
+        u32x4 sel1, sel2, sel3;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          sel1[d] = li < 15 ? cur[d] : prev[d];
+          sel2[d] = li < 14 ? cur[d] : prev[d];
+          sel3[d] = li < 13 ? cur[d] : prev[d];
+        }
+        float xw[4][CH];
+        unpack(tag, cur, xw[3]);
+        unpack(tag, row_ror<1>(sel1), xw[2]);
+        unpack(tag, row_ror<2>(sel2), xw[1]);
+        unpack(tag, row_ror<3>(sel3), xw[0]);
+        if (pc[s] < 3) {  // the window reaches before the sequence: conv state or zeros there
+          const int p = pc[s];
+          const int64_t tok = tok0 + 16 * s + li;
+          const int64_t b = tok / a.seqlen;
+#pragma unroll
+          for (int jj = 1; jj <= 3; ++jj) {
+            if (jj > p) {
+              const int idx = (K - 1) + p - jj;  // position in the conv state, oldest first
+#pragma unroll
+              for (int e = 0; e < CH; ++e) {
+                const int64_t ch = ch0 + e;
+                const bool ok = a.conv_state && idx >= 0 && tok < M && ch < dim;
+                const uint32_t off = ok ? static_cast<uint32_t>(((b * dim + ch) * (K - 1) + idx) * 4) : kDropOffset;
+                xw[3 - jj][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rcs, off, 0, 0));
+              }
+            }
+          }
+          // wait here (vmcnt(0)) for these loads: waited for after the branch, they would
+          // make every stage wait for all the prefetched ones
+          __builtin_amdgcn_s_waitcnt(0x0f70);
+        }
+        float uv[CH];
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+          float p = wv[4][e];
+          p = __builtin_fmaf(wv[0][e], xw[0][e], p);
+          p = __builtin_fmaf(wv[1][e], xw[1][e], p);
+          p = __builtin_fmaf(wv[2][e], xw[2][e], p);
+          p = __builtin_fmaf(wv[3][e], xw[3][e], p);
+          uv[e] = silu(p);
+        }
+        if constexpr (!BF) {
+          const u32x4 ub = {__float_as_uint(uv[0]), __float_as_uint(uv[1]), __float_as_uint(uv[2]),
+                            __float_as_uint(uv[3])};
 #pragma unroll
           for (int e = 0; e < KSTEP; ++e)
 #pragma unroll
-            for (int c = 0; c < T1; ++c)
+            for (int c = 0; c < T1; ++c) acc[s][c] = mfma_step(tag, wq[j][c], ub, e, acc[s][c]);
+        } else {
+          u32x4 uh, ul;
 #pragma unroll
-              for (int s = 0; s < S; ++s) acc[s][c] = mfma_step(tag, av[c], xq[j][s][kb], e, acc[s][c]);
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t h0 = bf16_bits(uv[2 * d]), h1 = bf16_bits(uv[2 * d + 1]);
+            const uint32_t l0 = bf16_bits(uv[2 * d] - bf16_value(h0)), l1 = bf16_bits(uv[2 * d + 1] - bf16_value(h1));
+            uh[d] = h0 | (h1 << 16);
+            ul[d] = l0 | (l1 << 16);
+          }
+#pragma unroll
+          for (int c = 0; c < T1; ++c) acc[s][c] = mfma_step(tag, wq[j][c], uh, 0, acc[s][c]);
+#pragma unroll
+          for (int c = 0; c < T1; ++c) acc[s][c] = mfma_step(tag, wq[j][c], ul, 0, acc[s][c]);
         }
-        if (ci + 1 < nchunks) store_wx(wq[(j + 1) % PD], static_cast<int>((ci + 1) & 1));
-        if (ci + 1 + PD < nchunks) load_wx(wq[(j + 1) % PD], (ci + 1 + PD) * KB);
-        if (ci + PD < nchunks) load_x(xq[j], (ci + PD) * KB);
-        __syncthreads();
       }
     }
-  }
+  };
 
-  // ---- B and C ----------------------------------------------------------------------------
+  // Stage kb + PD - 1 goes into the slot stage kb - 1 has finished with, before stage kb's
+  // products, so PD - 1 stages of products cover each load. The loop runs whole groups of PD
+  // stages with no branch inside (a stage past the wave's range multiplies zeros): loads or
+  // products under a branch make the compiler wait for every load in flight.
+#pragma unroll
+  for (int j = 0; j + 1 < PD; ++j) {
+    load_stage(j, kb_lo + j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int64_t base = kb_lo; base < kb_hi; base += PD) {
+#pragma unroll
+    for (int j = 0; j < PD; ++j) {
+      const int64_t kb = base + j;
+      // (scheduling barriers keep each stage's loads ahead of its products: left alone, the
+      // scheduler moves products of later stages up and the loads down)
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage((j + PD - 1) % PD, kb + PD - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_stage(j, kb);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- reduction of the four K quarters ------------------------------------------------------
   {
-    const int64_t bc0 = wg_tok0 * N;
-    const auto rb = rsrc(static_cast<T*>(a.B) + bc0, (M - wg_tok0) * N * ES);
-    const auto rc = rsrc(static_cast<T*>(a.C) + bc0, (M - wg_tok0) * N * ES);
+    const auto rb = rsrc(static_cast<T*>(a.B) + tok0 * N, (M - tok0) * N * ES);
+    const auto rc = rsrc(static_cast<T*>(a.C) + tok0 * N, (M - tok0) * N * ES);
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int64_t tok = w * 16 * S + s * 16 + li;  // local token of this lane's column
+    for (int r = 0; r < NR; ++r) {
+      const int buf = r & 1;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = 4 * lq + r;
-        const uint32_t off = n < N ? static_cast<uint32_t>((tok * N + n) * ES) : kDropOffset;
-        store_elem(tag, rb, off, acc[s][RT][r]);
-        store_elem(tag, rc, off, acc[s][RT + 1][r]);
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int cc = 0; cc < RC; ++cc)
+          if (r * RC + cc < T1) part[buf][w][s * RC + cc][l] = acc[s][r * RC + cc];
+      __syncthreads();
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const int unit = w + 4 * uu, s = unit / RC, c = r * RC + unit % RC;
+        if (c < T1) {
+          const f32x4 v = ((part[buf][0][unit][l] + part[buf][1][unit][l]) + part[buf][2][unit][l]) +
+                          part[buf][3][unit][l];
+          const int tl = 16 * s + li;  // lane (li, lq) holds xp[token tl][16 c + 4 lq + 0..3]
+          if (c < RT) {
+            if constexpr (BF) {
+              uint32_t h[4], lo[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                h[e] = bf16_bits(v[e]);
+                lo[e] = bf16_bits(v[e] - bf16_value(h[e]));
+              }
+              *reinterpret_cast<u32x2*>(xph + tl * XS + 16 * c + 4 * lq) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+              *reinterpret_cast<u32x2*>(xpl + tl * XS + 16 * c + 4 * lq) =
+                  u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+            } else {
+              *reinterpret_cast<f32x4*>(xph + tl * XS + 16 * c + 4 * lq) = v;
+            }
+          } else {
+            const auto& ro = c == RT ? rb : rc;
+            const int n0 = 4 * lq;
+            if (N == 16) {
+              const uint32_t off = static_cast<uint32_t>((tl * 16 + n0) * ES);
+              if constexpr (BF) {
+                const u32x2 pk = {bf16_bits(v[0]) | (bf16_bits(v[1]) << 16), bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+                __builtin_amdgcn_raw_buffer_store_b64(pk, ro, off, 0, 0);
+              } else {
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])},
+                    ro, off, 0, 0);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t off = n0 + e < N ? static_cast<uint32_t>((tl * N + n0 + e) * ES) : kDropOffset;
+                if constexpr (BF)
+                  __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bf16_bits(v[e])), ro, off, 0, 0);
+                else
+                  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), ro, off, 0, 0);
+              }
+            }
+          }
+        }
       }
     }
+    __syncthreads();
   }
 
-  // ---- phase 2: delta_raw = xp[:, :rank] W_dt^T --------------------------------------------
-  // The intermediate as phase-2 A operands: fp32 uses acc directly; bf16 packs tiles 2s, 2s+1
-  // into 8 bf16 values, as a hi part and a lo (remainder) part.
-  constexpr int NS = (ES == 4) ? RT : RT / 2;  // bf16 steps (RT is even for bf16)
-  i16x8 ahi[S][NS], alo[S][NS];
-  if constexpr (ES == 2) {
+  // ---- phase 2: delta_raw^T = W_dt xp^T --------------------------------------------------------
+  const auto rdt = rsrc(a.W_dt, dim * rank * ES);
+  const auto rd = rsrc(static_cast<T*>(a.delta_raw) + tok0 * dim, (M - tok0) * row_bytes);
+  const int64_t ngroups = (dim + GC - 1) / GC;
+  const int64_t ngw = ngroups > w ? (ngroups - w + 3) / 4 : 0;
+  u32x4 wd[2][NS][TG];
+  // Row li of tile t in group g: bf16 pairs (t even, t odd) take channels so that lane
+  // (i, q) ends with channels 32 (t/2) + 8q .. + 7; fp32 tile t takes 16 t + li.
+  auto dt_chan = [&](int64_t g, int t) -> int64_t {
+    if constexpr (BF) return g * GC + 32 * (t >> 1) + 8 * (li >> 2) + 4 * (t & 1) + (li & 3);
+    else return g * GC + 16 * t + li;
+  };
+  auto load_group = [&](u32x4 (&v)[NS][TG], int64_t g, bool live) {  // live = false: all dropped
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const int64_t d = live ? dt_chan(g, t) : dim;
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int64_t kk = BF ? 32 * st + 8 * lq : 16 * st + 4 * lq;
+        const uint32_t off = (d < dim && kk < rank) ? static_cast<uint32_t>((d * rank + kk) * ES) : kDropOffset;
+        v[st][t] = __builtin_amdgcn_raw_buffer_load_b128(rdt, off, 0, 0);
+      }
+    }
+  };
+  auto run_group = [&](const u32x4 (&v)[NS][TG], int64_t g) {
+    f32x4 o[S][TG];
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
-      for (int st = 0; st < NS; ++st)
+      for (int t = 0; t < TG; ++t) o[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = acc[s][2 * st + (e >> 2)][e & 3];
-          const uint32_t h = bf16_bits(v);
-          ahi[s][st][e] = static_cast<short>(h);
-          alo[s][st][e] = static_cast<short>(bf16_bits(v - bf16_value(h)));
+    for (int st = 0; st < NS; ++st) {
+      if constexpr (BF) {
+        u32x4 bh[S], bl[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int at = (16 * s + li) * XS + 32 * st + 8 * lq;
+          bh[s] = *reinterpret_cast<const u32x4*>(xph + at);
+          bl[s] = *reinterpret_cast<const u32x4*>(xpl + at);
         }
-  }
-
-  const auto rdt = rsrc(a.W_dt, dim * rank * ES);
-  constexpr int GPL = (GC * RPU + 255) / 256;  // staged W_dt units per lane and group
-  auto load_dt = [&](u32x4 (&v)[GPL], int64_t d0) {
 #pragma unroll
-    for (int m = 0; m < GPL; ++m) {
-      const int e = tid + 256 * m;
-      const int r = e / RPU, un = e % RPU;  // channel row within the group, unit along rank
-      const int64_t d = d0 + r, rk = static_cast<int64_t>(un) * CH;
-      const uint32_t off = (e < GC * RPU && d < dim && rk < rank) ? static_cast<uint32_t>((d * rank + rk) * ES)
-                                                                   : kDropOffset;
-      v[m] = __builtin_amdgcn_raw_buffer_load_b128(rdt, off, 0, 0);
-    }
-  };
-  auto store_dt = [&](const u32x4 (&v)[GPL], int buf) {
+        for (int t = 0; t < TG; ++t)
 #pragma unroll
-    for (int m = 0; m < GPL; ++m) {
-      const int e = tid + 256 * m;
-      if (e < GC * RPU) lds[buf * HALF + (e / RPU) * (RPU + 1) + e % RPU] = v[m];
-    }
-  };
-
-  const auto rd = rsrc(static_cast<T*>(a.delta_raw) + wg_tok0 * dim, (M - wg_tok0) * row_bytes);
-  const int64_t ngroups = (dim + GC - 1) / GC;
-  u32x4 dq[PD][GPL];
-  {
-    u32x4 d0v[GPL];
-    load_dt(d0v, 0);
-    store_dt(d0v, 0);
-  }
+          for (int s = 0; s < S; ++s) o[s][t] = mfma_step(tag, v[st][t], bh[s], 0, o[s][t]);
 #pragma unroll
-  for (int j = 0; j < PD; ++j)
-    if (j + 1 < ngroups) load_dt(dq[(j + 1) % PD], (j + 1) * GC);
-  __syncthreads();
-  for (int64_t base = 0; base < ngroups; base += PD) {
+        for (int t = 0; t < TG; ++t)
 #pragma unroll
-    for (int j = 0; j < PD; ++j) {
-      const int64_t g = base + j;
-      if (g < ngroups) {
-        const u32x4* lb = lds + static_cast<int>(g & 1) * HALF;
-        f32x4 o[S][TG];
+          for (int s = 0; s < S; ++s) o[s][t] = mfma_step(tag, v[st][t], bl[s], 0, o[s][t]);
+      } else {
+        u32x4 bx[S];
 #pragma unroll
         for (int s = 0; s < S; ++s)
+          bx[s] = *reinterpret_cast<const u32x4*>(xph + (16 * s + li) * XS + 16 * st + 4 * lq);
 #pragma unroll
-          for (int t = 0; t < TG; ++t) o[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (ES == 4) {
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-          for (int c = 0; c < RT; ++c) {
-            u32x4 bv[TG];
+          for (int t = 0; t < TG; ++t)
 #pragma unroll
-            for (int t = 0; t < TG; ++t) bv[t] = lb[(16 * t + li) * (RPU + 1) + 4 * c + lq];  // ranks 16c + 4lq ..
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-              for (int t = 0; t < TG; ++t)
-#pragma unroll
-                for (int s = 0; s < S; ++s)
-                  o[s][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(acc[s][c][r], __uint_as_float(bv[t][r]), o[s][t],
-                                                                 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int st = 0; st < NS; ++st) {
-            bf16x8 b8[TG];
-#pragma unroll
-            for (int t = 0; t < TG; ++t) {
-              // ranks 16(2st) + 4lq .. +3 and 16(2st+1) + 4lq .. +3, 4 bf16 each
-              const u32x2* row2 = reinterpret_cast<const u32x2*>(lb + (16 * t + li) * (RPU + 1));
-              const u32x2 lo8 = row2[8 * st + lq];
-              const u32x2 hi8 = row2[8 * st + 4 + lq];
-              const u32x4 bv = {lo8[0], lo8[1], hi8[0], hi8[1]};
-              b8[t] = __builtin_bit_cast(bf16x8, bv);
-            }
-#pragma unroll
-            for (int t = 0; t < TG; ++t)
-#pragma unroll
-              for (int s = 0; s < S; ++s)
-                o[s][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ahi[s][st]), b8[t], o[s][t],
-                                                                  0, 0, 0);
-#pragma unroll
-            for (int t = 0; t < TG; ++t)
-#pragma unroll
-              for (int s = 0; s < S; ++s)
-                o[s][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo[s][st]), b8[t], o[s][t],
-                                                                  0, 0, 0);
-          }
-        }
-        // lane (channel li, q) holds tokens 4q .. 4q+3 of each strip for channel g*GC + 16t + li
-        if constexpr (ES == 4) {
-#pragma unroll
-          for (int t = 0; t < TG; ++t) {
-            const int64_t d = g * GC + 16 * t + li;
-#pragma unroll
-            for (int s = 0; s < S; ++s)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int64_t tok = w * 16 * S + s * 16 + 4 * lq + r;
-                const uint32_t off = d < dim ? static_cast<uint32_t>(tok * row_bytes + d * ES) : kDropOffset;
-                store_elem(tag, rd, off, o[s][t][r]);
-              }
-          }
-        } else {
-          uint16_t* st = stage + w * (S * 16 * SROW);
-#pragma unroll
-          for (int s = 0; s < S; ++s)
-#pragma unroll
-            for (int t = 0; t < TG; ++t)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                st[(s * 16 + 4 * lq + r) * SROW + 16 * t + li] = static_cast<uint16_t>(bf16_bits(o[s][t][r]));
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-          // 16 tokens x 128 bytes per strip = 128 pieces of 16 bytes: pieces l and l + 64
-#pragma unroll
-          for (int s = 0; s < S; ++s)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int piece = l + 64 * h, tok = piece >> 3, col = (piece & 7) * 8;
-              const u32x4 v = *reinterpret_cast<const u32x4*>(st + (s * 16 + tok) * SROW + col);
-              const int64_t d = g * GC + col;
-              const int64_t tk = w * 16 * S + s * 16 + tok;
-              __builtin_amdgcn_raw_buffer_store_b128(
-                  v, rd, d < dim ? static_cast<uint32_t>(tk * row_bytes + d * ES) : kDropOffset, 0, 0);
-            }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        }
-        if (g + 1 < ngroups) store_dt(dq[(j + 1) % PD], static_cast<int>((g + 1) & 1));
-        if (g + 1 + PD < ngroups) load_dt(dq[(j + 1) % PD], (g + 1 + PD) * GC);
-        __syncthreads();
+            for (int s = 0; s < S; ++s) o[s][t] = mfma_step(tag, v[st][t], bx[s], e, o[s][t]);
       }
+    }
+    // lane (i, q), register r of tile t: delta_raw[token 16 s + i][channel of row 4q + r]
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int64_t tl = 16 * s + li;
+      if constexpr (BF) {
+#pragma unroll
+        for (int p = 0; p < TG / 2; ++p) {
+          const int64_t d = g * GC + 32 * p + 8 * lq;
+          const f32x4 e0 = o[s][2 * p], e1 = o[s][2 * p + 1];
+          const u32x4 pk = {bf16_bits(e0[0]) | (bf16_bits(e0[1]) << 16), bf16_bits(e0[2]) | (bf16_bits(e0[3]) << 16),
+                            bf16_bits(e1[0]) | (bf16_bits(e1[1]) << 16), bf16_bits(e1[2]) | (bf16_bits(e1[3]) << 16)};
+          __builtin_amdgcn_raw_buffer_store_b128(
+              pk, rd, d < dim ? static_cast<uint32_t>(tl * row_bytes + d * ES) : kDropOffset, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < TG; ++t) {
+          const int64_t d = g * GC + 16 * t + 4 * lq;
+          const f32x4 e0 = o[s][t];
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u32x4{__float_as_uint(e0[0]), __float_as_uint(e0[1]), __float_as_uint(e0[2]), __float_as_uint(e0[3])}, rd,
+              d < dim ? static_cast<uint32_t>(tl * row_bytes + d * ES) : kDropOffset, 0, 0);
+        }
+      }
+    }
+  };
+
+  load_group(wd[0], w, ngw > 0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int64_t j = 0; j < ngw; j += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_group(wd[h ^ 1], w + 4 * (j + h + 1), j + h + 1 < ngw);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + h < ngw) run_group(wd[h], w + 4 * (j + h));
     }
   }
 }
 
-template <typename T, int RT, int S>
+
+// Strips per workgroup: the accumulators take 4 T1 S registers per lane, the convolution's
+// window and taps about 100 more (the choices keep every variant free of spills).
+constexpr int strips(int rt, bool conv, int es) {
+  if (conv) return rt <= 4 ? 4 : (rt <= 10 ? 2 : 1);
+  return rt <= 10 ? 4 : ((rt <= 12 || es == 2) ? 2 : 1);
+}
+
+template <typename T, int RT, bool CONV>
 hipError_t launch_proj(const ProjArgs& a, hipStream_t s) {
-  const int64_t per = 64 * S;
+  constexpr int S = strips(RT, CONV, static_cast<int>(sizeof(T)));
+  const int64_t per = 16 * S;
   const dim3 grid(static_cast<unsigned>((a.tokens + per - 1) / per));
-  hipLaunchKernelGGL((proj_kernel<T, RT, S>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((proj_kernel<T, RT, S, CONV>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t proj_t(const ProjArgs& a, int rt, int strips, hipStream_t s) {
+template <typename T, bool CONV>
+hipError_t proj_t(const ProjArgs& a, int rt, hipStream_t s) {
   if constexpr (sizeof(T) == 4) {  // fp32 also has 3 step tiles (rank 48: 1536 / 32)
-    if (rt == 3) return strips == 2 ? launch_proj<T, 3, 2>(a, s) : launch_proj<T, 3, 1>(a, s);
-  }
-  if (strips == 2) {
-    switch (rt) {
-      case 2: return launch_proj<T, 2, 2>(a, s);
-      case 4: return launch_proj<T, 4, 2>(a, s);
-      case 6: return launch_proj<T, 6, 2>(a, s);
-      case 8: return launch_proj<T, 8, 2>(a, s);
-      default: return launch_proj<T, 10, 2>(a, s);
-    }
+    if (rt == 3) return launch_proj<T, 3, CONV>(a, s);
   }
   switch (rt) {
-    case 2: return launch_proj<T, 2, 1>(a, s);
-    case 4: return launch_proj<T, 4, 1>(a, s);
-    case 6: return launch_proj<T, 6, 1>(a, s);
-    case 8: return launch_proj<T, 8, 1>(a, s);
-    case 10: return launch_proj<T, 10, 1>(a, s);
-    case 12: return launch_proj<T, 12, 1>(a, s);
-    default: return launch_proj<T, 16, 1>(a, s);
+    case 2: return launch_proj<T, 2, CONV>(a, s);
+    case 4: return launch_proj<T, 4, CONV>(a, s);
+    case 6: return launch_proj<T, 6, CONV>(a, s);
+    case 8: return launch_proj<T, 8, CONV>(a, s);
+    case 10: return launch_proj<T, 10, CONV>(a, s);
+    case 12: return launch_proj<T, 12, CONV>(a, s);
+    default: return launch_proj<T, 16, CONV>(a, s);
   }
 }
 
@@ -420,13 +533,11 @@ int proj_step_tiles(int64_t rank, int dtype) {
   return 16;
 }
 
-// Two strips per wave (128 tokens per workgroup) halve the W_x and W_dt reads per token and
-// are used when that still leaves at least two workgroups per CU and the accumulators fit.
-hipError_t proj(const ProjArgs& a, int cus, hipStream_t s) {
+hipError_t proj(const ProjArgs& a, int, hipStream_t s) {
   const int rt = proj_step_tiles(a.rank, a.dtype);
-  const int max_rt = a.dtype == kBF16 ? 6 : 10;  // the bf16 hi/lo operands need more registers
-  const int strips = (rt <= max_rt && (a.tokens + 127) / 128 >= 2 * static_cast<int64_t>(cus)) ? 2 : 1;
-  return a.dtype == kBF16 ? proj_t<uint16_t>(a, rt, strips, s) : proj_t<float>(a, rt, strips, s);
+  const bool conv = a.kconv > 0;
+  if (a.dtype == kBF16) return conv ? proj_t<uint16_t, true>(a, rt, s) : proj_t<uint16_t, false>(a, rt, s);
+  return conv ? proj_t<float, true>(a, rt, s) : proj_t<float, false>(a, rt, s);
 }
 
 }  // namespace ss

@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss_abi_version() == _binding.ABI_VERSION == 6
+    assert lib.ss_abi_version() == _binding.ABI_VERSION == 7
     for s in range(0, 9):
         assert lib.ss_status_string(s)
     assert b"unknown" in lib.ss_status_string(99)
@@ -236,3 +236,27 @@ def test_proj_empty_sequence_needs_no_token_arrays(lib):
     query answers (SS_OK on a gfx950; SS_ERR_HIP without a GPU, SS_ERR_DEVICE on another)."""
     rc = proj_call(lib, u=None, dr=None, B=None, C=None, L=0)
     assert rc in (0, 6, 7)
+
+
+def proj_conv_call(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, cb=None, cs=None, K=4, wx=FAKE, wdt=FAKE, dr=FAKE, B=FAKE, C=FAKE, batch=1, L=4,
+             dim=64, N=16, rank=16, dtype=0)
+    a.update(kw)
+    return lib.ss_proj_conv(a["x"], a["w"], a["cb"], a["cs"], a["K"], a["wx"], a["wdt"], a["dr"], a["B"], a["C"],
+                            a["batch"], a["L"], a["dim"], a["N"], a["rank"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=None), 1), (dict(x=None), 1), (dict(wx=None), 1), (dict(K=0), 2), (dict(K=5), 2),
+    (dict(w=FAKE + 2), 5), (dict(cb=FAKE + 1), 5), (dict(cs=FAKE + 3), 5), (dict(x=FAKE + 8), 5),
+    (dict(dim=60), 2), (dict(rank=12), 2), (dict(N=17), 4), (dict(dtype=2), 3),
+])
+def test_proj_conv_validation(lib, kw, code):
+    """ss_proj_conv rejects bad arguments (its own and ss_proj's) before any device work."""
+    assert proj_conv_call(lib, **kw) == code
+
+
+def test_proj_conv_empty_sequence_reaches_the_device_query(lib):
+    """With seqlen 0 every argument check passes (token arrays NULL); the answer is then the
+    device query's (SS_OK on a gfx950, SS_ERR_HIP without a GPU, SS_ERR_DEVICE on another)."""
+    assert proj_conv_call(lib, L=0, x=None, dr=None, B=None, C=None, cb=FAKE, cs=FAKE) in (0, 6, 7)

@@ -160,3 +160,125 @@ def test_proj_then_scan_matches_oracle():
     # the GPU scan sees the fp32-rounded projections; the oracle the exact ones
     assert pu.scaled_err(y.double().cpu().numpy(), y_ref) <= 1e-4
     assert pu.scaled_err(st.double().cpu().numpy(), st_ref) <= 1e-4
+
+
+# ---- the fused prologue (ss_proj_conv) ----------------------------------------------------------
+
+def conv_params(batch, dim, K, seed, bias=True, state=True):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    w = (torch.randn((dim, K), generator=g, device=DEV) * 0.5).contiguous()
+    b = torch.randn((dim,), generator=g, device=DEV) * 0.1 if bias else None
+    st = torch.randn((batch, dim, K - 1), generator=g, device=DEV) if state and K > 1 else None
+    return w, b, st
+
+
+def oracle_proj_conv(x, rank, N, w, b, st):
+    n = inputs.to_numpy
+    return oracle.proj(n(x["u"]), n(x["W_x"]), n(x["W_dt"]), rank, N, conv_w=w.cpu().numpy(),
+                       conv_b=None if b is None else b.cpu().numpy(),
+                       conv_state=None if st is None else st.cpu().numpy())
+
+
+def run_conv_case(batch, L, dim, N, rank, dt, K, seed, bias=True, state=True):
+    w = inputs.WORKLOADS["mamba130m"].replace(name=f"pc{batch}x{L}x{dim}x{N}r{rank}{dt}k{K}", batch=batch,
+                                              seqlen=L, dim=dim, dstate=N, dtype=dt)
+    x = inputs.make_proj(w, rank, seed=seed, device=DEV)
+    cw, cb, cs = conv_params(batch, dim, K, seed, bias, state)
+    _announce(f"{w.name} bias={bias} state={state}")
+    got = ss.proj_conv(x["u"], cw, x["W_x"], x["W_dt"], rank, conv_b=cb, conv_state=cs)
+    torch.cuda.synchronize()
+    check(got, oracle_proj_conv(x, rank, N, cw, cb, cs), x["u"].dtype, w.name)
+
+
+@pytest.mark.parametrize("batch,L,dim,N,rank,dt,K", [
+    (2, 37, 64, 16, 16, "f32", 4), (3, 20, 136, 16, 48, "f32", 4), (1, 65, 256, 5, 8, "bf16", 4),
+    (2, 129, 520, 16, 64, "bf16", 3), (4, 1, 40, 16, 16, "f32", 4), (5, 2, 72, 16, 24, "bf16", 4),
+    (2, 3, 96, 16, 32, "f32", 2), (1, 300, 1032, 7, 160, "bf16", 4), (2, 77, 200, 16, 96, "f32", 1),
+    (3, 50, 64, 16, 200, "bf16", 4), (1, 40, 48, 16, 256, "f32", 3), (2, 100, 4096, 16, 128, "bf16", 4),
+])
+def test_proj_conv_matches_oracle(batch, L, dim, N, rank, dt, K):
+    """Sequences shorter than the window, sequence starts inside a strip, every kconv, ragged
+    channel counts, and one case of each strip count (4 strips up to 4 step tiles, 2 up to 10, 1
+    beyond)."""
+    run_conv_case(batch, L, dim, N, rank, dt, K, seed=201)
+
+
+@pytest.mark.parametrize("bias,state", [(False, False), (True, False), (False, True)])
+def test_proj_conv_optional_bias_and_state(bias, state):
+    run_conv_case(3, 45, 96, 16, 48, "f32", 4, seed=202, bias=bias, state=state)
+    run_conv_case(3, 45, 96, 16, 48, "bf16", 4, seed=203, bias=bias, state=state)
+
+
+def test_proj_conv_130m_full_every_element():
+    w = inputs.WORKLOADS["mamba130m"]
+    rank = inputs.proj_rank(w.dim)
+    _announce(f"{w.name} conv full, rank {rank}")
+    x = inputs.make_proj(w, rank, seed=204, device=DEV)
+    cw, cb, cs = conv_params(w.batch, w.dim, 4, 204)
+    got = ss.proj_conv(x["u"], cw, x["W_x"], x["W_dt"], rank, conv_b=cb, conv_state=cs)
+    torch.cuda.synchronize()
+    check(got, oracle_proj_conv(x, rank, w.dstate, cw, cb, cs), x["u"].dtype, w.name)
+
+
+@pytest.mark.parametrize("name", ["mamba1.4b", "mamba3b-long"])
+def test_proj_conv_full_size_sampled_tokens(name):
+    """At full size the oracle takes each sampled token's window on its own: the convolution
+    is causal with kconv = 4, so token t >= 3 depends on x[t-3 .. t] only, a sequence of
+    four tokens whose last output is the token's; the first tokens of each sequence are
+    checked against the oracle on a prefix of the sequences with the conv state."""
+    w = inputs.WORKLOADS[name]
+    rank = inputs.proj_rank(w.dim)
+    _announce(f"{name} conv sampled tokens, rank {rank}")
+    x = inputs.make_proj(w, rank, seed=205, device=DEV)
+    cw, cb, cs = conv_params(w.batch, w.dim, 4, 205)
+    got = ss.proj_conv(x["u"], cw, x["W_x"], x["W_dt"], rank, conv_b=cb, conv_state=cs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(205)
+    k = 64
+    tokens = np.stack([rng.integers(0, w.batch, k), rng.integers(3, w.seqlen, k)], axis=1)
+    tokens[0] = (w.batch - 1, w.seqlen - 1)
+    t = torch.as_tensor(tokens, device=DEV)
+    win = torch.stack([x["u"][b, s - 3:s + 1] for b, s in tokens.tolist()])  # (k, 4, dim)
+    n = inputs.to_numpy
+    ref = oracle.proj(n(win), n(x["W_x"]), n(x["W_dt"]), rank, w.dstate, conv_w=cw.cpu().numpy(),
+                      conv_b=cb.cpu().numpy())
+    ref = tuple(r[:, 3:4].reshape(1, k, -1) for r in ref)
+    check(got, ref, x["u"].dtype, name, tokens=t)
+    # the first 40 tokens of every sequence, with the conv state
+    P = 40
+    ref = oracle.proj(n(x["u"][:, :P]), n(x["W_x"]), n(x["W_dt"]), rank, w.dstate, conv_w=cw.cpu().numpy(),
+                      conv_b=cb.cpu().numpy(), conv_state=cs.cpu().numpy())
+    check(tuple(g[:, :P] for g in got), ref, x["u"].dtype, name + " prefix")
+
+
+def test_proj_conv_then_scan_matches_oracle():
+    """The block's SSM path from its input: ss_proj_conv then ss_fwd_conv (both form u from x)
+    against the oracle's proj with the prologue, then its fwd_conv."""
+    w = inputs.WORKLOADS["mamba130m"].replace(name="pcscan", batch=2, seqlen=203, dim=96)
+    rank = 16
+    x = inputs.make_proj(w, rank, seed=206, device=DEV)
+    s = inputs.make(w, seed=206, device=DEV)
+    cw, cb, cs = conv_params(w.batch, w.dim, 4, 206)
+    dr, B, C = ss.proj_conv(x["u"], cw, x["W_x"], x["W_dt"], rank, conv_b=cb, conv_state=cs)
+    y, st = ss.fwd_conv(x["u"], cw, dr, s["A"], B, C, conv_b=cb, conv_state=cs, D=s["D"], z=s["z"],
+                        delta_bias=s["delta_bias"])
+    torch.cuda.synchronize()
+    n = inputs.to_numpy
+    odr, oB, oC = oracle_proj_conv(x, rank, w.dstate, cw, cb, cs)
+    y_ref, st_ref, _ = oracle.fwd_conv(n(x["u"]).astype(np.float64), cw.cpu().numpy(), odr, n(s["A"]), oB, oC,
+                                       conv_b=cb.cpu().numpy(), conv_state=cs.cpu().numpy(), D=n(s["D"]),
+                                       z=n(s["z"]).astype(np.float64), delta_bias=n(s["delta_bias"]))
+    assert pu.scaled_err(y.double().cpu().numpy(), y_ref) <= 1e-4
+    assert pu.scaled_err(st.double().cpu().numpy(), st_ref) <= 1e-4
+
+
+def test_proj_conv_deterministic():
+    w = inputs.WORKLOADS["mamba130m"].replace(name="pcdet", batch=2, seqlen=300, dim=256, dtype="bf16")
+    x = inputs.make_proj(w, 48, seed=207, device=DEV)
+    cw, cb, cs = conv_params(2, 256, 4, 207)
+    a = ss.proj_conv(x["u"], cw, x["W_x"], x["W_dt"], 48, conv_b=cb, conv_state=cs)
+    b = ss.proj_conv(x["u"], cw, x["W_x"], x["W_dt"], 48, conv_b=cb, conv_state=cs)
+    torch.cuda.synchronize()
+    for p, q in zip(a, b):
+        assert torch.equal(p, q)
