@@ -14,25 +14,29 @@
 // accumulation either way.
 //
 // A workgroup is 4 waves and owns TOK = 16 S consecutive tokens (S strips of 16).
-//  * Phase 1 (xp^T = W_x X^T) is split over K: wave w takes a quarter of the channel blocks
+//  * Phase 1 (xp^T = W_x X^T) is split over K: wave w takes a quarter of the channel lines
 //    and computes all T1 = RT + 2 output tiles (RT for the step part, rows >= rank zero; one
 //    for B, one for C) for all S strips, so each fragment it loads feeds T1 or S MFMAs and
-//    nothing is shared in the main loop. Both operands come straight from global memory, 16
-//    bytes per lane (lane (i, q) holds channels k0 + q CH .. + CH - 1 of token or row i), with
-//    a few stages in flight. With the convolution, the window x_{t-1..t-3} of lane i is
-//    taken from lanes i-1..i-3 of the same 16-lane row (DPP row rotates; the previous strip,
-//    or a halo load for the first one, supplies the rows' first lanes), and a token whose
-//    window crosses the start of its sequence takes the conv state (or zeros) there. A bf16
-//    convolution output enters the MFMA as a hi and a lo bf16 part, so it keeps ~2^-17
-//    relative precision.
+//    nothing is shared in the main loop. Both operands come straight from global memory as
+//    whole 128-byte lines (two K blocks per stage), turned into MFMA fragments with one DPP
+//    row rotate per register; each tile's registers are reloaded for the next stage right
+//    after they are turned into fragments, so one stage of products covers every load.
+//    With the convolution, the window x_{t-1..t-3} of lane i is taken from lanes i-1..i-3 of
+//    the same 16-lane row (DPP row rotates; the previous strip, or a halo load for the first
+//    one, supplies the rows' first lanes), and a token whose window crosses the start of its
+//    sequence takes the conv state (or zeros) there. A bf16 convolution output enters the
+//    MFMA as a hi and a lo bf16 part, so it keeps ~2^-17 relative precision.
 //  * The four partial sums of every (strip, tile) are added in a fixed order through LDS,
 //    two (strip, tile) units per wave per round; B and C leave from there, the step part goes
 //    to an LDS copy of xp (fp32, or bf16 hi and lo parts).
 //  * Phase 2 computes delta_raw^T = W_dt xp^T: wave w takes every fourth group of 16 TG
-//    channels, with the W_dt fragments (the A operand) from global memory one group ahead
-//    and the xp fragments (the B operand) from the LDS copy. The A rows of a group are
-//    permuted so that each lane ends up with consecutive channels of one token: every store
-//    is 16 bytes of a row.
+//    channels, with the W_dt fragments (the A operand) from global memory as line pairs of K
+//    steps, reloaded for the next group as they are used, and the xp fragments (the B
+//    operand) from the LDS copy. The A rows of a group are permuted so that each lane ends up
+//    with consecutive channels of one token: every store is 16 bytes of a row.
+// The loads are bound by the L1's request rate (64-byte requests, a few dozen in flight per
+// CU), so the weights, which every workgroup reads in full, set the time at small token
+// counts.
 // Shapes the host side guarantees: dim % 8 == 0, rank % 8 == 0, rank <= 16 RT, dstate <= 16,
 // 16-byte aligned u, W_x, W_dt and delta_raw, element-aligned B and C, 1 <= kconv <= 4.
 #include "ss_chunk_ops.h"
@@ -76,6 +80,21 @@ __device__ __forceinline__ u32x4 row_ror(const u32x4& v) {
   return r;
 }
 
+// Full-line loads to MFMA fragments. Load h of a 16-row block gives lane (i, q) row 8h + (i & 7),
+// 16-byte piece q + 4 (i >> 3) of a 128-byte line (each load reads 8 whole lines: the L1
+// tags and requests go by the line, and half-line loads run at half the rate); the fragment
+// of the line's half t wants row i, piece q + 4t in lane (i, q). Rows i < 8 of half 0 and
+// rows i >= 8 of half 1 are already in place; the rest are 8 lanes away in the other load.
+__device__ __forceinline__ void line_halves(const u32x4& g0, const u32x4& g1, int li, u32x4& t0, u32x4& t1) {
+  const u32x4 r0 = row_ror<8>(g0), r1 = row_ror<8>(g1);
+  const bool lo = li < 8;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    t0[d] = lo ? g0[d] : r1[d];
+    t1[d] = lo ? r0[d] : g1[d];
+  }
+}
+
 // the CH channel values of a 16-byte piece as floats
 __device__ __forceinline__ void unpack(float*, const u32x4& v, float (&f)[4]) {
 #pragma unroll
@@ -89,23 +108,19 @@ __device__ __forceinline__ void unpack(uint16_t*, const u32x4& v, float (&f)[8])
   }
 }
 
-// stage depth: fragments of a few stages in flight, within a register budget
-constexpr int stage_depth(int stage_regs) { return stage_regs <= 40 ? 4 : (stage_regs <= 64 ? 3 : 2); }
-
 template <typename T, int RT, int S, bool CONV>
 __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
   constexpr int ES = static_cast<int>(sizeof(T));
   constexpr bool BF = ES == 2;
   constexpr int T1 = RT + 2;            // phase-1 output tiles
   constexpr int CH = 16 / ES;           // channels per lane and stage
-  constexpr int KBW = 4 * CH;           // channels per stage (16 fp32, 32 bf16)
+  constexpr int KBW = 4 * CH;           // channels per K block (16 fp32, 32 bf16)
   constexpr int KSTEP = BF ? 1 : 4;     // MFMA steps per 16-byte K block
   constexpr int TOK = 16 * S;
-  constexpr int PD = CONV ? 2 : stage_depth(4 * (T1 + S));
   constexpr int RC = 8 / S;             // tiles per reduction round (8 units, 2 per wave)
   constexpr int NR = (T1 + RC - 1) / RC;
   constexpr int NS = BF ? RT / 2 : RT;  // phase-2 K steps (32 ranks bf16, 16 ranks fp32)
-  constexpr int TG = BF ? (NS <= 5 ? 4 : 2) : (NS <= 6 ? 2 : 1);  // phase-2 tiles per group
+  constexpr int TG = BF ? 4 : 2;        // phase-2 tiles per group
   constexpr int GC = 16 * TG;           // channels per phase-2 group
   constexpr int XS = BF ? 16 * RT + 8 : 16 * RT + 4;  // xp copy row stride (elements; odd 16-byte units)
   T* tag = nullptr;
@@ -113,7 +128,7 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
   __shared__ f32x4 part[2][4][8][64];                   // partial tiles, double-buffered by round
   __shared__ __attribute__((aligned(16))) T xph[TOK * XS];               // xp (fp32) or its hi part
   __shared__ __attribute__((aligned(16))) uint16_t xpl[BF ? TOK * XS : 8];  // bf16 lo part
-  __shared__ __attribute__((aligned(16))) float cwl[CONV ? 4 * 2 * 5 * KBW : 4];  // conv taps per wave
+  __shared__ __attribute__((aligned(16))) float cwl[CONV ? 4 * 2 * 5 * 2 * KBW : 4];  // conv taps per wave
 
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int li = l & 15, lq = l >> 4;
@@ -122,27 +137,37 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
   const int64_t row_bytes = dim * ES;
 
   // ---- phase 1 -------------------------------------------------------------------------------
-  const int64_t nkb = (dim + KBW - 1) / KBW;
+  // A stage is one 128-byte line of every row: two K blocks of KBW channels.
+  constexpr int KL = 2 * KBW;
+  const int lr = li & 7, lp = lq + 4 * (li >> 3);  // row within 8 and 16-byte piece of a line load
+  const int64_t nkb = (dim + KL - 1) / KL;
   const int64_t kb_lo = nkb * w / 4, kb_hi = nkb * (w + 1) / 4;
 
   // this workgroup's input rows (and, with the convolution, the 16 before them)
   const int hb = (CONV && tok0 >= 16) ? 16 : 0;
   const int64_t rows_here = (M - tok0 + hb) < (TOK + hb) ? (M - tok0 + hb) : (TOK + hb);
   const auto rx = rsrc(static_cast<const T*>(a.u) + (tok0 - hb) * dim, rows_here * row_bytes);
-  uint32_t xoff[S];
+  uint32_t xoff[S][2];
 #pragma unroll
-  for (int s = 0; s < S; ++s) xoff[s] = static_cast<uint32_t>((hb + 16 * s + li) * row_bytes);
-  const uint32_t hoff = hb ? static_cast<uint32_t>(li * row_bytes) : kDropOffset;
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) xoff[s][h] = static_cast<uint32_t>((hb + 16 * s + 8 * h + lr) * row_bytes);
+  uint32_t hoff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) hoff[h] = hb ? static_cast<uint32_t>((8 * h + lr) * row_bytes) : kDropOffset;
 
   const auto rwx = rsrc(a.W_x, (rank + 2 * N) * row_bytes);
-  uint32_t woff[T1];  // byte offset of row li of each tile (kDropOffset: a zero row)
+  uint32_t woff[T1][2];  // byte offset of row 8h + lr of each tile (kDropOffset: a zero row)
 #pragma unroll
-  for (int c = 0; c < T1; ++c) {
-    int64_t r = -1;
-    if (c < RT) r = 16 * c + li < rank ? 16 * c + li : -1;
-    else if (li < N) r = (c == RT ? rank : rank + N) + li;
-    woff[c] = r >= 0 ? static_cast<uint32_t>(r * row_bytes) : kDropOffset;
-  }
+  for (int c = 0; c < T1; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 8 * h + lr;
+      int64_t r = -1;
+      if (c < RT) r = 16 * c + i < rank ? 16 * c + i : -1;
+      else if (i < N) r = (c == RT ? rank : rank + N) + i;
+      woff[c][h] = r >= 0 ? static_cast<uint32_t>(r * row_bytes) : kDropOffset;
+    }
 
   // convolution: taps right-aligned to 4 (zeros in front for kconv < 4) and the bias
   const int K = a.kconv;
@@ -164,161 +189,186 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
 #pragma unroll
     for (int c = 0; c < T1; ++c) acc[s][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  u32x4 wq[PD][T1], xq[PD][S], hq[PD];
-  float cq[PD][5];
-  // (issued for every slot, also past the wave's last block, where every offset is dropped:
+  // Raw line loads of the next stage. Each stage reloads a tile's registers right after
+  // turning them into fragments, so one stage of products covers every load and the live
+  // registers stay near one stage's worth.
+  u32x4 wr[T1][2], xr[S][2], hr[2];
+  float cr[5];
+  // (issued for every stage, also past the wave's last block, where every offset is dropped:
   // loads under a branch would make the compiler wait for all of them before each stage)
-  auto load_stage = [&](int j, int64_t kb) {
-    const int64_t kk = kb * KBW + lq * CH;
+  auto load_w = [&](int c, int64_t kb) {
+    const int64_t kk = kb * KL + lp * CH;
     const bool in = kb < kb_hi && kk < dim;
     const uint32_t ko = static_cast<uint32_t>(kk * ES);
 #pragma unroll
-    for (int c = 0; c < T1; ++c)
-      wq[j][c] = __builtin_amdgcn_raw_buffer_load_b128(rwx, (in && woff[c] != kDropOffset) ? woff[c] + ko : kDropOffset,
-                                                       0, 0);
+    for (int h = 0; h < 2; ++h)
+      wr[c][h] = __builtin_amdgcn_raw_buffer_load_b128(
+          rwx, (in && woff[c][h] != kDropOffset) ? woff[c][h] + ko : kDropOffset, 0, 0);
+  };
+  auto load_x = [&](int64_t kb) {
+    const int64_t kk = kb * KL + lp * CH;
+    const bool in = kb < kb_hi && kk < dim;
+    const uint32_t ko = static_cast<uint32_t>(kk * ES);
 #pragma unroll
     for (int s = 0; s < S; ++s)
-      xq[j][s] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? xoff[s] + ko : kDropOffset, 0, 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        xr[s][h] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? xoff[s][h] + ko : kDropOffset, 0, 0);
     if constexpr (CONV) {
-      hq[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (in && hb) ? hoff + ko : kDropOffset, 0, 0);
-      // lane l < KBW: the taps and bias of channel kb*KBW + l
-      const int64_t ch = kb * KBW + l;
-      const bool cin = kb < kb_hi && l < KBW && ch < dim;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        hr[h] = __builtin_amdgcn_raw_buffer_load_b128(rx, (in && hb) ? hoff[h] + ko : kDropOffset, 0, 0);
+      // lane l < KL: the taps and bias of channel kb*KL + l
+      const int64_t ch = kb * KL + l;
+      const bool cin = kb < kb_hi && l < KL && ch < dim;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int t = m - (4 - K);
         const uint32_t off = (cin && t >= 0) ? static_cast<uint32_t>((ch * K + t) * 4) : kDropOffset;
-        cq[j][m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rcw, off, 0, 0));
+        cr[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rcw, off, 0, 0));
       }
-      cq[j][4] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      cr[4] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
           rcb, (cin && a.conv_b) ? static_cast<uint32_t>(ch * 4) : kDropOffset, 0, 0));
     }
   };
 
-  auto compute_stage = [&](int j, int64_t kb) {
+  // the B operands of one stage: the inputs, or u from the convolution over them (bf16: a hi
+  // and a lo part, BP = 2 operands per strip and K block)
+  constexpr int BP = (CONV && BF) ? 2 : 1;
+  auto make_operands = [&](int64_t kb, u32x4 (&xb)[S][2][BP]) {
+    u32x4 xf[S][2];
+#pragma unroll
+    for (int s = 0; s < S; ++s) line_halves(xr[s][0], xr[s][1], li, xf[s][0], xf[s][1]);
     if constexpr (!CONV) {
 #pragma unroll
-      for (int e = 0; e < KSTEP; ++e)
+      for (int s = 0; s < S; ++s)
 #pragma unroll
-        for (int c = 0; c < T1; ++c)
-#pragma unroll
-          for (int s = 0; s < S; ++s) acc[s][c] = mfma_step(tag, wq[j][c], xq[j][s], e, acc[s][c]);
+        for (int kh = 0; kh < 2; ++kh) xb[s][kh][0] = xf[s][kh];
     } else {
+      u32x4 hf[2];
+      line_halves(hr[0], hr[1], li, hf[0], hf[1]);
       // the stage's taps through a wave-private LDS slot, read back per lane's channels
-      float* cs = cwl + (w * 2 + static_cast<int>(kb & 1)) * (5 * KBW);
-      if (l < KBW) {
+      float* cs = cwl + (w * 2 + static_cast<int>(kb & 1)) * (5 * KL);
+      if (l < KL) {
 #pragma unroll
-        for (int m = 0; m < 5; ++m) cs[m * KBW + l] = cq[j][m];
+        for (int m = 0; m < 5; ++m) cs[m * KL + l] = cr[m];
       }
       // (LDS executes a wave's operations in order; the fences only keep the compiler from
       // moving the accesses across the other lanes' writes)
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      float wv[5][CH];
 #pragma unroll
-      for (int m = 0; m < 5; ++m)
+      for (int kh = 0; kh < 2; ++kh) {
+        float wv[5][CH];
 #pragma unroll
-        for (int v = 0; v < CH / 4; ++v) {
-          const f32x4 t4 = *reinterpret_cast<const f32x4*>(cs + m * KBW + lq * CH + 4 * v);
+        for (int m = 0; m < 5; ++m)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) wv[m][4 * v + e] = t4[e];
-        }
-      const int64_t ch0 = kb * KBW + lq * CH;
+          for (int v = 0; v < CH / 4; ++v) {
+            const f32x4 t4 = *reinterpret_cast<const f32x4*>(cs + m * KL + kh * KBW + lq * CH + 4 * v);
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const u32x4 cur = xq[j][s];
-        const u32x4 prev = s == 0 ? hq[j] : xq[j][s - 1];
-        // window position m holds x_{t-3+m}; the value lane i needs from x_{t-J} sits in lane
-        // i - J of this strip or, for i < J, in lane 16 + i - J of the previous one: select
-        // at the source lane, then rotate
-        u32x4 sel1, sel2, sel3;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          sel1[d] = li < 15 ? cur[d] : prev[d];
-          sel2[d] = li < 14 ? cur[d] : prev[d];
-          sel3[d] = li < 13 ? cur[d] : prev[d];
-        }
-        float xw[4][CH];
-        unpack(tag, cur, xw[3]);
-        unpack(tag, row_ror<1>(sel1), xw[2]);
-        unpack(tag, row_ror<2>(sel2), xw[1]);
-        unpack(tag, row_ror<3>(sel3), xw[0]);
-        if (pc[s] < 3) {  // the window reaches before the sequence: conv state or zeros there
-          const int p = pc[s];
-          const int64_t tok = tok0 + 16 * s + li;
-          const int64_t b = tok / a.seqlen;
-#pragma unroll
-          for (int jj = 1; jj <= 3; ++jj) {
-            if (jj > p) {
-              const int idx = (K - 1) + p - jj;  // position in the conv state, oldest first
-#pragma unroll
-              for (int e = 0; e < CH; ++e) {
-                const int64_t ch = ch0 + e;
-                const bool ok = a.conv_state && idx >= 0 && tok < M && ch < dim;
-                const uint32_t off = ok ? static_cast<uint32_t>(((b * dim + ch) * (K - 1) + idx) * 4) : kDropOffset;
-                xw[3 - jj][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rcs, off, 0, 0));
-              }
-            }
+            for (int e = 0; e < 4; ++e) wv[m][4 * v + e] = t4[e];
           }
-          // wait here (vmcnt(0)) for these loads: waited for after the branch, they would
-          // make every stage wait for all the prefetched ones
-          __builtin_amdgcn_s_waitcnt(0x0f70);
-        }
-        float uv[CH];
+        const int64_t ch0 = kb * KL + kh * KBW + lq * CH;
 #pragma unroll
-        for (int e = 0; e < CH; ++e) {
-          float p = wv[4][e];
-          p = __builtin_fmaf(wv[0][e], xw[0][e], p);
-          p = __builtin_fmaf(wv[1][e], xw[1][e], p);
-          p = __builtin_fmaf(wv[2][e], xw[2][e], p);
-          p = __builtin_fmaf(wv[3][e], xw[3][e], p);
-          uv[e] = silu(p);
-        }
-        if constexpr (!BF) {
-          const u32x4 ub = {__float_as_uint(uv[0]), __float_as_uint(uv[1]), __float_as_uint(uv[2]),
-                            __float_as_uint(uv[3])};
-#pragma unroll
-          for (int e = 0; e < KSTEP; ++e)
-#pragma unroll
-            for (int c = 0; c < T1; ++c) acc[s][c] = mfma_step(tag, wq[j][c], ub, e, acc[s][c]);
-        } else {
-          u32x4 uh, ul;
+        for (int s = 0; s < S; ++s) {
+          const u32x4 cur = xf[s][kh];
+          const u32x4 prev = s == 0 ? hf[kh] : xf[s - 1][kh];
+          // window position m holds x_{t-3+m}; the value lane i needs from x_{t-J} sits in lane
+          // i - J of this strip or, for i < J, in lane 16 + i - J of the previous one: select
+          // at the source lane, then rotate
+          u32x4 sel1, sel2, sel3;
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
-            const uint32_t h0 = bf16_bits(uv[2 * d]), h1 = bf16_bits(uv[2 * d + 1]);
-            const uint32_t l0 = bf16_bits(uv[2 * d] - bf16_value(h0)), l1 = bf16_bits(uv[2 * d + 1] - bf16_value(h1));
-            uh[d] = h0 | (h1 << 16);
-            ul[d] = l0 | (l1 << 16);
+            sel1[d] = li < 15 ? cur[d] : prev[d];
+            sel2[d] = li < 14 ? cur[d] : prev[d];
+            sel3[d] = li < 13 ? cur[d] : prev[d];
           }
+          float xw[4][CH];
+          unpack(tag, cur, xw[3]);
+          unpack(tag, row_ror<1>(sel1), xw[2]);
+          unpack(tag, row_ror<2>(sel2), xw[1]);
+          unpack(tag, row_ror<3>(sel3), xw[0]);
+          if (pc[s] < 3) {  // the window reaches before the sequence: conv state or zeros there
+            const int p = pc[s];
+            const int64_t tok = tok0 + 16 * s + li;
+            const int64_t b = tok / a.seqlen;
 #pragma unroll
-          for (int c = 0; c < T1; ++c) acc[s][c] = mfma_step(tag, wq[j][c], uh, 0, acc[s][c]);
+            for (int jj = 1; jj <= 3; ++jj) {
+              if (jj > p) {
+                const int idx = (K - 1) + p - jj;  // position in the conv state, oldest first
 #pragma unroll
-          for (int c = 0; c < T1; ++c) acc[s][c] = mfma_step(tag, wq[j][c], ul, 0, acc[s][c]);
+                for (int e = 0; e < CH; ++e) {
+                  const int64_t ch = ch0 + e;
+                  const bool ok = a.conv_state && idx >= 0 && tok < M && ch < dim;
+                  const uint32_t off =
+                      ok ? static_cast<uint32_t>(((b * dim + ch) * (K - 1) + idx) * 4) : kDropOffset;
+                  xw[3 - jj][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rcs, off, 0, 0));
+                }
+              }
+            }
+            // wait here (vmcnt(0)) for these loads: waited for after the branch, they would
+            // make every stage wait for all the prefetched ones
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+          }
+          float uv[CH];
+#pragma unroll
+          for (int e = 0; e < CH; ++e) {
+            float p = wv[4][e];
+            p = __builtin_fmaf(wv[0][e], xw[0][e], p);
+            p = __builtin_fmaf(wv[1][e], xw[1][e], p);
+            p = __builtin_fmaf(wv[2][e], xw[2][e], p);
+            p = __builtin_fmaf(wv[3][e], xw[3][e], p);
+            uv[e] = silu(p);
+          }
+          if constexpr (!BF) {
+            xb[s][kh][0] = u32x4{__float_as_uint(uv[0]), __float_as_uint(uv[1]), __float_as_uint(uv[2]),
+                                 __float_as_uint(uv[3])};
+          } else {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const uint32_t h0 = bf16_bits(uv[2 * d]), h1 = bf16_bits(uv[2 * d + 1]);
+              const uint32_t l0 = bf16_bits(uv[2 * d] - bf16_value(h0)), l1 = bf16_bits(uv[2 * d + 1] - bf16_value(h1));
+              xb[s][kh][0][d] = h0 | (h1 << 16);
+              xb[s][kh][BP - 1][d] = l0 | (l1 << 16);
+            }
+          }
         }
       }
     }
   };
 
-  // Stage kb + PD - 1 goes into the slot stage kb - 1 has finished with, before stage kb's
-  // products, so PD - 1 stages of products cover each load. The loop runs whole groups of PD
-  // stages with no branch inside (a stage past the wave's range multiplies zeros): loads or
-  // products under a branch make the compiler wait for every load in flight.
+  // (the prologue issues its loads in the loop's order, so the waits at the loop head can
+  // count on it)
+  load_x(kb_lo);
 #pragma unroll
-  for (int j = 0; j + 1 < PD; ++j) {
-    load_stage(j, kb_lo + j);
+  for (int c = 0; c < T1; ++c) {
     __builtin_amdgcn_sched_barrier(0);
+    load_w(c, kb_lo);
   }
-  for (int64_t base = kb_lo; base < kb_hi; base += PD) {
+  for (int64_t kb = kb_lo; kb < kb_hi; ++kb) {
+    // (scheduling barriers keep each reload right after the fragments it replaces were made
+    // and ahead of the products: left alone, the scheduler moves loads down and products up)
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 xb[S][2][BP];
+    make_operands(kb, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(kb + 1);
 #pragma unroll
-    for (int j = 0; j < PD; ++j) {
-      const int64_t kb = base + j;
-      // (scheduling barriers keep each stage's loads ahead of its products: left alone, the
-      // scheduler moves products of later stages up and the loads down)
+    for (int c = 0; c < T1; ++c) {
       __builtin_amdgcn_sched_barrier(0);
-      load_stage((j + PD - 1) % PD, kb + PD - 1);
+      u32x4 wf[2];
+      line_halves(wr[c][0], wr[c][1], li, wf[0], wf[1]);
+      load_w(c, kb + 1);
       __builtin_amdgcn_sched_barrier(0);
-      compute_stage(j, kb);
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int e = 0; e < KSTEP; ++e)
+#pragma unroll
+          for (int b = 0; b < BP; ++b)
+#pragma unroll
+            for (int s = 0; s < S; ++s) acc[s][c] = mfma_step(tag, wf[kh], xb[s][kh][b], e, acc[s][c]);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -392,60 +442,68 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
   const auto rd = rsrc(static_cast<T*>(a.delta_raw) + tok0 * dim, (M - tok0) * row_bytes);
   const int64_t ngroups = (dim + GC - 1) / GC;
   const int64_t ngw = ngroups > w ? (ngroups - w + 3) / 4 : 0;
-  u32x4 wd[2][NS][TG];
-  // Row li of tile t in group g: bf16 pairs (t even, t odd) take channels so that lane
-  // (i, q) ends with channels 32 (t/2) + 8q .. + 7; fp32 tile t takes 16 t + li.
-  auto dt_chan = [&](int64_t g, int t) -> int64_t {
-    if constexpr (BF) return g * GC + 32 * (t >> 1) + 8 * (li >> 2) + 4 * (t & 1) + (li & 3);
-    else return g * GC + 16 * t + li;
+  // W_dt fragments come as line pairs of K steps (128 bytes of a row), like phase 1's loads
+  constexpr int NP = (NS + 1) / 2;
+  constexpr int SW = BF ? 32 : 16;  // ranks per K step
+  u32x4 vr[NP][TG][2];  // raw line loads of the next group, reloaded as they are used
+  // Row i of tile t in group g: bf16 pairs (t even, t odd) take channels so that lane
+  // (i, q) ends with channels 32 (t/2) + 8q .. + 7; fp32 tile t takes 16 t + i.
+  auto dt_chan = [&](int64_t g, int t, int i) -> int64_t {
+    if constexpr (BF) return g * GC + 32 * (t >> 1) + 8 * (i >> 2) + 4 * (t & 1) + (i & 3);
+    else return g * GC + 16 * t + i;
   };
-  auto load_group = [&](u32x4 (&v)[NS][TG], int64_t g, bool live) {  // live = false: all dropped
+  auto load_dt = [&](int p, int t, int64_t g, bool live) {  // live = false: all dropped
 #pragma unroll
-    for (int t = 0; t < TG; ++t) {
-      const int64_t d = live ? dt_chan(g, t) : dim;
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const int64_t kk = BF ? 32 * st + 8 * lq : 16 * st + 4 * lq;
-        const uint32_t off = (d < dim && kk < rank) ? static_cast<uint32_t>((d * rank + kk) * ES) : kDropOffset;
-        v[st][t] = __builtin_amdgcn_raw_buffer_load_b128(rdt, off, 0, 0);
-      }
+    for (int h = 0; h < 2; ++h) {
+      const int64_t d = live ? dt_chan(g, t, 8 * h + lr) : dim;
+      const int64_t kk = 2 * p * SW + lp * CH;
+      const uint32_t off = (d < dim && kk < rank) ? static_cast<uint32_t>((d * rank + kk) * ES) : kDropOffset;
+      vr[p][t][h] = __builtin_amdgcn_raw_buffer_load_b128(rdt, off, 0, 0);
     }
   };
-  auto run_group = [&](const u32x4 (&v)[NS][TG], int64_t g) {
+  auto run_group = [&](int64_t g, bool next_live) {
     f32x4 o[S][TG];
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
       for (int t = 0; t < TG; ++t) o[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      if constexpr (BF) {
-        u32x4 bh[S], bl[S];
+    for (int p = 0; p < NP; ++p) {
+      // B operands of steps 2p, 2p+1 from the LDS copy of xp (bf16: hi and lo parts)
+      constexpr int NB = BF ? 2 : 1;
+      u32x4 bx[2][S][NB];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const int st = 2 * p + kh;
+        if (st >= NS) break;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          const int at = (16 * s + li) * XS + 32 * st + 8 * lq;
-          bh[s] = *reinterpret_cast<const u32x4*>(xph + at);
-          bl[s] = *reinterpret_cast<const u32x4*>(xpl + at);
+          if constexpr (BF) {
+            const int at = (16 * s + li) * XS + 32 * st + 8 * lq;
+            bx[kh][s][0] = *reinterpret_cast<const u32x4*>(xph + at);
+            bx[kh][s][NB - 1] = *reinterpret_cast<const u32x4*>(xpl + at);
+          } else {
+            bx[kh][s][0] = *reinterpret_cast<const u32x4*>(xph + (16 * s + li) * XS + 16 * st + 4 * lq);
+          }
         }
+      }
 #pragma unroll
-        for (int t = 0; t < TG; ++t)
+      for (int t = 0; t < TG; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 af[2];
+        line_halves(vr[p][t][0], vr[p][t][1], li, af[0], af[1]);
+        load_dt(p, t, g + 4, next_live);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int s = 0; s < S; ++s) o[s][t] = mfma_step(tag, v[st][t], bh[s], 0, o[s][t]);
+        for (int kh = 0; kh < 2; ++kh) {
+          if (2 * p + kh >= NS) break;
 #pragma unroll
-        for (int t = 0; t < TG; ++t)
+          for (int e = 0; e < KSTEP; ++e)
 #pragma unroll
-          for (int s = 0; s < S; ++s) o[s][t] = mfma_step(tag, v[st][t], bl[s], 0, o[s][t]);
-      } else {
-        u32x4 bx[S];
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int s = 0; s < S; ++s)
-          bx[s] = *reinterpret_cast<const u32x4*>(xph + (16 * s + li) * XS + 16 * st + 4 * lq);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int t = 0; t < TG; ++t)
-#pragma unroll
-            for (int s = 0; s < S; ++s) o[s][t] = mfma_step(tag, v[st][t], bx[s], e, o[s][t]);
+              for (int s = 0; s < S; ++s) o[s][t] = mfma_step(tag, af[kh], bx[kh][s][b], e, o[s][t]);
+        }
       }
     }
     // lane (i, q), register r of tile t: delta_raw[token 16 s + i][channel of row 4q + r]
@@ -475,24 +533,22 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
     }
   };
 
-  load_group(wd[0], w, ngw > 0);
   __builtin_amdgcn_sched_barrier(0);
-  for (int64_t j = 0; j < ngw; j += 2) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
       __builtin_amdgcn_sched_barrier(0);
-      load_group(wd[h ^ 1], w + 4 * (j + h + 1), j + h + 1 < ngw);
-      __builtin_amdgcn_sched_barrier(0);
-      if (j + h < ngw) run_group(wd[h], w + 4 * (j + h));
+      load_dt(p, t, w, ngw > 0);
     }
-  }
+  for (int64_t j = 0; j < ngw; ++j) run_group(w + 4 * j, j + 1 < ngw);
+  __builtin_amdgcn_sched_barrier(0);
 }
-
 
 // Strips per workgroup: the accumulators take 4 T1 S registers per lane, the convolution's
 // window and taps about 100 more (the choices keep every variant free of spills).
 constexpr int strips(int rt, bool conv, int es) {
-  if (conv) return rt <= 4 ? 4 : (rt <= 10 ? 2 : 1);
+  if (conv) return (rt <= 2 || (es == 4 && rt <= 4)) ? 4 : (rt <= 10 ? 2 : 1);
   return rt <= 10 ? 4 : ((rt <= 12 || es == 2) ? 2 : 1);
 }
 
