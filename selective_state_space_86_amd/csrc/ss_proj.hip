@@ -545,6 +545,319 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjArgs a) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Token-split variant for many tokens: each wave owns 64 tokens (four strips) and the whole K
+// range, and the weights go through LDS once per workgroup of 256 tokens, so every weight byte
+// fetched through L1 serves four times the tokens of the split-K kernel. Phase 1 stages one
+// 128-byte line of every W_x row per step (two K blocks, double-buffered, one barrier per
+// step); each wave reads its A fragments from there and its own inputs from global memory.
+// The accumulators hold complete sums, so B, C and the phase-2 operands come straight from
+// them. Phase 2 stages W_dt a group of 64 channels at a time (contiguous rows, read as whole
+// lines) and every wave applies each group to its own tokens.
+template <typename T, int RT>
+__global__ __launch_bounds__(256) void proj_tok_kernel(ProjArgs a) {
+  constexpr int ES = static_cast<int>(sizeof(T));
+  constexpr bool BF = ES == 2;
+  constexpr int T1 = RT + 2;
+  constexpr int CH = 16 / ES;
+  constexpr int KBW = 4 * CH;
+  constexpr int KL = 2 * KBW;                       // channels per staged line
+  constexpr int KSTEP = BF ? 1 : 4;
+  constexpr int S = 4;                              // strips per wave
+  constexpr int NS = BF ? RT / 2 : RT;              // phase-2 K steps
+  constexpr int TG = 4, GC = 64;                    // phase-2 tiles and channels per group
+  constexpr int LROW = 144;                         // staged W_x row: one line + 16 bytes
+  constexpr int WST = T1 * 16 * LROW;               // one staged line of every tile
+  constexpr int WPT = (T1 * 128 + 255) / 256;       // 16-byte pieces per thread and step
+  constexpr int DROW = 16 * RT * ES + 16;           // staged W_dt row (bytes)
+  constexpr int DST = GC * DROW;
+  constexpr int DPT = (GC * RT * ES + 255) / 256;   // 16-byte pieces per thread and group
+  constexpr int JUNK = (WST > DST ? WST : DST) * 2;  // 16 bytes per thread for pieces past the end
+  __shared__ __attribute__((aligned(16))) unsigned char lds[JUNK + 256 * 16];
+  T* tag = nullptr;
+
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const int li = l & 15, lq = l >> 4;
+  const int lr = li & 7, lp = lq + 4 * (li >> 3);
+  const int64_t M = a.tokens, dim = a.dim, N = a.dstate, rank = a.rank;
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * (64 * S);
+  const int64_t row_bytes = dim * ES;
+  const int tw = 64 * w;  // this wave's first token within the workgroup
+
+  // ---- phase 1 ------------------------------------------------------------------------------
+  const int64_t nkb = (dim + KL - 1) / KL;
+  const int64_t rows_here = (M - tok0) < 64 * S ? (M - tok0) : 64 * S;
+  const auto rx = rsrc(static_cast<const T*>(a.u) + tok0 * dim, rows_here * row_bytes);
+  uint32_t xoff[S][2];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) xoff[s][h] = static_cast<uint32_t>((tw + 16 * s + 8 * h + lr) * row_bytes);
+
+  // staging map: piece k = tid + 256 j is tile k / 128, row (k / 8) % 16, 16-byte piece k % 8
+  const auto rwx = rsrc(a.W_x, (rank + 2 * N) * row_bytes);
+  uint32_t goff[WPT], loff[WPT];
+  int gpc[WPT];
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int k = tid + 256 * j;
+    const int c = k >> 7, r = (k >> 3) & 15, pc = k & 7;
+    int64_t row = -1;
+    if (k < T1 * 128) {
+      if (c < RT) row = 16 * c + r < rank ? 16 * c + r : -1;
+      else if (r < N) row = (c == RT ? rank : rank + N) + r;
+    }
+    goff[j] = row >= 0 ? static_cast<uint32_t>(row * row_bytes) : kDropOffset;
+    // (a piece past the last tile loads nothing and is stored to this thread's junk slot:
+    // stores under a branch would make the compiler wait for every load in flight)
+    loff[j] = k < T1 * 128 ? static_cast<uint32_t>(c * 16 * LROW + r * LROW + pc * 16)
+                           : static_cast<uint32_t>(JUNK + 16 * tid);
+    gpc[j] = k < T1 * 128 ? pc : -1;
+  }
+  u32x4 wst[WPT], xr[S][2];
+  auto load_w = [&](int64_t kb) {
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int64_t kk = kb * KL + gpc[j] * CH;
+      const bool in = gpc[j] >= 0 && kb < nkb && kk < dim && goff[j] != kDropOffset;
+      wst[j] = __builtin_amdgcn_raw_buffer_load_b128(rwx, in ? goff[j] + static_cast<uint32_t>(kk * ES) : kDropOffset,
+                                                     0, 0);
+    }
+  };
+  auto store_w = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < WPT; ++j)
+      *reinterpret_cast<u32x4*>(lds + (gpc[j] >= 0 ? buf * WST + loff[j] : loff[j])) = wst[j];
+  };
+  auto load_x = [&](int64_t kb) {
+    const int64_t kk = kb * KL + lp * CH;
+    const bool in = kb < nkb && kk < dim;
+    const uint32_t ko = static_cast<uint32_t>(kk * ES);
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        xr[s][h] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? xoff[s][h] + ko : kDropOffset, 0, 0);
+  };
+
+  f32x4 acc[S][T1];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int c = 0; c < T1; ++c) acc[s][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Step kb: after the barrier the staged line kb is complete in buffer kb & 1 and every wave
+  // is done with buffer (kb + 1) & 1, which then takes line kb + 1 (loaded during step kb - 1).
+  load_w(0);
+  store_w(0);
+  load_w(1);
+  load_x(0);
+  for (int64_t kb = 0; kb < nkb; ++kb) {
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    store_w(static_cast<int>((kb + 1) & 1));
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(kb + 2);
+    u32x4 xf[S][2];
+#pragma unroll
+    for (int s = 0; s < S; ++s) line_halves(xr[s][0], xr[s][1], li, xf[s][0], xf[s][1]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(kb + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned char* lb = lds + static_cast<int>(kb & 1) * WST + li * LROW + lq * 16;
+    // tile c + 1's fragments are read while tile c's products run
+    u32x4 af[2][2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) af[0][kh] = *reinterpret_cast<const u32x4*>(lb + kh * 64);
+#pragma unroll
+    for (int c = 0; c < T1; ++c) {
+      if (c + 1 < T1) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+          af[(c + 1) & 1][kh] = *reinterpret_cast<const u32x4*>(lb + (c + 1) * 16 * LROW + kh * 64);
+      }
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int e = 0; e < KSTEP; ++e)
+#pragma unroll
+          for (int s = 0; s < S; ++s) acc[s][c] = mfma_step(tag, af[c & 1][kh], xf[s][kh], e, acc[s][c]);
+      // (keep the reads of tile c + 1 ahead of tile c's products)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KSTEP * S, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- B and C: lane (i, q), register r of tile RT / RT+1 holds B / C[token i][4q + r] ---------
+  {
+    const auto rb = rsrc(static_cast<T*>(a.B) + tok0 * N, (M - tok0) * N * ES);
+    const auto rc = rsrc(static_cast<T*>(a.C) + tok0 * N, (M - tok0) * N * ES);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int tl = tw + 16 * s + li;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const f32x4 v = acc[s][RT + cc];
+        const auto& ro = cc == 0 ? rb : rc;
+        const int n0 = 4 * lq;
+        if (N == 16) {
+          const uint32_t off = static_cast<uint32_t>((tl * 16 + n0) * ES);
+          if constexpr (BF) {
+            const u32x2 pk = {bf16_bits(v[0]) | (bf16_bits(v[1]) << 16), bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+            __builtin_amdgcn_raw_buffer_store_b64(pk, ro, off, 0, 0);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])}, ro,
+                off, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t off = n0 + e < N ? static_cast<uint32_t>((tl * N + n0 + e) * ES) : kDropOffset;
+            if constexpr (BF)
+              __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(bf16_bits(v[e])), ro, off, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), ro, off, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- phase 2: delta_raw^T = W_dt xp^T ------------------------------------------------------
+  // B operands from the accumulators: fp32 step (c, e) is register e of tile c (rank
+  // 16c + 4q + e); bf16 step st packs tiles 2st and 2st+1 (ranks 32st + 16 (e/4) + 4q + e%4)
+  // as a hi and a lo part.
+  constexpr int NB = BF ? NS : 1;
+  u32x4 xh[S][NB], xl[S][NB];
+  if constexpr (BF) {
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          uint32_t hv[2], lv[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int e = 2 * d + u;
+            const float v = acc[s][2 * st + (e >> 2)][e & 3];
+            hv[u] = bf16_bits(v);
+            lv[u] = bf16_bits(v - bf16_value(hv[u]));
+          }
+          xh[s][st][d] = hv[0] | (hv[1] << 16);
+          xl[s][st][d] = lv[0] | (lv[1] << 16);
+        }
+  }
+
+  const auto rdt = rsrc(a.W_dt, dim * rank * ES);
+  const auto rd = rsrc(static_cast<T*>(a.delta_raw) + tok0 * dim, (M - tok0) * row_bytes);
+  const int64_t ngroups = (dim + GC - 1) / GC;
+  const int64_t grp_bytes = GC * rank * ES;  // a group's rows are contiguous in W_dt
+  uint32_t dl[DPT];
+  int drow[DPT];
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    const int64_t o = 16 * static_cast<int64_t>(tid + 256 * j);
+    const int64_t row = o / (rank * ES), col = o % (rank * ES);
+    drow[j] = o < grp_bytes ? static_cast<int>(row) : -1;
+    dl[j] = o < grp_bytes ? static_cast<uint32_t>(row * DROW + col) : static_cast<uint32_t>(JUNK + 16 * tid);
+  }
+  u32x4 dst[DPT];
+  auto load_dt = [&](int64_t g) {
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+      const bool in = drow[j] >= 0 && g < ngroups && g * GC + drow[j] < dim;
+      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(
+          rdt, in ? static_cast<uint32_t>(g * grp_bytes + 16 * (tid + 256 * j)) : kDropOffset, 0, 0);
+    }
+  };
+  auto store_dt = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < DPT; ++j)
+      *reinterpret_cast<u32x4*>(lds + (drow[j] >= 0 ? buf * DST + dl[j] : dl[j])) = dst[j];
+  };
+
+  __syncthreads();  // phase 1 is done with the staging area
+  load_dt(0);
+  store_dt(0);
+  load_dt(1);
+  for (int64_t g = 0; g < ngroups; ++g) {
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    store_dt(static_cast<int>((g + 1) & 1));
+    __builtin_amdgcn_sched_barrier(0);
+    load_dt(g + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned char* db = lds + static_cast<int>(g & 1) * DST;
+    f32x4 o[S][TG];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int t = 0; t < TG; ++t) o[s][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // A fragment of (step st, tile t); the next one is read while the current products run
+    auto read_a = [&](int st, int t) -> u32x4 {
+      if constexpr (BF) {
+        // row li of tile t: channel 32 (t/2) + 8 (li/4) + 4 (t%2) + li%4 of the group
+        const int dm = 32 * (t >> 1) + 8 * (li >> 2) + 4 * (t & 1) + (li & 3);
+        const unsigned char* rp = db + dm * DROW + (32 * st + 4 * lq) * 2;
+        const u32x2 lo8 = *reinterpret_cast<const u32x2*>(rp);
+        const u32x2 hi8 = *reinterpret_cast<const u32x2*>(rp + 32);
+        return u32x4{lo8[0], lo8[1], hi8[0], hi8[1]};
+      } else {
+        return *reinterpret_cast<const u32x4*>(db + (16 * t + li) * DROW + (16 * st + 4 * lq) * 4);
+      }
+    };
+    u32x4 av[2];
+    av[0] = read_a(0, 0);
+#pragma unroll
+    for (int it = 0; it < NS * TG; ++it) {
+      const int st = it / TG, t = it % TG;
+      if (it + 1 < NS * TG) av[(it + 1) & 1] = read_a((it + 1) / TG, (it + 1) % TG);
+      const u32x4 a0 = av[it & 1];
+      if constexpr (BF) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) o[s][t] = mfma_step(tag, a0, xh[s][st], 0, o[s][t]);
+#pragma unroll
+        for (int s = 0; s < S; ++s) o[s][t] = mfma_step(tag, a0, xl[s][st], 0, o[s][t]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+            o[s][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a0[e]), acc[s][st][e], o[s][t], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, BF ? 2 : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, BF ? 2 * S : 4 * S, 0);
+    }
+    // lane (i, q), register r of tile t: delta_raw[token i][channel of row 4q + r]
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int64_t tl = tw + 16 * s + li;
+      if constexpr (BF) {
+#pragma unroll
+        for (int pp = 0; pp < TG / 2; ++pp) {
+          const int64_t d = g * GC + 32 * pp + 8 * lq;
+          const f32x4 e0 = o[s][2 * pp], e1 = o[s][2 * pp + 1];
+          const u32x4 pk = {bf16_bits(e0[0]) | (bf16_bits(e0[1]) << 16), bf16_bits(e0[2]) | (bf16_bits(e0[3]) << 16),
+                            bf16_bits(e1[0]) | (bf16_bits(e1[1]) << 16), bf16_bits(e1[2]) | (bf16_bits(e1[3]) << 16)};
+          __builtin_amdgcn_raw_buffer_store_b128(
+              pk, rd, d < dim ? static_cast<uint32_t>(tl * row_bytes + d * ES) : kDropOffset, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < TG; ++t) {
+          const int64_t d = g * GC + 16 * t + 4 * lq;
+          const f32x4 e0 = o[s][t];
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u32x4{__float_as_uint(e0[0]), __float_as_uint(e0[1]), __float_as_uint(e0[2]), __float_as_uint(e0[3])}, rd,
+              d < dim ? static_cast<uint32_t>(tl * row_bytes + d * ES) : kDropOffset, 0, 0);
+        }
+      }
+    }
+  }
+}
+
 // Strips per workgroup: the accumulators take 4 T1 S registers per lane, the convolution's
 // window and taps about 100 more (the choices keep every variant free of spills).
 constexpr int strips(int rt, bool conv, int es) {
@@ -559,6 +872,27 @@ hipError_t launch_proj(const ProjArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((a.tokens + per - 1) / per));
   hipLaunchKernelGGL((proj_kernel<T, RT, S, CONV>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename T, int RT>
+hipError_t launch_proj_tok(const ProjArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((a.tokens + 255) / 256));
+  hipLaunchKernelGGL((proj_tok_kernel<T, RT>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t proj_tok_t(const ProjArgs& a, int rt, hipStream_t s) {
+  if constexpr (sizeof(T) == 4) {
+    if (rt == 3) return launch_proj_tok<T, 3>(a, s);
+  }
+  switch (rt) {
+    case 2: return launch_proj_tok<T, 2>(a, s);
+    case 4: return launch_proj_tok<T, 4>(a, s);
+    case 6: return launch_proj_tok<T, 6>(a, s);
+    case 8: return launch_proj_tok<T, 8>(a, s);
+    default: return launch_proj_tok<T, 10>(a, s);
+  }
 }
 
 template <typename T, bool CONV>
@@ -589,9 +923,12 @@ int proj_step_tiles(int64_t rank, int dtype) {
   return 16;
 }
 
-hipError_t proj(const ProjArgs& a, int, hipStream_t s) {
+hipError_t proj(const ProjArgs& a, int cus, hipStream_t s) {
   const int rt = proj_step_tiles(a.rank, a.dtype);
   const bool conv = a.kconv > 0;
+  // the token-split kernel once there are enough tokens for a workgroup of 256 on every CU
+  if (!conv && rt <= 10 && a.tokens >= 256 * static_cast<int64_t>(cus))
+    return a.dtype == kBF16 ? proj_tok_t<uint16_t>(a, rt, s) : proj_tok_t<float>(a, rt, s);
   if (a.dtype == kBF16) return conv ? proj_t<uint16_t, true>(a, rt, s) : proj_t<uint16_t, false>(a, rt, s);
   return conv ? proj_t<float, true>(a, rt, s) : proj_t<float, false>(a, rt, s);
 }

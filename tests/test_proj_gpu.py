@@ -6,8 +6,9 @@ significant bits, so its rounding alone reaches 2^-8 relative (more than 2e-3 (1
 accumulation allowance: |gpu - ref| <= ulp_bf16(ref) / 2 + 1e-4 (1 + |ref|). The oracle gets
 the identical inputs. Shapes cover several token tiles with a ragged last one, channel counts that are
 not multiples of the 32-channel groups, dstate below 16, every instantiated count of step
-tiles (rank 8 .. 256), the two-strip launch, and the full 130M-layer size; at the 1.4B and
-3B sizes tokens are sampled (the projections are per token, so a sample is its own problem).
+tiles (rank 8 .. 256), the token-split kernel taken for large token counts, and the full
+130M-layer size; at the 1.4B and 3B sizes tokens are sampled (the projections are per token, so
+a sample is its own problem).
 """
 import numpy as np
 import pytest
@@ -87,17 +88,20 @@ def test_proj_every_step_tile_count(rank):
     run_case(1, 48, 72, 16, rank, "bf16", seed=103)
 
 
-@pytest.mark.parametrize("dt,rank", [("f32", 48), ("bf16", 48), ("f32", 160)])
-def test_proj_two_strip_launch(dt, rank):
-    """Enough tokens (>= 2 workgroups of 128 per CU) for the two-strip variant where it applies
-    (fp32 up to 10 step tiles, bf16 up to 6); the bf16 rank-160 case is there for contrast."""
-    w = inputs.WORKLOADS["mamba130m"].replace(name=f"p2s{dt}{rank}", batch=2, seqlen=40000, dim=64, dstate=16,
+@pytest.mark.parametrize("dt,rank,dim,N,L", [("f32", 48, 64, 16, 40000), ("bf16", 48, 64, 16, 40000),
+                                              ("f32", 160, 64, 16, 40000), ("f32", 40, 136, 16, 35001),
+                                              ("bf16", 152, 200, 7, 35001), ("bf16", 8, 1032, 16, 33333),
+                                              ("f32", 96, 520, 5, 33000)])
+def test_proj_token_split_kernel(dt, rank, dim, N, L):
+    """Enough tokens (two sequences of L, at least 256 per CU) for the token-split kernel, up to
+    10 step tiles: ragged channel groups and lines, dstate below 16, a ragged last workgroup."""
+    w = inputs.WORKLOADS["mamba130m"].replace(name=f"ptok{dt}{rank}x{dim}", batch=2, seqlen=L, dim=dim, dstate=N,
                                               dtype=dt)
     x = inputs.make_proj(w, rank, seed=104, device=DEV)
     _announce(w.name)
     got = ss.proj(x["u"], x["W_x"], x["W_dt"], rank)
     torch.cuda.synchronize()
-    check(got, oracle_proj(x, rank, 16), x["u"].dtype, w.name)
+    check(got, oracle_proj(x, rank, N), x["u"].dtype, w.name)
 
 
 def test_proj_empty_sequence():
