@@ -108,10 +108,12 @@ typedef struct {
                             2 for dstate == 16, else 3 when it applies, else 1 */
   int chunk_len;      /* tokens per lane and tile for kernel 2: 0 (automatic), 4 or 8 */
   int discretization; /* an ss_discretization value */
-  int chunk_rows;     /* time chunks per workgroup tile for kernel 2: 0 (automatic), 16 or 12;
-                         12 needs chunk_len 0 or 4 (else SS_ERR_BAD_SHAPE) and is chosen
+  int chunk_rows;     /* time chunks per workgroup tile for kernel 2: 0 (automatic), 16, 12 or
+                         32; 12 needs chunk_len 0 or 4 (else SS_ERR_BAD_SHAPE) and is chosen
                          automatically when channel groups of 16 per CU fill 4 slots of 3-wave
-                         workgroups better than 3 slots of 4-wave ones */
+                         workgroups better than 3 slots of 4-wave ones; 32 (8 waves) is chosen
+                         for at most 2 groups per CU and needs 256 * dim * 4 < 2^31 (else
+                         SS_ERR_BAD_SHAPE) */
 } ss_fwd_options;
 
 /*

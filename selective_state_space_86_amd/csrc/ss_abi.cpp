@@ -81,7 +81,9 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
   const int disc = opt ? opt->discretization : SS_DISC_DT;
   const int rows = opt ? opt->chunk_rows : 0;
   if (kernel < 0 || kernel > 3 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
-  if (!(rows == 0 || rows == 16 || rows == 12) || (rows == 12 && chunk == 8)) return SS_ERR_BAD_SHAPE;
+  if (!(rows == 0 || rows == 16 || rows == 12 || rows == 32) || (rows == 12 && chunk == 8)) return SS_ERR_BAD_SHAPE;
+  // (a tile of 32 rows of 8 tokens spans 256 tokens of the (.., dim) arrays from 32-bit offsets)
+  if (rows == 32 && 256 * dim * 4 >= (1LL << 31)) return SS_ERR_BAD_SHAPE;
   if (disc != SS_DISC_DT && disc != SS_DISC_ZOH) return SS_ERR_BAD_SHAPE;
   if (kernel == 2 && dstate != 16) return SS_ERR_UNSUPPORTED_N;
   const size_t es = elem_size(in_dtype);

@@ -44,14 +44,16 @@ using namespace chunk;
 
 constexpr int kLdsChunkStride = 16 * 16 + 16;  // [chunk][n][lane], padded against bank conflicts
 
-// R rows (time chunks) per workgroup: 16 (4 waves) or 12 (3 waves; four such workgroups fit
-// a CU where three of 16 do, for shapes with between 3 and 4 channel groups per CU).
+// R rows (time chunks) per workgroup: 16 (4 waves), 12 (3 waves; four such workgroups fit
+// a CU where three of 16 do, for shapes with between 3 and 4 channel groups per CU) or 32
+// (8 waves, two per SIMD from one workgroup, for shapes with at most 2 groups per CU, where
+// 4-wave workgroups leave most SIMDs with a single wave, which issues at about half rate).
 // Register budget: TC = 4 must fit 3 waves per SIMD, TC = 8 two; the zero-order-hold
 // variant holds 16 more values (1/A) and runs at two.
 template <typename T, bool GATE, int TC, bool EARLY, bool ZOH, bool CONV, int R>
-__global__ __launch_bounds__(R * 16) __attribute__((amdgpu_waves_per_eu(TC <= 4 && !ZOH ? 3 : 2)))
+__global__ __launch_bounds__(R * 16) __attribute__((amdgpu_waves_per_eu(TC <= 4 && !ZOH && R <= 16 ? 3 : 2)))
 void fwd_chunked_kernel(FwdArgs a) {
-  static_assert(R == 16 || R == 12, "16 or 12 chunks per tile");
+  static_assert(R == 16 || R == 12 || R == 32, "12, 16 or 32 chunks per tile");
   constexpr int NOWN = (16 + R - 1) / R;  // states each lane folds: n = k, k + R (when < 16)
   // The prod-abar/carry array alternates between two buffers by tile, so a tile's
   // aggregates never overwrite carries a slower wave may still be reading after the second
@@ -167,24 +169,30 @@ void fwd_chunked_kernel(FwdArgs a) {
     __syncthreads();
 
     // combine: this lane owns state n = k (and k + R) of channel i and folds the R chunks in
-    // order. Each lane reads exactly the LDS words it then overwrites with carries, so the
-    // carry array can alias the prod-abar array without another barrier.
+    // order (with 32 rows, rows 16..31 own none). Each lane reads exactly the LDS words it then
+    // overwrites with carries, so the carry array can alias the prod-abar array without another
+    // barrier.
 #pragma unroll
     for (int m = 0; m < NOWN; ++m) {
       const int n = k + m * R;
-      if (m == 0 || n < 16) {
+      if (n < 16) {
         float* sa = lds_a + n * 16 + i;
         const float* sh = lds_h + n * 16 + i;
-        float av[R], hv[R];
+        // (in blocks of at most 16 chunks: all reads of a block first, then its fold)
+        constexpr int CB = R < 16 ? R : 16;
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-          av[j] = sa[j * kLdsChunkStride];
-          hv[j] = sh[j * kLdsChunkStride];
-        }
+        for (int j0 = 0; j0 < R; j0 += CB) {
+          float av[CB], hv[CB];
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
-          sa[j * kLdsChunkStride] = carry[m];  // carry into chunk j
-          carry[m] = __builtin_fmaf(av[j], carry[m], hv[j]);
+          for (int j = 0; j < CB; ++j) {
+            av[j] = sa[(j0 + j) * kLdsChunkStride];
+            hv[j] = sh[(j0 + j) * kLdsChunkStride];
+          }
+#pragma unroll
+          for (int j = 0; j < CB; ++j) {
+            sa[(j0 + j) * kLdsChunkStride] = carry[m];  // carry into chunk j0 + j
+            carry[m] = __builtin_fmaf(av[j], carry[m], hv[j]);
+          }
         }
       }
     }
@@ -245,6 +253,7 @@ hipError_t launch_chunked_g(const FwdArgs& a, hipStream_t s) {
 template <typename T>
 hipError_t launch_chunked_t(const FwdArgs& a, ChunkPlan p, hipStream_t s) {
   if (p.rows == 12) return launch_chunked_g<T, 4, 12>(a, s);
+  if (p.rows == 32) return p.chunk_len == 4 ? launch_chunked_g<T, 4, 32>(a, s) : launch_chunked_g<T, 8, 32>(a, s);
   return p.chunk_len == 4 ? launch_chunked_g<T, 4, 16>(a, s) : launch_chunked_g<T, 8, 16>(a, s);
 }
 
@@ -257,7 +266,8 @@ bool fwd_chunked_supported(const FwdArgs& a) { return a.dstate == 16 && a.seqlen
 // workgroups share a CU where three of 16 rows do. The channel groups of 16 are dealt to
 // the resident slots in rounds, and a partly filled last round runs at low occupancy, so
 // the plan maximises the filled fraction of the slots:
-//  - at most 2 groups per CU (the 3B long-context shape: 320 groups): length 8, 16 rows;
+//  - at most 2 groups per CU (the 3B long-context shape: 320 groups): length 8, 32 rows, so
+//    every SIMD holding a group has two of its waves;
 //  - otherwise length 4 with 16 rows (3 slots per CU) unless 12 rows (4 slots) fill the
 //    rounds better by more than 5% (1024 groups, the 1.4B shape: 1 full round of 4 against
 //    2/3 of a second round of 3; 768 groups, the 130M shape: 16 rows, one full round).
@@ -265,7 +275,8 @@ bool fwd_chunked_supported(const FwdArgs& a) { return a.dstate == 16 && a.seqlen
 ChunkPlan fwd_chunked_pick(const FwdArgs& a, int cus) {
   const int64_t groups = a.batch * ((a.dim + 15) / 16);
   if (a.zoh) return {4, 16};  // the zero-order-hold variant spills registers at 8
-  if (groups <= 2 * static_cast<int64_t>(cus)) return {8, 16};
+  // (32 rows of 8 tokens span 256 tokens of the (.., dim) arrays from one 32-bit tile offset)
+  if (groups <= 2 * static_cast<int64_t>(cus)) return (256 * a.dim * 4 < (1LL << 31)) ? ChunkPlan{8, 32} : ChunkPlan{8, 16};
   auto filled = [&](int64_t slots_per_cu) {
     const int64_t slots = slots_per_cu * cus;
     const int64_t rounds = (groups + slots - 1) / slots;

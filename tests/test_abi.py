@@ -126,12 +126,14 @@ def test_fwd_ex_discretization_validation(lib, disc, kw, code):
 
 
 @pytest.mark.parametrize("chunk,rows,kw,code", [
-    (0, 8, {}, 2), (0, 15, {}, 2), (0, -12, {}, 2), (8, 12, {}, 2), (4, 32, {}, 2),
+    (0, 8, {}, 2), (0, 15, {}, 2), (0, -12, {}, 2), (8, 12, {}, 2), (4, 24, {}, 2), (0, 64, {}, 2),
+    (8, 32, dict(dim=1 << 21), 2), (8, 32, dict(u=None), 1), (4, 32, dict(y=FAKE + 2), 5),
     (4, 12, dict(u=None), 1), (0, 12, dict(dtype=5), 3), (0, 16, dict(y=FAKE + 1), 5),
 ])
 def test_fwd_ex_chunk_rows_validation(lib, chunk, rows, kw, code):
-    """chunk_rows is 0, 16 or 12, and 12 only with chunk length 0 or 4; errors are reported
-    before any device work (no GPU is needed to reach them)."""
+    """chunk_rows is 0, 16, 12 or 32; 12 only with chunk length 0 or 4, 32 only while a tile
+    of 256 tokens of (.., dim) fp32 rows spans less than 2^31 bytes; errors are reported before
+    any device work (no GPU is needed to reach them)."""
     assert fwd_ex_call(lib, 2, chunk, rows=rows, **kw) == code
 
 

@@ -161,7 +161,7 @@ def test_mamba3b_long_full_size_sampled():
     _check_sampled(inputs.WORKLOADS["mamba3b-long"], k=48)
 
 
-KERNELS = [(1, 0, 0), (2, 4, 16), (2, 8, 16), (2, 4, 12), (3, 0, 0)]  # (kernel, chunk_len, chunk_rows)
+KERNELS = [(1, 0, 0), (2, 4, 16), (2, 8, 16), (2, 4, 12), (2, 8, 32), (2, 4, 32), (3, 0, 0)]  # (kernel, chunk_len, chunk_rows)
 
 
 @pytest.mark.parametrize("kernel,chunk,rows", KERNELS)

@@ -17,7 +17,7 @@ from tests import parity_util as pu
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-KERNELS = [(1, 0, 0), (2, 4, 16), (2, 8, 16), (2, 4, 12)]  # (kernel, chunk_len, chunk_rows)
+KERNELS = [(1, 0, 0), (2, 4, 16), (2, 8, 16), (2, 4, 12), (2, 8, 32), (2, 4, 32)]  # (kernel, chunk_len, chunk_rows)
 
 
 def _announce(msg):
