@@ -366,6 +366,10 @@ template <typename T>
 __device__ __forceinline__ float ld(const void* p, int64_t i) {
   return load_elem(static_cast<const T*>(p), i);
 }
+// An element kept as stored (bf16 bits or fp32), widened where it is used: a conversion
+// right after a prefetching load would make the wave wait for that load there.
+__device__ __forceinline__ float widen(float v) { return v; }
+__device__ __forceinline__ float widen(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
 
 struct Lane {
   int64_t b, c0, c, cc;
@@ -443,7 +447,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
     for (int n = 0; n < 16; ++n) h[n] = 0.0f;
 #pragma unroll
     for (int j = 0; j < CTC; ++j) {
-      const float x = cur.x[j] + bias;
+      const float x = widen(cur.x[j]) + bias;
       float dt = a.softplus ? softplus(x) : x;
       dt = (t0 + l.k * CTC + j < L) ? dt : 0.0f;  // a zero step is the identity
       dsum += dt;
@@ -499,28 +503,43 @@ void bwd_chunked_kernel(BwdArgs a) {
   // raw inputs of a tile's chunk for this lane (tokens past the end re-read the last one);
   // the tile processed next (the earlier one) is requested before this one is computed
   struct Raw {
-    float x[TC], u[TC], z[TC], dy[TC], b[TC], c[TC];
+    T x[TC], u[TC], z[TC], b[TC], c[TC];
+    float dy[TC];
   };
+  // (every load is issued unconditionally, lanes past dstate reading state dstate - 1 and
+  // discarding it: loads under a branch make the compiler wait for all of them at the join,
+  // which would turn the prefetch of the next tile into a stall)
   auto fetch = [&](Raw& r, int64_t t0) {
+    const int64_t nb = l.i < N ? l.i : N - 1;
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
       const int64_t t = t0 + l.k * TC + j;
       const int64_t tt = t < L ? t : L - 1;
       const int64_t e = (l.b * L + tt) * a.dim + l.cc;
-      r.x[j] = ld<T>(a.delta, e);
-      r.u[j] = ld<T>(a.u, e);
-      r.z[j] = GATE ? ld<T>(a.z, e) : 0.0f;
+      r.x[j] = static_cast<const T*>(a.delta)[e];
+      r.u[j] = static_cast<const T*>(a.u)[e];
+      r.z[j] = GATE ? static_cast<const T*>(a.z)[e] : T();
       r.dy[j] = a.dy[e];
-      r.b[j] = l.i < N ? ld<T>(a.B, (l.b * L + tt) * N + l.i) : 0.0f;
-      r.c[j] = l.i < N ? ld<T>(a.C, (l.b * L + tt) * N + l.i) : 0.0f;
+      // (zeroed past dstate where the tile is used, so nothing here waits for the loads)
+      r.b[j] = static_cast<const T*>(a.B)[(l.b * L + tt) * N + nb];
+      r.c[j] = static_cast<const T*>(a.C)[(l.b * L + tt) * N + nb];
     }
   };
   Raw cur, nxt;
-  if (a.ntiles > 0) fetch(cur, (a.ntiles - 1) * TT);
+  // the checkpointed state entering each tile (lane (k, i): state n = k of channel i), also
+  // requested a tile ahead: read where it is used, its latency would stall every tile
+  auto ckpt_of = [&](int64_t tile) { return a.ckpt[((l.b * a.ntiles + tile) * dimp + l.c) * 16 + l.k]; };
+  float ck_cur = 0.0f, ck_nxt = 0.0f;
+  if (a.ntiles > 0) {
+    fetch(cur, (a.ntiles - 1) * TT);
+    ck_cur = ckpt_of(a.ntiles - 1);
+  }
   for (int64_t tile = a.ntiles - 1; tile >= 0; --tile) {
     progress_priority(a.ntiles - 1 - tile, a.ntiles);
     const int64_t t0 = tile * TT;
-    if (tile > 0) fetch(nxt, t0 - TT);
+    // (the tile before the first one re-reads tile 0: unused, but no branch around the loads)
+    fetch(nxt, tile > 0 ? t0 - TT : 0);
+    ck_nxt = ckpt_of(tile > 0 ? tile - 1 : 0);
     // per-token inputs of this lane's chunk (tokens past the end: zero step, zero dy)
     float dt[TC], dtu[TC], uu[TC], ds[TC], sg[TC], vb[TC], vc[TC], dyv[TC], dsl[TC];
     bool ok[TC];
@@ -529,23 +548,23 @@ void bwd_chunked_kernel(BwdArgs a) {
       const int64_t t = t0 + l.k * TC + j;
       const bool tv = t < L;
       ok[j] = tv && l.cvalid;
-      const float x = cur.x[j] + bias;
+      const float x = widen(cur.x[j]) + bias;
       dt[j] = tv ? (a.softplus ? softplus(x) : x) : 0.0f;
       sg[j] = a.softplus ? sigmoid(x) : 1.0f;
-      uu[j] = cur.u[j];
+      uu[j] = widen(cur.u[j]);
       dtu[j] = dt[j] * uu[j];
       dyv[j] = ok[j] ? cur.dy[j] : 0.0f;
       float g = 1.0f;
       dsl[j] = 0.0f;
       if (GATE) {
-        const float zv = cur.z[j];
+        const float zv = widen(cur.z[j]);
         const float s = fast_rcp(1.0f + fast_exp2(-zv * kLog2e));
         g = zv * s;
         dsl[j] = s * __builtin_fmaf(zv, 1.0f - s, 1.0f);
       }
       ds[j] = dyv[j] * g;
-      vb[j] = cur.b[j];
-      vc[j] = cur.c[j];
+      vb[j] = l.i < N ? widen(cur.b[j]) : 0.0f;
+      vc[j] = l.i < N ? widen(cur.c[j]) : 0.0f;
     }
 
     // forward local pass from a zero state: decays and chunk aggregates
@@ -576,7 +595,7 @@ void bwd_chunked_kernel(BwdArgs a) {
     {  // lane (k, i) owns state n = k of channel i: the forward fold from the checkpoint,
        // then the reverse fold from the adjoint of the later tile; each lane overwrites
        // exactly the words it read
-      float carry = a.ckpt[((l.b * a.ntiles + tile) * dimp + l.c) * 16 + l.k];
+      float carry = ck_cur;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const int o = jj * kS + l.k * 16 + l.i;
@@ -601,15 +620,28 @@ void bwd_chunked_kernel(BwdArgs a) {
     }
     __syncthreads();  // every lane has its carries: lds_eh is free for the reductions
 
+    // Stores go through buffer resources based at this tile, a masked lane's to an offset
+    // past the range (dropped), so no store sits under a branch: the compiler would wait there
+    // for every memory operation in flight, the next tile's prefetch included.
+    const int64_t eb = (l.b * L + t0) * a.dim;
+    const int64_t eleft = (a.batch * L * a.dim - eb) * 4;
+    const auto rdu = chunk::rsrc(a.du + eb, eleft);
+    const auto rdd = chunk::rsrc(a.ddelta + eb, eleft);
+    const auto rdz = chunk::rsrc(GATE ? a.dz + eb : a.du + eb, GATE ? eleft : 0);
+    const int64_t plane = a.batch * a.ngroups * L * N;
+    const int64_t pb = ((l.b * a.ngroups + (l.c0 >> 4)) * L + t0) * N;
+    const auto rpb = chunk::rsrc(a.part_bc + pb, (plane - pb) * 4);
+    const auto rpc = chunk::rsrc(a.part_bc + plane + pb, (plane - pb) * 4);
+
     // true states of the chunk, the pre-gate output s and dz
     float H[TC][16];
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
       float s = Dd * uu[j];
       bwd_true(j == 0 ? q : H[j > 0 ? j - 1 : 0], H[j], ex[j], dtu[j], vb[j], vc[j], s);
-      if (GATE && ok[j]) {
-        const int64_t e = (l.b * L + t0 + l.k * TC + j) * a.dim + l.c;
-        a.dz[e] = dyv[j] * s * dsl[j];
+      if (GATE) {
+        const uint32_t off = ok[j] ? static_cast<uint32_t>(((l.k * TC + j) * a.dim + l.c) * 4) : chunk::kDropOffset;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dyv[j] * s * dsl[j]), rdz, off, 0, 0);
       }
     }
 
@@ -622,19 +654,21 @@ void bwd_chunked_kernel(BwdArgs a) {
       float sb = 0.0f, ga = 0.0f;
       bwd_grad(mu, dAacc, H[j], ex[j], A2, dt[j], dtu[j], ds[j], vb[j], vc[j], ga, sb, rad);
       const int64_t t = t0 + l.k * TC + j;
-      if (ok[j]) {
-        const int64_t e = (l.b * L + t) * a.dim + l.c;
+      {
+        const uint32_t off = ok[j] ? static_cast<uint32_t>(((l.k * TC + j) * a.dim + l.c) * 4) : chunk::kDropOffset;
         const float ddt = __builtin_fmaf(uu[j], sb, ga * kLn2);
         const float dd = ddt * sg[j];
-        a.du[e] = __builtin_fmaf(ds[j], Dd, dt[j] * sb);
-        a.ddelta[e] = dd;
-        dbacc += dd;
-        dDacc = __builtin_fmaf(ds[j], uu[j], dDacc);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__builtin_fmaf(ds[j], Dd, dt[j] * sb)), rdu, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dd), rdd, off, 0, 0);
+        dbacc += ok[j] ? dd : 0.0f;
+        dDacc = ok[j] ? __builtin_fmaf(ds[j], uu[j], dDacc) : dDacc;
       }
-      // sum the 16 channels of this row: lane i takes state n = i
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      // sum the 16 channels of this row: lane i takes state n = i (the block is this row's
+      // own and LDS runs a wave's operations in order: the fences only keep the compiler
+      // from moving the accesses across the other lanes' writes)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       float sB = 0.0f, sC = 0.0f;
       {
         const float4* qb = reinterpret_cast<const float4*>(rB + l.i * 16);
@@ -646,16 +680,17 @@ void bwd_chunked_kernel(BwdArgs a) {
           sC += (vc4.x + vc4.y) + (vc4.z + vc4.w);
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      if (t < L && l.i < N) {
-        const int64_t o = ((l.b * a.ngroups + (l.c0 >> 4)) * L + t) * N + l.i;
-        a.part_bc[o] = sB;
-        a.part_bc[a.batch * a.ngroups * L * N + o] = sC;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      {
+        const uint32_t off = (t < L && l.i < N) ? static_cast<uint32_t>(((l.k * TC + j) * N + l.i) * 4) : chunk::kDropOffset;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sB), rpb, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sC), rpc, off, 0, 0);
       }
     }
     cur = nxt;
+    ck_cur = ck_nxt;
   }
   if (a.dh0 && l.cvalid && l.k < N) a.dh0[(l.b * a.dim + l.c) * N + l.k] = rcarry;
 
