@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 7
+#define SS_ABI_VERSION 8
 #define SS_MAX_DSTATE 16
 
 typedef enum {
@@ -114,6 +114,21 @@ typedef struct {
                          workgroups better than 3 slots of 4-wave ones; 32 (8 waves) is chosen
                          for at most 2 groups per CU and needs 256 * dim * 4 < 2^31 (else
                          SS_ERR_BAD_SHAPE) */
+  int split_parts;    /* kernel 2 only: cut every sequence into this many parts of whole tiles
+                         (fewer when it is too short), processed by successive workgroups
+                         that hand the chunk state on (the associative combine of
+                         "架构变体：Mamba/SSM", section "硬件感知算法", one level above the
+                         tiles). 0: automatic (split when the channel groups leave part of the
+                         last round of resident workgroups empty and outnumber the resident
+                         slots, e.g. 320 groups on 256 CUs); 1: never; 2..16: that many
+                         (else SS_ERR_BAD_SHAPE). Results equal the unsplit kernel's up to
+                         fp32 rounding order. A split call uses a device workspace the library
+                         keeps per (device, stream): allocated (hipMalloc, then cleared by a
+                         kernel on the stream) on the first split call on that pair and when a
+                         larger one is needed, kept until the process ends, left zeroed by
+                         every call; calls on one stream are ordered, so they never share it
+                         concurrently. Its size: 1028 B per channel group and part after the
+                         first (at least doubled when it grows), plus 1.25 KiB. */
 } ss_fwd_options;
 
 /*

@@ -12,7 +12,7 @@ _lib = None
 
 F32, BF16 = 0, 1
 DISC_DT, DISC_ZOH = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_fwd_conv", "ss_step",
            "ss_step_ex", "ss_bwd_workspace_size", "ss_bwd", "ss_proj", "ss_proj_conv")
 
@@ -20,9 +20,11 @@ EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_fwd_
 class FwdOptions(ctypes.Structure):
     """ss_fwd_options: kernel 0 automatic / 1 sequential / 2 time-chunked / 3 state-parallel;
     chunk_len 0, 4, 8; discretization 0 (input term dt*B) / 1 (exact zero-order hold);
-    chunk_rows 0 (automatic), 16 or 12 time chunks per workgroup tile."""
+    chunk_rows 0 (automatic), 16, 12 or 32 time chunks per workgroup tile; split_parts 0
+    (automatic), 1 (never) or 2..16 sequence parts for the time-chunked kernel."""
     _fields_ = [("kernel", ctypes.c_int), ("chunk_len", ctypes.c_int),
-                ("discretization", ctypes.c_int), ("chunk_rows", ctypes.c_int)]
+                ("discretization", ctypes.c_int), ("chunk_rows", ctypes.c_int),
+                ("split_parts", ctypes.c_int)]
 
 
 class SSError(RuntimeError):
@@ -114,9 +116,9 @@ def _stream(device, stream):
 
 def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=None,
         last_state=None, return_last_state=True, stream=None, kernel=0, chunk_len=0, h0=None,
-        zoh=False, chunk_rows=0):
-    """Selective-scan forward (``ss_fwd``; ``ss_fwd_ex`` when h0, kernel, chunk_len, chunk_rows
-    or zoh are given). u, delta, z: (batch, L, dim); B, C: (batch, L, N); A: (dim, N) fp32; D,
+        zoh=False, chunk_rows=0, split_parts=0):
+    """Selective-scan forward (``ss_fwd``; ``ss_fwd_ex`` when h0, kernel, chunk_len, chunk_rows,
+    split_parts or zoh are given). u, delta, z: (batch, L, dim); B, C: (batch, L, N); A: (dim, N) fp32; D,
     delta_bias: (dim,) fp32; h0: (batch, dim, N) fp32 initial state or None; zoh: exact
     zero-order-hold input term. Returns y (fp32) and, unless return_last_state is False,
     the final state (batch, dim, N) fp32."""
@@ -143,8 +145,9 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=Non
     head = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
             int(bool(softplus)), _ptr(y), _ptr(last_state))
     tail = (batch, L, dim, N, dt)
-    if kernel or chunk_len or chunk_rows or h0 is not None or zoh:
-        opt = FwdOptions(int(kernel), int(chunk_len), DISC_ZOH if zoh else DISC_DT, int(chunk_rows))
+    if kernel or chunk_len or chunk_rows or split_parts or h0 is not None or zoh:
+        opt = FwdOptions(int(kernel), int(chunk_len), DISC_ZOH if zoh else DISC_DT, int(chunk_rows),
+                         int(split_parts))
         rc = lib.ss_fwd_ex(*head, _ptr(h0), *tail, ctypes.byref(opt), _stream(dev, stream))
     else:
         rc = lib.ss_fwd(*head, *tail, _stream(dev, stream))
@@ -155,7 +158,7 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=Non
 
 def fwd_conv(x, conv_w, delta, A, B, C, conv_b=None, conv_state=None, D=None, z=None,
              delta_bias=None, softplus=True, y=None, last_state=None, h0=None, u_out=None,
-             stream=None, kernel=0, chunk_len=0, zoh=False, chunk_rows=0):
+             stream=None, kernel=0, chunk_len=0, zoh=False, chunk_rows=0, split_parts=0):
     """Forward with the fused prologue (``ss_fwd_conv``): u = silu(causal depthwise
     conv1d(x) + conv_b), then the scan of ``fwd`` on it. x: (batch, L, dim); conv_w
     (dim, K) fp32, K <= 4; conv_b (dim,) fp32 or None; conv_state (batch, dim, K-1) fp32 or
@@ -192,7 +195,8 @@ def fwd_conv(x, conv_w, delta, A, B, C, conv_b=None, conv_state=None, D=None, z=
     if not want_u:
         u_out = None
     _check(u_out, "u_out", dev, torch.float32, (batch, L, dim))
-    opt = FwdOptions(int(kernel), int(chunk_len), DISC_ZOH if zoh else DISC_DT, int(chunk_rows))
+    opt = FwdOptions(int(kernel), int(chunk_len), DISC_ZOH if zoh else DISC_DT, int(chunk_rows),
+                     int(split_parts))
     rc = load_library().ss_fwd_conv(_ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), K, _ptr(delta),
                                     _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                                     int(bool(softplus)), _ptr(y), _ptr(last_state), _ptr(h0), _ptr(u_out),

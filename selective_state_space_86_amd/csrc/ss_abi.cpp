@@ -2,8 +2,11 @@
 // dispatch to the gfx950 kernels on the caller's stream. See include/ss.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "../../include/ss.h"
 #include "ss_kernels.h"
@@ -35,6 +38,55 @@ int check_device(int* cus) {
     g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_release);
   }
   return ok ? SS_OK : SS_ERR_DEVICE;
+}
+
+// Split workspaces of the chunked forward, one per (device, stream) that used the split,
+// kept until the process ends. A kernel leaves its workspace zeroed, and kernels on one
+// stream run in order, so a stream's calls can share one buffer.
+struct SplitWs {
+  int dev;
+  hipStream_t stream;
+  uint32_t* ptr;
+  int64_t cap;  // published-state slots
+};
+std::mutex g_split_mu;
+std::vector<SplitWs> g_split_ws;
+
+// The split workspace of the current device and stream s with at least `items` slots (its
+// capacity in *cap), or null on a HIP error. A new or grown buffer is cleared by a kernel on
+// s, ahead of the caller's; a grown one gets twice the old capacity at least.
+uint32_t* split_workspace(int64_t items, hipStream_t s, int64_t* cap) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(g_split_mu);
+  SplitWs* w = nullptr;
+  for (auto& e : g_split_ws)
+    if (e.dev == dev && e.stream == s) w = &e;
+  if (w && w->cap >= items) {
+    *cap = w->cap;
+    return w->ptr;
+  }
+  int64_t want = items;
+  if (w) {  // grow: the old buffer may still be in use by work queued on s
+    if (hipStreamSynchronize(s) != hipSuccess || hipFree(w->ptr) != hipSuccess) return nullptr;
+    want = std::max(items, 2 * w->cap);
+    w->ptr = nullptr;
+    w->cap = 0;
+  } else {
+    g_split_ws.push_back(SplitWs{dev, s, nullptr, 0});
+    w = &g_split_ws.back();
+  }
+  const size_t bytes = ss::fwd_split_ws_bytes(want);
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
+  if (ss::fwd_split_ws_clear(static_cast<uint32_t*>(p), bytes, s) != hipSuccess) {
+    (void)hipFree(p);
+    return nullptr;
+  }
+  w->ptr = static_cast<uint32_t*>(p);
+  w->cap = want;
+  *cap = want;
+  return w->ptr;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -80,7 +132,9 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
   const int chunk = opt ? opt->chunk_len : 0;
   const int disc = opt ? opt->discretization : SS_DISC_DT;
   const int rows = opt ? opt->chunk_rows : 0;
+  const int split_parts = opt ? opt->split_parts : 0;
   if (kernel < 0 || kernel > 3 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
+  if (split_parts < 0 || split_parts > 16) return SS_ERR_BAD_SHAPE;
   if (!(rows == 0 || rows == 16 || rows == 12 || rows == 32) || (rows == 12 && chunk == 8)) return SS_ERR_BAD_SHAPE;
   // (a tile of 32 rows of 8 tokens spans 256 tokens of the (.., dim) arrays from 32-bit offsets)
   if (rows == 32 && 256 * dim * 4 >= (1LL << 31)) return SS_ERR_BAD_SHAPE;
@@ -118,6 +172,18 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
     if (plan.rows == 12 && plan.chunk_len != 4) {
       if (rows == 12) plan.chunk_len = 4;  // rows asked for, chunk length automatic
       else plan.rows = 16;                 // chunk length 8 asked for, rows automatic
+    }
+    int parts = split_parts == 0 ? ss::fwd_split_parts(a, plan, cus) : split_parts;
+    const int64_t groups = batch * ((dim + 15) / 16);
+    if (parts > 1) {  // whole tiles per part: a short sequence gets fewer parts
+      a.part_len = ss::fwd_split_part_len(seqlen, plan, parts);
+      parts = static_cast<int>((seqlen + a.part_len - 1) / a.part_len);
+      if (groups * parts > 0x7fffffffLL) parts = 1;
+    }
+    if (parts > 1) {
+      a.split_ws = split_workspace(ss::fwd_split_items(groups, parts), s, &a.split_cap);
+      if (!a.split_ws) return SS_ERR_HIP;
+      a.parts = parts;
     }
     e = ss::fwd_chunked(a, plan, s);
   } else if (kernel == 0 && ss::fwd_state_supported(a))

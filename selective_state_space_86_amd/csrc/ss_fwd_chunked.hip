@@ -35,6 +35,8 @@
 // so the loads and stores need no per-access vector address arithmetic. The next tile's
 // inputs are requested right after the local pass, so the combine and the fix-up of the
 // current tile overlap their latency.
+#include <algorithm>
+
 #include "ss_chunk_ops.h"
 
 namespace ss {
@@ -44,13 +46,52 @@ using namespace chunk;
 
 constexpr int kLdsChunkStride = 16 * 16 + 16;  // [chunk][n][lane], padded against bank conflicts
 
+// Sequence split. When the channel groups do not fill the resident workgroup slots in whole
+// rounds (the 3B long-context shape: 320 groups for 256 one-workgroup CUs, so a second round
+// of 64 would run on a quarter of the chip), every group's sequence is cut into `parts`
+// parts of whole tiles, and each workgroup takes one work item (part q, group g) from a
+// counter in the order q-major. The chunk state that part q - 1 ends with is the carry part
+// q starts from (the same associative combine as between tiles, one level up), so part q
+// waits until part q - 1 has published it. A work item's predecessor always holds a smaller
+// counter value, so it was taken by a workgroup that is already running and whose own wait
+// is on an even earlier item: every wait ends. The wait is bounded all the same, and a wait
+// that hits the bound is counted in the workspace (it would leave a wrong carry).
+// The hand-off uses agent-scope atomic loads and stores for the flags and the states, which
+// are coherent across the XCDs' separate L2 caches by themselves: the producer waits until its
+// state stores have completed before the flag is stored, and the consumer loads the states
+// only after it has seen the flag. Agent-scope acquire/release fences would do the same with
+// a write-back and an invalidation of the whole L2 of the XCD at every hand-off, which cost
+// more than the split saved at short parts.
+// Work-item queues: workgroup ids are dealt to the 8 XCDs round-robin, and neighbouring groups
+// share 128-byte lines of u, delta, z and y in an XCD's L2, so when the groups divide by 8 the
+// workgroups with id = x (mod 8) take items from queue x, which holds the parts of the x-th
+// eighth of the groups (a contiguous slice, as the unsplit kernel gives XCD x), again in the
+// order (part, group). Each queue gets exactly as many workgroups as it has items, and an
+// item's predecessor is in the same queue with a smaller counter value, so the argument above
+// holds per queue; a workgroup's queue is a function of its id alone, so the result never
+// depends on where it runs.
+// Workspace (32-bit words) of `cap` slots: the counter of queue x at word 32 x (x < 8), the
+// count of waits that hit the bound at word 255, then from word kSplitHeader one flag per
+// slot (padded to 64 words), then the
+// published states, 16 x 16 fp32 per slot ([state n][channel i]). Item (part q, group gi)
+// publishes in slot q * groups + gi. The layout depends on the capacity only, never on the
+// call, so a flag word is never a state word of another call. The last workgroup to take an
+// item resets the counter and every consumer resets the flag it waited on, so counter and
+// flags are zero again when the kernel ends (the states are left as they are).
+constexpr int64_t kSplitHeader = 256;
+constexpr uint32_t kSplitSpinLimit = 1u << 22;  // several seconds of polling
+__host__ __device__ inline int64_t split_flag_words(int64_t items) { return (items + 63) / 64 * 64; }
+__device__ inline float* split_states(const FwdArgs& a) {
+  return reinterpret_cast<float*>(a.split_ws + kSplitHeader + split_flag_words(a.split_cap));
+}
+
 // R rows (time chunks) per workgroup: 16 (4 waves), 12 (3 waves; four such workgroups fit
 // a CU where three of 16 do, for shapes with between 3 and 4 channel groups per CU) or 32
 // (8 waves, two per SIMD from one workgroup, for shapes with at most 2 groups per CU, where
 // 4-wave workgroups leave most SIMDs with a single wave, which issues at about half rate).
 // Register budget: TC = 4 must fit 3 waves per SIMD, TC = 8 two; the zero-order-hold
 // variant holds 16 more values (1/A) and runs at two.
-template <typename T, bool GATE, int TC, bool EARLY, bool ZOH, bool CONV, int R>
+template <typename T, bool GATE, int TC, bool EARLY, bool ZOH, bool CONV, int R, bool SPLIT>
 __global__ __launch_bounds__(R * 16) __attribute__((amdgpu_waves_per_eu(TC <= 4 && !ZOH && R <= 16 ? 3 : 2)))
 void fwd_chunked_kernel(FwdArgs a) {
   static_assert(R == 16 || R == 12 || R == 32, "12, 16 or 32 chunks per tile");
@@ -63,16 +104,37 @@ void fwd_chunked_kernel(FwdArgs a) {
   __shared__ float lds_h[R * kLdsChunkStride];      // chunk end states
 
   const int64_t ngd = (a.dim + 15) / 16;
-  const int64_t g = group_of(blockIdx.x, a.batch * ngd);
+  const int64_t groups = a.batch * ngd;
+  const int tid = threadIdx.x;
+  const int64_t L = a.seqlen;
+  int64_t gi = blockIdx.x, part = 0;  // work item: group index gi, sequence part
+  __shared__ uint32_t item_s;
+  if (SPLIT) {
+    if (tid == 0) {
+      const bool by_xcd = groups % 8 == 0;
+      const uint32_t qx = by_xcd ? blockIdx.x % 8 : 0;
+      const uint32_t slice = static_cast<uint32_t>(by_xcd ? groups / 8 : groups);  // groups per queue
+      uint32_t* counter = a.split_ws + 32 * qx;
+      const uint32_t t = atomicAdd(counter, 1u);
+      if (t == slice * static_cast<uint32_t>(a.parts) - 1)  // every item of the queue is taken
+        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      item_s = (t / slice) * static_cast<uint32_t>(groups) + qx * slice + t % slice;  // part * groups + gi
+    }
+    __syncthreads();
+    const uint32_t item = __builtin_amdgcn_readfirstlane(item_s);  // (uniform: keep it in SGPRs)
+    part = item / groups;
+    gi = item % groups;
+  }
+  const int64_t t_begin = SPLIT ? part * a.part_len : 0;
+  const int64_t t_end = SPLIT ? min(L, t_begin + a.part_len) : L;
+  const int64_t g = SPLIT ? gi : group_of(gi, groups);
   const int64_t b = g / ngd;
   const int64_t c0 = (g % ngd) * 16;
-  const int tid = threadIdx.x;
   const int i = tid & 15;  // channel within the group == the state index this lane owns in the combine
   const int k = tid >> 4;  // time chunk within the tile (row of 16 lanes)
   const int64_t c = c0 + i;
   const bool cvalid = c < a.dim;
   const int64_t cc = cvalid ? c : a.dim - 1;
-  const int64_t L = a.seqlen;
   TileLoader<T, GATE, TC, R> K(a, b, c0, k, i, cc);
 
   float A2[16], iA[16];
@@ -90,20 +152,42 @@ void fwd_chunked_kernel(FwdArgs a) {
 #pragma unroll
   for (int m = 0; m < NOWN; ++m) {
     const int n = k + m * R;
-    carry[m] = (a.h0 && n < 16) ? a.h0[(b * a.dim + cc) * 16 + n] : 0.0f;
+    carry[m] = (a.h0 && part == 0 && n < 16) ? a.h0[(b * a.dim + cc) * 16 + n] : 0.0f;
+  }
+  if (SPLIT && part > 0) {  // start from the state the previous part of this group ends with
+    const int64_t item = (part - 1) * groups + gi;
+    uint32_t* flag = a.split_ws + kSplitHeader + item;
+    uint32_t spins = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      if (++spins == kSplitSpinLimit) {
+        if ((tid & 63) == 0) atomicAdd(a.split_ws + 255, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // (the state loads stay after the flag)
+    const float* src = split_states(a) + item * 256;
+#pragma unroll
+    for (int m = 0; m < NOWN; ++m) {
+      const int n = k + m * R;
+      if (n < 16) carry[m] = __hip_atomic_load(src + n * 16 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();  // every wave has seen the flag: clear it for the next call
+    if (tid == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const uint32_t y_row = static_cast<uint32_t>(a.dim * 4);
   const uint32_t y_off = static_cast<uint32_t>(k * TC) * y_row + static_cast<uint32_t>(i * 4);
 
   TileIn<TC> cur, nxt;
-  K.load(cur, 0);
+  K.load(cur, t_begin);
   int buf = 0;
-  for (int64_t t0 = 0; t0 < L; t0 += R * TC, buf ^= 1) {
-    progress_priority(t0, L);
-    const bool full = t0 + R * TC <= L;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += R * TC, buf ^= 1) {
+    // (a split kernel is the one-workgroup-per-CU plan, where priorities change nothing)
+    if (!SPLIT) progress_priority(t0, L);
+    const bool full = t0 + R * TC <= t_end;  // (a part other than the last ends on a tile boundary)
     float* lds_a = lds_a2[buf];
     // request the next tile first: the whole tile's work hides its latency
-    if (EARLY && t0 + R * TC < L) K.load(nxt, t0 + R * TC);
+    if (EARLY && t0 + R * TC < t_end) K.load(nxt, t0 + R * TC);
 
     // local pass from a zero state
     float h[16], ex[TC][16], y[TC], gate[TC], vc[TC];
@@ -146,7 +230,7 @@ void fwd_chunked_kernel(FwdArgs a) {
     }
 
     // otherwise request it now: the combine and fix-up below hide its latency
-    if (!EARLY && t0 + R * TC < L) K.load(nxt, t0 + R * TC);
+    if (!EARLY && t0 + R * TC < t_end) K.load(nxt, t0 + R * TC);
 
     // chunk aggregates (prod abar = exp(A * sum dt), end state) to LDS
     {
@@ -217,7 +301,21 @@ void fwd_chunked_kernel(FwdArgs a) {
     }
     cur = nxt;
   }
-  if (a.last_state && cvalid) {
+  if (SPLIT && item_s / groups < a.parts - 1) {  // publish this part's end state for the next
+    const int64_t item = __builtin_amdgcn_readfirstlane(item_s);  // (re-read: nothing kept live)
+    float* dst = split_states(a) + item * 256;
+#pragma unroll
+    for (int m = 0; m < NOWN; ++m) {
+      const int n = k + m * R;
+      if (n < 16) __hip_atomic_store(dst + n * 16 + i, carry[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // every wave's state stores have completed (agent-coherent) before the flag is stored
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(a.split_ws + kSplitHeader + item, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (a.last_state && cvalid) {
 #pragma unroll
     for (int m = 0; m < NOWN; ++m) {
       const int n = k + m * R;
@@ -226,14 +324,30 @@ void fwd_chunked_kernel(FwdArgs a) {
   }
 }
 
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t j = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; j < n;
+       j += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[j] = 0u;
+}
+
 template <typename T, bool GATE, int TC, bool ZOH, int R>
 void launch_chunked_c(const FwdArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.batch * ((a.dim + 15) / 16)));
+  const int64_t groups = a.batch * ((a.dim + 15) / 16);
   constexpr bool early = TC <= 4 && !GATE;
-  if (a.kconv > 0)
-    hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, ZOH, true, R>), grid, dim3(R * 16), 0, s, a);
-  else
-    hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, ZOH, false, R>), grid, dim3(R * 16), 0, s, a);
+  const dim3 block(R * 16);
+  if (a.parts > 1) {
+    const dim3 grid(static_cast<unsigned>(groups * a.parts));
+    if (a.kconv > 0)
+      hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, ZOH, true, R, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, ZOH, false, R, true>), grid, block, 0, s, a);
+  } else {
+    const dim3 grid(static_cast<unsigned>(groups));
+    if (a.kconv > 0)
+      hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, ZOH, true, R, false>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_chunked_kernel<T, GATE, TC, early, ZOH, false, R, false>), grid, block, 0, s, a);
+  }
 }
 
 template <typename T, bool GATE, int TC, int R>
@@ -283,6 +397,61 @@ ChunkPlan fwd_chunked_pick(const FwdArgs& a, int cus) {
     return static_cast<double>(groups) / static_cast<double>(rounds * slots);
   };
   return filled(4) > filled(3) + 0.05 ? ChunkPlan{4, 12} : ChunkPlan{4, 16};
+}
+
+// Resident workgroups per CU of a tile plan (VGPR and LDS budgets): 32 rows, 8 waves at two
+// per SIMD: 1; 12 rows: 4; 16 rows: 3 with 4-token chunks (2 with the zero-order hold), 2
+// with 8-token chunks.
+static int plan_slots_per_cu(const FwdArgs& a, ChunkPlan p) {
+  if (p.rows == 32) return 1;
+  if (p.rows == 12) return a.zoh ? 2 : 4;
+  return (p.chunk_len == 4 && !a.zoh) ? 3 : 2;
+}
+
+int64_t fwd_split_part_len(int64_t seqlen, ChunkPlan plan, int parts) {
+  const int64_t tile = static_cast<int64_t>(plan.rows) * plan.chunk_len;
+  const int64_t per = (seqlen + parts - 1) / parts;
+  return (per + tile - 1) / tile * tile;
+}
+
+// The split pays when the groups leave part of the last round of resident slots empty and
+// there are more groups than slots (a group's parts run one after another, so with fewer
+// groups than slots the split cannot shorten anything). Model: a sequence part takes 1/parts
+// of a whole-sequence time and the work items run in rounds of `slots`; the time is
+// max(1, ceil(groups * parts / slots) / parts). Take the fewest parts within 5% of the best.
+int fwd_split_parts(const FwdArgs& a, ChunkPlan plan, int cus) {
+  const int64_t groups = a.batch * ((a.dim + 15) / 16);
+  const int64_t slots = static_cast<int64_t>(plan_slots_per_cu(a, plan)) * cus;
+  if (groups <= slots || a.seqlen <= 0) return 1;
+  auto time = [&](int p) {
+    const double rounds = static_cast<double>((groups * p + slots - 1) / slots);
+    return std::max(1.0, rounds / p);
+  };
+  int best = 1;
+  double tbest = time(1);
+  for (int p = 2; p <= 8; ++p) {
+    const int64_t len = fwd_split_part_len(a.seqlen, plan, p);
+    if ((a.seqlen + len - 1) / len != p) continue;  // too short for p parts of whole tiles
+    const double t = time(p);
+    if (t < 0.95 * tbest) {
+      best = p;
+      tbest = t;
+    }
+  }
+  return best;
+}
+
+int64_t fwd_split_items(int64_t groups, int parts) { return groups * (parts - 1); }
+
+size_t fwd_split_ws_bytes(int64_t cap) {
+  return static_cast<size_t>(kSplitHeader + split_flag_words(cap) + cap * 256) * 4;
+}
+
+hipError_t fwd_split_ws_clear(uint32_t* ws, size_t bytes, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(bytes / 4);
+  const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 1024));
+  hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, s, ws, n);
+  return hipGetLastError();
 }
 
 hipError_t fwd_chunked(const FwdArgs& a, ChunkPlan plan, hipStream_t s) {

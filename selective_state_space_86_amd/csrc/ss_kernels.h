@@ -32,6 +32,15 @@ struct FwdArgs {
   const float* conv_b;      // (dim), may be null
   const float* conv_state;  // (batch, dim, kconv - 1) inputs before t = 0, may be null
   float* u_out;             // (batch, seqlen, dim) the prologue output, may be null
+  // sequence split of the chunked kernel (parts > 1): the sequence of every channel group is
+  // cut into parts of part_len tokens; workgroups take work items (part q, group g) from a
+  // counter in split_ws in that order, and part q > 0 starts from the state part q - 1
+  // publishes there (so the groups' work spreads evenly over the CUs)
+  int parts;                // 0 or 1: one workgroup per channel group over the whole sequence
+  int64_t part_len;         // tokens per part, a multiple of the tile; parts * part_len >= seqlen
+  uint32_t* split_ws;       // fwd_split_ws_bytes(split_cap) of device memory: the counter and
+                            // flags are zero before the call and zero again when it completes
+  int64_t split_cap;        // published-state slots of split_ws, >= (batch * groups) * (parts - 1)
 };
 
 // Validated arguments of one ss_step call.
@@ -117,6 +126,13 @@ struct ChunkPlan {
 };
 hipError_t fwd_chunked(const FwdArgs& a, ChunkPlan plan, hipStream_t s);
 ChunkPlan fwd_chunked_pick(const FwdArgs& a, int cus);
+// Parts per sequence for the split (1: no split) and the bytes of its workspace.
+int fwd_split_parts(const FwdArgs& a, ChunkPlan plan, int cus);
+int64_t fwd_split_part_len(int64_t seqlen, ChunkPlan plan, int parts);
+int64_t fwd_split_items(int64_t groups, int parts);  // published states of one call
+size_t fwd_split_ws_bytes(int64_t cap);
+// Zero a fresh split workspace on stream s (a fill kernel, no memset node).
+hipError_t fwd_split_ws_clear(uint32_t* ws, size_t bytes, hipStream_t s);
 hipError_t proj(const ProjArgs& a, int cus, hipStream_t s);
 int proj_step_tiles(int64_t rank, int dtype);
 hipError_t step(const StepArgs& a, hipStream_t s);

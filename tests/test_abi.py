@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss_abi_version() == _binding.ABI_VERSION == 7
+    assert lib.ss_abi_version() == _binding.ABI_VERSION == 8
     for s in range(0, 9):
         assert lib.ss_status_string(s)
     assert b"unknown" in lib.ss_status_string(99)
@@ -99,11 +99,11 @@ def test_binding_rejects_mixed_dtypes():
         _binding._in_dtype(torch.zeros(1), torch.zeros(1, dtype=torch.bfloat16))
 
 
-def fwd_ex_call(lib, kernel, chunk, disc=0, rows=0, **kw):
+def fwd_ex_call(lib, kernel, chunk, disc=0, rows=0, split=0, **kw):
     a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, sp=1, y=FAKE,
              st=None, h0=None, batch=1, L=4, dim=8, N=16, dtype=0)
     a.update(kw)
-    opt = _binding.FwdOptions(kernel, chunk, disc, rows)
+    opt = _binding.FwdOptions(kernel, chunk, disc, rows, split)
     return lib.ss_fwd_ex(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
                          a["y"], a["st"], a["h0"], a["batch"], a["L"], a["dim"], a["N"], a["dtype"],
                          ctypes.byref(opt), None)
@@ -135,6 +135,15 @@ def test_fwd_ex_chunk_rows_validation(lib, chunk, rows, kw, code):
     of 256 tokens of (.., dim) fp32 rows spans less than 2^31 bytes; errors are reported before
     any device work (no GPU is needed to reach them)."""
     assert fwd_ex_call(lib, 2, chunk, rows=rows, **kw) == code
+
+
+@pytest.mark.parametrize("split,kw,code", [
+    (-1, {}, 2), (17, {}, 2), (1 << 20, {}, 2), (4, dict(u=None), 1), (16, dict(dtype=4), 3),
+    (2, dict(y=FAKE + 2), 5), (0, dict(N=17), 4),
+])
+def test_fwd_ex_split_parts_validation(lib, split, kw, code):
+    """split_parts is 0 (automatic), 1 (never) or 2..16, checked before any device work."""
+    assert fwd_ex_call(lib, 2, 0, split=split, **kw) == code
 
 
 def step_ex_call(lib, disc, **kw):

@@ -1,0 +1,157 @@
+"""GPU parity of the sequence split of the time-chunked forward (ss_fwd_options.split_parts):
+every sequence is cut into parts of whole tiles, each part run by its own workgroup, and a
+part starts from the chunk state the previous part publishes (the associative combine of
+"架构变体：Mamba/SSM", section "硬件感知算法", one level above the tiles).
+
+Checks: y and the final state against the fp64 oracle element by element (|err| <= tol *
+(1 + |ref|), tol 1e-4 fp32 / 2e-3 bf16), and bit-equality with the unsplit kernel of the same
+tile plan (the parts start on tile boundaries, so the split changes no arithmetic); with an
+initial state, the exact zero-order hold and the conv prologue; repeated calls, a workspace
+that grows, and two streams (the workspace is kept per stream and left zeroed by every call).
+"""
+import pytest
+import torch
+
+import selective_state_space_86_amd as ss
+from selective_state_space_86_amd import inputs
+from tests import parity_util as pu
+from tests.test_conv_gpu import conv_params, gpu_conv, oracle_conv, check as check_conv
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+PLANS = [(4, 16), (8, 16), (4, 12), (8, 32), (4, 32)]  # (chunk_len, chunk_rows)
+
+
+def _announce(msg):
+    print(f"\n[split] {msg}", flush=True)
+
+
+def _workload(batch, L, dim, dt, seed_name):
+    return inputs.WORKLOADS["mamba130m"].replace(name=f"s{seed_name}{batch}x{L}x{dim}{dt}", batch=batch,
+                                                 seqlen=L, dim=dim, dstate=16, dtype=dt)
+
+
+def _close(x, got, ref):
+    tol = pu.tol_of(x)
+    for g, r, what in zip(got, ref, ("y", "state")):
+        err = pu.scaled_err(g.double().cpu().numpy(), r)
+        assert err <= tol, f"{what}: max scaled error {err:.3e} > {tol}"
+
+
+@pytest.mark.parametrize("chunk,rows", PLANS)
+@pytest.mark.parametrize("batch,L,dim,dt,parts", [(2, 700, 40, "f32", 2), (1, 1000, 130, "bf16", 3),
+                                                  (3, 257, 17, "f32", 5), (1, 4099, 64, "bf16", 16),
+                                                  (1, 1, 16, "f32", 4), (2, 1500, 128, "f32", 4),
+                                                  (1, 3000, 500, "bf16", 6)])
+def test_split_matches_oracle_and_unsplit(chunk, rows, batch, L, dim, dt, parts):
+    w = _workload(batch, L, dim, dt, "o")
+    x = inputs.make(w, seed=21, device=DEV)
+    _announce(f"chunk={chunk} rows={rows} parts={parts} {w.name}")
+    for gated in (False, True):
+        got = pu.gpu_fwd(x, gated, kernel=2, chunk_len=chunk, chunk_rows=rows, split_parts=parts)
+        one = pu.gpu_fwd(x, gated, kernel=2, chunk_len=chunk, chunk_rows=rows, split_parts=1)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], one[0]) and torch.equal(got[1], one[1])
+        _close(x, got, pu.oracle_full(x, gated))
+
+
+@pytest.mark.parametrize("chunk,rows", [(4, 16), (8, 32), (4, 12)])
+def test_split_with_initial_state(chunk, rows):
+    w = _workload(2, 1500, 50, "f32", "h")
+    x = inputs.make(w, seed=22, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9)
+    h0 = torch.randn((2, 50, 16), generator=g, device=DEV)
+    _announce(f"h0 chunk={chunk} rows={rows}")
+    got = pu.gpu_fwd(x, True, kernel=2, chunk_len=chunk, chunk_rows=rows, split_parts=4, h0=h0)
+    one = pu.gpu_fwd(x, True, kernel=2, chunk_len=chunk, chunk_rows=rows, split_parts=1, h0=h0)
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], one[0]) and torch.equal(got[1], one[1])
+    _close(x, got, pu.oracle_full(x, True, h0=h0))
+
+
+def test_split_zero_order_hold():
+    w = _workload(1, 1200, 70, "bf16", "z")
+    x = inputs.make(w, seed=23, device=DEV)
+    _announce("zoh split 3")
+    got = pu.gpu_fwd(x, True, kernel=2, split_parts=3, zoh=True)
+    one = pu.gpu_fwd(x, True, kernel=2, split_parts=1, zoh=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], one[0]) and torch.equal(got[1], one[1])
+    _close(x, got, pu.oracle_full(x, True, zoh=True))
+
+
+@pytest.mark.parametrize("chunk,rows,K", [(4, 16, 4), (8, 32, 3), (4, 12, 4)])
+def test_split_conv_prologue(chunk, rows, K):
+    """A part's first tokens take their conv window from the end of the previous part's
+    inputs (and the conv state only before t = 0)."""
+    w = _workload(2, 900, 40, "f32", "c")
+    x = inputs.make(w, seed=24, device=DEV)
+    cw, cb, cs = conv_params(2, 40, K, seed=3)
+    _announce(f"conv K={K} chunk={chunk} rows={rows}")
+    got = gpu_conv(x, cw, cb, cs, kernel=2, chunk_len=chunk, chunk_rows=rows, split_parts=3)
+    one = gpu_conv(x, cw, cb, cs, kernel=2, chunk_len=chunk, chunk_rows=rows, split_parts=1)
+    torch.cuda.synchronize()
+    for a, b in zip(got, one):
+        assert torch.equal(a, b)
+    check_conv(x, got, oracle_conv(x, cw, cb, cs), f"conv K={K} split")
+
+
+def test_split_repeated_calls_growing_workspace_and_streams():
+    """The workspace must be zero again after every call: the same call three times in a row
+    (with a larger split in between, which grows the stream's workspace) gives the same bits,
+    and two streams running split calls at once each match the default stream."""
+    xa = inputs.make(_workload(2, 800, 48, "f32", "a"), seed=25, device=DEV)
+    xb = inputs.make(_workload(3, 2000, 200, "bf16", "b"), seed=26, device=DEV)
+    kw = dict(kernel=2, chunk_len=4, chunk_rows=16)
+    _announce("repeated calls / streams")
+    ref_a = pu.gpu_fwd(xa, True, split_parts=1, **kw)
+    ref_b = pu.gpu_fwd(xb, True, split_parts=1, **kw)
+    for parts in (3, 8, 3):
+        got_a = pu.gpu_fwd(xa, True, split_parts=parts, **kw)
+        got_b = pu.gpu_fwd(xb, True, split_parts=parts + 1, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(got_a[0], ref_a[0]) and torch.equal(got_a[1], ref_a[1])
+        assert torch.equal(got_b[0], ref_b[0]) and torch.equal(got_b[1], ref_b[1])
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            ya = pu.gpu_fwd(xa, True, split_parts=5, **kw)
+        with torch.cuda.stream(s2):
+            yb = pu.gpu_fwd(xb, True, split_parts=6, **kw)
+        outs.append((ya, yb))
+    torch.cuda.synchronize()
+    for ya, yb in outs:
+        assert torch.equal(ya[0], ref_a[0]) and torch.equal(ya[1], ref_a[1])
+        assert torch.equal(yb[0], ref_b[0]) and torch.equal(yb[1], ref_b[1])
+
+
+@pytest.mark.parametrize("dim", [200, 256])
+def test_split_part_counts_in_sequence_share_the_workspace(dim):
+    """Calls with different part counts on one stream share its workspace: the flags of one
+    call must never sit where another call left its published states (a layout that moved
+    with the part count once gave a call with 3 parts after one with 2 stale 'published'
+    flags). Every call equals the unsplit kernel bit for bit."""
+    x = inputs.make(_workload(3, 2000, dim, "bf16", "q"), seed=26, device=DEV)
+    kw = dict(kernel=2, chunk_len=4, chunk_rows=16)
+    _announce(f"part counts in sequence dim={dim}")
+    ref = pu.gpu_fwd(x, True, split_parts=1, **kw)
+    for parts in (16, 2, 3, 5, 8, 2, 4, 3, 7, 16, 6):
+        got = pu.gpu_fwd(x, True, split_parts=parts, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), f"parts={parts}"
+
+
+def test_automatic_split_at_3b_shape_equals_unsplit_sampled():
+    """At the 3B long-context shape (320 channel groups) the automatic plan splits; its
+    result equals the unsplit kernel's bit for bit. Checked on a shortened sequence
+    (L = 8192, whole tiles and a ragged tail) over every element."""
+    w = inputs.WORKLOADS["mamba3b-long"].replace(name="mamba3b-L8200", seqlen=8200)
+    x = inputs.make(w, seed=27, device=DEV)
+    _announce("3B shape automatic split vs none")
+    auto = pu.gpu_fwd(x, True)
+    one = pu.gpu_fwd(x, True, split_parts=1)
+    torch.cuda.synchronize()
+    assert torch.equal(auto[0], one[0]) and torch.equal(auto[1], one[1])
