@@ -92,6 +92,9 @@ const char* ss_status_string(int status);
  *   seqlen == 0 is allowed: no token is read, y is not written, last_state is set to
  *   zero; u, delta, z, B, C and y may then be NULL (A is still required).
  * Limits: dstate <= 16; batch * seqlen * dim < 2^62.
+ * Where the automatic plan splits the sequences (ss_fwd_options.split_parts: more channel
+ * groups of 16 than resident workgroup slots, e.g. 320 groups on 256 CUs), the first such
+ * call on a stream allocates a small device workspace that the library keeps (see there).
  */
 int ss_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
            const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
@@ -121,14 +124,18 @@ typedef struct {
                          tiles). 0: automatic (split when the channel groups leave part of the
                          last round of resident workgroups empty and outnumber the resident
                          slots, e.g. 320 groups on 256 CUs); 1: never; 2..16: that many
-                         (else SS_ERR_BAD_SHAPE). Results equal the unsplit kernel's up to
-                         fp32 rounding order. A split call uses a device workspace the library
-                         keeps per (device, stream): allocated (hipMalloc, then cleared by a
-                         kernel on the stream) on the first split call on that pair and when a
-                         larger one is needed, kept until the process ends, left zeroed by
-                         every call; calls on one stream are ordered, so they never share it
-                         concurrently. Its size: 1028 B per channel group and part after the
-                         first (at least doubled when it grows), plus 1.25 KiB. */
+                         (else SS_ERR_BAD_SHAPE). The parts start on tile boundaries, so the
+                         results are bit-identical to the unsplit kernel's.
+                         A split call uses a device workspace the library keeps per (device,
+                         stream): allocated (hipMalloc, then cleared by a kernel on the stream)
+                         on the first split call on that pair and when a larger one is needed,
+                         kept until the process ends, and left with zeroed counters and flags
+                         by every call; calls on one stream run in order, so they never share
+                         it concurrently. Its size: 1028 B per channel group and part after the
+                         first (at least doubled when it grows), plus 1.25 KiB. Under graph
+                         capture, make one split call of at least the same size on the
+                         capturing stream before the capture, so nothing is allocated while
+                         capturing. */
 } ss_fwd_options;
 
 /*

@@ -155,3 +155,36 @@ def test_automatic_split_at_3b_shape_equals_unsplit_sampled():
     one = pu.gpu_fwd(x, True, split_parts=1)
     torch.cuda.synchronize()
     assert torch.equal(auto[0], one[0]) and torch.equal(auto[1], one[1])
+
+
+def test_split_in_a_captured_graph():
+    """A split call captured in a HIP graph and replayed: the counters and flags are zero
+    again after every run, so every replay (with eager split calls on another stream in
+    between) gives the eager result. The capture stream's workspace is allocated by a call
+    on that stream before the capture (the first split call on a stream allocates)."""
+    x = inputs.make(_workload(1, 3000, 256, "bf16", "g"), seed=28, device=DEV)
+    kw = dict(kernel=2, chunk_len=4, chunk_rows=16)
+    _announce("graph capture")
+    ref = pu.gpu_fwd(x, True, split_parts=1, **kw)
+    y = torch.empty_like(ref[0])
+    st = torch.empty_like(ref[1])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pu.gpu_fwd(x, True, split_parts=4, y=y, last_state=st, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        pu.gpu_fwd(x, True, split_parts=4, y=y, last_state=st, **kw)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        y.fill_(7.0)
+        st.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref[0]) and torch.equal(st, ref[1])
+        other = pu.gpu_fwd(x, True, split_parts=3, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(other[0], ref[0])
