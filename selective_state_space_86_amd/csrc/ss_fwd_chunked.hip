@@ -38,6 +38,7 @@
 #include <algorithm>
 
 #include "ss_chunk_ops.h"
+#include "ss_split.h"
 
 namespace ss {
 namespace {
@@ -46,44 +47,11 @@ using namespace chunk;
 
 constexpr int kLdsChunkStride = 16 * 16 + 16;  // [chunk][n][lane], padded against bank conflicts
 
-// Sequence split. When the channel groups do not fill the resident workgroup slots in whole
-// rounds (the 3B long-context shape: 320 groups for 256 one-workgroup CUs, so a second round
-// of 64 would run on a quarter of the chip), every group's sequence is cut into `parts`
-// parts of whole tiles, and each workgroup takes one work item (part q, group g) from a
-// counter in the order q-major. The chunk state that part q - 1 ends with is the carry part
-// q starts from (the same associative combine as between tiles, one level up), so part q
-// waits until part q - 1 has published it. A work item's predecessor always holds a smaller
-// counter value, so it was taken by a workgroup that is already running and whose own wait
-// is on an even earlier item: every wait ends. The wait is bounded all the same, and a wait
-// that hits the bound is counted in the workspace (it would leave a wrong carry).
-// The hand-off uses agent-scope atomic loads and stores for the flags and the states, which
-// are coherent across the XCDs' separate L2 caches by themselves: the producer waits until its
-// state stores have completed before the flag is stored, and the consumer loads the states
-// only after it has seen the flag. Agent-scope acquire/release fences would do the same with
-// a write-back and an invalidation of the whole L2 of the XCD at every hand-off, which cost
-// more than the split saved at short parts.
-// Work-item queues: workgroup ids are dealt to the 8 XCDs round-robin, and neighbouring groups
-// share 128-byte lines of u, delta, z and y in an XCD's L2, so when the groups divide by 8 the
-// workgroups with id = x (mod 8) take items from queue x, which holds the parts of the x-th
-// eighth of the groups (a contiguous slice, as the unsplit kernel gives XCD x), again in the
-// order (part, group). Each queue gets exactly as many workgroups as it has items, and an
-// item's predecessor is in the same queue with a smaller counter value, so the argument above
-// holds per queue; a workgroup's queue is a function of its id alone, so the result never
-// depends on where it runs.
-// Workspace (32-bit words) of `cap` slots: the counter of queue x at word 32 x (x < 8), the
-// count of waits that hit the bound at word 255, then from word kSplitHeader one flag per
-// slot (padded to 64 words), then the
-// published states, 16 x 16 fp32 per slot ([state n][channel i]). Item (part q, group gi)
-// publishes in slot q * groups + gi. The layout depends on the capacity only, never on the
-// call, so a flag word is never a state word of another call. The last workgroup to take an
-// item resets the counter and every consumer resets the flag it waited on, so counter and
-// flags are zero again when the kernel ends (the states are left as they are).
-constexpr int64_t kSplitHeader = 256;
-constexpr uint32_t kSplitSpinLimit = 1u << 22;  // several seconds of polling
-__host__ __device__ inline int64_t split_flag_words(int64_t items) { return (items + 63) / 64 * 64; }
-__device__ inline float* split_states(const FwdArgs& a) {
-  return reinterpret_cast<float*>(a.split_ws + kSplitHeader + split_flag_words(a.split_cap));
-}
+// Sequence split (SPLIT): the work queue and state hand-off of ss_split.h. When the channel
+// groups do not fill the resident workgroup slots in whole rounds (the 3B long-context shape:
+// 320 groups for 256 one-workgroup CUs, so a second round of 64 would run on a quarter of
+// the chip), every group's sequence is cut into parts of whole tiles, one workgroup each;
+// part q starts from the carry part q - 1 publishes.
 
 // R rows (time chunks) per workgroup: 16 (4 waves), 12 (3 waves; four such workgroups fit
 // a CU where three of 16 do, for shapes with between 3 and 4 channel groups per CU) or 32
@@ -110,16 +78,7 @@ void fwd_chunked_kernel(FwdArgs a) {
   int64_t gi = blockIdx.x, part = 0;  // work item: group index gi, sequence part
   __shared__ uint32_t item_s;
   if (SPLIT) {
-    if (tid == 0) {
-      const bool by_xcd = groups % 8 == 0;
-      const uint32_t qx = by_xcd ? blockIdx.x % 8 : 0;
-      const uint32_t slice = static_cast<uint32_t>(by_xcd ? groups / 8 : groups);  // groups per queue
-      uint32_t* counter = a.split_ws + 32 * qx;
-      const uint32_t t = atomicAdd(counter, 1u);
-      if (t == slice * static_cast<uint32_t>(a.parts) - 1)  // every item of the queue is taken
-        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      item_s = (t / slice) * static_cast<uint32_t>(groups) + qx * slice + t % slice;  // part * groups + gi
-    }
+    if (tid == 0) item_s = split::take(a.split_ws, groups, a.parts);  // part * groups + gi
     __syncthreads();
     const uint32_t item = __builtin_amdgcn_readfirstlane(item_s);  // (uniform: keep it in SGPRs)
     part = item / groups;
@@ -155,25 +114,15 @@ void fwd_chunked_kernel(FwdArgs a) {
     carry[m] = (a.h0 && part == 0 && n < 16) ? a.h0[(b * a.dim + cc) * 16 + n] : 0.0f;
   }
   if (SPLIT && part > 0) {  // start from the state the previous part of this group ends with
-    const int64_t item = (part - 1) * groups + gi;
-    uint32_t* flag = a.split_ws + kSplitHeader + item;
-    uint32_t spins = 0;
-    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-      if (++spins == kSplitSpinLimit) {
-        if ((tid & 63) == 0) atomicAdd(a.split_ws + 255, 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(8);
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // (the state loads stay after the flag)
-    const float* src = split_states(a) + item * 256;
+    const int64_t slot = (part - 1) * groups + gi;
+    split::wait(a.split_ws, slot);
 #pragma unroll
     for (int m = 0; m < NOWN; ++m) {
       const int n = k + m * R;
-      if (n < 16) carry[m] = __hip_atomic_load(src + n * 16 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (n < 16) carry[m] = split::load_state(a.split_ws, a.split_cap, slot, n, i);
     }
     __syncthreads();  // every wave has seen the flag: clear it for the next call
-    if (tid == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) split::clear(a.split_ws, slot);
   }
   const uint32_t y_row = static_cast<uint32_t>(a.dim * 4);
   const uint32_t y_off = static_cast<uint32_t>(k * TC) * y_row + static_cast<uint32_t>(i * 4);
@@ -302,19 +251,15 @@ void fwd_chunked_kernel(FwdArgs a) {
     cur = nxt;
   }
   if (SPLIT && item_s / groups < a.parts - 1) {  // publish this part's end state for the next
-    const int64_t item = __builtin_amdgcn_readfirstlane(item_s);  // (re-read: nothing kept live)
-    float* dst = split_states(a) + item * 256;
+    const int64_t slot = __builtin_amdgcn_readfirstlane(item_s);  // (re-read: nothing kept live)
 #pragma unroll
     for (int m = 0; m < NOWN; ++m) {
       const int n = k + m * R;
-      if (n < 16) __hip_atomic_store(dst + n * 16 + i, carry[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (n < 16) split::store_state(a.split_ws, a.split_cap, slot, n, i, carry[m]);
     }
-    // every wave's state stores have completed (agent-coherent) before the flag is stored
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    split::finish_stores();
     __syncthreads();
-    if (tid == 0) __hip_atomic_store(a.split_ws + kSplitHeader + item, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) split::publish(a.split_ws, slot);
   } else if (a.last_state && cvalid) {
 #pragma unroll
     for (int m = 0; m < NOWN; ++m) {
@@ -443,9 +388,7 @@ int fwd_split_parts(const FwdArgs& a, ChunkPlan plan, int cus) {
 
 int64_t fwd_split_items(int64_t groups, int parts) { return groups * (parts - 1); }
 
-size_t fwd_split_ws_bytes(int64_t cap) {
-  return static_cast<size_t>(kSplitHeader + split_flag_words(cap) + cap * 256) * 4;
-}
+size_t fwd_split_ws_bytes(int64_t cap) { return split::ws_bytes(cap); }
 
 hipError_t fwd_split_ws_clear(uint32_t* ws, size_t bytes, hipStream_t s) {
   const int64_t n = static_cast<int64_t>(bytes / 4);
