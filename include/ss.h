@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 8
+#define SS_ABI_VERSION 9
 #define SS_MAX_DSTATE 16
 
 typedef enum {
@@ -206,7 +206,8 @@ int ss_step_ex(float* state, const void* u, const void* delta, const float* A, c
 /*
  * ss_bwd_workspace_size -- bytes of device workspace ss_bwd needs for these sizes
  * (about 4/(16*2) * 16 bytes per (b, t, d) of tile-start states plus 8 bytes per
- * (b, t, n) per group of 16 channels of partial sums; see ss_bwd).
+ * (b, t, n) per group of 16 channels of partial sums, plus 8 * 72 bytes per (b, d) for
+ * the partial sums of up to 8 sequence parts; see ss_bwd).
  */
 size_t ss_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
@@ -236,6 +237,11 @@ size_t ss_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t
  * seqlen == 0 is allowed (the per-token arrays may then be NULL): dh0 = dlast_state and
  * dA, dD, ddelta_bias are zero. Sums over channels, tokens and batch rows have a fixed
  * order, so the result is deterministic. Errors as ss_fwd, plus SS_ERR_WORKSPACE.
+ * With fewer channel groups of 16 than twice the CUs the kernels run 8-wave workgroups, and
+ * with more groups than CUs they also split every sequence into parts (as
+ * ss_fwd_options.split_parts describes; the reverse pass hands the adjoint from each part to
+ * the one before it), using the library-kept workspace of the stream that ss_fwd's split
+ * uses (allocated at the first split call on that stream; see there).
  */
 int ss_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
            const float* D, const void* z, const float* delta_bias, int softplus_flag,

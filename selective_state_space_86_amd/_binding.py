@@ -12,7 +12,7 @@ _lib = None
 
 F32, BF16 = 0, 1
 DISC_DT, DISC_ZOH = 0, 1
-ABI_VERSION = 8
+ABI_VERSION = 9
 EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_fwd_conv", "ss_step",
            "ss_step_ex", "ss_bwd_workspace_size", "ss_bwd", "ss_proj", "ss_proj_conv")
 

@@ -370,8 +370,16 @@ int ss_bwd(const void* u, const void* delta, const float* A, const void* B, cons
   ss::BwdArgs a{u, delta, A, B, C, D, z, delta_bias, h0, dy, dlast_state,
                 du, ddelta, z ? dz : nullptr, dh0, dA, dB, dC, dD, ddelta_bias,
                 ckpt, part_bc, part_ch, batch, seqlen, dim, dstate, ngroups, ntiles,
-                in_dtype, softplus_flag ? 1 : 0};
-  const hipError_t e = ss::bwd(a, static_cast<hipStream_t>(stream));
+                in_dtype, softplus_flag ? 1 : 0, ss::bwd_rows(batch * ngroups, seqlen, cus)};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int parts = ss::bwd_split_parts(batch * ngroups, a.rows, seqlen, cus);
+  if (parts > 1 && batch * ngroups * parts <= 0x7fffffffLL) {
+    a.part_len = ss::bwd_split_part_len(seqlen, a.rows, parts);
+    a.split_ws = split_workspace(batch * ngroups * (parts - 1), s, &a.split_cap);
+    if (!a.split_ws) return SS_ERR_HIP;
+    a.parts = parts;
+  }
+  const hipError_t e = ss::bwd(a, s);
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 

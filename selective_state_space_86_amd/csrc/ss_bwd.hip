@@ -35,6 +35,7 @@
 #include <utility>
 
 #include "ss_chunk_ops.h"
+#include "ss_split.h"
 
 namespace ss {
 namespace {
@@ -377,9 +378,8 @@ struct Lane {
   bool cvalid;
 };
 
-__device__ __forceinline__ Lane lane_of(const BwdArgs& a) {
+__device__ __forceinline__ Lane lane_at(const BwdArgs& a, int64_t g) {
   Lane l;
-  const int64_t g = blockIdx.x;
   l.b = g / a.ngroups;
   l.c0 = (g % a.ngroups) * 16;
   l.i = threadIdx.x & 15;
@@ -390,26 +390,62 @@ __device__ __forceinline__ Lane lane_of(const BwdArgs& a) {
   return l;
 }
 
+// The workgroup's group index gi and sequence part: with SPLIT a work item from the queue
+// (ss_split.h), the chain running from the last part to the first when `reverse`.
+template <bool SPLIT>
+__device__ __forceinline__ void work_item(const BwdArgs& a, bool reverse, uint32_t& item_s, int64_t& gi,
+                                          int64_t& part) {
+  gi = blockIdx.x;
+  part = 0;
+  if (SPLIT) {
+    const int64_t groups = a.batch * a.ngroups;
+    if (threadIdx.x == 0) item_s = split::take(a.split_ws, groups, a.parts);
+    __syncthreads();
+    const uint32_t item = __builtin_amdgcn_readfirstlane(item_s);  // rank * groups + gi
+    const int64_t rank = item / groups;
+    gi = item % groups;
+    part = reverse ? a.parts - 1 - rank : rank;
+  }
+}
+
 // Forward scan from h0 (or zero), storing the state at the start of every tile of the
 // reverse kernel (bwd_tile_tokens() = 32 tokens): ckpt[((b * ntiles + tile) * dimp + c) * 16
 // + n]. It runs its own, longer chunks (CTC tokens, tiles of 16 * CTC tokens) with the
 // hand-scheduled local step; the folding lane writes a checkpoint whenever the state it
 // carries reaches a multiple of 32 tokens. The inputs of the next tile are requested before
 // the current one is computed.
-template <typename T, int CTC>
-__global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
+// R rows (time chunks): 16 (4 waves) or 32 (8 waves, for shapes with fewer channel groups
+// than twice the CUs, where 4-wave workgroups would leave SIMDs with one wave); with 32 the
+// rows 16..31 own no state in the fold.
+// With SPLIT, a workgroup scans one part of its group's sequence, from the state the previous
+// part publishes, and publishes its own end state.
+template <typename T, int CTC, int R, bool SPLIT>
+__global__ __launch_bounds__(R * 16) void bwd_ckpt_kernel(BwdArgs a) {
   static_assert(CTC * 4 == 32 || CTC * 8 == 32 || CTC * 16 == 32, "checkpoints every 32 tokens");
+  static_assert(R == 16 || R == 32, "16 or 32 chunks per tile");
   constexpr int kPer = 32 / CTC;  // chunks per checkpoint interval
-  __shared__ float lds_p[16 * kS];
-  __shared__ float lds_h[16 * kS];
-  const Lane l = lane_of(a);
-  const int64_t L = a.seqlen, N = a.dstate, dimp = a.ngroups * 16;
-  constexpr int TT = 16 * CTC;
+  __shared__ float lds_p[R * kS];
+  __shared__ float lds_h[R * kS];
+  __shared__ uint32_t item_s;
+  int64_t gi, part;
+  work_item<SPLIT>(a, false, item_s, gi, part);
+  const Lane l = lane_at(a, gi);
+  const int64_t L = a.seqlen, N = a.dstate, dimp = a.ngroups * 16, groups = a.batch * a.ngroups;
+  constexpr int TT = R * CTC;
+  const int64_t t_begin = SPLIT ? part * a.part_len : 0;
+  const int64_t t_end = SPLIT ? min(L, t_begin + a.part_len) : L;
   float A2[16];
 #pragma unroll
   for (int n = 0; n < 16; ++n) A2[n] = n < N ? a.A[l.cc * N + n] * kLog2e : 0.0f;
   const float bias = a.delta_bias ? a.delta_bias[l.cc] : 0.0f;
-  float carry = (a.h0 && l.k < N) ? a.h0[(l.b * a.dim + l.cc) * N + l.k] : 0.0f;
+  float carry = (a.h0 && part == 0 && l.k < N) ? a.h0[(l.b * a.dim + l.cc) * N + l.k] : 0.0f;
+  if (SPLIT && part > 0) {  // start from the state the previous part ends with
+    const int64_t slot = (part - 1) * groups + gi;
+    split::wait(a.split_ws, slot);
+    if (l.k < 16) carry = split::load_state(a.split_ws, a.split_cap, slot, l.k, l.i);
+    __syncthreads();  // every wave has seen the flag: clear it for the next kernel
+    if (threadIdx.x == 0) split::clear(a.split_ws, slot);
+  }
 
   // lane (k, i): tokens t0 + k*CTC + j of channel cc and B_t[i]; fixed 32-bit byte offsets
   const uint32_t tok_row = static_cast<uint32_t>(a.dim * sizeof(T));
@@ -438,10 +474,10 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
     }
   };
   In cur, nxt;
-  if (a.ntiles > 0) fetch(cur, 0);
-  for (int64_t t0 = 0; t0 < L; t0 += TT) {
-    progress_priority(t0, L);
-    if (t0 + TT < L) fetch(nxt, t0 + TT);
+  if (a.ntiles > 0) fetch(cur, t_begin);
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += TT) {
+    if (!SPLIT) progress_priority(t0, L);
+    if (t0 + TT < t_end) fetch(nxt, t0 + TT);
     float h[16], e[16], dsum = 0.0f;
 #pragma unroll
     for (int n = 0; n < 16; ++n) h[n] = 0.0f;
@@ -459,33 +495,57 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
       lds_h[l.k * kS + n * 16 + l.i] = h[n];
     }
     __syncthreads();
-    // lane (k, i) owns state n = k of channel i: fold the 16 chunks in order, writing the
-    // state at every multiple of 32 tokens that starts a reverse-kernel tile
+    // lane (k, i), k < 16, owns state n = k of channel i: fold the R chunks in order, writing
+    // the state at every multiple of 32 tokens (the checkpoint interval)
+    if (R == 16 || l.k < 16) {
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      if (jj % kPer == 0) {
-        const int64_t tile = (t0 + jj * CTC) / 32;
-        if (tile < a.ntiles) a.ckpt[((l.b * a.ntiles + tile) * dimp + l.c) * 16 + l.k] = carry;
+      for (int jj = 0; jj < R; ++jj) {
+        if (jj % kPer == 0) {
+          const int64_t tile = (t0 + jj * CTC) / 32;
+          if (tile < a.ntiles) a.ckpt[((l.b * a.ntiles + tile) * dimp + l.c) * 16 + l.k] = carry;
+        }
+        const int o = jj * kS + l.k * 16 + l.i;
+        carry = __builtin_fmaf(lds_p[o], carry, carry + lds_h[o]);
       }
-      const int o = jj * kS + l.k * 16 + l.i;
-      carry = __builtin_fmaf(lds_p[o], carry, carry + lds_h[o]);
     }
     __syncthreads();
     cur = nxt;
   }
+  if (SPLIT && part < a.parts - 1) {  // publish the end state for the next part
+    const int64_t slot = part * groups + gi;
+    if (l.k < 16) split::store_state(a.split_ws, a.split_cap, slot, l.k, l.i, carry);
+    split::finish_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) split::publish(a.split_ws, slot);
+  }
 }
 
-template <typename T, bool GATE, int TC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// R rows (time chunks) as the checkpoint kernel: 16 (4 waves, two workgroups per CU) or 32
+// (8 waves, one workgroup per CU); a tile is R * TC tokens (32 or 64), a multiple of the
+// checkpoint interval. With SPLIT, a workgroup runs one part of its group's sequence, the
+// chain going from the last part to the first: it starts from the adjoint the later part
+// publishes, publishes the adjoint entering its own first tile, and leaves its dA/dD/dbias
+// sums in its part's block of part_ch.
+template <typename T, bool GATE, int TC, int R, bool SPLIT>
+__global__ __launch_bounds__(R * 16) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_chunked_kernel(BwdArgs a) {
+  static_assert(R == 16 || R == 32, "16 or 32 chunks per tile");
   // [0]: chunk decays - 1, [1]: chunk end states then forward carries; after the carries
-  // are read, the same 8704 floats hold the per-wave dB/dC reduction blocks
-  // [wave][dB or dC][row][n][lane] (4 x 2 x 4 x kS floats)
-  __shared__ __attribute__((aligned(16))) float lds_eh[2][16 * kS];
-  __shared__ float lds_m[16 * kS];  // chunk adjoint aggregates, then reverse carries
-  const Lane l = lane_of(a);
-  const int64_t L = a.seqlen, N = a.dstate, dimp = a.ngroups * 16;
-  constexpr int TT = 16 * TC;
+  // are read, the same 2 R kS floats hold the per-wave dB/dC reduction blocks
+  // [wave][dB or dC][row][n][lane] (R/4 x 2 x 4 x kS floats)
+  __shared__ __attribute__((aligned(16))) float lds_eh[2][R * kS];
+  __shared__ float lds_m[R * kS];  // chunk adjoint aggregates, then reverse carries
+  __shared__ uint32_t item_s;
+  int64_t gi, part;
+  work_item<SPLIT>(a, true, item_s, gi, part);
+  const Lane l = lane_at(a, gi);
+  const int64_t L = a.seqlen, N = a.dstate, dimp = a.ngroups * 16, groups = a.batch * a.ngroups;
+  constexpr int TT = R * TC;
+  constexpr int CK = TT / 32;  // checkpoint intervals per tile
+  static_assert(CK * 32 == TT, "a tile is a whole number of checkpoint intervals");
+  const int64_t nt = (L + TT - 1) / TT;  // this kernel's tiles
+  const int64_t tile_lo = SPLIT ? part * (a.part_len / TT) : 0;                      // first tile
+  const int64_t tile_hi = SPLIT ? min(nt, tile_lo + a.part_len / TT) : nt;  // past the last
   const int w = threadIdx.x >> 6, rw = l.k & 3;
 
   float A2[16];
@@ -494,7 +554,15 @@ void bwd_chunked_kernel(BwdArgs a) {
   const float bias = a.delta_bias ? a.delta_bias[l.cc] : 0.0f;
   const float Dd = a.D ? a.D[l.cc] : 0.0f;
   // adjoint carried from later tiles: lane (k, i) owns state n = k of channel i
-  float rcarry = (a.dlast && l.cvalid && l.k < N) ? a.dlast[(l.b * a.dim + l.c) * N + l.k] : 0.0f;
+  float rcarry = (a.dlast && (!SPLIT || part == a.parts - 1) && l.cvalid && l.k < N)
+                     ? a.dlast[(l.b * a.dim + l.c) * N + l.k] : 0.0f;
+  if (SPLIT && part < a.parts - 1) {  // start from the adjoint the later part publishes
+    const int64_t slot = part * groups + gi;
+    split::wait(a.split_ws, slot);
+    if (l.k < 16) rcarry = split::load_state(a.split_ws, a.split_cap, slot, l.k, l.i);
+    __syncthreads();  // every wave has seen the flag: clear it for the next kernel
+    if (threadIdx.x == 0) split::clear(a.split_ws, slot);
+  }
   float dAacc[16];
 #pragma unroll
   for (int n = 0; n < 16; ++n) dAacc[n] = 0.0f;
@@ -528,14 +596,17 @@ void bwd_chunked_kernel(BwdArgs a) {
   Raw cur, nxt;
   // the checkpointed state entering each tile (lane (k, i): state n = k of channel i), also
   // requested a tile ahead: read where it is used, its latency would stall every tile
-  auto ckpt_of = [&](int64_t tile) { return a.ckpt[((l.b * a.ntiles + tile) * dimp + l.c) * 16 + l.k]; };
+  // (rows 16..31 of a 32-row tile own no state: they read state k - 16, unused)
+  auto ckpt_of = [&](int64_t tile) {
+    return a.ckpt[((l.b * a.ntiles + tile * CK) * dimp + l.c) * 16 + (l.k & 15)];
+  };
   float ck_cur = 0.0f, ck_nxt = 0.0f;
-  if (a.ntiles > 0) {
-    fetch(cur, (a.ntiles - 1) * TT);
-    ck_cur = ckpt_of(a.ntiles - 1);
+  if (tile_hi > tile_lo) {
+    fetch(cur, (tile_hi - 1) * TT);
+    ck_cur = ckpt_of(tile_hi - 1);
   }
-  for (int64_t tile = a.ntiles - 1; tile >= 0; --tile) {
-    progress_priority(a.ntiles - 1 - tile, a.ntiles);
+  for (int64_t tile = tile_hi - 1; tile >= tile_lo; --tile) {
+    if (!SPLIT) progress_priority(nt - 1 - tile, nt);
     const int64_t t0 = tile * TT;
     // (the tile before the first one re-reads tile 0: unused, but no branch around the loads)
     fetch(nxt, tile > 0 ? t0 - TT : 0);
@@ -595,20 +666,22 @@ void bwd_chunked_kernel(BwdArgs a) {
     {  // lane (k, i) owns state n = k of channel i: the forward fold from the checkpoint,
        // then the reverse fold from the adjoint of the later tile; each lane overwrites
        // exactly the words it read
-      float carry = ck_cur;
+      if (R == 16 || l.k < 16) {
+        float carry = ck_cur;
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int o = jj * kS + l.k * 16 + l.i;
-        const float pm = lds_eh[0][o], hv = lds_eh[1][o];
-        lds_eh[1][o] = carry;  // state entering chunk jj
-        carry = __builtin_fmaf(pm, carry, carry + hv);
-      }
+        for (int jj = 0; jj < R; ++jj) {
+          const int o = jj * kS + l.k * 16 + l.i;
+          const float pm = lds_eh[0][o], hv = lds_eh[1][o];
+          lds_eh[1][o] = carry;  // state entering chunk jj
+          carry = __builtin_fmaf(pm, carry, carry + hv);
+        }
 #pragma unroll
-      for (int jj = 15; jj >= 0; --jj) {
-        const int o = jj * kS + l.k * 16 + l.i;
-        const float pm = lds_eh[0][o], mv = lds_m[o];
-        lds_m[o] = rcarry;  // adjoint entering chunk jj from its end
-        rcarry = __builtin_fmaf(pm, rcarry, rcarry + mv);
+        for (int jj = R - 1; jj >= 0; --jj) {
+          const int o = jj * kS + l.k * 16 + l.i;
+          const float pm = lds_eh[0][o], mv = lds_m[o];
+          lds_m[o] = rcarry;  // adjoint entering chunk jj from its end
+          rcarry = __builtin_fmaf(pm, rcarry, rcarry + mv);
+        }
       }
     }
     __syncthreads();
@@ -692,25 +765,33 @@ void bwd_chunked_kernel(BwdArgs a) {
     cur = nxt;
     ck_cur = ck_nxt;
   }
-  if (a.dh0 && l.cvalid && l.k < N) a.dh0[(l.b * a.dim + l.c) * N + l.k] = rcarry;
+  if (SPLIT && part > 0) {  // publish the adjoint entering this part for the earlier one
+    const int64_t slot = (part - 1) * groups + gi;
+    if (l.k < 16) split::store_state(a.split_ws, a.split_cap, slot, l.k, l.i, rcarry);
+    split::finish_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) split::publish(a.split_ws, slot);
+  } else if (a.dh0 && l.cvalid && l.k < N) {
+    a.dh0[(l.b * a.dim + l.c) * N + l.k] = rcarry;
+  }
 
-  // dA, dD and dbias of this workgroup: sum the 16 rows
+  // dA, dD and dbias of this workgroup: sum the R rows
   __syncthreads();
 #pragma unroll
   for (int n = 0; n < 16; ++n) lds_eh[0][l.k * kS + n * 16 + l.i] = dAacc[n];
   lds_m[l.k * 16 + l.i] = dDacc;
-  lds_m[256 + l.k * 16 + l.i] = dbacc;
+  lds_m[R * 16 + l.k * 16 + l.i] = dbacc;
   __syncthreads();
-  {
+  if (R == 16 || l.k < 16) {
     float s = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) s += lds_eh[0][kk * kS + l.k * 16 + l.i];
-    float* pc = a.part_ch + (l.b * dimp + l.c) * 18;
+    for (int kk = 0; kk < R; ++kk) s += lds_eh[0][kk * kS + l.k * 16 + l.i];
+    float* pc = a.part_ch + ((part * a.batch + l.b) * dimp + l.c) * 18;
     if (l.k < N) pc[l.k] = s;
     if (l.k == 0 || l.k == 1) {
       float t = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) t += lds_m[l.k * 256 + kk * 16 + l.i];
+      for (int kk = 0; kk < R; ++kk) t += lds_m[l.k * R * 16 + kk * 16 + l.i];
       pc[16 + l.k] = t;
     }
   }
@@ -738,21 +819,35 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
     const int64_t d = jc / (a.dstate + 2), q = jc % (a.dstate + 2);
     const int slot = q < a.dstate ? static_cast<int>(q) : static_cast<int>(16 + (q - a.dstate));
     float s = 0.0f;
-    for (int64_t b = 0; b < a.batch; ++b) s += a.part_ch[(b * dimp + d) * 18 + slot];
+    const int64_t nparts = a.parts > 1 ? a.parts : 1;
+    for (int64_t p = 0; p < nparts; ++p)
+      for (int64_t b = 0; b < a.batch; ++b) s += a.part_ch[((p * a.batch + b) * dimp + d) * 18 + slot];
     if (q < a.dstate) a.dA[d * a.dstate + q] = s;
     else if (q == a.dstate) { if (a.dD) a.dD[d] = s; }
     else if (a.dbias) a.dbias[d] = s;
   }
 }
 
+template <typename T, int TC, int R, bool SPLIT>
+void launch_bwd_scans(const BwdArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.batch * a.ngroups * (SPLIT ? a.parts : 1)));
+  hipLaunchKernelGGL((bwd_ckpt_kernel<T, 8, R, SPLIT>), grid, dim3(R * 16), 0, s, a);
+  if (a.z)
+    hipLaunchKernelGGL((bwd_chunked_kernel<T, true, TC, R, SPLIT>), grid, dim3(R * 16), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_chunked_kernel<T, false, TC, R, SPLIT>), grid, dim3(R * 16), 0, s, a);
+}
+
 template <typename T, int TC>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.batch * a.ngroups));
-  hipLaunchKernelGGL((bwd_ckpt_kernel<T, 8>), grid, dim3(256), 0, s, a);
-  if (a.z)
-    hipLaunchKernelGGL((bwd_chunked_kernel<T, true, TC>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_chunked_kernel<T, false, TC>), grid, dim3(256), 0, s, a);
+  if (a.rows == 32) {  // (the split is planned for 32-row tiles only)
+    if (a.parts > 1)
+      launch_bwd_scans<T, TC, 32, true>(a, s);
+    else
+      launch_bwd_scans<T, TC, 32, false>(a, s);
+  } else {
+    launch_bwd_scans<T, TC, 16, false>(a, s);
+  }
   const int64_t total = a.batch * a.seqlen * a.dstate + a.dim * (a.dstate + 2);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -762,13 +857,56 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
 
 int64_t bwd_tile_tokens() { return 16 * kBwdChunk; }
 
+// 32 rows (8 waves, one workgroup per CU at two waves per SIMD) or 16 (4 waves, two per CU).
+// A CU finishes one 8-wave workgroup's group in ~0.6 of the time it takes for two 4-wave
+// workgroups sharing it (L = 32K, bf16: 256 groups 4.45 ms with 32 rows, 512 groups 7.4 ms
+// with 16), so 32 rows pay while their rounds (with the split) stay under 1/0.6 of the one
+// round that 16-row pairs need for at most two groups per CU.
+int bwd_rows(int64_t groups, int64_t seqlen, int cus) {
+  if (groups >= 2 * static_cast<int64_t>(cus)) return 16;
+  const int p = bwd_split_parts(groups, 32, seqlen, cus);
+  const double rounds = static_cast<double>((groups * p + cus - 1) / cus) / p;
+  return 0.6 * (rounds > 1.0 ? rounds : 1.0) < 1.0 ? 32 : 16;
+}
+
 size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   const int64_t ngroups = (dim + 15) / 16, dimp = ngroups * 16;
   const int64_t ntiles = seqlen > 0 ? (seqlen + bwd_tile_tokens() - 1) / bwd_tile_tokens() : 0;
   const int64_t floats = batch * ntiles * dimp * 16              // tile-start states
                          + 2 * batch * ngroups * seqlen * dstate  // dB, dC per channel group
-                         + batch * dimp * 18;                     // dA, dD, dbias per batch row
+                         + kBwdMaxParts * batch * dimp * 18;      // dA, dD, dbias per part and row
   return static_cast<size_t>(floats) * sizeof(float);
+}
+
+// Parts of whole tiles of both kernels (the checkpoint kernel's tile, R * 8 tokens, is the
+// longer).
+int64_t bwd_split_part_len(int64_t seqlen, int rows, int parts) {
+  const int64_t tile = static_cast<int64_t>(rows) * 8;
+  const int64_t per = (seqlen + parts - 1) / parts;
+  return (per + tile - 1) / tile * tile;
+}
+
+// With 32-row tiles (one workgroup per CU) and more groups than CUs, a second round would run
+// on part of the chip: split as the forward does (the fewest parts within 5% of the best of
+// max(1, ceil(groups * parts / CUs) / parts)). 16-row tiles (two workgroups per CU) are not
+// split: moving parts between CUs does not help a CU that holds one 4-wave workgroup.
+int bwd_split_parts(int64_t groups, int rows, int64_t seqlen, int cus) {
+  if (rows != 32 || groups <= cus || seqlen <= 0) return 1;
+  auto time = [&](int p) {
+    const double rounds = static_cast<double>((groups * p + cus - 1) / cus);
+    return rounds / p > 1.0 ? rounds / p : 1.0;
+  };
+  int best = 1;
+  double tbest = time(1);
+  for (int p = 2; p <= kBwdMaxParts; ++p) {
+    const int64_t len = bwd_split_part_len(seqlen, rows, p);
+    if ((seqlen + len - 1) / len != p) continue;  // too short for p parts of whole tiles
+    if (time(p) < 0.95 * tbest) {
+      best = p;
+      tbest = time(p);
+    }
+  }
+  return best;
 }
 
 hipError_t bwd(const BwdArgs& a, hipStream_t s) {

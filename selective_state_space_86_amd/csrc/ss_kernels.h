@@ -90,10 +90,20 @@ struct BwdArgs {
   float* part_ch;
   int64_t batch, seqlen, dim, dstate;
   int64_t ngroups;          // channel groups of 16 per batch row
-  int64_t ntiles;           // tiles of bwd_tile_tokens() tokens
+  int64_t ntiles;           // checkpoint intervals of bwd_tile_tokens() tokens
   int dtype;
   int softplus;
+  int rows;                 // time chunks per workgroup tile: 16 (4 waves) or 32 (8 waves)
+  // sequence split (parts > 1) of the checkpoint and reverse kernels (ss_split.h): parts of
+  // part_len tokens (whole tiles of both kernels); part_ch then holds one (batch,
+  // ngroups*16, 18) block per part
+  int parts;
+  int64_t part_len;
+  uint32_t* split_ws;
+  int64_t split_cap;
 };
+
+constexpr int kBwdMaxParts = 8;  // sequence parts of the backward split at most
 
 constexpr int kBwdChunk = 2;  // tokens per lane and chunk in the backward kernels
 
@@ -137,6 +147,10 @@ hipError_t proj(const ProjArgs& a, int cus, hipStream_t s);
 int proj_step_tiles(int64_t rank, int dtype);
 hipError_t step(const StepArgs& a, hipStream_t s);
 int64_t bwd_tile_tokens();
+int bwd_rows(int64_t groups, int64_t seqlen, int cus);  // the tile rows for these channel groups
+// Parts per sequence of the backward split for this tile plan (1: none) and their length.
+int bwd_split_parts(int64_t groups, int rows, int64_t seqlen, int cus);
+int64_t bwd_split_part_len(int64_t seqlen, int rows, int parts);
 size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 hipError_t bwd(const BwdArgs& a, hipStream_t s);
 

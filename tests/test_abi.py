@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss_abi_version() == _binding.ABI_VERSION == 8
+    assert lib.ss_abi_version() == _binding.ABI_VERSION == 9
     for s in range(0, 9):
         assert lib.ss_status_string(s)
     assert b"unknown" in lib.ss_status_string(99)
@@ -196,10 +196,11 @@ def test_bwd_workspace_too_small(lib):
 
 def test_bwd_workspace_size_formula(lib):
     """Tile-start states (tiles of 32 tokens, channel groups of 16, 16 states), dB/dC partial
-    sums per channel group, and dA/dD/dbias partial sums per batch row."""
+    sums per channel group, and dA/dD/dbias partial sums per batch row and sequence part (at
+    most 8 parts)."""
     batch, L, dim, N = 3, 100, 40, 5
     groups, tiles = 3, 4
-    floats = batch * tiles * groups * 16 * 16 + 2 * batch * groups * L * N + batch * groups * 16 * 18
+    floats = batch * tiles * groups * 16 * 16 + 2 * batch * groups * L * N + 8 * batch * groups * 16 * 18
     assert lib.ss_bwd_workspace_size(batch, L, dim, N) == 4 * floats
     assert lib.ss_bwd_workspace_size(0, L, dim, N) == 0
     assert lib.ss_bwd_workspace_size(batch, L, dim, 17) == 0
