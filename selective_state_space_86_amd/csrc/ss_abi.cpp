@@ -54,11 +54,13 @@ std::vector<SplitWs> g_split_ws;
 
 // The split workspace of the current device and stream s with at least `items` slots (its
 // capacity in *cap), or null on a HIP error. A new or grown buffer is cleared by a kernel on
-// s, ahead of the caller's; a grown one gets twice the old capacity at least.
-uint32_t* split_workspace(int64_t items, hipStream_t s, int64_t* cap) {
+// s, ahead of the caller's; a grown one gets twice the old capacity at least. `lock` is
+// left holding the cache's mutex: the caller enqueues its kernel before releasing it, so
+// another host thread on the same stream cannot free the buffer (by growing it) first.
+uint32_t* split_workspace(int64_t items, hipStream_t s, int64_t* cap, std::unique_lock<std::mutex>& lock) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lock(g_split_mu);
+  lock = std::unique_lock<std::mutex>(g_split_mu);
   SplitWs* w = nullptr;
   for (auto& e : g_split_ws)
     if (e.dev == dev && e.stream == s) w = &e;
@@ -180,8 +182,9 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
       parts = static_cast<int>((seqlen + a.part_len - 1) / a.part_len);
       if (groups * parts > 0x7fffffffLL) parts = 1;
     }
+    std::unique_lock<std::mutex> ws_lock;  // (held until the kernel is enqueued)
     if (parts > 1) {
-      a.split_ws = split_workspace(ss::fwd_split_items(groups, parts), s, &a.split_cap);
+      a.split_ws = split_workspace(ss::fwd_split_items(groups, parts), s, &a.split_cap, ws_lock);
       if (!a.split_ws) return SS_ERR_HIP;
       a.parts = parts;
     }
@@ -373,9 +376,10 @@ int ss_bwd(const void* u, const void* delta, const float* A, const void* B, cons
                 in_dtype, softplus_flag ? 1 : 0, ss::bwd_rows(batch * ngroups, seqlen, cus)};
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int parts = ss::bwd_split_parts(batch * ngroups, a.rows, seqlen, cus);
+  std::unique_lock<std::mutex> ws_lock;  // (held until the kernels are enqueued)
   if (parts > 1 && batch * ngroups * parts <= 0x7fffffffLL) {
     a.part_len = ss::bwd_split_part_len(seqlen, a.rows, parts);
-    a.split_ws = split_workspace(batch * ngroups * (parts - 1), s, &a.split_cap);
+    a.split_ws = split_workspace(batch * ngroups * (parts - 1), s, &a.split_cap, ws_lock);
     if (!a.split_ws) return SS_ERR_HIP;
     a.parts = parts;
   }

@@ -188,3 +188,43 @@ def test_split_in_a_captured_graph():
         other = pu.gpu_fwd(x, True, split_parts=3, **kw)
         torch.cuda.synchronize()
         assert torch.equal(other[0], ref[0])
+
+
+def test_split_from_several_host_threads():
+    """Split calls from four host threads: two share one stream (with part counts that grow its
+    workspace while the other thread's calls are queued on it), two have a stream each. The
+    library keeps the workspace cache locked until a call's kernel is enqueued, so a buffer is
+    never freed under a queued kernel; every result equals the unsplit one."""
+    import threading
+
+    kw = dict(kernel=2, chunk_len=4, chunk_rows=16)
+    xa = inputs.make(_workload(2, 900, 64, "f32", "ta"), seed=31, device=DEV)
+    xb = inputs.make(_workload(1, 3000, 512, "bf16", "tb"), seed=32, device=DEV)
+    _announce("several host threads")
+    ref_a = pu.gpu_fwd(xa, True, split_parts=1, **kw)
+    ref_b = pu.gpu_fwd(xb, True, split_parts=1, **kw)
+    torch.cuda.synchronize()
+    shared, s1, s2 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    errors = []
+
+    def worker(x, ref, stream, part_counts):
+        try:
+            for parts in part_counts:
+                with torch.cuda.stream(stream):
+                    got = pu.gpu_fwd(x, True, split_parts=parts, **kw)
+                stream.synchronize()
+                if not (torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])):
+                    errors.append(f"parts={parts}: result differs")
+        except Exception as e:  # reported below, on the test's own thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(xa, ref_a, shared, (2, 3, 8, 4, 16, 2))),
+               threading.Thread(target=worker, args=(xb, ref_b, shared, (3, 16, 5, 12, 2))),
+               threading.Thread(target=worker, args=(xa, ref_a, s1, (4, 2, 6))),
+               threading.Thread(target=worker, args=(xb, ref_b, s2, (8, 3, 16)))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
