@@ -744,11 +744,15 @@ void bwd_chunked_kernel(BwdArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       float sB = 0.0f, sC = 0.0f;
       {
+        // (lane i reads the quarters of its 64-byte row in the order starting at i / 4: rows
+        // of lanes i and i + 4 sit 256 bytes apart, on the same banks, so in one 16-byte read
+        // the 16 lanes of a row touch 16 different bank groups only when their quarters differ)
         const float4* qb = reinterpret_cast<const float4*>(rB + l.i * 16);
         const float4* qc = reinterpret_cast<const float4*>(rC + l.i * 16);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const float4 vb4 = qb[m], vc4 = qc[m];
+          const int mm = (m + (l.i >> 2)) & 3;
+          const float4 vb4 = qb[mm], vc4 = qc[mm];
           sB += (vb4.x + vb4.y) + (vb4.z + vb4.w);
           sC += (vc4.x + vc4.y) + (vc4.z + vc4.w);
         }
