@@ -112,11 +112,10 @@ typedef struct {
   int chunk_len;      /* tokens per lane and tile for kernel 2: 0 (automatic), 4 or 8 */
   int discretization; /* an ss_discretization value */
   int chunk_rows;     /* time chunks per workgroup tile for kernel 2: 0 (automatic), 16, 12 or
-                         32; 12 needs chunk_len 0 or 4 (else SS_ERR_BAD_SHAPE) and is chosen
-                         automatically when channel groups of 16 per CU fill 4 slots of 3-wave
-                         workgroups better than 3 slots of 4-wave ones; 32 (8 waves) is chosen
-                         for at most 2 groups per CU and needs 256 * dim * 4 < 2^31 (else
-                         SS_ERR_BAD_SHAPE) */
+                         32; 12 needs chunk_len 0 or 4 (else SS_ERR_BAD_SHAPE) and is never
+                         chosen automatically; 32 (8 waves) is chosen for at most 2 groups of
+                         16 channels per CU and needs 256 * dim * 4 < 2^31 (else
+                         SS_ERR_BAD_SHAPE); otherwise 16 */
   int split_parts;    /* kernel 2 only: cut every sequence into this many parts of whole tiles
                          (fewer when it is too short), processed by successive workgroups
                          that hand the chunk state on (the associative combine of

@@ -321,27 +321,22 @@ hipError_t launch_chunked_t(const FwdArgs& a, ChunkPlan p, hipStream_t s) {
 bool fwd_chunked_supported(const FwdArgs& a) { return a.dstate == 16 && a.seqlen > 0; }
 
 // Tile shape. Chunk length 8 halves the per-tile combine cost but needs ~2x the registers
-// of 4 (2 resident workgroups of 16 rows per CU instead of 3); 12 rows (3 waves) let four
-// workgroups share a CU where three of 16 rows do. The channel groups of 16 are dealt to
-// the resident slots in rounds, and a partly filled last round runs at low occupancy, so
-// the plan maximises the filled fraction of the slots:
+// of 4 (2 resident workgroups of 16 rows per CU instead of 3). The plan:
 //  - at most 2 groups per CU (the 3B long-context shape: 320 groups): length 8, 32 rows, so
-//    every SIMD holding a group has two of its waves;
-//  - otherwise length 4 with 16 rows (3 slots per CU) unless 12 rows (4 slots) fill the
-//    rounds better by more than 5% (1024 groups, the 1.4B shape: 1 full round of 4 against
-//    2/3 of a second round of 3; 768 groups, the 130M shape: 16 rows, one full round).
+//    every SIMD holding a group has two of its waves (with the sequence split when the groups
+//    outnumber the CUs);
+//  - otherwise length 4 with 16 rows (3 resident workgroups per CU). 12-row tiles (3 waves,
+//    4 per CU) fill the resident slots better at 1024 groups (the 1.4B shape) but measured
+//    slower at steady clock (420 against 398 us at 1.4B, 169 against 136 us at 130M): in a
+//    12-row tile a quarter of the folding lanes fold two states. They stay available through
+//    ss_fwd_options.chunk_rows.
 // The zero-order-hold variant runs at two waves per SIMD either way and keeps 16 rows.
 ChunkPlan fwd_chunked_pick(const FwdArgs& a, int cus) {
   const int64_t groups = a.batch * ((a.dim + 15) / 16);
   if (a.zoh) return {4, 16};  // the zero-order-hold variant spills registers at 8
   // (32 rows of 8 tokens span 256 tokens of the (.., dim) arrays from one 32-bit tile offset)
   if (groups <= 2 * static_cast<int64_t>(cus)) return (256 * a.dim * 4 < (1LL << 31)) ? ChunkPlan{8, 32} : ChunkPlan{8, 16};
-  auto filled = [&](int64_t slots_per_cu) {
-    const int64_t slots = slots_per_cu * cus;
-    const int64_t rounds = (groups + slots - 1) / slots;
-    return static_cast<double>(groups) / static_cast<double>(rounds * slots);
-  };
-  return filled(4) > filled(3) + 0.05 ? ChunkPlan{4, 12} : ChunkPlan{4, 16};
+  return ChunkPlan{4, 16};
 }
 
 // Resident workgroups per CU of a tile plan (VGPR and LDS budgets): 32 rows, 8 waves at two
