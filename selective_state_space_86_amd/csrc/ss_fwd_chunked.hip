@@ -278,7 +278,7 @@ __global__ void zero_words_kernel(uint32_t* p, int64_t n) {
 template <typename T, bool GATE, int TC, bool ZOH, int R>
 void launch_chunked_c(const FwdArgs& a, hipStream_t s) {
   const int64_t groups = a.batch * ((a.dim + 15) / 16);
-  constexpr bool early = TC <= 4 && !GATE;
+  constexpr bool early = TC <= 4;
   const dim3 block(R * 16);
   if (a.parts > 1) {
     const dim3 grid(static_cast<unsigned>(groups * a.parts));
