@@ -236,11 +236,12 @@ size_t ss_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t
  * seqlen == 0 is allowed (the per-token arrays may then be NULL): dh0 = dlast_state and
  * dA, dD, ddelta_bias are zero. Sums over channels, tokens and batch rows have a fixed
  * order, so the result is deterministic. Errors as ss_fwd, plus SS_ERR_WORKSPACE.
- * With fewer channel groups of 16 than twice the CUs the kernels run 8-wave workgroups, and
- * with more groups than CUs they also split every sequence into parts (as
- * ss_fwd_options.split_parts describes; the reverse pass hands the adjoint from each part to
- * the one before it), using the library-kept workspace of the stream that ss_fwd's split
- * uses (allocated at the first split call on that stream; see there).
+ * With fewer channel groups of 16 than twice the CUs the kernels run 8-wave workgroups (one
+ * per CU), else 4-wave ones (two per CU). When the groups fill those resident slots in more
+ * than one round and leave part of the last round empty, they also split every sequence into
+ * parts (as ss_fwd_options.split_parts describes; the reverse pass hands the adjoint from
+ * each part to the one before it), using the library-kept workspace of the stream that
+ * ss_fwd's split uses (allocated at the first split call on that stream; see there).
  */
 int ss_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
            const float* D, const void* z, const float* delta_bias, int softplus_flag,

@@ -375,13 +375,23 @@ int ss_bwd(const void* u, const void* delta, const float* A, const void* B, cons
                 ckpt, part_bc, part_ch, batch, seqlen, dim, dstate, ngroups, ntiles,
                 in_dtype, softplus_flag ? 1 : 0, ss::bwd_rows(batch * ngroups, seqlen, cus)};
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const int parts = ss::bwd_split_parts(batch * ngroups, a.rows, seqlen, cus);
+  const int64_t groups = batch * ngroups;
+  int parts = ss::bwd_split_parts(groups, a.rows, false, seqlen, cus);
+  int ckpt_parts = ss::bwd_split_parts(groups, a.rows, true, seqlen, cus);
+  if (groups * ss::kBwdMaxParts > 0x7fffffffLL) parts = ckpt_parts = 1;
   std::unique_lock<std::mutex> ws_lock;  // (held until the kernels are enqueued)
-  if (parts > 1 && batch * ngroups * parts <= 0x7fffffffLL) {
-    a.part_len = ss::bwd_split_part_len(seqlen, a.rows, parts);
-    a.split_ws = split_workspace(batch * ngroups * (parts - 1), s, &a.split_cap, ws_lock);
+  if (parts > 1 || ckpt_parts > 1) {  // one workspace for both kernels, used one after the other
+    const int most = parts > ckpt_parts ? parts : ckpt_parts;
+    a.split_ws = split_workspace(groups * (most - 1), s, &a.split_cap, ws_lock);
     if (!a.split_ws) return SS_ERR_HIP;
+  }
+  if (parts > 1) {
     a.parts = parts;
+    a.part_len = ss::bwd_split_part_len(seqlen, a.rows, parts);
+  }
+  if (ckpt_parts > 1) {
+    a.ckpt_parts = ckpt_parts;
+    a.ckpt_part_len = ss::bwd_split_part_len(seqlen, a.rows, ckpt_parts);
   }
   const hipError_t e = ss::bwd(a, s);
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;

@@ -832,26 +832,36 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
   }
 }
 
-template <typename T, int TC, int R, bool SPLIT>
+template <typename T, int TC, int R>
 void launch_bwd_scans(const BwdArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.batch * a.ngroups * (SPLIT ? a.parts : 1)));
-  hipLaunchKernelGGL((bwd_ckpt_kernel<T, 8, R, SPLIT>), grid, dim3(R * 16), 0, s, a);
-  if (a.z)
-    hipLaunchKernelGGL((bwd_chunked_kernel<T, true, TC, R, SPLIT>), grid, dim3(R * 16), 0, s, a);
+  const unsigned groups = static_cast<unsigned>(a.batch * a.ngroups);
+  BwdArgs c = a;  // the checkpoint kernel runs its own parts
+  c.parts = a.ckpt_parts;
+  c.part_len = a.ckpt_part_len;
+  if (c.parts > 1)
+    hipLaunchKernelGGL((bwd_ckpt_kernel<T, 8, R, true>), dim3(groups * c.parts), dim3(R * 16), 0, s, c);
   else
-    hipLaunchKernelGGL((bwd_chunked_kernel<T, false, TC, R, SPLIT>), grid, dim3(R * 16), 0, s, a);
+    hipLaunchKernelGGL((bwd_ckpt_kernel<T, 8, R, false>), dim3(groups), dim3(R * 16), 0, s, c);
+  const dim3 grid(groups * static_cast<unsigned>(a.parts > 1 ? a.parts : 1));
+  if (a.parts > 1) {
+    if (a.z)
+      hipLaunchKernelGGL((bwd_chunked_kernel<T, true, TC, R, true>), grid, dim3(R * 16), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_chunked_kernel<T, false, TC, R, true>), grid, dim3(R * 16), 0, s, a);
+  } else {
+    if (a.z)
+      hipLaunchKernelGGL((bwd_chunked_kernel<T, true, TC, R, false>), grid, dim3(R * 16), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_chunked_kernel<T, false, TC, R, false>), grid, dim3(R * 16), 0, s, a);
+  }
 }
 
 template <typename T, int TC>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
-  if (a.rows == 32) {  // (the split is planned for 32-row tiles only)
-    if (a.parts > 1)
-      launch_bwd_scans<T, TC, 32, true>(a, s);
-    else
-      launch_bwd_scans<T, TC, 32, false>(a, s);
-  } else {
-    launch_bwd_scans<T, TC, 16, false>(a, s);
-  }
+  if (a.rows == 32)
+    launch_bwd_scans<T, TC, 32>(a, s);
+  else
+    launch_bwd_scans<T, TC, 16>(a, s);
   const int64_t total = a.batch * a.seqlen * a.dstate + a.dim * (a.dstate + 2);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -868,7 +878,7 @@ int64_t bwd_tile_tokens() { return 16 * kBwdChunk; }
 // round that 16-row pairs need for at most two groups per CU.
 int bwd_rows(int64_t groups, int64_t seqlen, int cus) {
   if (groups >= 2 * static_cast<int64_t>(cus)) return 16;
-  const int p = bwd_split_parts(groups, 32, seqlen, cus);
+  const int p = bwd_split_parts(groups, 32, false, seqlen, cus);
   const double rounds = static_cast<double>((groups * p + cus - 1) / cus) / p;
   return 0.6 * (rounds > 1.0 ? rounds : 1.0) < 1.0 ? 32 : 16;
 }
@@ -890,14 +900,18 @@ int64_t bwd_split_part_len(int64_t seqlen, int rows, int parts) {
   return (per + tile - 1) / tile * tile;
 }
 
-// With 32-row tiles (one workgroup per CU) and more groups than CUs, a second round would run
-// on part of the chip: split as the forward does (the fewest parts within 5% of the best of
-// max(1, ceil(groups * parts / CUs) / parts)). 16-row tiles (two workgroups per CU) are not
-// split: moving parts between CUs does not help a CU that holds one 4-wave workgroup.
-int bwd_split_parts(int64_t groups, int rows, int64_t seqlen, int cus) {
-  if (rows != 32 || groups <= cus || seqlen <= 0) return 1;
+// When the groups leave part of the last round of resident slots empty, split as the forward
+// does: the fewest parts within 5% of the best of max(1, ceil(groups * parts / slots) /
+// parts). The reverse kernel (~195 VGPRs) holds one 32-row or two 16-row workgroups per CU,
+// the checkpoint kernel (~140) one 32-row or three 16-row ones. At the 130M shape (768 groups
+// of 16-row tiles) the reverse kernel's two parts took it from 569 to 526 us, and the
+// checkpoint kernel, which fills its 768 slots once, ran 9 us slower split; at 1024 groups
+// (two whole rounds of the reverse kernel) two parts measured 2% slower.
+int bwd_split_parts(int64_t groups, int rows, bool ckpt, int64_t seqlen, int cus) {
+  const int64_t slots = static_cast<int64_t>(rows == 32 ? 1 : (ckpt ? 3 : 2)) * cus;
+  if (groups <= slots || seqlen <= 0) return 1;
   auto time = [&](int p) {
-    const double rounds = static_cast<double>((groups * p + cus - 1) / cus);
+    const double rounds = static_cast<double>((groups * p + slots - 1) / slots);
     return rounds / p > 1.0 ? rounds / p : 1.0;
   };
   int best = 1;

@@ -94,13 +94,16 @@ struct BwdArgs {
   int dtype;
   int softplus;
   int rows;                 // time chunks per workgroup tile: 16 (4 waves) or 32 (8 waves)
-  // sequence split (parts > 1) of the checkpoint and reverse kernels (ss_split.h): parts of
-  // part_len tokens (whole tiles of both kernels); part_ch then holds one (batch,
-  // ngroups*16, 18) block per part
+  // sequence split (parts > 1) of the reverse kernel (ss_split.h): parts of part_len tokens
+  // (whole tiles of both kernels); part_ch then holds one (batch, ngroups*16, 18) block per
+  // part. The checkpoint kernel, which holds more workgroups per CU, has its own ckpt_parts
+  // of ckpt_part_len tokens. Both kernels use the one workspace, one after the other.
   int parts;
   int64_t part_len;
   uint32_t* split_ws;
   int64_t split_cap;
+  int ckpt_parts;
+  int64_t ckpt_part_len;
 };
 
 constexpr int kBwdMaxParts = 8;  // sequence parts of the backward split at most
@@ -148,8 +151,9 @@ int proj_step_tiles(int64_t rank, int dtype);
 hipError_t step(const StepArgs& a, hipStream_t s);
 int64_t bwd_tile_tokens();
 int bwd_rows(int64_t groups, int64_t seqlen, int cus);  // the tile rows for these channel groups
-// Parts per sequence of the backward split for this tile plan (1: none) and their length.
-int bwd_split_parts(int64_t groups, int rows, int64_t seqlen, int cus);
+// Parts per sequence of the backward split for this tile plan (1: none) and their length,
+// for the reverse kernel or (ckpt) the checkpoint kernel.
+int bwd_split_parts(int64_t groups, int rows, bool ckpt, int64_t seqlen, int cus);
 int64_t bwd_split_part_len(int64_t seqlen, int rows, int parts);
 size_t bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 hipError_t bwd(const BwdArgs& a, hipStream_t s);

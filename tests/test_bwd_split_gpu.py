@@ -1,6 +1,10 @@
 """GPU parity of the backward's 8-wave tiles and sequence split (ss_bwd with fewer channel
-groups than twice the CUs: 32-row tiles; with more groups than CUs as well: the
-recomputation and the reverse pass run every sequence in parts, the reverse pass handing the
+groups than twice the CUs: 32-row tiles; with more groups than CUs as well, or with 4-wave
+tiles and more groups than twice the CUs that leave part of the last round of slots empty:
+the recomputation and the reverse pass run every sequence in parts — each kernel its own
+number, as the checkpoint kernel holds three 4-wave workgroups per CU and the reverse kernel
+two (4 groups per CU: only the checkpoint kernel splits; 3.5: 6 parts against 4) — the
+reverse pass handing the
 adjoint from each part to the one before it — the associative combine of "架构变体：
 Mamba/SSM", section "硬件感知算法", in reverse time).
 
@@ -34,7 +38,9 @@ def _shape(L, dt, groups_per_cu=1.2, seed_name="s"):
 
 
 @pytest.mark.parametrize("L,dt,gpc", [(600, "f32", 1.2), (1000, "bf16", 1.2), (300, "f32", 1.2),
-                                      (700, "f32", 0.5), (2100, "bf16", 1.9)])
+                                      (700, "f32", 0.5), (2100, "bf16", 1.9), (300, "f32", 3.0),
+                                      (520, "bf16", 2.5), (900, "f32", 2.25), (300, "f32", 4.0),
+                                      (2000, "bf16", 3.5)])
 def test_bwd_split_matches_oracle(L, dt, gpc):
     w = _shape(L, dt, gpc)
     x = inputs.make(w, seed=71, device=DEV)
@@ -45,13 +51,15 @@ def test_bwd_split_matches_oracle(L, dt, gpc):
     _compare(g, _oracle(x, dy, True), pu.tol_of(x), f"split {w.name}")
 
 
-def test_bwd_split_per_channel_gradients_equal_unsplit():
-    """Channel groups are independent but for dB and dC: the first 64 groups computed alone
-    (no split) give the same per-channel gradients as inside the split call."""
-    w = _shape(700, "f32", seed_name="e")
+@pytest.mark.parametrize("gpc", [1.2, 3.0])
+def test_bwd_split_per_channel_gradients_equal_unsplit(gpc):
+    """Channel groups are independent but for dB and dC: the first groups computed alone
+    (no split: 64 groups of 8-wave tiles, or as many 4-wave ones as fill the slots once) give
+    the same per-channel gradients as inside the split call with the same tiles."""
+    w = _shape(700, "f32", gpc, seed_name="e")
     x = inputs.make(w, seed=73, device=DEV)
     dy = _dy((w.batch, w.seqlen, w.dim), 74)
-    sub = 64 * 16
+    sub = (64 if gpc < 2 else 2 * _cus()) * 16
     xs = {k: (v[..., :sub].contiguous() if k in ("u", "delta", "z") else
               v[:sub].contiguous() if k in ("A", "D", "delta_bias") else v) for k, v in x.items()}
     _announce("split vs unsplit per-channel gradients")
