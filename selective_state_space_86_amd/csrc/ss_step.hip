@@ -92,6 +92,20 @@ struct Vec4In<uint16_t> {
   }
 };
 
+// The state is read once and written once per step and not touched again until the next
+// step: its loads and stores carry the non-temporal hint. At 256 x 5120 x 16 (84 MB) the
+// step took 35.0 us with it against 39.9 us without (hinting only the stores changed
+// nothing).
+typedef float nt4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_nt(const float4* p) {
+  const nt4_t v = __builtin_nontemporal_load(reinterpret_cast<const nt4_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(float4* p, float4 v) {
+  nt4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<nt4_t*>(p));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float quad_perm(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
@@ -117,7 +131,7 @@ __device__ __forceinline__ void step_quad_channel(const StepArgs& a, int64_t j, 
   }
   acc += quad_perm<0xB1>(acc);  // quad_perm [1,0,3,2]
   acc += quad_perm<0x4E>(acc);  // quad_perm [2,3,0,1]
-  *st = make_float4(h[0], h[1], h[2], h[3]);
+  st_nt(st, make_float4(h[0], h[1], h[2], h[3]));
   if (q == 0) {
     float yv = __builtin_fmaf(a.D ? a.D[d] : 0.0f, uv, acc);
     if (GATE) yv *= silu(zv);
@@ -151,7 +165,7 @@ __global__ __launch_bounds__(256) void step_quad_kernel(StepArgs a) {
       jj[r] = j;
       bb[r] = b;
       dd[r] = d;
-      hv[r] = reinterpret_cast<const float4*>(a.state)[j * 4 + q];
+      hv[r] = ld_nt(reinterpret_cast<const float4*>(a.state) + j * 4 + q);
       av[r] = a4;
       bv[r] = Vec4In<T>::load(static_cast<const T*>(a.B) + b * 16 + 4 * q);
       cv[r] = Vec4In<T>::load(static_cast<const T*>(a.C) + b * 16 + 4 * q);
@@ -170,7 +184,7 @@ __global__ __launch_bounds__(256) void step_quad_kernel(StepArgs a) {
       jj[r] = j;
       bb[r] = b;
       dd[r] = d;
-      hv[r] = reinterpret_cast<const float4*>(a.state)[jc * 4 + q];
+      hv[r] = ld_nt(reinterpret_cast<const float4*>(a.state) + jc * 4 + q);
       av[r] = reinterpret_cast<const float4*>(a.A)[d * 4 + q];
       bv[r] = Vec4In<T>::load(static_cast<const T*>(a.B) + b * 16 + 4 * q);
       cv[r] = Vec4In<T>::load(static_cast<const T*>(a.C) + b * 16 + 4 * q);
