@@ -20,8 +20,10 @@
  *
  * Conventions shared by every entry point:
  *  - All data pointers are DEVICE pointers on the current HIP device, owned by the
- *    caller. The library allocates and frees nothing, keeps no per-call state, and is
- *    safe to call from several host threads.
+ *    caller. The library allocates and frees nothing, keeps no state between calls (beyond
+ *    a cache of each device's architecture and CU count), never blocks in an enqueueing
+ *    call, and is safe to call from several host threads. Scratch memory comes from the
+ *    caller as a workspace argument (ss_fwd_options.workspace, ss_bwd's workspace).
  *  - Tensors are dense, row-major, with no padding or strides.
  *  - in_dtype selects the element type of u, delta, z, B and C (all the same);
  *    A, D, delta_bias, y and the state are always fp32.
@@ -41,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 9
+#define SS_ABI_VERSION 10
 #define SS_MAX_DSTATE 16
 
 typedef enum {
@@ -53,7 +55,8 @@ typedef enum {
   SS_ERR_MISALIGNED = 5,    /* a pointer is not aligned to its element size */
   SS_ERR_HIP = 6,           /* a HIP runtime call or kernel launch failed */
   SS_ERR_DEVICE = 7,        /* the current device is not a gfx950 GPU */
-  SS_ERR_WORKSPACE = 8      /* workspace NULL or smaller than ss_bwd_workspace_size() */
+  SS_ERR_WORKSPACE = 8,     /* workspace NULL or smaller than its size query returns */
+  SS_ERR_SPLIT_WAIT = 9     /* ss_workspace_status: a sequence-split hand-off wait gave up */
 } ss_status;
 
 typedef enum {
@@ -91,10 +94,11 @@ const char* ss_status_string(int status);
  *   last_state    (batch, dim, dstate)     fp32 output, may be NULL: the state after the last token.
  *   seqlen == 0 is allowed: no token is read, y is not written, last_state is set to
  *   zero; u, delta, z, B, C and y may then be NULL (A is still required).
- * Limits: dstate <= 16; batch * seqlen * dim < 2^62.
- * Where the automatic plan splits the sequences (ss_fwd_options.split_parts: more channel
- * groups of 16 than resident workgroup slots, e.g. 320 groups on 256 CUs), the first such
- * call on a stream allocates a small device workspace that the library keeps (see there).
+ * Limits: dstate <= 16; batch * seqlen * dim < 2^62; for dstate == 16, 64 * dim * 4 < 2^31
+ * (dim below 8,388,608: the time-chunked kernel addresses a tile of 64 tokens of the fp32
+ * rows from 32-bit offsets; larger plans are taken only where their tile fits too).
+ * ss_fwd takes no workspace and so never splits the sequences (ss_fwd_options.split_parts);
+ * ss_fwd_ex with a workspace does where the automatic plan splits.
  */
 int ss_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
            const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
@@ -107,8 +111,12 @@ typedef struct {
   int kernel;         /* 0: automatic; 1: one lane per channel, sequential in t (any dstate);
                          2: time-chunked (dstate == 16 only, else SS_ERR_UNSUPPORTED_N);
                          3: one lane per (channel, state), sequential in t (default input
-                            term, no conv prologue, else SS_ERR_BAD_SHAPE); automatic picks
-                            2 for dstate == 16, else 3 when it applies, else 1 */
+                            term, no conv prologue, else SS_ERR_BAD_SHAPE);
+                         4: time-chunked in phases (8-wave tiles of 32 chunks of 4 tokens;
+                            dstate == 16, else SS_ERR_UNSUPPORTED_N; default input term and no
+                            conv prologue, else SS_ERR_BAD_SHAPE; chunk_len and chunk_rows are
+                            ignored); automatic picks 2 for dstate == 16, else 3 when it
+                            applies, else 1 */
   int chunk_len;      /* tokens per lane and tile for kernel 2: 0 (automatic), 4 or 8 */
   int discretization; /* an ss_discretization value */
   int chunk_rows;     /* time chunks per workgroup tile for kernel 2: 0 (automatic), 16, 12 or
@@ -122,20 +130,49 @@ typedef struct {
                          "架构变体：Mamba/SSM", section "硬件感知算法", one level above the
                          tiles). 0: automatic (split when the channel groups leave part of the
                          last round of resident workgroups empty and outnumber the resident
-                         slots, e.g. 320 groups on 256 CUs); 1: never; 2..16: that many
-                         (else SS_ERR_BAD_SHAPE). The parts start on tile boundaries, so the
-                         results are bit-identical to the unsplit kernel's.
-                         A split call uses a device workspace the library keeps per (device,
-                         stream): allocated (hipMalloc, then cleared by a kernel on the stream)
-                         on the first split call on that pair and when a larger one is needed,
-                         kept until the process ends, and left with zeroed counters and flags
-                         by every call; calls on one stream run in order, so they never share
-                         it concurrently. Its size: 1028 B per channel group and part after the
-                         first (at least doubled when it grows), plus 1.25 KiB. Under graph
-                         capture, make one split call of at least the same size on the
-                         capturing stream before the capture, so nothing is allocated while
-                         capturing. */
+                         slots, e.g. 320 groups on 256 CUs, and the workspace below is large
+                         enough; otherwise run unsplit); 1: never; 2..16: that many (else
+                         SS_ERR_BAD_SHAPE; SS_ERR_WORKSPACE without a large enough
+                         workspace). The parts start on tile boundaries, so the results are
+                         bit-identical to the unsplit kernel's. */
+  void* workspace;    /* device memory for the split's work queue, flags and hand-off states,
+                         owned by the caller, 16-byte aligned, or NULL (no split). Its size for
+                         a call: ss_fwd_workspace_size (about 1 KiB per channel group and part
+                         after the first: 1 MB at batch 1, dim 5120, 4 parts). Its contents on
+                         entry do not matter: the call first enqueues a small kernel on `stream`
+                         that clears what must start at zero (no memset, so the call can be
+                         captured in a graph). Calls that use one workspace must not overlap:
+                         give each stream its own, or order the streams. */
+  size_t workspace_bytes; /* bytes at workspace */
+  int split_wait_limit; /* testing the failure path: 0 (default) bounds each hand-off wait at
+                           about two seconds of polling; n > 0 at n polls; < 0 makes every
+                           wait give up at once. A wait that gives up continues its part from a
+                           NaN state, so that part's outputs (and those of the later parts of
+                           its channel group, and last_state) are NaN, and counts itself in the
+                           workspace: see ss_workspace_status. Every kernel still ends. */
 } ss_fwd_options;
+
+/*
+ * ss_fwd_workspace_size -- the workspace bytes (*bytes) an ss_fwd_ex / ss_fwd_conv call with
+ * these sizes, in_dtype and options would use on the current device: nonzero when its plan
+ * splits the sequences, else 0 (opt->workspace and workspace_bytes are ignored here; opt may
+ * be NULL). Errors: SS_ERR_NULL_ARG (bytes NULL), the size and option errors of ss_fwd_ex,
+ * SS_ERR_DEVICE, SS_ERR_HIP. Enqueues nothing.
+ */
+int ss_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int in_dtype,
+                          const ss_fwd_options* opt, size_t* bytes);
+
+/*
+ * ss_workspace_status -- whether a hand-off wait of the sequence split gave up in the most
+ * recent split call that used this workspace (the workspace given to ss_fwd_ex / ss_fwd_conv,
+ * or to ss_bwd). Waits hold until the previous part has published its state, which it always
+ * does; this reports the bounded wait's safety net (or split_wait_limit < 0). Synchronises
+ * `stream` (blocking the host) and reads a 4-byte counter. Returns SS_OK (no give-up) or
+ * SS_ERR_SPLIT_WAIT, with the number of waits that gave up in *giveups (may be NULL).
+ * Errors: SS_ERR_NULL_ARG (workspace NULL), SS_ERR_MISALIGNED (not 16-byte aligned),
+ * SS_ERR_WORKSPACE (workspace_bytes < 1024), SS_ERR_HIP.
+ */
+int ss_workspace_status(const void* workspace, size_t workspace_bytes, uint32_t* giveups, void* stream);
 
 /*
  * ss_fwd_ex -- ss_fwd from a given initial state, with a choice of input term and kernel.
@@ -144,9 +181,9 @@ typedef struct {
  *        With h0 = the last_state of a call over tokens [0, t0), a call over [t0, L)
  *        continues that scan (chunked prefill; the update is associative, "架构变体：
  *        Mamba/SSM" section "硬件感知算法"); with seqlen == 0, last_state = h0.
- *   opt  options, may be NULL (automatic kernel, bbar = dt). Every kernel choice computes
- *        the same result up to fp32 rounding order. An out-of-range option returns
- *        SS_ERR_BAD_SHAPE.
+ *   opt  options, may be NULL (automatic kernel, bbar = dt, no workspace). Every kernel
+ *        choice computes the same result up to fp32 rounding order. An out-of-range option
+ *        returns SS_ERR_BAD_SHAPE; a misaligned workspace SS_ERR_MISALIGNED.
  */
 int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
               const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
@@ -206,7 +243,8 @@ int ss_step_ex(float* state, const void* u, const void* delta, const float* A, c
  * ss_bwd_workspace_size -- bytes of device workspace ss_bwd needs for these sizes
  * (about 4/(16*2) * 16 bytes per (b, t, d) of tile-start states plus 8 bytes per
  * (b, t, n) per group of 16 channels of partial sums, plus 8 * 72 bytes per (b, d) for
- * the partial sums of up to 8 sequence parts; see ss_bwd).
+ * the partial sums of up to 8 sequence parts, plus the sequence split's region at the
+ * start: about 7 KiB per group of 16 channels; see ss_bwd). 0 for invalid sizes.
  */
 size_t ss_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate);
 
@@ -232,7 +270,7 @@ size_t ss_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t
  *   dh0           (batch, dim, dstate), may be NULL: dL/dh0 (of the zero state if h0 is NULL).
  *   workspace     device memory of at least ss_bwd_workspace_size() bytes, 4-byte
  *                 aligned, owned by the caller; its contents on entry do not matter and
- *                 are undefined on return.
+ *                 are undefined on return (ss_workspace_status reads its split region).
  * seqlen == 0 is allowed (the per-token arrays may then be NULL): dh0 = dlast_state and
  * dA, dD, ddelta_bias are zero. Sums over channels, tokens and batch rows have a fixed
  * order, so the result is deterministic. Errors as ss_fwd, plus SS_ERR_WORKSPACE.
@@ -240,8 +278,8 @@ size_t ss_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t
  * per CU), else 4-wave ones (two per CU). When the groups fill those resident slots in more
  * than one round and leave part of the last round empty, they also split every sequence into
  * parts (as ss_fwd_options.split_parts describes; the reverse pass hands the adjoint from
- * each part to the one before it), using the library-kept workspace of the stream that
- * ss_fwd's split uses (allocated at the first split call on that stream; see there).
+ * each part to the one before it), with the hand-off in the split region at the start of
+ * the workspace.
  */
 int ss_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
            const float* D, const void* z, const float* delta_bias, int softplus_flag,

@@ -12,19 +12,24 @@ _lib = None
 
 F32, BF16 = 0, 1
 DISC_DT, DISC_ZOH = 0, 1
-ABI_VERSION = 9
-EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_fwd_conv", "ss_step",
-           "ss_step_ex", "ss_bwd_workspace_size", "ss_bwd", "ss_proj", "ss_proj_conv")
+ABI_VERSION = 10
+EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_fwd_conv",
+           "ss_fwd_workspace_size", "ss_workspace_status", "ss_step", "ss_step_ex",
+           "ss_bwd_workspace_size", "ss_bwd", "ss_proj", "ss_proj_conv")
+SS_ERR_SPLIT_WAIT = 9
 
 
 class FwdOptions(ctypes.Structure):
     """ss_fwd_options: kernel 0 automatic / 1 sequential / 2 time-chunked / 3 state-parallel;
     chunk_len 0, 4, 8; discretization 0 (input term dt*B) / 1 (exact zero-order hold);
     chunk_rows 0 (automatic), 16, 12 or 32 time chunks per workgroup tile; split_parts 0
-    (automatic), 1 (never) or 2..16 sequence parts for the time-chunked kernel."""
+    (automatic), 1 (never) or 2..16 sequence parts for the time-chunked kernel; workspace and
+    workspace_bytes: the caller's device memory for the split (or NULL); split_wait_limit:
+    0 default, n > 0 polls, < 0 every hand-off wait gives up (testing)."""
     _fields_ = [("kernel", ctypes.c_int), ("chunk_len", ctypes.c_int),
                 ("discretization", ctypes.c_int), ("chunk_rows", ctypes.c_int),
-                ("split_parts", ctypes.c_int)]
+                ("split_parts", ctypes.c_int), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("split_wait_limit", ctypes.c_int)]
 
 
 class SSError(RuntimeError):
@@ -58,6 +63,11 @@ def load_library():
     lib.ss_fwd_conv.restype = i32
     lib.ss_fwd_conv.argtypes = [vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                 i64, i64, i64, i64, i32, ctypes.POINTER(FwdOptions), vp]
+    lib.ss_fwd_workspace_size.restype = i32
+    lib.ss_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(FwdOptions),
+                                          ctypes.POINTER(ctypes.c_size_t)]
+    lib.ss_workspace_status.restype = i32
+    lib.ss_workspace_status.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint32), vp]
     lib.ss_step.restype = i32
     lib.ss_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, vp]
     lib.ss_step_ex.restype = i32
@@ -114,14 +124,60 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _options(kernel=0, chunk_len=0, zoh=False, chunk_rows=0, split_parts=0, workspace=None,
+             split_wait_limit=0):
+    ws = None if workspace is None else workspace
+    return FwdOptions(int(kernel), int(chunk_len), DISC_ZOH if zoh else DISC_DT, int(chunk_rows),
+                      int(split_parts), None if ws is None else ws.data_ptr(),
+                      0 if ws is None else ws.numel() * ws.element_size(), int(split_wait_limit))
+
+
+def fwd_workspace_size(batch, seqlen, dim, dstate, dtype=torch.float32, kernel=0, chunk_len=0,
+                       zoh=False, chunk_rows=0, split_parts=0) -> int:
+    """Bytes of workspace (``ss_fwd_workspace_size``) a forward call with these sizes and
+    options uses on the current device (0: its plan does not split the sequences)."""
+    opt = _options(kernel, chunk_len, zoh, chunk_rows, split_parts)
+    out = ctypes.c_size_t(0)
+    dt = BF16 if dtype == torch.bfloat16 else F32
+    rc = load_library().ss_fwd_workspace_size(batch, seqlen, dim, dstate, dt, ctypes.byref(opt),
+                                              ctypes.byref(out))
+    if rc != 0:
+        raise SSError(rc, "ss_fwd_workspace_size")
+    return int(out.value)
+
+
+def workspace_status(workspace, stream=None):
+    """``ss_workspace_status``: (status, give-ups) of the most recent split call that used
+    this workspace; synchronises the stream. status is 0 or SS_ERR_SPLIT_WAIT (9)."""
+    n = ctypes.c_uint32(0)
+    rc = load_library().ss_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            ctypes.byref(n), _stream(workspace.device, stream))
+    if rc not in (0, SS_ERR_SPLIT_WAIT):
+        raise SSError(rc, "ss_workspace_status")
+    return rc, int(n.value)
+
+
+def _fwd_workspace(workspace, dev, batch, L, dim, N, dtype, **opt):
+    """The workspace tensor of a forward call: the given one, none (False), or, for None, a
+    new uint8 device tensor of the size the library asks for (None when it needs none)."""
+    if workspace is False:
+        return None
+    if workspace is not None:
+        _check(workspace, "workspace", dev, torch.uint8)
+        return workspace
+    need = fwd_workspace_size(batch, L, dim, N, dtype, **opt)
+    return torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
+
+
 def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=None,
         last_state=None, return_last_state=True, stream=None, kernel=0, chunk_len=0, h0=None,
-        zoh=False, chunk_rows=0, split_parts=0):
-    """Selective-scan forward (``ss_fwd``; ``ss_fwd_ex`` when h0, kernel, chunk_len, chunk_rows,
-    split_parts or zoh are given). u, delta, z: (batch, L, dim); B, C: (batch, L, N); A: (dim, N) fp32; D,
-    delta_bias: (dim,) fp32; h0: (batch, dim, N) fp32 initial state or None; zoh: exact
-    zero-order-hold input term. Returns y (fp32) and, unless return_last_state is False,
-    the final state (batch, dim, N) fp32."""
+        zoh=False, chunk_rows=0, split_parts=0, workspace=None, split_wait_limit=0):
+    """Selective-scan forward (``ss_fwd_ex``). u, delta, z: (batch, L, dim); B, C: (batch, L,
+    N); A: (dim, N) fp32; D, delta_bias: (dim,) fp32; h0: (batch, dim, N) fp32 initial state
+    or None; zoh: exact zero-order-hold input term. workspace: a uint8 device tensor for the
+    sequence split, False for none (no split), or None to allocate one of the size
+    ``fwd_workspace_size`` gives for this call. Returns y (fp32) and, unless
+    return_last_state is False, the final state (batch, dim, N) fp32."""
     dev = u.device
     batch, L, dim = u.shape
     N = A.shape[1]
@@ -142,23 +198,45 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=Non
         last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     _check(last_state, "last_state", dev, torch.float32, (batch, dim, N))
     lib = load_library()
-    head = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-            int(bool(softplus)), _ptr(y), _ptr(last_state))
-    tail = (batch, L, dim, N, dt)
-    if kernel or chunk_len or chunk_rows or split_parts or h0 is not None or zoh:
-        opt = FwdOptions(int(kernel), int(chunk_len), DISC_ZOH if zoh else DISC_DT, int(chunk_rows),
-                         int(split_parts))
-        rc = lib.ss_fwd_ex(*head, _ptr(h0), *tail, ctypes.byref(opt), _stream(dev, stream))
-    else:
-        rc = lib.ss_fwd(*head, *tail, _stream(dev, stream))
+    plan = dict(kernel=kernel, chunk_len=chunk_len, zoh=zoh, chunk_rows=chunk_rows, split_parts=split_parts)
+    ws = _fwd_workspace(workspace, dev, batch, L, dim, N, u.dtype, **plan)
+    opt = _options(workspace=ws, split_wait_limit=split_wait_limit, **plan)
+    rc = lib.ss_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                       int(bool(softplus)), _ptr(y), _ptr(last_state), _ptr(h0), batch, L, dim, N, dt,
+                       ctypes.byref(opt), _stream(dev, stream))
     if rc != 0:
         raise SSError(rc, "ss_fwd")
     return (y, last_state) if return_last_state else y
 
 
+def fwd_plain(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=None,
+              last_state=None, stream=None):
+    """``ss_fwd`` itself (no options, no workspace, never split). Returns (y, last_state)."""
+    dev = u.device
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    dt = _in_dtype(u, delta, B, C, z)
+    for t, name in ((u, "u"), (delta, "delta"), (z, "z"), (B, "B"), (C, "C")):
+        _check(t, name, dev)
+    _check(A, "A", dev, torch.float32, (dim, N))
+    if y is None:
+        y = torch.empty((batch, L, dim), dtype=torch.float32, device=dev)
+    if last_state is None:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _check(y, "y", dev, torch.float32, (batch, L, dim))
+    _check(last_state, "last_state", dev, torch.float32, (batch, dim, N))
+    rc = load_library().ss_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(delta_bias), int(bool(softplus)), _ptr(y), _ptr(last_state), batch, L,
+                               dim, N, dt, _stream(dev, stream))
+    if rc != 0:
+        raise SSError(rc, "ss_fwd")
+    return y, last_state
+
+
 def fwd_conv(x, conv_w, delta, A, B, C, conv_b=None, conv_state=None, D=None, z=None,
              delta_bias=None, softplus=True, y=None, last_state=None, h0=None, u_out=None,
-             stream=None, kernel=0, chunk_len=0, zoh=False, chunk_rows=0, split_parts=0):
+             stream=None, kernel=0, chunk_len=0, zoh=False, chunk_rows=0, split_parts=0,
+             workspace=None):
     """Forward with the fused prologue (``ss_fwd_conv``): u = silu(causal depthwise
     conv1d(x) + conv_b), then the scan of ``fwd`` on it. x: (batch, L, dim); conv_w
     (dim, K) fp32, K <= 4; conv_b (dim,) fp32 or None; conv_state (batch, dim, K-1) fp32 or
@@ -195,8 +273,9 @@ def fwd_conv(x, conv_w, delta, A, B, C, conv_b=None, conv_state=None, D=None, z=
     if not want_u:
         u_out = None
     _check(u_out, "u_out", dev, torch.float32, (batch, L, dim))
-    opt = FwdOptions(int(kernel), int(chunk_len), DISC_ZOH if zoh else DISC_DT, int(chunk_rows),
-                     int(split_parts))
+    plan = dict(kernel=kernel, chunk_len=chunk_len, zoh=zoh, chunk_rows=chunk_rows, split_parts=split_parts)
+    ws = _fwd_workspace(workspace, dev, batch, L, dim, N, x.dtype, **plan)
+    opt = _options(workspace=ws, **plan)
     rc = load_library().ss_fwd_conv(_ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state), K, _ptr(delta),
                                     _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                                     int(bool(softplus)), _ptr(y), _ptr(last_state), _ptr(h0), _ptr(u_out),

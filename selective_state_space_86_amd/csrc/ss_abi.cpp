@@ -5,11 +5,10 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
-#include <mutex>
-#include <vector>
 
 #include "../../include/ss.h"
 #include "ss_kernels.h"
+#include "ss_split.h"
 
 namespace {
 
@@ -40,57 +39,6 @@ int check_device(int* cus) {
   return ok ? SS_OK : SS_ERR_DEVICE;
 }
 
-// Split workspaces of the chunked forward, one per (device, stream) that used the split,
-// kept until the process ends. A kernel leaves its workspace zeroed, and kernels on one
-// stream run in order, so a stream's calls can share one buffer.
-struct SplitWs {
-  int dev;
-  hipStream_t stream;
-  uint32_t* ptr;
-  int64_t cap;  // published-state slots
-};
-std::mutex g_split_mu;
-std::vector<SplitWs> g_split_ws;
-
-// The split workspace of the current device and stream s with at least `items` slots (its
-// capacity in *cap), or null on a HIP error. A new or grown buffer is cleared by a kernel on
-// s, ahead of the caller's; a grown one gets twice the old capacity at least. `lock` is
-// left holding the cache's mutex: the caller enqueues its kernel before releasing it, so
-// another host thread on the same stream cannot free the buffer (by growing it) first.
-uint32_t* split_workspace(int64_t items, hipStream_t s, int64_t* cap, std::unique_lock<std::mutex>& lock) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  lock = std::unique_lock<std::mutex>(g_split_mu);
-  SplitWs* w = nullptr;
-  for (auto& e : g_split_ws)
-    if (e.dev == dev && e.stream == s) w = &e;
-  if (w && w->cap >= items) {
-    *cap = w->cap;
-    return w->ptr;
-  }
-  int64_t want = items;
-  if (w) {  // grow: the old buffer may still be in use by work queued on s
-    if (hipStreamSynchronize(s) != hipSuccess || hipFree(w->ptr) != hipSuccess) return nullptr;
-    want = std::max(items, 2 * w->cap);
-    w->ptr = nullptr;
-    w->cap = 0;
-  } else {
-    g_split_ws.push_back(SplitWs{dev, s, nullptr, 0});
-    w = &g_split_ws.back();
-  }
-  const size_t bytes = ss::fwd_split_ws_bytes(want);
-  void* p = nullptr;
-  if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
-  if (ss::fwd_split_ws_clear(static_cast<uint32_t*>(p), bytes, s) != hipSuccess) {
-    (void)hipFree(p);
-    return nullptr;
-  }
-  w->ptr = static_cast<uint32_t*>(p);
-  w->cap = want;
-  *cap = want;
-  return w->ptr;
-}
-
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int elem_size(int dtype) { return dtype == SS_DTYPE_BF16 ? 2 : 4; }
@@ -116,13 +64,9 @@ struct ConvArgs {
   float* u_out;
 };
 
-int fwd_common(const void* u, const void* delta, const float* A, const void* B, const void* C,
-               const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
-               float* last_state, const float* h0, int64_t batch, int64_t seqlen, int64_t dim,
-               int64_t dstate, int in_dtype, const ss_fwd_options* opt, const ConvArgs& cv,
-               void* stream) {
-  // with seqlen == 0 no token is read or written: the per-token arrays may be NULL
-  if (!A || (seqlen != 0 && (!u || !delta || !B || !C || !y))) return SS_ERR_NULL_ARG;
+// Sizes and options of a forward call, validated without touching any pointer.
+int check_fwd_sizes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int in_dtype,
+                    const ss_fwd_options* opt) {
   if (in_dtype != SS_DTYPE_F32 && in_dtype != SS_DTYPE_BF16) return SS_ERR_BAD_DTYPE;
   if (batch < 1 || dim < 1 || dstate < 1 || seqlen < 0) return SS_ERR_BAD_SHAPE;
   if (dstate > SS_MAX_DSTATE) return SS_ERR_UNSUPPORTED_N;
@@ -135,38 +79,68 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
   const int disc = opt ? opt->discretization : SS_DISC_DT;
   const int rows = opt ? opt->chunk_rows : 0;
   const int split_parts = opt ? opt->split_parts : 0;
-  if (kernel < 0 || kernel > 3 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
+  if (kernel < 0 || kernel > 4 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
   if (split_parts < 0 || split_parts > 16) return SS_ERR_BAD_SHAPE;
   if (!(rows == 0 || rows == 16 || rows == 12 || rows == 32) || (rows == 12 && chunk == 8)) return SS_ERR_BAD_SHAPE;
   // (a tile of 32 rows of 8 tokens spans 256 tokens of the (.., dim) arrays from 32-bit offsets)
   if (rows == 32 && 256 * dim * 4 >= (1LL << 31)) return SS_ERR_BAD_SHAPE;
   if (disc != SS_DISC_DT && disc != SS_DISC_ZOH) return SS_ERR_BAD_SHAPE;
-  if (kernel == 2 && dstate != 16) return SS_ERR_UNSUPPORTED_N;
-  const size_t es = elem_size(in_dtype);
-  if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
-      (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
-      (delta_bias && !aligned(delta_bias, 4)) || !aligned(y, 4) ||
-      (last_state && !aligned(last_state, 4)) || (h0 && !aligned(h0, 4)) || !aligned(cv.conv_w, 4) ||
-      (cv.conv_b && !aligned(cv.conv_b, 4)) || (cv.conv_state && !aligned(cv.conv_state, 4)) ||
-      (cv.u_out && !aligned(cv.u_out, 4)))
-    return SS_ERR_MISALIGNED;
-  int cus = 0;
-  const int dv = check_device(&cus);
-  if (dv != SS_OK) return dv;
+  if ((kernel == 2 || kernel == 4) && dstate != 16) return SS_ERR_UNSUPPORTED_N;
+  return SS_OK;
+}
 
-  ss::FwdArgs a{u, delta, A, B, C, D, z, delta_bias, y, last_state,
-                batch, seqlen, dim, dstate, in_dtype, softplus_flag ? 1 : 0, h0,
-                disc == SS_DISC_ZOH ? 1 : 0, static_cast<int>(cv.kconv), cv.conv_w, cv.conv_b,
-                cv.conv_state, cv.u_out};
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (kernel == 3 && seqlen > 0) {
-    if (!ss::fwd_state_supported(a)) return SS_ERR_BAD_SHAPE;
-    const hipError_t es = ss::fwd_state(a, s);
-    return es == hipSuccess ? SS_OK : SS_ERR_HIP;
+// The kernel a forward call runs, and for the time-chunked kernel its tile plan and split.
+struct FwdPlan {
+  int kind;              // 1 sequential, 2 time-chunked, 3 state-parallel, 4 phased time-chunked
+  ss::ChunkPlan chunk;   // kinds 2 and 4
+  int parts;             // kinds 2 and 4: sequence parts (1: none)
+  int64_t part_len;      // with parts > 1
+  size_t split_bytes;    // workspace the split needs (0: none)
+};
+
+// Plan a forward call (sizes validated) on a device with `cus` CUs. The time-chunked kernel
+// addresses a tile of R rows of TC tokens of the (.., dim) arrays from 32-bit offsets, so a
+// plan whose tile spans 2^31 bytes or more of fp32 rows is not taken (an explicit choice of
+// it is an error); the state-parallel kernel spans 16 tokens of the input rows.
+int plan_fwd(ss::FwdArgs& a, const ss_fwd_options* opt, int cus, FwdPlan* pl) {
+  const int kernel = opt ? opt->kernel : 0;
+  const int chunk = opt ? opt->chunk_len : 0;
+  const int rows = opt ? opt->chunk_rows : 0;
+  const int split_parts = opt ? opt->split_parts : 0;
+  const int64_t groups = a.batch * ((a.dim + 15) / 16);
+  const int64_t es = elem_size(a.dtype);
+  auto tile_fits = [&](const ss::ChunkPlan& p) {
+    return static_cast<int64_t>(p.rows) * p.chunk_len * a.dim * 4 < (1LL << 31);
+  };
+  const bool state_fits = 16 * a.dim * es < (1LL << 31);
+  *pl = FwdPlan{1, {4, 16}, 1, 0, 0};
+  if (a.seqlen == 0) return SS_OK;  // the sequential kernel writes the final state (h0 or zero)
+  if (kernel == 3) {
+    if (!ss::fwd_state_supported(a) || !state_fits) return SS_ERR_BAD_SHAPE;
+    pl->kind = 3;
+    return SS_OK;
+  }
+  if (kernel == 1) return SS_OK;
+  auto split_plan = [&](const ss::ChunkPlan& plan) {
+    int parts = split_parts == 0 ? ss::fwd_split_parts(a, plan, cus) : split_parts;
+    if (parts > 1) {  // whole tiles per part: a short sequence gets fewer parts
+      pl->part_len = ss::fwd_split_part_len(a.seqlen, plan, parts);
+      parts = static_cast<int>((a.seqlen + pl->part_len - 1) / pl->part_len);
+      if (groups * parts > 0x7fffffffLL) parts = 1;
+    }
+    pl->parts = parts;
+    if (parts > 1) pl->split_bytes = ss::split::region_bytes(ss::fwd_split_items(groups, parts));
+  };
+  if (kernel == 4) {
+    if (!ss::fwd_phased_supported(a)) return SS_ERR_BAD_SHAPE;
+    if (!tile_fits(ss::fwd_phased_plan())) return SS_ERR_BAD_SHAPE;
+    pl->kind = 4;
+    pl->chunk = ss::fwd_phased_plan();
+    split_plan(pl->chunk);
+    return SS_OK;
   }
   const bool chunked = kernel == 2 || (kernel == 0 && ss::fwd_chunked_supported(a));
-  if (chunked && seqlen > 0) {
+  if (chunked) {
     // explicit choices override the automatic plan; 12 rows exist only with 4-token chunks
     ss::ChunkPlan plan = ss::fwd_chunked_pick(a, cus);
     if (chunk != 0) plan.chunk_len = chunk;
@@ -175,24 +149,82 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
       if (rows == 12) plan.chunk_len = 4;  // rows asked for, chunk length automatic
       else plan.rows = 16;                 // chunk length 8 asked for, rows automatic
     }
-    int parts = split_parts == 0 ? ss::fwd_split_parts(a, plan, cus) : split_parts;
-    const int64_t groups = batch * ((dim + 15) / 16);
-    if (parts > 1) {  // whole tiles per part: a short sequence gets fewer parts
-      a.part_len = ss::fwd_split_part_len(seqlen, plan, parts);
-      parts = static_cast<int>((seqlen + a.part_len - 1) / a.part_len);
-      if (groups * parts > 0x7fffffffLL) parts = 1;
+    if (!tile_fits(plan)) {
+      if (kernel == 2 && (chunk != 0 || rows != 0)) return SS_ERR_BAD_SHAPE;
+      plan = ss::ChunkPlan{4, 16};
+      if (!tile_fits(plan)) {
+        if (kernel == 2) return SS_ERR_BAD_SHAPE;
+        return SS_OK;  // the sequential kernel, which takes 64-bit addresses
+      }
     }
-    std::unique_lock<std::mutex> ws_lock;  // (held until the kernel is enqueued)
-    if (parts > 1) {
-      a.split_ws = split_workspace(ss::fwd_split_items(groups, parts), s, &a.split_cap, ws_lock);
-      if (!a.split_ws) return SS_ERR_HIP;
-      a.parts = parts;
+    pl->kind = 2;
+    pl->chunk = plan;
+    split_plan(plan);
+    return SS_OK;
+  }
+  if (kernel == 0 && ss::fwd_state_supported(a) && state_fits) pl->kind = 3;  // dstate != 16
+  return SS_OK;
+}
+
+// Bytes at the start of ss_bwd's workspace that hold the split region (header, flags and
+// states for up to ss::kBwdMaxParts parts of every channel group), rounded to 256 bytes.
+size_t bwd_split_region(int64_t batch, int64_t dim) {
+  const int64_t groups = batch * ((dim + 15) / 16);
+  return (ss::split::region_bytes(groups * (ss::kBwdMaxParts - 1)) + 255) / 256 * 256;
+}
+
+int fwd_common(const void* u, const void* delta, const float* A, const void* B, const void* C,
+               const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
+               float* last_state, const float* h0, int64_t batch, int64_t seqlen, int64_t dim,
+               int64_t dstate, int in_dtype, const ss_fwd_options* opt, const ConvArgs& cv,
+               void* stream) {
+  // with seqlen == 0 no token is read or written: the per-token arrays may be NULL
+  if (!A || (seqlen != 0 && (!u || !delta || !B || !C || !y))) return SS_ERR_NULL_ARG;
+  const int sv = check_fwd_sizes(batch, seqlen, dim, dstate, in_dtype, opt);
+  if (sv != SS_OK) return sv;
+  const size_t es = elem_size(in_dtype);
+  void* ws = opt ? opt->workspace : nullptr;
+  const size_t ws_bytes = opt ? opt->workspace_bytes : 0;
+  if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
+      (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+      (delta_bias && !aligned(delta_bias, 4)) || !aligned(y, 4) ||
+      (last_state && !aligned(last_state, 4)) || (h0 && !aligned(h0, 4)) || !aligned(cv.conv_w, 4) ||
+      (cv.conv_b && !aligned(cv.conv_b, 4)) || (cv.conv_state && !aligned(cv.conv_state, 4)) ||
+      (cv.u_out && !aligned(cv.u_out, 4)) || !aligned(ws, 16))
+    return SS_ERR_MISALIGNED;
+  int cus = 0;
+  const int dv = check_device(&cus);
+  if (dv != SS_OK) return dv;
+
+  ss::FwdArgs a{u, delta, A, B, C, D, z, delta_bias, y, last_state,
+                batch, seqlen, dim, dstate, in_dtype, softplus_flag ? 1 : 0, h0,
+                (opt && opt->discretization == SS_DISC_ZOH) ? 1 : 0, static_cast<int>(cv.kconv), cv.conv_w,
+                cv.conv_b, cv.conv_state, cv.u_out};
+  FwdPlan pl;
+  const int pv = plan_fwd(a, opt, cus, &pl);
+  if (pv != SS_OK) return pv;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (pl.kind == 2 || pl.kind == 4) {
+    if (pl.parts > 1 && (!ws || ws_bytes < pl.split_bytes)) {
+      // the split needs the caller's workspace: without one an explicit split is an error and
+      // the automatic plan runs unsplit
+      if (opt && opt->split_parts > 1) return SS_ERR_WORKSPACE;
+      pl.parts = 1;
     }
-    e = ss::fwd_chunked(a, plan, s);
-  } else if (kernel == 0 && ss::fwd_state_supported(a))
-    e = ss::fwd_state(a, s);  // dstate != 16
-  else
-    e = ss::fwd_seq(a, s);
+    if (pl.parts > 1) {
+      a.parts = pl.parts;
+      a.part_len = pl.part_len;
+      a.split_ws = static_cast<uint32_t*>(ws);
+      a.split_cap = ss::fwd_split_items(batch * ((dim + 15) / 16), pl.parts);
+      a.split_wait_limit = opt ? opt->split_wait_limit : 0;
+      e = ss::split::clear(a.split_ws, a.split_cap, s);
+      if (e != hipSuccess) return SS_ERR_HIP;
+    }
+    e = pl.kind == 4 ? ss::fwd_phased(a, s) : ss::fwd_chunked(a, pl.chunk, s);
+  } else {
+    e = pl.kind == 3 ? ss::fwd_state(a, s) : ss::fwd_seq(a, s);
+  }
   return e == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
@@ -212,7 +244,8 @@ const char* ss_status_string(int s) {
     case SS_ERR_MISALIGNED: return "a pointer is not aligned to its element size";
     case SS_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case SS_ERR_DEVICE: return "the current device is not a gfx950 GPU";
-    case SS_ERR_WORKSPACE: return "the workspace is NULL or smaller than ss_bwd_workspace_size()";
+    case SS_ERR_WORKSPACE: return "the workspace is NULL or smaller than the size query returns";
+    case SS_ERR_SPLIT_WAIT: return "a sequence-split hand-off wait gave up: the affected outputs are NaN";
     default: return "unknown status code";
   }
 }
@@ -242,6 +275,44 @@ int ss_fwd(const void* u, const void* delta, const float* A, const void* B, cons
            int in_dtype, void* stream) {
   return ss_fwd_ex(u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state, nullptr, batch,
                    seqlen, dim, dstate, in_dtype, nullptr, stream);
+}
+
+int ss_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int in_dtype,
+                          const ss_fwd_options* opt, size_t* bytes) {
+  if (!bytes) return SS_ERR_NULL_ARG;
+  *bytes = 0;
+  const int sv = check_fwd_sizes(batch, seqlen, dim, dstate, in_dtype, opt);
+  if (sv != SS_OK) return sv;
+  int cus = 0;
+  const int dv = check_device(&cus);
+  if (dv != SS_OK) return dv;
+  ss::FwdArgs a{};
+  a.batch = batch;
+  a.seqlen = seqlen;
+  a.dim = dim;
+  a.dstate = dstate;
+  a.dtype = in_dtype;
+  a.zoh = (opt && opt->discretization == SS_DISC_ZOH) ? 1 : 0;
+  FwdPlan pl;
+  const int pv = plan_fwd(a, opt, cus, &pl);
+  if (pv != SS_OK) return pv;
+  *bytes = (pl.kind == 2 || pl.kind == 4) && pl.parts > 1 ? pl.split_bytes : 0;
+  return SS_OK;
+}
+
+int ss_workspace_status(const void* workspace, size_t workspace_bytes, uint32_t* giveups, void* stream) {
+  if (giveups) *giveups = 0;
+  if (!workspace) return SS_ERR_NULL_ARG;
+  if (!aligned(workspace, 16)) return SS_ERR_MISALIGNED;
+  if (workspace_bytes < static_cast<size_t>(ss::split::kHeader) * 4) return SS_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t count = 0;
+  const uint32_t* word = static_cast<const uint32_t*>(workspace) + ss::split::kGiveUpWord;
+  if (hipMemcpyAsync(&count, word, sizeof(count), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return SS_ERR_HIP;
+  if (giveups) *giveups = count;
+  return count == 0 ? SS_OK : SS_ERR_SPLIT_WAIT;
 }
 
 int ss_step_ex(float* state, const void* u, const void* delta, const float* A, const void* B,
@@ -329,7 +400,7 @@ int ss_proj_conv(const void* x, const float* conv_w, const float* conv_b, const 
 size_t ss_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate) {
   if (batch < 1 || dim < 1 || dstate < 1 || seqlen < 0 || dstate > SS_MAX_DSTATE) return 0;
   if (!product_ok(batch, seqlen, dim) || !product_ok(batch, seqlen, 16 * dstate)) return 0;
-  return ss::bwd_workspace_bytes(batch, seqlen, dim, dstate);
+  return bwd_split_region(batch, dim) + ss::bwd_workspace_bytes(batch, seqlen, dim, dstate);
 }
 
 int ss_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -359,14 +430,15 @@ int ss_bwd(const void* u, const void* delta, const float* A, const void* B, cons
       (dz && !aligned(dz, 4)) || (ddelta_bias && !aligned(ddelta_bias, 4)) || (dh0 && !aligned(dh0, 4)) ||
       !aligned(workspace, 4))
     return SS_ERR_MISALIGNED;
-  const size_t need = ss::bwd_workspace_bytes(batch, seqlen, dim, dstate);
+  const size_t split_region = bwd_split_region(batch, dim);
+  const size_t need = split_region + ss::bwd_workspace_bytes(batch, seqlen, dim, dstate);
   if (!workspace || workspace_bytes < need) return SS_ERR_WORKSPACE;
   int cus = 0;
   const int dv = check_device(&cus);
   if (dv != SS_OK) return dv;
 
   const int64_t ntiles = seqlen > 0 ? (seqlen + ss::bwd_tile_tokens() - 1) / ss::bwd_tile_tokens() : 0;
-  float* ws = static_cast<float*>(workspace);
+  float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_region);
   float* ckpt = ws;
   float* part_bc = ckpt + batch * ntiles * ngroups * 16 * 16;
   float* part_ch = part_bc + 2 * batch * ngroups * seqlen * dstate;
@@ -379,11 +451,9 @@ int ss_bwd(const void* u, const void* delta, const float* A, const void* B, cons
   int parts = ss::bwd_split_parts(groups, a.rows, false, seqlen, cus);
   int ckpt_parts = ss::bwd_split_parts(groups, a.rows, true, seqlen, cus);
   if (groups * ss::kBwdMaxParts > 0x7fffffffLL) parts = ckpt_parts = 1;
-  std::unique_lock<std::mutex> ws_lock;  // (held until the kernels are enqueued)
-  if (parts > 1 || ckpt_parts > 1) {  // one workspace for both kernels, used one after the other
-    const int most = parts > ckpt_parts ? parts : ckpt_parts;
-    a.split_ws = split_workspace(groups * (most - 1), s, &a.split_cap, ws_lock);
-    if (!a.split_ws) return SS_ERR_HIP;
+  if (parts > 1 || ckpt_parts > 1) {  // one split region for both kernels, used one after the other
+    a.split_ws = static_cast<uint32_t*>(workspace);
+    a.split_cap = groups * (ss::kBwdMaxParts - 1);
   }
   if (parts > 1) {
     a.parts = parts;

@@ -399,7 +399,7 @@ __device__ __forceinline__ void work_item(const BwdArgs& a, bool reverse, uint32
   part = 0;
   if (SPLIT) {
     const int64_t groups = a.batch * a.ngroups;
-    if (threadIdx.x == 0) item_s = split::take(a.split_ws, groups, a.parts);
+    if (threadIdx.x == 0) item_s = split::take(a.split_ws, groups);
     __syncthreads();
     const uint32_t item = __builtin_amdgcn_readfirstlane(item_s);  // rank * groups + gi
     const int64_t rank = item / groups;
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(R * 16) void bwd_ckpt_kernel(BwdArgs a) {
   constexpr int kPer = 32 / CTC;  // chunks per checkpoint interval
   __shared__ float lds_p[R * kS];
   __shared__ float lds_h[R * kS];
-  __shared__ uint32_t item_s;
+  __shared__ uint32_t item_s, seen_s;
   int64_t gi, part;
   work_item<SPLIT>(a, false, item_s, gi, part);
   const Lane l = lane_at(a, gi);
@@ -441,10 +441,12 @@ __global__ __launch_bounds__(R * 16) void bwd_ckpt_kernel(BwdArgs a) {
   float carry = (a.h0 && part == 0 && l.k < N) ? a.h0[(l.b * a.dim + l.cc) * N + l.k] : 0.0f;
   if (SPLIT && part > 0) {  // start from the state the previous part ends with
     const int64_t slot = (part - 1) * groups + gi;
-    split::wait(a.split_ws, slot);
-    if (l.k < 16) carry = split::load_state(a.split_ws, a.split_cap, slot, l.k, l.i);
-    __syncthreads();  // every wave has seen the flag: clear it for the next kernel
-    if (threadIdx.x == 0) split::clear(a.split_ws, slot);
+    if (threadIdx.x == 0) seen_s = split::poll(a.split_ws, slot, a.split_wait_limit) ? 1u : 0u;
+    __syncthreads();  // (the state loads are issued after thread 0 has seen the flag)
+    // a wait that gave up leaves the state unknown: continue from NaN (counted in the header)
+    if (l.k < 16)
+      carry = __builtin_amdgcn_readfirstlane(seen_s) ? split::load_state(a.split_ws, a.split_cap, slot, l.k, l.i)
+                                                     : __builtin_nanf("");
   }
 
   // lane (k, i): tokens t0 + k*CTC + j of channel cc and B_t[i]; fixed 32-bit byte offsets
@@ -535,7 +537,7 @@ void bwd_chunked_kernel(BwdArgs a) {
   // [wave][dB or dC][row][n][lane] (R/4 x 2 x 4 x kS floats)
   __shared__ __attribute__((aligned(16))) float lds_eh[2][R * kS];
   __shared__ float lds_m[R * kS];  // chunk adjoint aggregates, then reverse carries
-  __shared__ uint32_t item_s;
+  __shared__ uint32_t item_s, seen_s;
   int64_t gi, part;
   work_item<SPLIT>(a, true, item_s, gi, part);
   const Lane l = lane_at(a, gi);
@@ -558,10 +560,11 @@ void bwd_chunked_kernel(BwdArgs a) {
                      ? a.dlast[(l.b * a.dim + l.c) * N + l.k] : 0.0f;
   if (SPLIT && part < a.parts - 1) {  // start from the adjoint the later part publishes
     const int64_t slot = part * groups + gi;
-    split::wait(a.split_ws, slot);
-    if (l.k < 16) rcarry = split::load_state(a.split_ws, a.split_cap, slot, l.k, l.i);
-    __syncthreads();  // every wave has seen the flag: clear it for the next kernel
-    if (threadIdx.x == 0) split::clear(a.split_ws, slot);
+    if (threadIdx.x == 0) seen_s = split::poll(a.split_ws, slot, a.split_wait_limit) ? 1u : 0u;
+    __syncthreads();  // (the state loads are issued after thread 0 has seen the flag)
+    if (l.k < 16)
+      rcarry = __builtin_amdgcn_readfirstlane(seen_s) ? split::load_state(a.split_ws, a.split_cap, slot, l.k, l.i)
+                                                      : __builtin_nanf("");
   }
   float dAacc[16];
 #pragma unroll
@@ -856,12 +859,16 @@ void launch_bwd_scans(const BwdArgs& a, hipStream_t s) {
   BwdArgs c = a;  // the checkpoint kernel runs its own parts
   c.parts = a.ckpt_parts;
   c.part_len = a.ckpt_part_len;
-  if (c.parts > 1)
+  // each split kernel starts from a cleared region header and flags (ss_split.h)
+  if (c.parts > 1) {
+    (void)split::clear(a.split_ws, a.split_cap, s);
     hipLaunchKernelGGL((bwd_ckpt_kernel<T, 8, R, true>), dim3(groups * c.parts), dim3(R * 16), 0, s, c);
-  else
+  } else {
     hipLaunchKernelGGL((bwd_ckpt_kernel<T, 8, R, false>), dim3(groups), dim3(R * 16), 0, s, c);
+  }
   const dim3 grid(groups * static_cast<unsigned>(a.parts > 1 ? a.parts : 1));
   if (a.parts > 1) {
+    (void)split::clear(a.split_ws, a.split_cap, s);
     if (a.z)
       hipLaunchKernelGGL((bwd_chunked_kernel<T, true, TC, R, true>), grid, dim3(R * 16), 0, s, a);
     else

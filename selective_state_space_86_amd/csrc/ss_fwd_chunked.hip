@@ -76,9 +76,9 @@ void fwd_chunked_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int64_t L = a.seqlen;
   int64_t gi = blockIdx.x, part = 0;  // work item: group index gi, sequence part
-  __shared__ uint32_t item_s;
+  __shared__ uint32_t item_s, seen_s;
   if (SPLIT) {
-    if (tid == 0) item_s = split::take(a.split_ws, groups, a.parts);  // part * groups + gi
+    if (tid == 0) item_s = split::take(a.split_ws, groups);  // part * groups + gi
     __syncthreads();
     const uint32_t item = __builtin_amdgcn_readfirstlane(item_s);  // (uniform: keep it in SGPRs)
     part = item / groups;
@@ -115,14 +115,15 @@ void fwd_chunked_kernel(FwdArgs a) {
   }
   if (SPLIT && part > 0) {  // start from the state the previous part of this group ends with
     const int64_t slot = (part - 1) * groups + gi;
-    split::wait(a.split_ws, slot);
+    if (tid == 0) seen_s = split::poll(a.split_ws, slot, a.split_wait_limit) ? 1u : 0u;
+    __syncthreads();  // (the state loads are issued after thread 0 has seen the flag)
+    const bool seen = __builtin_amdgcn_readfirstlane(seen_s) != 0u;
 #pragma unroll
     for (int m = 0; m < NOWN; ++m) {
       const int n = k + m * R;
-      if (n < 16) carry[m] = split::load_state(a.split_ws, a.split_cap, slot, n, i);
+      // a wait that gave up leaves the carry unknown: continue from NaN (reported in the header)
+      if (n < 16) carry[m] = seen ? split::load_state(a.split_ws, a.split_cap, slot, n, i) : __builtin_nanf("");
     }
-    __syncthreads();  // every wave has seen the flag: clear it for the next call
-    if (tid == 0) split::clear(a.split_ws, slot);
   }
   const uint32_t y_row = static_cast<uint32_t>(a.dim * 4);
   const uint32_t y_off = static_cast<uint32_t>(k * TC) * y_row + static_cast<uint32_t>(i * 4);
@@ -269,12 +270,6 @@ void fwd_chunked_kernel(FwdArgs a) {
   }
 }
 
-__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
-  for (int64_t j = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; j < n;
-       j += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    p[j] = 0u;
-}
-
 template <typename T, bool GATE, int TC, bool ZOH, int R>
 void launch_chunked_c(const FwdArgs& a, hipStream_t s) {
   const int64_t groups = a.batch * ((a.dim + 15) / 16);
@@ -383,11 +378,17 @@ int fwd_split_parts(const FwdArgs& a, ChunkPlan plan, int cus) {
 
 int64_t fwd_split_items(int64_t groups, int parts) { return groups * (parts - 1); }
 
-size_t fwd_split_ws_bytes(int64_t cap) { return split::ws_bytes(cap); }
+namespace {
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t j = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; j < n;
+       j += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[j] = 0u;
+}
+}  // namespace
 
-hipError_t fwd_split_ws_clear(uint32_t* ws, size_t bytes, hipStream_t s) {
-  const int64_t n = static_cast<int64_t>(bytes / 4);
-  const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 1024));
+hipError_t split::clear(uint32_t* ws, int64_t cap, hipStream_t s) {
+  const int64_t n = split::clear_words(cap);
+  const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 64));
   hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, s, ws, n);
   return hipGetLastError();
 }

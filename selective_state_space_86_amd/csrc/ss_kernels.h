@@ -38,9 +38,10 @@ struct FwdArgs {
   // publishes there (so the groups' work spreads evenly over the CUs)
   int parts;                // 0 or 1: one workgroup per channel group over the whole sequence
   int64_t part_len;         // tokens per part, a multiple of the tile; parts * part_len >= seqlen
-  uint32_t* split_ws;       // fwd_split_ws_bytes(split_cap) of device memory: the counter and
-                            // flags are zero before the call and zero again when it completes
+  uint32_t* split_ws;       // split::region_bytes(split_cap) of device memory whose header and
+                            // flags were cleared (split::clear) on the kernel's stream
   int64_t split_cap;        // published-state slots of split_ws, >= (batch * groups) * (parts - 1)
+  int split_wait_limit;     // polls before a hand-off wait gives up: 0 the default, < 0 none
 };
 
 // Validated arguments of one ss_step call.
@@ -104,6 +105,7 @@ struct BwdArgs {
   int64_t split_cap;
   int ckpt_parts;
   int64_t ckpt_part_len;
+  int split_wait_limit;     // as FwdArgs::split_wait_limit
 };
 
 constexpr int kBwdMaxParts = 8;  // sequence parts of the backward split at most
@@ -138,14 +140,16 @@ struct ChunkPlan {
   int rows;
 };
 hipError_t fwd_chunked(const FwdArgs& a, ChunkPlan plan, hipStream_t s);
+// The phased time-chunked forward (dstate 16, default input term, no conv prologue): 8-wave
+// workgroups of 32 chunks of 4 tokens; its tile plan for the split.
+bool fwd_phased_supported(const FwdArgs& a);
+ChunkPlan fwd_phased_plan();
+hipError_t fwd_phased(const FwdArgs& a, hipStream_t s);
 ChunkPlan fwd_chunked_pick(const FwdArgs& a, int cus);
 // Parts per sequence for the split (1: no split) and the bytes of its workspace.
 int fwd_split_parts(const FwdArgs& a, ChunkPlan plan, int cus);
 int64_t fwd_split_part_len(int64_t seqlen, ChunkPlan plan, int parts);
 int64_t fwd_split_items(int64_t groups, int parts);  // published states of one call
-size_t fwd_split_ws_bytes(int64_t cap);
-// Zero a fresh split workspace on stream s (a fill kernel, no memset node).
-hipError_t fwd_split_ws_clear(uint32_t* ws, size_t bytes, hipStream_t s);
 hipError_t proj(const ProjArgs& a, int cus, hipStream_t s);
 int proj_step_tiles(int64_t rank, int dtype);
 hipError_t step(const StepArgs& a, hipStream_t s);

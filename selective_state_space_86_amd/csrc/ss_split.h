@@ -8,8 +8,9 @@
 // the chain runs (part-major, first parts first). A part waits until its predecessor in the
 // chain has published the state it starts from. The predecessor always holds a smaller
 // counter value, so it was taken by a workgroup that is already running and whose own wait is
-// on an even earlier item: every wait ends. The wait is bounded all the same, and a wait that
-// hits the bound is counted in the workspace (it would leave a wrong carry).
+// on an even earlier item: every wait ends. The wait is bounded all the same. A wait that
+// reaches the bound is counted in the region's header and the waiting part continues from a
+// NaN state, so its outputs (and every later part's) are NaN rather than silently wrong.
 //
 // Queues: workgroup ids are dealt to the 8 XCDs round-robin, and neighbouring groups share
 // 128-byte lines of the (.., dim) arrays in an XCD's L2, so when the groups divide by 8 the
@@ -17,25 +18,20 @@
 // eighth of the groups (a contiguous slice, as the unsplit kernels give XCD x). Each queue
 // gets exactly as many workgroups as it has items, and an item's predecessor is in the same
 // queue with a smaller counter value; a workgroup's queue is a function of its id alone, so
-// results never depend on where it runs. (One queue for the whole chip scattered neighbouring
-// groups over the XCDs and ran 12% slower.)
+// results never depend on where it runs.
 //
 // Hand-off: agent-scope atomic loads and stores (coherent across the XCDs' separate L2s by
 // themselves) for the flags and the states; the producer waits until its state stores have
-// completed before it stores the flag, and the consumer loads the states only after it has
-// seen the flag. (Agent-scope acquire/release fences do the same with a write-back and an
-// invalidation of the XCD's whole L2 at every hand-off, which cost more than the split saved
-// on short parts.)
+// completed before it stores the flag; in the consumer, thread 0 polls the flag and the other
+// threads load the states only after the workgroup barrier that follows the poll.
 //
-// Workspace (32-bit words) of `cap` slots: the counter of queue x at word 32 x (x < 8), the
-// count of waits that hit the bound at word 255, then from word kHeader one flag per slot
-// (padded to 64 words), then the published states, 16 x 16 fp32 per slot ([state n][channel
-// i]). The state crossing the boundary after part q of group gi goes through slot
-// q * groups + gi. The layout depends on the capacity only, never on the call, so a flag word
-// is never a state word of another call. The last workgroup to take an item of a queue resets
-// its counter and every consumer resets the flag it waited on, so counters and flags are zero
-// again when a kernel ends (the states are left as they are): kernels on one stream can share
-// one workspace.
+// Region (32-bit words), owned by the caller, of `cap` slots: the counter of queue x at word
+// 32 x (x < 8), the count of waits that reached the bound at word kGiveUpWord, then from word
+// kHeader one flag per slot (padded to 64 words), then the published states, 16 x 16 fp32 per
+// slot ([state n][channel i]). The state crossing the boundary after part q of group gi goes
+// through slot q * groups + gi. Before every split launch the host enqueues clear() of the
+// header and the flags on the same stream, so no flag or count of an earlier call survives
+// into a later one, whatever that call did.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -45,47 +41,49 @@ namespace ss {
 namespace split {
 
 constexpr int64_t kHeader = 256;
-constexpr uint32_t kSpinLimit = 1u << 22;  // several seconds of polling
+constexpr int kGiveUpWord = 255;
+constexpr uint32_t kSpinLimit = 1u << 22;  // polls of ~8 x 64 cycles: about two seconds
 
 __host__ __device__ inline int64_t flag_words(int64_t cap) { return (cap + 63) / 64 * 64; }
-__host__ __device__ inline size_t ws_bytes(int64_t cap) {
+// bytes of a region with cap slots, and the words the clear before a launch zeroes
+__host__ __device__ inline size_t region_bytes(int64_t cap) {
   return static_cast<size_t>(kHeader + flag_words(cap) + cap * 256) * 4;
 }
+__host__ __device__ inline int64_t clear_words(int64_t cap) { return kHeader + flag_words(cap); }
 __device__ inline float* states(uint32_t* ws, int64_t cap) {
   return reinterpret_cast<float*>(ws + kHeader + flag_words(cap));
 }
 
 // Thread 0 only: take this workgroup's work item; returns part * groups + gi.
-__device__ inline uint32_t take(uint32_t* ws, int64_t groups, int parts) {
+__device__ inline uint32_t take(uint32_t* ws, int64_t groups) {
   const bool by_xcd = groups % 8 == 0;
   const uint32_t qx = by_xcd ? blockIdx.x % 8 : 0;
   const uint32_t slice = static_cast<uint32_t>(by_xcd ? groups / 8 : groups);  // groups per queue
-  uint32_t* counter = ws + 32 * qx;
-  const uint32_t t = atomicAdd(counter, 1u);
-  if (t == slice * static_cast<uint32_t>(parts) - 1)  // every item of the queue is taken
-    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t t = atomicAdd(ws + 32 * qx, 1u);
   return (t / slice) * static_cast<uint32_t>(groups) + qx * slice + t % slice;
 }
 
-// Every thread of the workgroup: wait until slot `slot` is published. Then each thread loads
-// its states with load_state(); afterwards (after a barrier) thread 0 calls clear().
-__device__ inline void wait(uint32_t* ws, int64_t slot) {
+// Thread 0 only: poll until slot `slot` is published, at most `limit` polls (limit < 0: do not
+// poll at all, a testing mode in which every wait gives up). Returns false when it gave up,
+// after counting that in the header.
+__device__ inline bool poll(uint32_t* ws, int64_t slot, int limit) {
   uint32_t* flag = ws + kHeader + slot;
-  uint32_t spins = 0;
-  while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-    if (++spins == kSpinLimit) {
-      if ((threadIdx.x & 63) == 0) atomicAdd(ws + 255, 1u);
-      break;
+  const uint32_t lim = limit > 0 ? static_cast<uint32_t>(limit) : kSpinLimit;
+  bool seen = false;
+  if (limit >= 0) {
+    for (uint32_t spins = 0; spins < lim; ++spins) {
+      if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+        seen = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
     }
-    __builtin_amdgcn_s_sleep(8);
   }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);  // (the state loads stay after the flag)
+  if (!seen) atomicAdd(ws + kGiveUpWord, 1u);
+  return seen;
 }
 __device__ inline float load_state(uint32_t* ws, int64_t cap, int64_t slot, int n, int i) {
   return __hip_atomic_load(states(ws, cap) + slot * 256 + n * 16 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void clear(uint32_t* ws, int64_t slot) {
-  __hip_atomic_store(ws + kHeader + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Every thread stores its states with store_state(), then all call finish_stores(); after a
@@ -102,6 +100,10 @@ __device__ inline void finish_stores() {
 __device__ inline void publish(uint32_t* ws, int64_t slot) {
   __hip_atomic_store(ws + kHeader + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Host: enqueue the zeroing of the header and flags of a region of cap slots on stream s (a
+// fill kernel, so a captured graph holds no memset node).
+hipError_t clear(uint32_t* ws, int64_t cap, hipStream_t s);
 
 }  // namespace split
 }  // namespace ss

@@ -36,8 +36,8 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss_abi_version() == _binding.ABI_VERSION == 9
-    for s in range(0, 9):
+    assert lib.ss_abi_version() == _binding.ABI_VERSION == 10
+    for s in range(0, 10):
         assert lib.ss_status_string(s)
     assert b"unknown" in lib.ss_status_string(99)
 
@@ -195,13 +195,18 @@ def test_bwd_workspace_too_small(lib):
 
 
 def test_bwd_workspace_size_formula(lib):
-    """Tile-start states (tiles of 32 tokens, channel groups of 16, 16 states), dB/dC partial
-    sums per channel group, and dA/dD/dbias partial sums per batch row and sequence part (at
-    most 8 parts)."""
+    """The split region first (a 256-word header, one flag per hand-off slot padded to 64,
+    and 16 x 16 fp32 per slot, for 7 slots per channel group: up to 8 parts; rounded up to
+    256 bytes), then the tile-start states (tiles of 32 tokens, channel groups of 16, 16
+    states), dB/dC partial sums per channel group, and dA/dD/dbias partial sums per batch row
+    and sequence part (at most 8 parts)."""
     batch, L, dim, N = 3, 100, 40, 5
     groups, tiles = 3, 4
+    slots = batch * groups * 7
+    region = 4 * (256 + (slots + 63) // 64 * 64 + slots * 256)
+    region = (region + 255) // 256 * 256
     floats = batch * tiles * groups * 16 * 16 + 2 * batch * groups * L * N + 8 * batch * groups * 16 * 18
-    assert lib.ss_bwd_workspace_size(batch, L, dim, N) == 4 * floats
+    assert lib.ss_bwd_workspace_size(batch, L, dim, N) == region + 4 * floats
     assert lib.ss_bwd_workspace_size(0, L, dim, N) == 0
     assert lib.ss_bwd_workspace_size(batch, L, dim, 17) == 0
 
@@ -272,3 +277,62 @@ def test_proj_conv_empty_sequence_reaches_the_device_query(lib):
     """With seqlen 0 every argument check passes (token arrays NULL); the answer is then the
     device query's (SS_OK on a gfx950, SS_ERR_HIP without a GPU, SS_ERR_DEVICE on another)."""
     assert proj_conv_call(lib, L=0, x=None, dr=None, B=None, C=None, cb=FAKE, cs=FAKE) in (0, 6, 7)
+
+
+def ws_size_call(lib, batch=1, L=4096, dim=5120, N=16, dtype=1, opt=None, out=True):
+    n = ctypes.c_size_t(12345)
+    rc = lib.ss_fwd_workspace_size(batch, L, dim, N, dtype, ctypes.byref(opt) if opt is not None else None,
+                                   ctypes.byref(n) if out else None)
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=False), 1), (dict(batch=0), 2), (dict(L=-1), 2), (dict(dim=0), 2), (dict(N=17), 4),
+    (dict(dtype=2), 3), (dict(opt=_binding.FwdOptions(0, 0, 0, 0, 17)), 2),
+    (dict(opt=_binding.FwdOptions(0, 5)), 2), (dict(opt=_binding.FwdOptions(2, 0, 0, 0, 0), N=8), 4),
+    (dict(opt=_binding.FwdOptions(0, 0, 3)), 2),
+])
+def test_fwd_workspace_size_validation(lib, kw, code):
+    """ss_fwd_workspace_size checks its output pointer, the sizes and the options before it
+    asks the device anything, and writes 0 on an error."""
+    rc, n = ws_size_call(lib, **kw)
+    assert rc == code
+    if kw.get("out", True):
+        assert n == 0
+
+
+def test_fwd_workspace_size_reaches_the_device_query(lib):
+    """Valid sizes pass every check; the answer is then the device's (SS_OK on a gfx950,
+    SS_ERR_HIP without a GPU, SS_ERR_DEVICE on another)."""
+    assert ws_size_call(lib)[0] in (0, 6, 7)
+
+
+def test_fwd_ex_split_needs_a_workspace(lib):
+    """An explicit split without a workspace is refused; a misaligned workspace too. (Both are
+    argument checks and need no GPU; a valid call reaches the device query.)"""
+    ws_opt = _binding.FwdOptions(2, 0, 0, 0, 4, FAKE + 8, 1 << 20, 0)
+    assert fwd_ex_call_opt(lib, ws_opt) == 5
+    ws_opt = _binding.FwdOptions(2, 0, 0, 0, 4, FAKE, 1 << 20, 0)
+    assert fwd_ex_call_opt(lib, ws_opt) in (0, 6, 7)
+
+
+def fwd_ex_call_opt(lib, opt, **kw):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, sp=1, y=FAKE,
+             st=None, h0=None, batch=1, L=4, dim=8, N=16, dtype=0)
+    a.update(kw)
+    return lib.ss_fwd_ex(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
+                         a["y"], a["st"], a["h0"], a["batch"], a["L"], a["dim"], a["N"], a["dtype"],
+                         ctypes.byref(opt), None)
+
+
+@pytest.mark.parametrize("ws,nbytes,code", [(None, 4096, 1), (FAKE + 4, 4096, 5), (FAKE, 1000, 8)])
+def test_workspace_status_validation(lib, ws, nbytes, code):
+    """ss_workspace_status: NULL, misaligned (16 bytes) and too-small (one 1 KiB header)
+    workspaces are refused before any device access; the give-up count is zeroed."""
+    n = ctypes.c_uint32(77)
+    assert lib.ss_workspace_status(ws, nbytes, ctypes.byref(n), None) == code
+    assert n.value == 0
+
+
+def test_status_string_of_the_split_wait(lib):
+    assert b"gave up" in lib.ss_status_string(9)

@@ -13,7 +13,8 @@ Checks: every gradient against the fp64 oracle's backward element by element (|e
 those of an unsplit call over a subset of the channels (du, ddelta, dz, dh0 bit for bit: the
 parts start on tile boundaries; dA, dD, ddelta_bias to rounding, as they are summed per
 part); initial state and final-state gradient; forward and backward split calls alternating
-on one stream (they share the stream's workspace).
+on one stream, the backward's workspace (whose split region both of its kernels use, one
+after the other) filled with garbage before every call.
 """
 import pytest
 import torch
@@ -86,22 +87,33 @@ def test_bwd_split_initial_state_and_final_state_gradient():
     _compare(g, _oracle(x, dy, True, h0=h0, dlast=dlast), pu.tol_of(x), "split h0/dlast")
 
 
-def test_forward_and_backward_splits_share_the_stream_workspace():
+def test_forward_and_backward_splits_with_dirty_workspaces():
     """Forward and backward split calls alternate on one stream (1.25 groups per CU: both
-    split); every call repeats the first one's bits."""
+    split), each with a persistent workspace filled with 0xff bytes before every call; every
+    call repeats the first one's bits and no hand-off wait gives up."""
+    import selective_state_space_86_amd as ss
+
     w = _shape(2000, "bf16", groups_per_cu=1.25, seed_name="m")
     x = inputs.make(w, seed=79, device=DEV)
     dy = _dy((w.batch, w.seqlen, w.dim), 80)
-    _announce("forward/backward splits alternating")
-    y0 = pu.gpu_fwd(x, True)
+    _announce("forward/backward splits alternating, dirty workspaces")
+    fws = torch.empty(ss.fwd_workspace_size(w.batch, w.seqlen, w.dim, 16, torch.bfloat16), dtype=torch.uint8,
+                      device=DEV)
+    bws = torch.empty(ss.bwd_workspace_size(w.batch, w.seqlen, w.dim, 16), dtype=torch.uint8, device=DEV)
+    assert fws.numel() > 0
+    y0 = pu.gpu_fwd(x, True, workspace=fws)
     g0 = _gpu(x, dy, True)
     y1 = pu.gpu_fwd(x, True, split_parts=1)
     torch.cuda.synchronize()
     assert torch.equal(y0[0], y1[0]) and torch.equal(y0[1], y1[1])
     for _ in range(3):
-        y = pu.gpu_fwd(x, True)
-        g = _gpu(x, dy, True)
+        fws.fill_(255)
+        bws.fill_(255)
+        y = pu.gpu_fwd(x, True, workspace=fws)
+        g = ss.bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"],
+                   delta_bias=x["delta_bias"], workspace=bws)
         torch.cuda.synchronize()
+        assert ss.workspace_status(fws) == (0, 0) and ss.workspace_status(bws) == (0, 0)
         assert torch.equal(y[0], y0[0]) and torch.equal(y[1], y0[1])
         for k in KEYS:
             if g[k] is not None:

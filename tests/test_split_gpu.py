@@ -6,8 +6,10 @@ part starts from the chunk state the previous part publishes (the associative co
 Checks: y and the final state against the fp64 oracle element by element (|err| <= tol *
 (1 + |ref|), tol 1e-4 fp32 / 2e-3 bf16), and bit-equality with the unsplit kernel of the same
 tile plan (the parts start on tile boundaries, so the split changes no arithmetic); with an
-initial state, the exact zero-order hold and the conv prologue; repeated calls, a workspace
-that grows, and two streams (the workspace is kept per stream and left zeroed by every call).
+initial state, the exact zero-order hold and the conv prologue; repeated calls, calls with
+different part counts on one caller-owned workspace, two streams, graph capture, a workspace
+full of garbage on entry, and the failure path of the bounded hand-off wait (forced from the
+host), which must be reported and leave every kernel ending normally.
 """
 import pytest
 import torch
@@ -98,9 +100,9 @@ def test_split_conv_prologue(chunk, rows, K):
 
 
 def test_split_repeated_calls_growing_workspace_and_streams():
-    """The workspace must be zero again after every call: the same call three times in a row
-    (with a larger split in between, which grows the stream's workspace) gives the same bits,
-    and two streams running split calls at once each match the default stream."""
+    """The same call three times in a row (with a larger split in between) gives the same
+    bits, and two streams running split calls at once (each call with its own workspace from
+    the binding) each match the default stream."""
     xa = inputs.make(_workload(2, 800, 48, "f32", "a"), seed=25, device=DEV)
     xb = inputs.make(_workload(3, 2000, 200, "bf16", "b"), seed=26, device=DEV)
     kw = dict(kernel=2, chunk_len=4, chunk_rows=16)
@@ -130,18 +132,89 @@ def test_split_repeated_calls_growing_workspace_and_streams():
 
 @pytest.mark.parametrize("dim", [200, 256])
 def test_split_part_counts_in_sequence_share_the_workspace(dim):
-    """Calls with different part counts on one stream share its workspace: the flags of one
-    call must never sit where another call left its published states (a layout that moved
-    with the part count once gave a call with 3 parts after one with 2 stale 'published'
-    flags). Every call equals the unsplit kernel bit for bit."""
+    """Calls with different part counts share one caller-owned workspace (sized for the
+    largest): whatever one call left in it (published flags and states) must not reach the
+    next. Every call equals the unsplit kernel bit for bit and reports no give-up."""
     x = inputs.make(_workload(3, 2000, dim, "bf16", "q"), seed=26, device=DEV)
     kw = dict(kernel=2, chunk_len=4, chunk_rows=16)
     _announce(f"part counts in sequence dim={dim}")
     ref = pu.gpu_fwd(x, True, split_parts=1, **kw)
+    need = max(ss.fwd_workspace_size(3, 2000, dim, 16, torch.bfloat16, split_parts=p, **kw) for p in (2, 16))
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
     for parts in (16, 2, 3, 5, 8, 2, 4, 3, 7, 16, 6):
-        got = pu.gpu_fwd(x, True, split_parts=parts, **kw)
+        got = pu.gpu_fwd(x, True, split_parts=parts, workspace=ws, **kw)
         torch.cuda.synchronize()
         assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), f"parts={parts}"
+        assert ss.workspace_status(ws) == (0, 0)
+
+
+def test_split_with_a_dirty_caller_workspace():
+    """The workspace's contents on entry do not matter: filled with 0xff bytes (every flag
+    'published', every counter huge) before each call, the split still equals the unsplit
+    kernel bit for bit (the call clears what must start at zero on its stream)."""
+    x = inputs.make(_workload(2, 3000, 96, "f32", "d"), seed=33, device=DEV)
+    kw = dict(kernel=2, chunk_len=4, chunk_rows=16)
+    _announce("dirty workspace")
+    ref = pu.gpu_fwd(x, True, split_parts=1, **kw)
+    need = ss.fwd_workspace_size(2, 3000, 96, 16, torch.float32, split_parts=5, **kw)
+    assert need > 0
+    ws = torch.empty(need + 100, dtype=torch.uint8, device=DEV)
+    for parts in (5, 3):
+        ws.fill_(255)
+        got = pu.gpu_fwd(x, True, split_parts=parts, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), f"parts={parts}"
+        assert ss.workspace_status(ws) == (0, 0)
+
+
+@pytest.mark.parametrize("chunk,rows", [(4, 16), (8, 32)])
+def test_split_wait_give_up_is_reported(chunk, rows):
+    """The bounded hand-off wait's failure path, forced from the host (split_wait_limit < 0:
+    every wait gives up at once, without reading the flag). Every kernel still ends; the
+    status call reports SS_ERR_SPLIT_WAIT with one give-up per part after the first of every
+    channel group; the first part's outputs equal the unsplit result and every later part's
+    outputs and the final state are NaN (never silently wrong). A normal call on the same
+    workspace afterwards reports no give-up and equals the unsplit kernel bit for bit."""
+    batch, L, dim, parts = 2, 1536, 40, 3
+    x = inputs.make(_workload(batch, L, dim, "f32", "w"), seed=34, device=DEV)
+    kw = dict(kernel=2, chunk_len=chunk, chunk_rows=rows)
+    _announce(f"give-up chunk={chunk} rows={rows}")
+    ref = pu.gpu_fwd(x, True, split_parts=1, **kw)
+    need = ss.fwd_workspace_size(batch, L, dim, 16, torch.float32, split_parts=parts, **kw)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    got = pu.gpu_fwd(x, True, split_parts=parts, workspace=ws, split_wait_limit=-1, **kw)
+    torch.cuda.synchronize()
+    groups = batch * ((dim + 15) // 16)
+    rc, n = ss.workspace_status(ws)
+    assert rc == 9 and n == groups * (parts - 1)
+    tile = rows * chunk
+    part_len = -(-(-(-L // parts)) // tile) * tile
+    assert torch.equal(got[0][:, :part_len], ref[0][:, :part_len])
+    assert torch.isnan(got[0][:, part_len:]).all() and torch.isnan(got[1]).all()
+    again = pu.gpu_fwd(x, True, split_parts=parts, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    assert ss.workspace_status(ws) == (0, 0)
+    assert torch.equal(again[0], ref[0]) and torch.equal(again[1], ref[1])
+
+
+def test_explicit_split_needs_a_workspace_and_plain_fwd_never_splits():
+    """An explicit split without a workspace is refused (SS_ERR_WORKSPACE, nothing written);
+    ss_fwd (no options, no workspace) and the automatic plan without a workspace run unsplit
+    and equal the split result bit for bit at the 3B long-context channel count."""
+    w = inputs.WORKLOADS["mamba3b-long"].replace(name="mamba3b-L4100", seqlen=4100)
+    x = inputs.make(w, seed=35, device=DEV)
+    _announce("explicit split without workspace / ss_fwd")
+    with pytest.raises(ss.SSError) as e:
+        pu.gpu_fwd(x, True, split_parts=4, workspace=False)
+    assert e.value.status == 8
+    auto = pu.gpu_fwd(x, True)  # (the binding gives the automatic plan its workspace)
+    none = pu.gpu_fwd(x, True, workspace=False)
+    plain = ss.fwd_plain(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                         delta_bias=x["delta_bias"])
+    torch.cuda.synchronize()
+    assert ss.fwd_workspace_size(1, 4100, 5120, 16, torch.bfloat16) > 0
+    for got in (none, plain):
+        assert torch.equal(got[0], auto[0]) and torch.equal(got[1], auto[1])
 
 
 def test_automatic_split_at_3b_shape_equals_unsplit_sampled():
@@ -158,25 +231,26 @@ def test_automatic_split_at_3b_shape_equals_unsplit_sampled():
 
 
 def test_split_in_a_captured_graph():
-    """A split call captured in a HIP graph and replayed: the counters and flags are zero
-    again after every run, so every replay (with eager split calls on another stream in
-    between) gives the eager result. The capture stream's workspace is allocated by a call
-    on that stream before the capture (the first split call on a stream allocates)."""
+    """A split call captured in a HIP graph and replayed: the call's clear of the workspace
+    header is a kernel node, so every replay (with eager split calls using the same
+    workspace in between) gives the eager result."""
     x = inputs.make(_workload(1, 3000, 256, "bf16", "g"), seed=28, device=DEV)
     kw = dict(kernel=2, chunk_len=4, chunk_rows=16)
     _announce("graph capture")
     ref = pu.gpu_fwd(x, True, split_parts=1, **kw)
     y = torch.empty_like(ref[0])
     st = torch.empty_like(ref[1])
+    ws = torch.empty(ss.fwd_workspace_size(1, 3000, 256, 16, torch.bfloat16, split_parts=4, **kw),
+                     dtype=torch.uint8, device=DEV)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        pu.gpu_fwd(x, True, split_parts=4, y=y, last_state=st, **kw)
+        pu.gpu_fwd(x, True, split_parts=4, y=y, last_state=st, workspace=ws, **kw)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        pu.gpu_fwd(x, True, split_parts=4, y=y, last_state=st, **kw)
+        pu.gpu_fwd(x, True, split_parts=4, y=y, last_state=st, workspace=ws, **kw)
     torch.cuda.synchronize()
     for _ in range(4):
         y.fill_(7.0)
@@ -185,16 +259,14 @@ def test_split_in_a_captured_graph():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, ref[0]) and torch.equal(st, ref[1])
-        other = pu.gpu_fwd(x, True, split_parts=3, **kw)
+        other = pu.gpu_fwd(x, True, split_parts=3, workspace=ws, **kw)
         torch.cuda.synchronize()
         assert torch.equal(other[0], ref[0])
 
 
 def test_split_from_several_host_threads():
-    """Split calls from four host threads: two share one stream (with part counts that grow its
-    workspace while the other thread's calls are queued on it), two have a stream each. The
-    library keeps the workspace cache locked until a call's kernel is enqueued, so a buffer is
-    never freed under a queued kernel; every result equals the unsplit one."""
+    """Split calls from four host threads: two share one stream, two have a stream each, every
+    call with its own workspace from the binding; every result equals the unsplit one."""
     import threading
 
     kw = dict(kernel=2, chunk_len=4, chunk_rows=16)
