@@ -111,12 +111,8 @@ typedef struct {
   int kernel;         /* 0: automatic; 1: one lane per channel, sequential in t (any dstate);
                          2: time-chunked (dstate == 16 only, else SS_ERR_UNSUPPORTED_N);
                          3: one lane per (channel, state), sequential in t (default input
-                            term, no conv prologue, else SS_ERR_BAD_SHAPE);
-                         4: time-chunked in phases (8-wave tiles of 32 chunks of 4 tokens;
-                            dstate == 16, else SS_ERR_UNSUPPORTED_N; default input term and no
-                            conv prologue, else SS_ERR_BAD_SHAPE; chunk_len and chunk_rows are
-                            ignored); automatic picks 2 for dstate == 16, else 3 when it
-                            applies, else 1 */
+                            term, no conv prologue, else SS_ERR_BAD_SHAPE); automatic picks
+                            2 for dstate == 16, else 3 when it applies, else 1 */
   int chunk_len;      /* tokens per lane and tile for kernel 2: 0 (automatic), 4 or 8 */
   int discretization; /* an ss_discretization value */
   int chunk_rows;     /* time chunks per workgroup tile for kernel 2: 0 (automatic), 16, 12 or

@@ -79,21 +79,21 @@ int check_fwd_sizes(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, 
   const int disc = opt ? opt->discretization : SS_DISC_DT;
   const int rows = opt ? opt->chunk_rows : 0;
   const int split_parts = opt ? opt->split_parts : 0;
-  if (kernel < 0 || kernel > 4 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
+  if (kernel < 0 || kernel > 3 || !(chunk == 0 || chunk == 4 || chunk == 8)) return SS_ERR_BAD_SHAPE;
   if (split_parts < 0 || split_parts > 16) return SS_ERR_BAD_SHAPE;
   if (!(rows == 0 || rows == 16 || rows == 12 || rows == 32) || (rows == 12 && chunk == 8)) return SS_ERR_BAD_SHAPE;
   // (a tile of 32 rows of 8 tokens spans 256 tokens of the (.., dim) arrays from 32-bit offsets)
   if (rows == 32 && 256 * dim * 4 >= (1LL << 31)) return SS_ERR_BAD_SHAPE;
   if (disc != SS_DISC_DT && disc != SS_DISC_ZOH) return SS_ERR_BAD_SHAPE;
-  if ((kernel == 2 || kernel == 4) && dstate != 16) return SS_ERR_UNSUPPORTED_N;
+  if (kernel == 2 && dstate != 16) return SS_ERR_UNSUPPORTED_N;
   return SS_OK;
 }
 
 // The kernel a forward call runs, and for the time-chunked kernel its tile plan and split.
 struct FwdPlan {
-  int kind;              // 1 sequential, 2 time-chunked, 3 state-parallel, 4 phased time-chunked
-  ss::ChunkPlan chunk;   // kinds 2 and 4
-  int parts;             // kinds 2 and 4: sequence parts (1: none)
+  int kind;              // 1 sequential, 2 time-chunked, 3 state-parallel
+  ss::ChunkPlan chunk;   // kind 2
+  int parts;             // kind 2: sequence parts (1: none)
   int64_t part_len;      // with parts > 1
   size_t split_bytes;    // workspace the split needs (0: none)
 };
@@ -131,14 +131,6 @@ int plan_fwd(ss::FwdArgs& a, const ss_fwd_options* opt, int cus, FwdPlan* pl) {
     pl->parts = parts;
     if (parts > 1) pl->split_bytes = ss::split::region_bytes(ss::fwd_split_items(groups, parts));
   };
-  if (kernel == 4) {
-    if (!ss::fwd_phased_supported(a)) return SS_ERR_BAD_SHAPE;
-    if (!tile_fits(ss::fwd_phased_plan())) return SS_ERR_BAD_SHAPE;
-    pl->kind = 4;
-    pl->chunk = ss::fwd_phased_plan();
-    split_plan(pl->chunk);
-    return SS_OK;
-  }
   const bool chunked = kernel == 2 || (kernel == 0 && ss::fwd_chunked_supported(a));
   if (chunked) {
     // explicit choices override the automatic plan; 12 rows exist only with 4-token chunks
@@ -205,7 +197,7 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
   if (pv != SS_OK) return pv;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (pl.kind == 2 || pl.kind == 4) {
+  if (pl.kind == 2) {
     if (pl.parts > 1 && (!ws || ws_bytes < pl.split_bytes)) {
       // the split needs the caller's workspace: without one an explicit split is an error and
       // the automatic plan runs unsplit
@@ -221,7 +213,7 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
       e = ss::split::clear(a.split_ws, a.split_cap, s);
       if (e != hipSuccess) return SS_ERR_HIP;
     }
-    e = pl.kind == 4 ? ss::fwd_phased(a, s) : ss::fwd_chunked(a, pl.chunk, s);
+    e = ss::fwd_chunked(a, pl.chunk, s);
   } else {
     e = pl.kind == 3 ? ss::fwd_state(a, s) : ss::fwd_seq(a, s);
   }
@@ -296,7 +288,7 @@ int ss_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
   FwdPlan pl;
   const int pv = plan_fwd(a, opt, cus, &pl);
   if (pv != SS_OK) return pv;
-  *bytes = (pl.kind == 2 || pl.kind == 4) && pl.parts > 1 ? pl.split_bytes : 0;
+  *bytes = pl.kind == 2 && pl.parts > 1 ? pl.split_bytes : 0;
   return SS_OK;
 }
 

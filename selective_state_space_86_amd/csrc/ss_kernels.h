@@ -140,11 +140,6 @@ struct ChunkPlan {
   int rows;
 };
 hipError_t fwd_chunked(const FwdArgs& a, ChunkPlan plan, hipStream_t s);
-// The phased time-chunked forward (dstate 16, default input term, no conv prologue): 8-wave
-// workgroups of 32 chunks of 4 tokens; its tile plan for the split.
-bool fwd_phased_supported(const FwdArgs& a);
-ChunkPlan fwd_phased_plan();
-hipError_t fwd_phased(const FwdArgs& a, hipStream_t s);
 ChunkPlan fwd_chunked_pick(const FwdArgs& a, int cus);
 // Parts per sequence for the split (1: no split) and the bytes of its workspace.
 int fwd_split_parts(const FwdArgs& a, ChunkPlan plan, int cus);
