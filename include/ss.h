@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 10
+#define SS_ABI_VERSION 11
 #define SS_MAX_DSTATE 16
 
 typedef enum {
@@ -185,6 +185,26 @@ int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, c
               const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
               float* last_state, const float* h0, int64_t batch, int64_t seqlen, int64_t dim,
               int64_t dstate, int in_dtype, const ss_fwd_options* opt, void* stream);
+
+/*
+ * ss_fwd_noalloc -- ss_fwd_ex for callers that cannot allocate device memory and have no
+ * workspace to give: code under graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments, results and errors as ss_fwd_ex, except that the sequence
+ * split takes its work queue, flags and hand-off states from a fixed array of
+ * SS_NOALLOC_SCRATCH_BYTES that the library holds in device memory on every device it runs
+ * on (from the first call on that device until the process ends); opt->workspace and
+ * workspace_bytes are ignored. Nothing is allocated or freed. The automatic plan splits only
+ * when the split fits the array (about 4000 hand-off slots of channel group x part after the
+ * first: 320 groups in 4 parts use 960); an explicit split_parts that does not fit returns
+ * SS_ERR_WORKSPACE. Every call on a device shares that device's array and first clears
+ * what must start at zero, on `stream`: calls that overlap on one device (on different
+ * streams, or from several host threads) race and must be ordered by the caller.
+ */
+#define SS_NOALLOC_SCRATCH_BYTES (4u << 20)
+int ss_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
+                   float* last_state, const float* h0, int64_t batch, int64_t seqlen, int64_t dim,
+                   int64_t dstate, int in_dtype, const ss_fwd_options* opt, void* stream);
 
 /*
  * ss_fwd_conv -- ss_fwd_ex with the block's prologue fused into the scan: the scan's input

@@ -12,8 +12,8 @@ _lib = None
 
 F32, BF16 = 0, 1
 DISC_DT, DISC_ZOH = 0, 1
-ABI_VERSION = 10
-EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_fwd_conv",
+ABI_VERSION = 11
+EXPORTS = ("ss_abi_version", "ss_status_string", "ss_fwd", "ss_fwd_ex", "ss_fwd_noalloc", "ss_fwd_conv",
            "ss_fwd_workspace_size", "ss_workspace_status", "ss_step", "ss_step_ex",
            "ss_bwd_workspace_size", "ss_bwd", "ss_proj", "ss_proj_conv")
 SS_ERR_SPLIT_WAIT = 9
@@ -60,6 +60,8 @@ def load_library():
     lib.ss_fwd_ex.restype = i32
     lib.ss_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i32,
                               ctypes.POINTER(FwdOptions), vp]
+    lib.ss_fwd_noalloc.restype = i32
+    lib.ss_fwd_noalloc.argtypes = lib.ss_fwd_ex.argtypes
     lib.ss_fwd_conv.restype = i32
     lib.ss_fwd_conv.argtypes = [vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                 i64, i64, i64, i64, i32, ctypes.POINTER(FwdOptions), vp]
@@ -207,6 +209,34 @@ def fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=Non
     if rc != 0:
         raise SSError(rc, "ss_fwd")
     return (y, last_state) if return_last_state else y
+
+
+def fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=None,
+                last_state=None, stream=None, kernel=0, chunk_len=0, h0=None, zoh=False, chunk_rows=0,
+                split_parts=0):
+    """``ss_fwd_noalloc``: ``fwd`` with the sequence split's scratch in the library's fixed
+    per-device array instead of a workspace (y and last_state must be given to allocate
+    nothing here either). Returns (y, last_state)."""
+    dev = u.device
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    dt = _in_dtype(u, delta, B, C, z)
+    for t, name in ((u, "u"), (delta, "delta"), (z, "z"), (B, "B"), (C, "C"), (h0, "h0")):
+        _check(t, name, dev)
+    _check(A, "A", dev, torch.float32, (dim, N))
+    if y is None:
+        y = torch.empty((batch, L, dim), dtype=torch.float32, device=dev)
+    if last_state is None:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    _check(y, "y", dev, torch.float32, (batch, L, dim))
+    _check(last_state, "last_state", dev, torch.float32, (batch, dim, N))
+    opt = _options(kernel, chunk_len, zoh, chunk_rows, split_parts)
+    rc = load_library().ss_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                       _ptr(delta_bias), int(bool(softplus)), _ptr(y), _ptr(last_state),
+                                       _ptr(h0), batch, L, dim, N, dt, ctypes.byref(opt), _stream(dev, stream))
+    if rc != 0:
+        raise SSError(rc, "ss_fwd_noalloc")
+    return y, last_state
 
 
 def fwd_plain(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, y=None,

@@ -10,6 +10,8 @@
 #include "ss_kernels.h"
 #include "ss_split.h"
 
+static_assert(ss::kNoallocScratchBytes == SS_NOALLOC_SCRATCH_BYTES, "the scratch size the header states");
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -169,14 +171,14 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
                const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
                float* last_state, const float* h0, int64_t batch, int64_t seqlen, int64_t dim,
                int64_t dstate, int in_dtype, const ss_fwd_options* opt, const ConvArgs& cv,
-               void* stream) {
+               void* stream, bool noalloc = false) {
   // with seqlen == 0 no token is read or written: the per-token arrays may be NULL
   if (!A || (seqlen != 0 && (!u || !delta || !B || !C || !y))) return SS_ERR_NULL_ARG;
   const int sv = check_fwd_sizes(batch, seqlen, dim, dstate, in_dtype, opt);
   if (sv != SS_OK) return sv;
   const size_t es = elem_size(in_dtype);
-  void* ws = opt ? opt->workspace : nullptr;
-  const size_t ws_bytes = opt ? opt->workspace_bytes : 0;
+  void* ws = (opt && !noalloc) ? opt->workspace : nullptr;
+  size_t ws_bytes = (opt && !noalloc) ? opt->workspace_bytes : 0;
   if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
       (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
       (delta_bias && !aligned(delta_bias, 4)) || !aligned(y, 4) ||
@@ -187,6 +189,12 @@ int fwd_common(const void* u, const void* delta, const float* A, const void* B, 
   int cus = 0;
   const int dv = check_device(&cus);
   if (dv != SS_OK) return dv;
+  if (noalloc) {  // the fixed per-device scratch array stands in for the workspace
+    uint32_t* p = nullptr;
+    if (ss::noalloc_scratch_ptr(&p) != hipSuccess) return SS_ERR_HIP;
+    ws = p;
+    ws_bytes = ss::kNoallocScratchBytes;
+  }
 
   ss::FwdArgs a{u, delta, A, B, C, D, z, delta_bias, y, last_state,
                 batch, seqlen, dim, dstate, in_dtype, softplus_flag ? 1 : 0, h0,
@@ -248,6 +256,14 @@ int ss_fwd_ex(const void* u, const void* delta, const float* A, const void* B, c
               int64_t dstate, int in_dtype, const ss_fwd_options* opt, void* stream) {
   return fwd_common(u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state, h0, batch, seqlen,
                     dim, dstate, in_dtype, opt, ConvArgs{0, nullptr, nullptr, nullptr, nullptr}, stream);
+}
+
+int ss_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, int softplus_flag, float* y,
+                   float* last_state, const float* h0, int64_t batch, int64_t seqlen, int64_t dim,
+                   int64_t dstate, int in_dtype, const ss_fwd_options* opt, void* stream) {
+  return fwd_common(u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state, h0, batch, seqlen,
+                    dim, dstate, in_dtype, opt, ConvArgs{0, nullptr, nullptr, nullptr, nullptr}, stream, true);
 }
 
 int ss_fwd_conv(const void* x, const float* conv_w, const float* conv_b, const float* conv_state,

@@ -36,6 +36,7 @@
 // inputs are requested right after the local pass, so the combine and the fix-up of the
 // current tile overlap their latency.
 #include <algorithm>
+#include <atomic>
 
 #include "ss_chunk_ops.h"
 #include "ss_split.h"
@@ -391,6 +392,34 @@ hipError_t split::clear(uint32_t* ws, int64_t cap, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 64));
   hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, s, ws, n);
   return hipGetLastError();
+}
+
+// The fixed scratch of ss_fwd_noalloc: one array per device (every GPU the library runs on
+// holds its own copy until the process ends). Host code never passes `noalloc_scratch`
+// itself to a kernel (in host code it names a host-side stand-in): it uses the device
+// address hipGetSymbolAddress gives, looked up once per device and kept.
+static __device__ __align__(256) uint32_t noalloc_scratch[kNoallocScratchBytes / 4];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<uint32_t*> g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t noalloc_scratch_ptr(uint32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  uint32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(noalloc_scratch));  // (the current device's copy)
+    if (e != hipSuccess) return e;
+    p = static_cast<uint32_t*>(q);
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t fwd_chunked(const FwdArgs& a, ChunkPlan plan, hipStream_t s) {

@@ -145,6 +145,10 @@ ChunkPlan fwd_chunked_pick(const FwdArgs& a, int cus);
 int fwd_split_parts(const FwdArgs& a, ChunkPlan plan, int cus);
 int64_t fwd_split_part_len(int64_t seqlen, ChunkPlan plan, int parts);
 int64_t fwd_split_items(int64_t groups, int parts);  // published states of one call
+// Bytes of the fixed per-device scratch array of the allocation-free forward entry point,
+// and its device address on the current device (looked up on first use, then kept).
+constexpr size_t kNoallocScratchBytes = size_t(4) << 20;
+hipError_t noalloc_scratch_ptr(uint32_t** out);
 hipError_t proj(const ProjArgs& a, int cus, hipStream_t s);
 int proj_step_tiles(int64_t rank, int dtype);
 hipError_t step(const StepArgs& a, hipStream_t s);

@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss_abi_version() == _binding.ABI_VERSION == 10
+    assert lib.ss_abi_version() == _binding.ABI_VERSION == 11
     for s in range(0, 10):
         assert lib.ss_status_string(s)
     assert b"unknown" in lib.ss_status_string(99)
@@ -336,3 +336,22 @@ def test_workspace_status_validation(lib, ws, nbytes, code):
 
 def test_status_string_of_the_split_wait(lib):
     assert b"gave up" in lib.ss_status_string(9)
+
+
+def noalloc_call(lib, opt=None, **kw):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, sp=1, y=FAKE,
+             st=None, h0=None, batch=1, L=4, dim=8, N=16, dtype=0)
+    a.update(kw)
+    return lib.ss_fwd_noalloc(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
+                              a["y"], a["st"], a["h0"], a["batch"], a["L"], a["dim"], a["N"], a["dtype"],
+                              ctypes.byref(opt) if opt is not None else None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(u=None), 1), (dict(A=None), 1), (dict(batch=0), 2), (dict(N=17), 4), (dict(dtype=2), 3),
+    (dict(y=FAKE + 2), 5), (dict(opt=_binding.FwdOptions(0, 0, 0, 0, 17)), 2),
+    (dict(opt=_binding.FwdOptions(9)), 2),
+])
+def test_fwd_noalloc_validation(lib, kw, code):
+    """ss_fwd_noalloc checks its arguments as ss_fwd_ex does, before any device work."""
+    assert noalloc_call(lib, **kw) == code
