@@ -470,9 +470,9 @@ __global__ __launch_bounds__(R * 16) void bwd_ckpt_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < CTC; ++j) {
       const uint32_t tt = static_cast<uint32_t>(min(l.k * CTC + j, last));  // past the end: last token
-      r.x[j] = chunk::ldb(tag, rd, tt * tok_row + col, 0);
-      r.u[j] = chunk::ldb(tag, ru, tt * tok_row + col, 0);
-      r.b[j] = chunk::ldb(tag, rb, bcol == 0x7fffffffu ? bcol : tt * bc_row + bcol, 0);
+      r.x[j] = chunk::ldf(tag, rd, tt * tok_row + col, 0);
+      r.u[j] = chunk::ldf(tag, ru, tt * tok_row + col, 0);
+      r.b[j] = chunk::ldf(tag, rb, bcol == 0x7fffffffu ? bcol : tt * bc_row + bcol, 0);
     }
   };
   In cur, nxt;

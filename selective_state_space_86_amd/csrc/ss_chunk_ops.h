@@ -54,6 +54,28 @@ __device__ __forceinline__ void local_step(float (&h)[16], float (&e)[16], const
       : SS_OPS16(a, "v"), [dt] "v"(dt), [du] "v"(du), [vb] "v"(vb), [vc] "v"(vc));
 }
 
+// The first token of a chunk, whose state before it is zero: h[n] = (dt u) B_t[n] with no
+// multiply-add, y += C_t[n] h[n], and the decays abar[n] = 2^(dt A'[n]) stored for the chunk
+// aggregate and the fix-up (3 VALU + 1 transcendental per state; none of the exps is read
+// here). Each h is read by its DPP fmac 2 instructions after the multiply that wrote it
+// (as a plain operand: only vb and vc are read through DPP).
+#define SS_UPD0(n)                                                           \
+  "v_mul_f32_dpp %[h" #n "], %[vb], %[du]" SS_DPP_ROW(n)                     \
+  "v_mul_f32 %[x], %[dt], %[a" #n "]\n"                                       \
+  "v_exp_f32 %[e" #n "], %[x]\n"                                              \
+  "v_fmac_f32_dpp %[y], %[vc], %[h" #n "]" SS_DPP_ROW(n)
+
+__device__ __forceinline__ void local_step_first(float (&h)[16], float (&e)[16], const float (&a)[16], float dt,
+                                                 float du, float vb, float vc, float& y) {
+  float x;
+  asm volatile(
+      "s_nop 1\n"  // (the first instruction reads vb through DPP: 2 wait states after its write)
+      SS_UPD0(0) SS_UPD0(1) SS_UPD0(2) SS_UPD0(3) SS_UPD0(4) SS_UPD0(5) SS_UPD0(6) SS_UPD0(7)
+      SS_UPD0(8) SS_UPD0(9) SS_UPD0(10) SS_UPD0(11) SS_UPD0(12) SS_UPD0(13) SS_UPD0(14) SS_UPD0(15)
+      : SS_OPS16(h, "=&v"), SS_OPS16(e, "=&v"), [y] "+v"(y), [x] "=&v"(x)
+      : SS_OPS16(a, "v"), [dt] "v"(dt), [du] "v"(du), [vb] "v"(vb), [vc] "v"(vc));
+}
+
 // State update of one token from precomputed input terms bbu[n] = bbar[n] * u:
 // h[n] = abar[n] h[n] + bbu[n] B_t[n]; y += C_t[n] h[n] (B_t, C_t by row_newbcast:n).
 // Pipelined like local_step: each h is read by its DPP fmac >= 2 instructions after the
@@ -101,16 +123,19 @@ __device__ __forceinline__ void local_step_zoh(float (&h)[16], float (&e)[16], c
 
 // Fix-up of one token: q[n] *= abar_t[n]; y += C_t[n] q[n] (C_t[n] via row_newbcast:n).
 // Each q is read by the DPP fmac >= 2 instructions after its multiply; even and odd states
-// accumulate into separate registers so consecutive fmacs do not wait on each other.
+// accumulate into separate registers so consecutive fmacs do not wait on each other (the odd
+// sum starts with a multiply instead of a cleared register).
 __device__ __forceinline__ void fixup_step(float (&q)[16], const float (&e)[16], float vc, float& y) {
-  float y2 = 0.0f;
+  float y2;
   asm volatile(
-      SS_FIX_M(0) SS_FIX_M(1) SS_FIX_M(2) SS_FIX_F(0, y) SS_FIX_M(3) SS_FIX_F(1, y2) SS_FIX_M(4)
+      SS_FIX_M(0) SS_FIX_M(1) SS_FIX_M(2) SS_FIX_F(0, y) SS_FIX_M(3)
+      "v_mul_f32_dpp %[y2], %[vc], %[q1]" SS_DPP_ROW(1)
+      SS_FIX_M(4)
       SS_FIX_F(2, y) SS_FIX_M(5) SS_FIX_F(3, y2) SS_FIX_M(6) SS_FIX_F(4, y) SS_FIX_M(7) SS_FIX_F(5, y2)
       SS_FIX_M(8) SS_FIX_F(6, y) SS_FIX_M(9) SS_FIX_F(7, y2) SS_FIX_M(10) SS_FIX_F(8, y) SS_FIX_M(11)
       SS_FIX_F(9, y2) SS_FIX_M(12) SS_FIX_F(10, y) SS_FIX_M(13) SS_FIX_F(11, y2) SS_FIX_M(14)
       SS_FIX_F(12, y) SS_FIX_M(15) SS_FIX_F(13, y2) SS_FIX_F(14, y) SS_FIX_F(15, y2)
-      : SS_OPS16(q, "+v"), [y] "+v"(y), [y2] "+v"(y2)
+      : SS_OPS16(q, "+v"), [y] "+v"(y), [y2] "=&v"(y2)
       : SS_OPS16(e, "v"), [vc] "v"(vc));
   y += y2;
 }
@@ -122,15 +147,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
   const int32_t n = bytes > 0x7fffffffLL ? 0x7fffffff : static_cast<int32_t>(bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
 }
+// A resource over [base, base + 2^31 - 1) for accesses known to be in bounds (a tile's
+// loads and stores; only kDropOffset lies outside): no per-tile range arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_tile(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), 0x7fffffff, 0x00020000);
+}
 // A per-lane byte offset beyond every range rsrc() creates (those are clamped to 2^31 - 1):
 // a buffer store at it is dropped by the range check, a load returns 0.
 constexpr uint32_t kDropOffset = 0x80000000u;
-// (the b32/b16 builtins move raw bits as unsigned integers: reinterpret, never convert)
-__device__ __forceinline__ float ldb(float*, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+// Raw element bits (the b32/b16 builtins move raw bits as unsigned integers), widened to
+// fp32 where they are used (as_f32): a prefetched tile stays in the registers the loads
+// wrote, so nothing reads them, and nothing waits for them, before the tile is consumed.
+__device__ __forceinline__ uint32_t ldb(float*, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
-__device__ __forceinline__ float ldb(uint16_t*, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16);
+__device__ __forceinline__ uint32_t ldb(uint16_t*, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+}
+template <typename T>
+__device__ __forceinline__ float as_f32(uint32_t w) {
+  return __uint_as_float(sizeof(T) == 2 ? w << 16 : w);  // bf16 is the top half of an fp32
+}
+// An element widened to fp32 at the load (for loads consumed soon after).
+template <typename T>
+__device__ __forceinline__ float ldf(T* tag, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return as_f32<T>(ldb(tag, r, voff, soff));
 }
 
 // Map the linear workgroup id to a channel group so that neighbouring groups (which share
@@ -142,8 +183,16 @@ __device__ __forceinline__ int64_t group_of(int64_t bid, int64_t ngroups) {
 }
 
 template <int TC>
-struct TileIn {
-  float raw[TC], uu[TC], zz[TC], vb[TC], vc[TC];
+struct TileIn {  // raw element bits of one lane's chunk (as_f32 widens them)
+  uint32_t raw[TC], uu[TC], zz[TC], vb[TC], vc[TC];
+  // Wait for this tile's loads here and give every register a definition that is not a
+  // load. For the first tile, before the tile loop: inside the loop the tile registers are
+  // copies of the prefetched ones, and a load on one path into the loop makes the compiler
+  // wait conservatively, at the loop's start, for loads issued in the loop.
+  __device__ __forceinline__ void settle() {
+#pragma unroll
+    for (int j = 0; j < TC; ++j) asm volatile("" : "+v"(raw[j]), "+v"(uu[j]), "+v"(zz[j]), "+v"(vb[j]), "+v"(vc[j]));
+  }
 };
 
 // ROWS chunks of TC tokens form one tile (16 for a workgroup tile, 4 for a wave-tile).
@@ -163,25 +212,35 @@ struct TileLoader {
     bc_off = static_cast<uint32_t>(k * TC) * bc_row + static_cast<uint32_t>(i * sizeof(T));
   }
 
-  // Request the inputs of the tile starting at t0. In a partial tile, tokens past the end
-  // re-read the last token (their step is forced to 0 later).
+  // Request the inputs of the tile starting at t0: load_full for a tile inside the sequence
+  // (fixed per-lane offsets, the token step in the SGPR offset), load_tail for the sequence's
+  // last, partial tile, whose tokens past the end re-read the last token (their step is
+  // forced to 0 where they are used).
+  __device__ __forceinline__ void load_full(TileIn<TC>& x, int64_t t0) const { load<true>(x, t0); }
+  __device__ __forceinline__ void load_tail(TileIn<TC>& x, int64_t t0) const { load<false>(x, t0); }
+
+  template <bool FULL>
   __device__ __forceinline__ void load(TileIn<TC>& x, int64_t t0) const {
+    // (every access below is in bounds: a tail tile re-reads its last token instead of
+    // reading past the sequence, and a lane past the last channel reads channel dim - 1)
     const int64_t tok0 = (b * L + t0) * dim + c0;
     const int64_t bc0 = (b * L + t0) * 16;
-    const int64_t tok_left = (a.batch * L * dim - tok0) * static_cast<int64_t>(sizeof(T));
-    const int64_t bc_left = (a.batch * L * 16 - bc0) * static_cast<int64_t>(sizeof(T));
-    const auto rd = rsrc(static_cast<const T*>(a.delta) + tok0, tok_left);
-    const auto ru = rsrc(static_cast<const T*>(a.u) + tok0, tok_left);
-    const auto rz = rsrc(GATE ? static_cast<const T*>(a.z) + tok0 : static_cast<const T*>(a.u), GATE ? tok_left : 0);
-    const auto rB = rsrc(static_cast<const T*>(a.B) + bc0, bc_left);
-    const auto rC = rsrc(static_cast<const T*>(a.C) + bc0, bc_left);
+    const auto rd = rsrc_tile(static_cast<const T*>(a.delta) + tok0);
+    const auto ru = rsrc_tile(static_cast<const T*>(a.u) + tok0);
+    const auto rz = rsrc_tile(GATE ? static_cast<const T*>(a.z) + tok0 : static_cast<const T*>(a.u));
+    const auto rB = rsrc_tile(static_cast<const T*>(a.B) + bc0);
+    const auto rC = rsrc_tile(static_cast<const T*>(a.C) + bc0);
     T* tag = nullptr;
-    if (t0 + ROWS * TC <= L) {
+    if (FULL) {
+      // (the token steps j * tok_row are formed here at every call from an opaque copy of the
+      // stride, so they occupy SGPRs only while the loads issue instead of across the loop)
+      uint32_t tr = tok_row;
+      asm volatile("" : "+s"(tr));
 #pragma unroll
       for (int j = 0; j < TC; ++j) {
-        x.raw[j] = ldb(tag, rd, tok_off, j * tok_row);
-        x.uu[j] = ldb(tag, ru, tok_off, j * tok_row);
-        if (GATE) x.zz[j] = ldb(tag, rz, tok_off, j * tok_row);
+        x.raw[j] = ldb(tag, rd, tok_off, j * tr);
+        x.uu[j] = ldb(tag, ru, tok_off, j * tr);
+        if (GATE) x.zz[j] = ldb(tag, rz, tok_off, j * tr);
         x.vb[j] = ldb(tag, rB, bc_off, j * bc_row);
         x.vc[j] = ldb(tag, rC, bc_off, j * bc_row);
       }

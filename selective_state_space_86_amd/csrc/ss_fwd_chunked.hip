@@ -37,6 +37,7 @@
 // current tile overlap their latency.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "ss_chunk_ops.h"
 #include "ss_split.h"
@@ -128,22 +129,32 @@ void fwd_chunked_kernel(FwdArgs a) {
   }
   const uint32_t y_row = static_cast<uint32_t>(a.dim * 4);
   const uint32_t y_off = static_cast<uint32_t>(k * TC) * y_row + static_cast<uint32_t>(i * 4);
+  // a lane past the last channel stores to an offset beyond every buffer range (dropped)
+  const uint32_t y_voff = cvalid ? y_off : kDropOffset;
 
-  TileIn<TC> cur, nxt;
-  K.load(cur, t_begin);
+  // One tile: local pass, chunk aggregates, combine, fix-up and stores. TAIL is the
+  // sequence's last, partial tile: steps of tokens past the end are forced to 0 (the
+  // identity) and their outputs are not stored; a full tile needs no per-token test.
+  // With load_next the inputs of the following (full) tile are requested into nxt.
   int buf = 0;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += R * TC, buf ^= 1) {
+  auto tile = [&](auto tail_c, TileIn<TC>& cur, TileIn<TC>& nxt, int64_t t0, bool load_next) {
+    constexpr bool TAIL = decltype(tail_c)::value;
     // (a split kernel is the one-workgroup-per-CU plan, where priorities change nothing)
     if (!SPLIT) progress_priority(t0, L);
-    const bool full = t0 + R * TC <= t_end;  // (a part other than the last ends on a tile boundary)
     float* lds_a = lds_a2[buf];
     // request the next tile first: the whole tile's work hides its latency
-    if (EARLY && t0 + R * TC < t_end) K.load(nxt, t0 + R * TC);
+    if (EARLY && load_next) K.load_full(nxt, t0 + R * TC);
+    // tokens of this lane's chunk inside the sequence (TC except in the tail tile)
+    const int nval = TAIL ? max(0, min(TC, static_cast<int>(L - t0) - k * TC)) : TC;
 
     // local pass from a zero state
-    float h[16], ex[TC][16], y[TC], gate[TC], vc[TC];
+    float h[16], ex[TC][16], y[TC], gate[TC], vc[TC], uu[TC];
 #pragma unroll
-    for (int n = 0; n < 16; ++n) h[n] = 0.0f;
+    for (int j = 0; j < TC; ++j) uu[j] = as_f32<T>(cur.uu[j]);
+    if (ZOH) {
+#pragma unroll
+      for (int n = 0; n < 16; ++n) h[n] = 0.0f;
+    }
     float dsum = 0.0f;
     if (CONV) {  // u = silu(conv(x)) over the window [3 inputs before the chunk, x_0 .. x_{TC-1}]
       // (the 3 earlier inputs are the end of the previous chunk: cache hits, loaded here
@@ -154,34 +165,37 @@ void fwd_chunked_kernel(FwdArgs a) {
         win[m] = conv_input(static_cast<const T*>(a.u), a.conv_state, a.kconv, b, cc,
                             min(t0 + k * TC - 3 + m, L - 1), L, a.dim);
 #pragma unroll
-      for (int j = 0; j < TC; ++j) win[j + 3] = cur.uu[j];
+      for (int j = 0; j < TC; ++j) win[j + 3] = as_f32<T>(cur.uu[j]);
       // u_out has y's layout; a null u_out gets an empty range, so every store is dropped
       const int64_t u0 = (b * L + t0) * a.dim + c0;
       const auto ru = rsrc(a.u_out ? a.u_out + u0 : a.y, a.u_out ? (a.batch * L * a.dim - u0) * 4 : 0);
 #pragma unroll
       for (int j = 0; j < TC; ++j) {
-        cur.uu[j] = conv4_silu(w4, cb, win[j], win[j + 1], win[j + 2], win[j + 3]);
-        const bool ok = full ? cvalid : (cvalid && t0 + k * TC + j < L);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cur.uu[j]), ru, ok ? y_off : kDropOffset, j * y_row, 0);
+        uu[j] = conv4_silu(w4, cb, win[j], win[j + 1], win[j + 2], win[j + 3]);
+        const uint32_t vo = TAIL ? ((cvalid && j < nval) ? y_off : kDropOffset) : y_voff;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(uu[j]), ru, vo, j * y_row, 0);
       }
     }
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
-      const float x = cur.raw[j] + bias;
+      const float x = as_f32<T>(cur.raw[j]) + bias;
+      const float vb = as_f32<T>(cur.vb[j]);
+      vc[j] = as_f32<T>(cur.vc[j]);
       float dt = a.softplus ? softplus(x) : x;
-      if (!full) dt = (t0 + k * TC + j < L) ? dt : 0.0f;  // a zero step is the identity
+      if (TAIL) dt = j < nval ? dt : 0.0f;  // a zero step is the identity
       dsum += dt;
-      y[j] = Dd * cur.uu[j];
+      y[j] = Dd * uu[j];
       if (ZOH)
-        local_step_zoh(h, ex[j], A2, iA, dt, cur.uu[j], cur.vb[j], cur.vc[j], y[j]);
+        local_step_zoh(h, ex[j], A2, iA, dt, uu[j], vb, vc[j], y[j]);
+      else if (j == 0)
+        local_step_first(h, ex[0], A2, dt, dt * uu[0], vb, vc[0], y[0]);
       else
-        local_step(h, ex[j], A2, dt, dt * cur.uu[j], cur.vb[j], cur.vc[j], y[j]);
-      gate[j] = GATE ? silu(cur.zz[j]) : 1.0f;
-      vc[j] = cur.vc[j];
+        local_step(h, ex[j], A2, dt, dt * uu[j], vb, vc[j], y[j]);
+      gate[j] = GATE ? silu(as_f32<T>(cur.zz[j])) : 1.0f;
     }
 
     // otherwise request it now: the combine and fix-up below hide its latency
-    if (!EARLY && t0 + R * TC < t_end) K.load(nxt, t0 + R * TC);
+    if (!EARLY && load_next) K.load_full(nxt, t0 + R * TC);
 
     // chunk aggregates (prod abar = exp(A * sum dt), end state) to LDS
     {
@@ -243,14 +257,33 @@ void fwd_chunked_kernel(FwdArgs a) {
     // offset past the buffer range and is dropped, so the compiler sees a fixed number of
     // outstanding stores and never waits for them when the prefetched loads are consumed)
     const int64_t y0 = (b * L + t0) * a.dim + c0;
-    const auto ry = rsrc(a.y + y0, (a.batch * L * a.dim - y0) * 4);
+    const auto ry = rsrc_tile(a.y + y0);
+    uint32_t yr = y_row;  // (token steps formed per tile, as in the loads)
+    asm volatile("" : "+s"(yr));
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
       fixup_step(q, ex[j], vc[j], y[j]);
-      const bool ok = full ? cvalid : (cvalid && t0 + k * TC + j < L);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[j] * gate[j]), ry, ok ? y_off : kDropOffset, j * y_row, 0);
+      const uint32_t vo = TAIL ? ((cvalid && j < nval) ? y_off : kDropOffset) : y_voff;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[j] * gate[j]), ry, vo, j * yr, 0);
     }
+    buf ^= 1;
+  };
+
+  // full tiles (a part other than the last holds only full tiles), then the partial tail
+  const int64_t nfull = (t_end - t_begin) / (R * TC);
+  TileIn<TC> cur, nxt;
+  int64_t t0 = t_begin;
+  if (nfull > 0) {
+    K.load_full(cur, t0);
+    cur.settle();
+  }
+  for (int64_t it = 0; it < nfull; ++it, t0 += R * TC) {
+    tile(std::false_type{}, cur, nxt, t0, it + 1 < nfull);
     cur = nxt;
+  }
+  if (t0 < t_end) {
+    K.load_tail(cur, t0);
+    tile(std::true_type{}, cur, nxt, t0, false);
   }
   if (SPLIT && item_s / groups < a.parts - 1) {  // publish this part's end state for the next
     const int64_t slot = __builtin_amdgcn_readfirstlane(item_s);  // (re-read: nothing kept live)

@@ -32,7 +32,7 @@
 namespace ss {
 namespace {
 
-using chunk::ldb;
+using chunk::ldf;
 using chunk::rsrc;
 
 constexpr int kRowStride = 16 * 16 + 16;  // LDS [row][token][lane], padded
@@ -124,14 +124,14 @@ __global__ __launch_bounds__(256) void fwd_state_kernel(FwdArgs a) {
     const int64_t left = (a.batch * L * a.dim - e0) * static_cast<int64_t>(sizeof(T));
     // (rows past the last channel read the last channel: computed, never stored)
     const uint32_t off = static_cast<uint32_t>(tn) * tok_row + static_cast<uint32_t>(cc * sizeof(T));
-    x.raw = ldb(tag, rsrc(DL + e0, left), off, 0);
-    x.uu = ldb(tag, rsrc(U + e0, left), off, 0);
-    x.zz = GATE ? ldb(tag, rsrc(Z + e0, left), off, 0) : 0.0f;
+    x.raw = ldf(tag, rsrc(DL + e0, left), off, 0);
+    x.uu = ldf(tag, rsrc(U + e0, left), off, 0);
+    x.zz = GATE ? ldf(tag, rsrc(Z + e0, left), off, 0) : 0.0f;
     // B and C rows of the block: tokens past the end read 0 (their step is 0 anyway)
     const int64_t bc0 = (b * L + t0) * N;
     const int64_t valid_bytes = min(static_cast<int64_t>(16), L - t0) * N * static_cast<int64_t>(sizeof(T));
-    x.bsh = ldb(tag, rsrc(Bm + bc0, valid_bytes), bc_off, 0);
-    x.csh = ldb(tag, rsrc(Cm + bc0, valid_bytes), bc_off, 0);
+    x.bsh = ldf(tag, rsrc(Bm + bc0, valid_bytes), bc_off, 0);
+    x.csh = ldf(tag, rsrc(Cm + bc0, valid_bytes), bc_off, 0);
   };
   auto stage = [&](const StateIn& x, int buf) {  // transpose the block's B, C into LDS
     lds_bc[buf][0][bn * kBcStride + bt] = x.bsh;

@@ -42,6 +42,8 @@ MUTANTS = [
                             "    double yv = acc;\n    if (z) yv *= silu(in_at(z, dtype, e));\n    yv += D_d * uv;")]),
     ("gate_is_sigmoid", [("if (z >= 0.0) return z / (1.0 + exp(-z));", "if (z >= 0.0) return 1.0 / (1.0 + exp(-z));"),
                          ("return z * e / (1.0 + e);", "return e / (1.0 + e);")]),
+    ("B_one_token_late", [("      h[n] = abar * h[n] + (bbar * in_at(B, dtype, bc + n)) * uv;\n",
+                           "      h[n] = abar * h[n] + (bbar * in_at(B, dtype, (t > 0 ? bc - dstate : bc) + n)) * uv;\n")]),
     ("B_ignores_batch", [("const int64_t bc = (b * seqlen + t) * dstate;", "const int64_t bc = t * dstate;")]),
     ("bf16_decode_shift", [("<< 16;", "<< 15;")]),
     ("state_not_carried_in_step", [("state + j * dstate, y ? y + j : NULL, 1);",
@@ -93,6 +95,7 @@ def pin_suite(lib):
         ("zero_step", lambda: pins.test_zero_step_keeps_state_exactly(lib)),
         ("huge_step", lambda: pins.test_huge_step_resets_state(lib)),
         ("page5", lambda: pins.test_page5_worked_example(lib)),
+        ("page5_selective", lambda: pins.test_page5_selective_example(lib)),
         ("step", lambda: pins.test_step_by_step_matches_forward(lib)),
         ("zoh_continuous", lambda: pins.test_zoh_matches_continuous_solution(lib)),
         ("zoh_half_steps", lambda: pins.test_zoh_half_steps_compose(lib)),

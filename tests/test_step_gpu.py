@@ -87,3 +87,34 @@ def test_step_zero_step_size_keeps_state():
     ss.step(st, u, z, A, B, C, softplus=False)
     torch.cuda.synchronize()
     assert torch.equal(st, st0)
+
+
+@pytest.mark.parametrize("batch,dim,dt,gated,zoh", [(2, 128, "bf16", True, False), (2, 128, "f32", False, False),
+                                                    (2, 128, "f32", True, True), (2, 128, "bf16", False, True),
+                                                    (4, 192, "bf16", True, False), (6, 64, "f32", False, False)])
+def test_two_row_decode_layout_matches_oracle_and_forward(batch, dim, dt, gated, zoh):
+    """An even batch with dim a multiple of 64 takes the layout in which a lane steps the same
+    channel in two batch rows and reads A once for both: bf16, ungated and zero-order-hold
+    streams there, every step against the oracle and the stream against ss_fwd."""
+    w = inputs.WORKLOADS["decode"].replace(name=f"r{batch}{dim}{dt}{gated}{zoh}", batch=batch, seqlen=24,
+                                           dim=dim, dstate=16, dtype=dt)
+    x = inputs.make(w, seed=11, device=DEV, time_major=True)
+    L = x["u"].shape[0]
+    state = torch.zeros((batch, dim, 16), dtype=torch.float32, device=DEV)
+    ys = []
+    for t in range(L):
+        ys.append(ss.step(state, x["u"][t], x["delta"][t], x["A"], x["B"][t], x["C"][t], D=x["D"],
+                          z=x["z"][t] if gated else None, delta_bias=x["delta_bias"], zoh=zoh))
+    y_fwd, st_fwd = pu.gpu_fwd(batch_major(x), gated, zoh=zoh)
+    torch.cuda.synchronize()
+    y_step = torch.stack(ys, dim=1)
+    tol = pu.tol_of(x)
+    n = {k: inputs.to_numpy(v) for k, v in x.items()}
+    ref = np.zeros((batch, dim, 16))
+    for t in range(L):
+        yr = oracle.step(ref, n["u"][t], n["delta"][t], n["A"], n["B"][t], n["C"][t], D=n["D"],
+                         z=n["z"][t] if gated else None, delta_bias=n["delta_bias"], zoh=zoh)
+        assert pu.scaled_err(y_step[:, t].double().cpu().numpy(), yr) <= tol, f"step {t}"
+    assert pu.scaled_err(state.double().cpu().numpy(), ref) <= tol
+    assert ((y_step - y_fwd).abs() / (1 + y_fwd.abs())).max().item() <= tol
+    assert ((state - st_fwd).abs() / (1 + st_fwd.abs())).max().item() <= tol
