@@ -174,6 +174,17 @@ __device__ __forceinline__ float ldf(T* tag, __amdgpu_buffer_rsrc_t r, uint32_t 
   return as_f32<T>(ldb(tag, r, voff, soff));
 }
 
+// The lane's index in its wave, formed anew where it is called (v_mbcnt; the asm keeps the
+// compiler from hoisting it): per-lane LDS addresses inside the tile loop are rebuilt from it
+// and the wave's first thread id (an SGPR) instead of being kept in a VGPR across the loop,
+// where at the register limit they were spilled and their reload waited for every load in
+// flight (vmcnt(0)), the next tile's included.
+__device__ __forceinline__ int lane_in_wave() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Map the linear workgroup id to a channel group so that neighbouring groups (which share
 // 128-byte lines of u, delta, z and y) land on the same XCD (workgroups are dealt to the 8
 // XCDs round-robin) and are dispatched close together.
@@ -218,6 +229,34 @@ struct TileLoader {
   // forced to 0 where they are used).
   __device__ __forceinline__ void load_full(TileIn<TC>& x, int64_t t0) const { load<true>(x, t0); }
   __device__ __forceinline__ void load_tail(TileIn<TC>& x, int64_t t0) const { load<false>(x, t0); }
+
+  // Token by token: the resources of the full tile at t0 (rsrcs), then the loads of token j
+  // (load_token), issued while the previous tile is being consumed.
+  struct Rsrcs {
+    __amdgpu_buffer_rsrc_t rd, ru, rz, rB, rC;
+    uint32_t tr;  // the token step (opaque copy, as in load)
+  };
+  __device__ __forceinline__ Rsrcs rsrcs(int64_t t0) const {
+    const int64_t tok0 = (b * L + t0) * dim + c0;
+    const int64_t bc0 = (b * L + t0) * 16;
+    Rsrcs r;
+    r.rd = rsrc_tile(static_cast<const T*>(a.delta) + tok0);
+    r.ru = rsrc_tile(static_cast<const T*>(a.u) + tok0);
+    r.rz = rsrc_tile(GATE ? static_cast<const T*>(a.z) + tok0 : static_cast<const T*>(a.u));
+    r.rB = rsrc_tile(static_cast<const T*>(a.B) + bc0);
+    r.rC = rsrc_tile(static_cast<const T*>(a.C) + bc0);
+    r.tr = tok_row;
+    asm volatile("" : "+s"(r.tr));
+    return r;
+  }
+  __device__ __forceinline__ void load_token(TileIn<TC>& x, const Rsrcs& r, int j) const {
+    T* tag = nullptr;
+    x.raw[j] = ldb(tag, r.rd, tok_off, j * r.tr);
+    x.uu[j] = ldb(tag, r.ru, tok_off, j * r.tr);
+    if (GATE) x.zz[j] = ldb(tag, r.rz, tok_off, j * r.tr);
+    x.vb[j] = ldb(tag, r.rB, bc_off, j * bc_row);
+    x.vc[j] = ldb(tag, r.rC, bc_off, j * bc_row);
+  }
 
   template <bool FULL>
   __device__ __forceinline__ void load(TileIn<TC>& x, int64_t t0) const {

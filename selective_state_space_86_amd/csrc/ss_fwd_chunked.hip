@@ -93,6 +93,7 @@ void fwd_chunked_kernel(FwdArgs a) {
   const int64_t c0 = (g % ngd) * 16;
   const int i = tid & 15;  // channel within the group == the state index this lane owns in the combine
   const int k = tid >> 4;  // time chunk within the tile (row of 16 lanes)
+  const int wave_tid0 = __builtin_amdgcn_readfirstlane(tid & ~63);  // the wave's first thread (SGPR)
   const int64_t c = c0 + i;
   const bool cvalid = c < a.dim;
   const int64_t cc = cvalid ? c : a.dim - 1;
@@ -127,6 +128,17 @@ void fwd_chunked_kernel(FwdArgs a) {
       if (n < 16) carry[m] = seen ? split::load_state(a.split_ws, a.split_cap, slot, n, i) : __builtin_nanf("");
     }
   }
+  // Wave priorities. Several workgroups per CU (unsplit plans of at most 16 rows): progress
+  // priority (ss_common.h). Otherwise: the fix-up at a raised priority. The waves of a SIMD
+  // drift apart because the SIMD issues from the oldest wave first: a younger wave's fix-up
+  // runs beside an older wave's next local pass, takes about three times as long, and the
+  // older wave then waits for it at the first barrier of every tile (8-wave 3B-layer tiles:
+  // 4.85 -> 4.25 ms with the raised fix-up).
+#ifndef SS_FIXUP_PRIO
+#define SS_FIXUP_PRIO 1
+#endif
+  constexpr bool kProgressPrio = !SPLIT && R <= 16;
+  constexpr int kFixupPrio = SS_FIXUP_PRIO;
   const uint32_t y_row = static_cast<uint32_t>(a.dim * 4);
   const uint32_t y_off = static_cast<uint32_t>(k * TC) * y_row + static_cast<uint32_t>(i * 4);
   // a lane past the last channel stores to an offset beyond every buffer range (dropped)
@@ -139,11 +151,19 @@ void fwd_chunked_kernel(FwdArgs a) {
   int buf = 0;
   auto tile = [&](auto tail_c, TileIn<TC>& cur, TileIn<TC>& nxt, int64_t t0, bool load_next) {
     constexpr bool TAIL = decltype(tail_c)::value;
-    // (a split kernel is the one-workgroup-per-CU plan, where priorities change nothing)
-    if (!SPLIT) progress_priority(t0, L);
+    if (kProgressPrio) progress_priority(t0, L);
+    else __builtin_amdgcn_s_setprio(0);
     float* lds_a = lds_a2[buf];
-    // request the next tile first: the whole tile's work hides its latency
-    if (EARLY && load_next) K.load_full(nxt, t0 + R * TC);
+#ifndef SS_TOKEN_LOADS
+#define SS_TOKEN_LOADS 1
+#endif
+    // The next tile's inputs: token j's loads are issued right after this tile's token j is
+    // consumed, into the registers it leaves (one tile of latency cover; the requests of a
+    // tile are spread over its local pass instead of arriving at the memory pipeline all at
+    // once). Without SS_TOKEN_LOADS: at the top of the tile (EARLY) or after the local pass.
+    typename TileLoader<T, GATE, TC, R>::Rsrcs nr;
+    if (SS_TOKEN_LOADS && load_next) nr = K.rsrcs(t0 + R * TC);
+    if (!SS_TOKEN_LOADS && EARLY && load_next) K.load_full(nxt, t0 + R * TC);
     // tokens of this lane's chunk inside the sequence (TC except in the tail tile)
     const int nval = TAIL ? max(0, min(TC, static_cast<int>(L - t0) - k * TC)) : TC;
 
@@ -192,15 +212,18 @@ void fwd_chunked_kernel(FwdArgs a) {
       else
         local_step(h, ex[j], A2, dt, dt * uu[j], vb, vc[j], y[j]);
       gate[j] = GATE ? silu(as_f32<T>(cur.zz[j])) : 1.0f;
+      if (SS_TOKEN_LOADS && load_next) K.load_token(nxt, nr, j);
     }
 
-    // otherwise request it now: the combine and fix-up below hide its latency
-    if (!EARLY && load_next) K.load_full(nxt, t0 + R * TC);
+    if (!SS_TOKEN_LOADS && !EARLY && load_next) K.load_full(nxt, t0 + R * TC);
 
     // chunk aggregates (prod abar = exp(A * sum dt), end state) to LDS
+    // (lane-dependent LDS addresses from the thread id formed here: see lane_in_wave)
+    const int tid_t = wave_tid0 + lane_in_wave();
+    const int k_t = tid_t >> 4, i_t = tid_t & 15;
     {
-      float* la = lds_a + k * kLdsChunkStride + i;
-      float* lh = lds_h + k * kLdsChunkStride + i;
+      float* la = lds_a + k_t * kLdsChunkStride + i_t;
+      float* lh = lds_h + k_t * kLdsChunkStride + i_t;
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
         float p;
@@ -225,8 +248,8 @@ void fwd_chunked_kernel(FwdArgs a) {
     for (int m = 0; m < NOWN; ++m) {
       const int n = k + m * R;
       if (n < 16) {
-        float* sa = lds_a + n * 16 + i;
-        const float* sh = lds_h + n * 16 + i;
+        float* sa = lds_a + (k_t + m * R) * 16 + i_t;
+        const float* sh = lds_h + (k_t + m * R) * 16 + i_t;
         // (in blocks of at most 16 chunks: all reads of a block first, then its fold)
         constexpr int CB = R < 16 ? R : 16;
 #pragma unroll
@@ -248,11 +271,12 @@ void fwd_chunked_kernel(FwdArgs a) {
     __syncthreads();
     float q[16];  // this chunk's carry-in
     {
-      const float* lc = lds_a + k * kLdsChunkStride + i;
+      const float* lc = lds_a + k_t * kLdsChunkStride + i_t;
 #pragma unroll
       for (int n = 0; n < 16; ++n) q[n] = lc[n * 16];
     }
 
+    if (!kProgressPrio) __builtin_amdgcn_s_setprio(kFixupPrio);
     // fix-up with the carry-in, gate, store (unconditionally: a masked lane's store goes to an
     // offset past the buffer range and is dropped, so the compiler sees a fixed number of
     // outstanding stores and never waits for them when the prefetched loads are consumed)
