@@ -135,7 +135,10 @@ void fwd_chunked_kernel(FwdArgs a) {
   // older wave then waits for it at the first barrier of every tile (8-wave 3B-layer tiles:
   // 4.85 -> 4.25 ms with the raised fix-up).
 #ifndef SS_FIXUP_PRIO
-#define SS_FIXUP_PRIO 1
+#define SS_FIXUP_PRIO 2
+#endif
+#ifndef SS_LOCAL_RAMP
+#define SS_LOCAL_RAMP 1
 #endif
   constexpr bool kProgressPrio = !SPLIT && R <= 16;
   constexpr int kFixupPrio = SS_FIXUP_PRIO;
@@ -198,6 +201,13 @@ void fwd_chunked_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
+      if (!kProgressPrio && SS_LOCAL_RAMP) {
+        switch ((3 * j) / TC) {  // (folds to one instruction per unrolled token)
+          case 0: __builtin_amdgcn_s_setprio(2); break;
+          case 1: __builtin_amdgcn_s_setprio(1); break;
+          default: __builtin_amdgcn_s_setprio(0); break;
+        }
+      }
       const float x = as_f32<T>(cur.raw[j]) + bias;
       const float vb = as_f32<T>(cur.vb[j]);
       vc[j] = as_f32<T>(cur.vc[j]);
@@ -243,7 +253,8 @@ void fwd_chunked_kernel(FwdArgs a) {
     // combine: this lane owns state n = k (and k + R) of channel i and folds the R chunks in
     // order (with 32 rows, rows 16..31 own none). Each lane reads exactly the LDS words it then
     // overwrites with carries, so the carry array can alias the prod-abar array without another
-    // barrier.
+    // barrier. (A two-level fold of 32 chunks, rows 16..31 folding the second half from zero
+    // and correcting it after one more barrier, measured 8% slower at the 3B shape.)
 #pragma unroll
     for (int m = 0; m < NOWN; ++m) {
       const int n = k + m * R;
