@@ -367,11 +367,6 @@ template <typename T>
 __device__ __forceinline__ float ld(const void* p, int64_t i) {
   return load_elem(static_cast<const T*>(p), i);
 }
-// An element kept as stored (bf16 bits or fp32), widened where it is used: a conversion
-// right after a prefetching load would make the wave wait for that load there.
-__device__ __forceinline__ float widen(float v) { return v; }
-__device__ __forceinline__ float widen(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
-
 struct Lane {
   int64_t b, c0, c, cc;
   int k, i;
@@ -420,7 +415,8 @@ __device__ __forceinline__ void work_item(const BwdArgs& a, bool reverse, uint32
 // With SPLIT, a workgroup scans one part of its group's sequence, from the state the previous
 // part publishes, and publishes its own end state.
 template <typename T, int CTC, int R, bool SPLIT>
-__global__ __launch_bounds__(R * 16) void bwd_ckpt_kernel(BwdArgs a) {
+__global__ __launch_bounds__(R * 16) __attribute__((amdgpu_waves_per_eu(R == 16 ? 4 : 2)))
+void bwd_ckpt_kernel(BwdArgs a) {
   static_assert(CTC * 4 == 32 || CTC * 8 == 32 || CTC * 16 == 32, "checkpoints every 32 tokens");
   static_assert(R == 16 || R == 32, "16 or 32 chunks per tile");
   constexpr int kPer = 32 / CTC;  // chunks per checkpoint interval
@@ -455,8 +451,8 @@ __global__ __launch_bounds__(R * 16) void bwd_ckpt_kernel(BwdArgs a) {
   const uint32_t col = static_cast<uint32_t>((l.cc - l.c0) * sizeof(T));
   const uint32_t bcol = l.i < N ? static_cast<uint32_t>(l.i * sizeof(T)) : 0x7fffffffu;
   T* tag = nullptr;
-  struct In {
-    float x[CTC], u[CTC], b[CTC];
+  struct In {  // raw element bits, widened where used (a widening next to the load would wait for it)
+    chunk::Bits<T> x[CTC], u[CTC], b[CTC];
   };
   auto fetch = [&](In& r, int64_t t0) {
     const int64_t e0 = (l.b * L + t0) * a.dim + l.c0;
@@ -470,26 +466,36 @@ __global__ __launch_bounds__(R * 16) void bwd_ckpt_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < CTC; ++j) {
       const uint32_t tt = static_cast<uint32_t>(min(l.k * CTC + j, last));  // past the end: last token
-      r.x[j] = chunk::ldf(tag, rd, tt * tok_row + col, 0);
-      r.u[j] = chunk::ldf(tag, ru, tt * tok_row + col, 0);
-      r.b[j] = chunk::ldf(tag, rb, bcol == 0x7fffffffu ? bcol : tt * bc_row + bcol, 0);
+      r.x[j] = chunk::ldr<T>(rd, tt * tok_row + col, 0);
+      r.u[j] = chunk::ldr<T>(ru, tt * tok_row + col, 0);
+      r.b[j] = chunk::ldr<T>(rb, bcol == 0x7fffffffu ? bcol : tt * bc_row + bcol, 0);
     }
   };
   In cur, nxt;
-  if (a.ntiles > 0) fetch(cur, t_begin);
+  if (a.ntiles > 0) {
+    fetch(cur, t_begin);
+    // (the first tile's registers get a definition that is not a load: with a load on one
+    // path into the loop and copies on the other, the compiler waits at the start of every
+    // tile for the loads just issued)
+#pragma unroll
+    for (int j = 0; j < CTC; ++j) asm volatile("" : "+v"(cur.x[j]), "+v"(cur.u[j]), "+v"(cur.b[j]));
+  }
+  asm volatile("" : "+v"(carry));  // (likewise the loaded initial state)
   for (int64_t t0 = t_begin; t0 < t_end; t0 += TT) {
     if (!SPLIT) progress_priority(t0, L);
-    if (t0 + TT < t_end) fetch(nxt, t0 + TT);
+    // (the last tile re-requests itself, unused: loads under a branch make the compiler wait
+    // for all of them where the paths join)
+    fetch(nxt, t0 + TT < t_end ? t0 + TT : t0);
     float h[16], e[16], dsum = 0.0f;
 #pragma unroll
     for (int n = 0; n < 16; ++n) h[n] = 0.0f;
 #pragma unroll
     for (int j = 0; j < CTC; ++j) {
-      const float x = widen(cur.x[j]) + bias;
+      const float x = chunk::as_f32<T>(cur.x[j]) + bias;
       float dt = a.softplus ? softplus(x) : x;
       dt = (t0 + l.k * CTC + j < L) ? dt : 0.0f;  // a zero step is the identity
       dsum += dt;
-      bwd_local(h, e, A2, dt, dt * cur.u[j], cur.b[j]);
+      bwd_local(h, e, A2, dt, dt * chunk::as_f32<T>(cur.u[j]), chunk::as_f32<T>(cur.b[j]));
     }
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
@@ -497,18 +503,32 @@ __global__ __launch_bounds__(R * 16) void bwd_ckpt_kernel(BwdArgs a) {
       lds_h[l.k * kS + n * 16 + l.i] = h[n];
     }
     __syncthreads();
-    // lane (k, i), k < 16, owns state n = k of channel i: fold the R chunks in order, writing
+    // lane (k, i), k < 16, owns state n = k of channel i: fold the R chunks in order, keeping
     // the state at every multiple of 32 tokens (the checkpoint interval)
+    constexpr int kCk = R / kPer;  // checkpoints per tile
+    float ckv[kCk];
     if (R == 16 || l.k < 16) {
 #pragma unroll
       for (int jj = 0; jj < R; ++jj) {
-        if (jj % kPer == 0) {
-          const int64_t tile = (t0 + jj * CTC) / 32;
-          if (tile < a.ntiles) a.ckpt[((l.b * a.ntiles + tile) * dimp + l.c) * 16 + l.k] = carry;
-        }
+        if (jj % kPer == 0) ckv[jj / kPer] = carry;
         const int o = jj * kS + l.k * 16 + l.i;
         carry = __builtin_fmaf(lds_p[o], carry, carry + lds_h[o]);
       }
+    }
+    {  // the checkpoints, stored unconditionally through a resource based at this tile's first
+       // one and ending with this batch row's last: a lane that owns no state stores to an
+       // offset past every range, checkpoints past the sequence fall past this one (dropped).
+       // A store under a branch would make the compiler wait for every memory operation in
+       // flight where the paths join, the next tile's loads included.
+      const int64_t tile0 = t0 / 32;
+      const int64_t ck0 = (l.b * a.ntiles + tile0) * dimp * 16;
+      const auto rck = chunk::rsrc(a.ckpt + ck0, (a.ntiles - tile0) * dimp * 16 * 4);
+      const uint32_t voff = (R == 16 || l.k < 16) ? static_cast<uint32_t>((l.c * 16 + l.k) * 4) : chunk::kDropOffset;
+      uint32_t ck_row = static_cast<uint32_t>(dimp * 16 * 4);  // bytes per checkpoint interval
+      asm volatile("" : "+s"(ck_row));
+#pragma unroll
+      for (int m = 0; m < kCk; ++m)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ckv[m]), rck, voff, m * ck_row, 0);
     }
     __syncthreads();
     cur = nxt;
@@ -553,8 +573,8 @@ void bwd_chunked_kernel(BwdArgs a) {
   float A2[16];
 #pragma unroll
   for (int n = 0; n < 16; ++n) A2[n] = n < N ? a.A[l.cc * N + n] * kLog2e : 0.0f;
-  const float bias = a.delta_bias ? a.delta_bias[l.cc] : 0.0f;
-  const float Dd = a.D ? a.D[l.cc] : 0.0f;
+  float bias = a.delta_bias ? a.delta_bias[l.cc] : 0.0f;
+  float Dd = a.D ? a.D[l.cc] : 0.0f;
   // adjoint carried from later tiles: lane (k, i) owns state n = k of channel i
   float rcarry = (a.dlast && (!SPLIT || part == a.parts - 1) && l.cvalid && l.k < N)
                      ? a.dlast[(l.b * a.dim + l.c) * N + l.k] : 0.0f;
@@ -571,74 +591,142 @@ void bwd_chunked_kernel(BwdArgs a) {
   for (int n = 0; n < 16; ++n) dAacc[n] = 0.0f;
   float dDacc = 0.0f, dbacc = 0.0f;
 
-  // raw inputs of a tile's chunk for this lane (tokens past the end re-read the last one);
-  // the tile processed next (the earlier one) is requested before this one is computed
+  // raw inputs of a tile's chunk for this lane, as stored bits (widened where used: a
+  // widening next to the load would wait for it); the tile processed next (the earlier one)
+  // is requested before this one is computed
   struct Raw {
-    T x[TC], u[TC], z[TC], b[TC], c[TC];
-    float dy[TC];
+    chunk::Bits<T> x[TC], u[TC], z[TC], b[TC], c[TC];
+    uint32_t dy[TC];
   };
-  // (every load is issued unconditionally, lanes past dstate reading state dstate - 1 and
-  // discarding it: loads under a branch make the compiler wait for all of them at the join,
-  // which would turn the prefetch of the next tile into a stall)
-  auto fetch = [&](Raw& r, int64_t t0) {
-    const int64_t nb = l.i < N ? l.i : N - 1;
+  // Buffer loads from fixed per-lane offsets, the token step in the SGPR offset (full tiles);
+  // the sequence's last tile, which may be partial, re-reads its last token instead of
+  // reading past the end. Lanes past dstate read state dstate - 1 and discard it. Every load
+  // of a call is issued unconditionally (loads under a branch make the compiler wait for all
+  // of them where the paths join, which would turn the prefetch into a stall).
+  const int64_t nb = l.i < N ? l.i : N - 1;
+  const uint32_t tok_row = static_cast<uint32_t>(a.dim * sizeof(T));
+  const uint32_t dy_row = static_cast<uint32_t>(a.dim * 4);
+  const uint32_t bc_row = static_cast<uint32_t>(N * sizeof(T));
+  const uint32_t col = static_cast<uint32_t>((l.cc - l.c0) * sizeof(T));
+  const uint32_t dcol = static_cast<uint32_t>((l.cc - l.c0) * 4);
+  const uint32_t bcol = static_cast<uint32_t>(nb * sizeof(T));
+  T* tag = nullptr;
+  float* ftag = nullptr;
+  auto tile_rsrc = [&](int64_t t0, __amdgpu_buffer_rsrc_t (&r)[6]) {
+    const int64_t e0 = (l.b * L + t0) * a.dim + l.c0;
+    const int64_t bc0 = (l.b * L + t0) * N;
+    r[0] = chunk::rsrc_tile(static_cast<const T*>(a.delta) + e0);
+    r[1] = chunk::rsrc_tile(static_cast<const T*>(a.u) + e0);
+    r[2] = chunk::rsrc_tile(GATE ? static_cast<const T*>(a.z) + e0 : static_cast<const T*>(a.u) + e0);
+    r[3] = chunk::rsrc_tile(a.dy + e0);
+    r[4] = chunk::rsrc_tile(static_cast<const T*>(a.B) + bc0);
+    r[5] = chunk::rsrc_tile(static_cast<const T*>(a.C) + bc0);
+  };
+  // (live = false: every load of the call is dropped by the range check and returns 0)
+  auto fetch_full = [&](Raw& r, int64_t t0, bool live) {
+    __amdgpu_buffer_rsrc_t rs[6];
+    tile_rsrc(t0, rs);
+    uint32_t tr = tok_row, dr = dy_row;  // (token steps formed here: SGPRs only while issuing)
+    asm volatile("" : "+s"(tr), "+s"(dr));
+    const uint32_t vt = live ? static_cast<uint32_t>(l.k * TC) * tok_row + col : chunk::kDropOffset;
+    const uint32_t vd = live ? static_cast<uint32_t>(l.k * TC) * dy_row + dcol : chunk::kDropOffset;
+    const uint32_t vbc = live ? static_cast<uint32_t>(l.k * TC) * bc_row + bcol : chunk::kDropOffset;
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
-      const int64_t t = t0 + l.k * TC + j;
-      const int64_t tt = t < L ? t : L - 1;
-      const int64_t e = (l.b * L + tt) * a.dim + l.cc;
-      r.x[j] = static_cast<const T*>(a.delta)[e];
-      r.u[j] = static_cast<const T*>(a.u)[e];
-      r.z[j] = GATE ? static_cast<const T*>(a.z)[e] : T();
-      r.dy[j] = a.dy[e];
-      // (zeroed past dstate where the tile is used, so nothing here waits for the loads)
-      r.b[j] = static_cast<const T*>(a.B)[(l.b * L + tt) * N + nb];
-      r.c[j] = static_cast<const T*>(a.C)[(l.b * L + tt) * N + nb];
+      r.x[j] = chunk::ldr<T>(rs[0], vt, j * tr);
+      r.u[j] = chunk::ldr<T>(rs[1], vt, j * tr);
+      r.z[j] = GATE ? chunk::ldr<T>(rs[2], vt, j * tr) : chunk::Bits<T>(0);
+      r.dy[j] = chunk::ldb(ftag, rs[3], vd, j * dr);
+      r.b[j] = chunk::ldr<T>(rs[4], vbc, j * bc_row);
+      r.c[j] = chunk::ldr<T>(rs[5], vbc, j * bc_row);
+    }
+  };
+  auto fetch_tail = [&](Raw& r, int64_t t0) {
+    __amdgpu_buffer_rsrc_t rs[6];
+    tile_rsrc(t0, rs);
+    const int last = static_cast<int>(min(L - 1 - t0, static_cast<int64_t>(TT - 1)));
+#pragma unroll
+    for (int j = 0; j < TC; ++j) {
+      const uint32_t tt = static_cast<uint32_t>(min(l.k * TC + j, last));  // past the end: last token
+      r.x[j] = chunk::ldr<T>(rs[0], tt * tok_row + col, 0);
+      r.u[j] = chunk::ldr<T>(rs[1], tt * tok_row + col, 0);
+      r.z[j] = GATE ? chunk::ldr<T>(rs[2], tt * tok_row + col, 0) : chunk::Bits<T>(0);
+      r.dy[j] = chunk::ldb(ftag, rs[3], tt * dy_row + dcol, 0);
+      r.b[j] = chunk::ldr<T>(rs[4], tt * bc_row + bcol, 0);
+      r.c[j] = chunk::ldr<T>(rs[5], tt * bc_row + bcol, 0);
     }
   };
   Raw cur, nxt;
   // the checkpointed state entering each tile (lane (k, i): state n = k of channel i), also
   // requested a tile ahead: read where it is used, its latency would stall every tile
   // (rows 16..31 of a 32-row tile own no state: they read state k - 16, unused)
+  const uint32_t ck_off = static_cast<uint32_t>((l.c * 16 + (l.k & 15)) * 4);
+  // store offsets of token 0 of this lane's chunk: (batch, L, dim) gradients and the dB/dC
+  // partials; a lane past the last channel (or past dstate) stores past every range
+  const uint32_t e_off = l.cvalid ? static_cast<uint32_t>((l.k * TC * a.dim + l.c) * 4) : chunk::kDropOffset;
+  const uint32_t bc_off = l.i < N ? static_cast<uint32_t>((l.k * TC * N + l.i) * 4) : chunk::kDropOffset;
   auto ckpt_of = [&](int64_t tile) {
-    return a.ckpt[((l.b * a.ntiles + tile * CK) * dimp + l.c) * 16 + (l.k & 15)];
+    const auto r = chunk::rsrc_tile(a.ckpt + (l.b * a.ntiles + tile * CK) * dimp * 16);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, ck_off, 0, 0);
   };
-  float ck_cur = 0.0f, ck_nxt = 0.0f;
+  uint32_t ck_cur = 0u, ck_nxt = 0u;
   if (tile_hi > tile_lo) {
-    fetch(cur, (tile_hi - 1) * TT);
-    ck_cur = ckpt_of(tile_hi - 1);
+    const int64_t tl = tile_hi - 1;
+    if ((tl + 1) * TT <= L)
+      fetch_full(cur, tl * TT, true);
+    else
+      fetch_tail(cur, tl * TT);
+    ck_cur = ckpt_of(tl);
+    // (a definition that is not a load for the first tile's registers: with a load on one path
+    // into the loop and copies on the other, the compiler waits at the start of every tile for
+    // the loads just issued)
+#pragma unroll
+    for (int j = 0; j < TC; ++j)
+      asm volatile("" : "+v"(cur.x[j]), "+v"(cur.u[j]), "+v"(cur.z[j]), "+v"(cur.b[j]), "+v"(cur.c[j]), "+v"(cur.dy[j]));
+    asm volatile("" : "+v"(ck_cur));
   }
+  // (also the per-channel constants, loaded on every path into the loop: one left in flight
+  // on a path that skips the loop makes the compiler wait at the top of every tile for all
+  // memory operations before it, the previous tile's stores included)
+  asm volatile("" : "+v"(rcarry), "+v"(bias), "+v"(Dd));
+#pragma unroll
+  for (int n = 0; n < 16; ++n) asm volatile("" : "+v"(A2[n]));
   for (int64_t tile = tile_hi - 1; tile >= tile_lo; --tile) {
     if (!SPLIT) progress_priority(nt - 1 - tile, nt);
     const int64_t t0 = tile * TT;
-    // (the tile before the first one re-reads tile 0: unused, but no branch around the loads)
-    fetch(nxt, tile > 0 ? t0 - TT : 0);
+    // the earlier tile, always a full one (the tile before the first re-reads tile 0, unused;
+    // a sequence of one, partial, tile has no full tile to read: its loads are all dropped).
+    // No branch around the loads: a loaded value that merges with another path's is widened
+    // where the paths join, and that waits for the load.
+    fetch_full(nxt, tile > 0 ? t0 - TT : 0, nt > 1);
     ck_nxt = ckpt_of(tile > 0 ? tile - 1 : 0);
+    // tokens of this lane's chunk inside the sequence (TC except in the last tile)
+    const int nval = static_cast<int>(min(static_cast<int64_t>(TC), max(static_cast<int64_t>(0), L - t0 - l.k * TC)));
     // per-token inputs of this lane's chunk (tokens past the end: zero step, zero dy)
     float dt[TC], dtu[TC], uu[TC], ds[TC], sg[TC], vb[TC], vc[TC], dyv[TC], dsl[TC];
-    bool ok[TC];
+    bool ok[TC], tvs[TC];
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
-      const int64_t t = t0 + l.k * TC + j;
-      const bool tv = t < L;
+      const bool tv = j < nval;
+      tvs[j] = tv;
       ok[j] = tv && l.cvalid;
-      const float x = widen(cur.x[j]) + bias;
+      const float x = chunk::as_f32<T>(cur.x[j]) + bias;
       dt[j] = tv ? (a.softplus ? softplus(x) : x) : 0.0f;
       sg[j] = a.softplus ? sigmoid(x) : 1.0f;
-      uu[j] = widen(cur.u[j]);
+      uu[j] = chunk::as_f32<T>(cur.u[j]);
       dtu[j] = dt[j] * uu[j];
-      dyv[j] = ok[j] ? cur.dy[j] : 0.0f;
+      dyv[j] = ok[j] ? __uint_as_float(cur.dy[j]) : 0.0f;
       float g = 1.0f;
       dsl[j] = 0.0f;
       if (GATE) {
-        const float zv = widen(cur.z[j]);
+        const float zv = chunk::as_f32<T>(cur.z[j]);
         const float s = fast_rcp(1.0f + fast_exp2(-zv * kLog2e));
         g = zv * s;
         dsl[j] = s * __builtin_fmaf(zv, 1.0f - s, 1.0f);
       }
       ds[j] = dyv[j] * g;
-      vb[j] = l.i < N ? widen(cur.b[j]) : 0.0f;
-      vc[j] = l.i < N ? widen(cur.c[j]) : 0.0f;
+      vb[j] = l.i < N ? chunk::as_f32<T>(cur.b[j]) : 0.0f;
+      vc[j] = l.i < N ? chunk::as_f32<T>(cur.c[j]) : 0.0f;
     }
 
     // forward local pass from a zero state: decays and chunk aggregates
@@ -670,7 +758,7 @@ void bwd_chunked_kernel(BwdArgs a) {
        // then the reverse fold from the adjoint of the later tile; each lane overwrites
        // exactly the words it read
       if (R == 16 || l.k < 16) {
-        float carry = ck_cur;
+        float carry = __uint_as_float(ck_cur);
 #pragma unroll
         for (int jj = 0; jj < R; ++jj) {
           const int o = jj * kS + l.k * 16 + l.i;
@@ -699,15 +787,19 @@ void bwd_chunked_kernel(BwdArgs a) {
     // Stores go through buffer resources based at this tile, a masked lane's to an offset
     // past the range (dropped), so no store sits under a branch: the compiler would wait there
     // for every memory operation in flight, the next tile's prefetch included.
+    // (resources based at this tile with offsets fixed per lane and the token step in the SGPR
+    // offset; every store of a token inside the sequence is in bounds, the others go to the
+    // drop offset)
     const int64_t eb = (l.b * L + t0) * a.dim;
-    const int64_t eleft = (a.batch * L * a.dim - eb) * 4;
-    const auto rdu = chunk::rsrc(a.du + eb, eleft);
-    const auto rdd = chunk::rsrc(a.ddelta + eb, eleft);
-    const auto rdz = chunk::rsrc(GATE ? a.dz + eb : a.du + eb, GATE ? eleft : 0);
+    const auto rdu = chunk::rsrc_tile(a.du + eb);
+    const auto rdd = chunk::rsrc_tile(a.ddelta + eb);
+    const auto rdz = chunk::rsrc_tile(GATE ? a.dz + eb : a.du + eb);
     const int64_t plane = a.batch * a.ngroups * L * N;
     const int64_t pb = ((l.b * a.ngroups + (l.c0 >> 4)) * L + t0) * N;
-    const auto rpb = chunk::rsrc(a.part_bc + pb, (plane - pb) * 4);
-    const auto rpc = chunk::rsrc(a.part_bc + plane + pb, (plane - pb) * 4);
+    const auto rpb = chunk::rsrc_tile(a.part_bc + pb);
+    const auto rpc = chunk::rsrc_tile(a.part_bc + plane + pb);
+    uint32_t er = dy_row, pr = static_cast<uint32_t>(N * 4);
+    asm volatile("" : "+s"(er), "+s"(pr));
 
     // true states of the chunk, the pre-gate output s and dz
     float H[TC][16];
@@ -715,10 +807,9 @@ void bwd_chunked_kernel(BwdArgs a) {
     for (int j = 0; j < TC; ++j) {
       float s = Dd * uu[j];
       bwd_true(j == 0 ? q : H[j > 0 ? j - 1 : 0], H[j], ex[j], dtu[j], vb[j], vc[j], s);
-      if (GATE) {
-        const uint32_t off = ok[j] ? static_cast<uint32_t>(((l.k * TC + j) * a.dim + l.c) * 4) : chunk::kDropOffset;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dyv[j] * s * dsl[j]), rdz, off, 0, 0);
-      }
+      if (GATE)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dyv[j] * s * dsl[j]), rdz,
+                                              tvs[j] ? e_off : chunk::kDropOffset, j * er, 0);
     }
 
     // true reverse recurrence and the gradient terms, token by token from the chunk end
@@ -729,13 +820,12 @@ void bwd_chunked_kernel(BwdArgs a) {
     for (int j = TC - 1; j >= 0; --j) {
       float sb = 0.0f, ga = 0.0f;
       bwd_grad(mu, dAacc, H[j], ex[j], A2, dt[j], dtu[j], ds[j], vb[j], vc[j], ga, sb, rad);
-      const int64_t t = t0 + l.k * TC + j;
       {
-        const uint32_t off = ok[j] ? static_cast<uint32_t>(((l.k * TC + j) * a.dim + l.c) * 4) : chunk::kDropOffset;
+        const uint32_t off = tvs[j] ? e_off : chunk::kDropOffset;
         const float ddt = __builtin_fmaf(uu[j], sb, ga * kLn2);
         const float dd = ddt * sg[j];
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__builtin_fmaf(ds[j], Dd, dt[j] * sb)), rdu, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dd), rdd, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__builtin_fmaf(ds[j], Dd, dt[j] * sb)), rdu, off, j * er, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dd), rdd, off, j * er, 0);
         dbacc += ok[j] ? dd : 0.0f;
         dDacc = ok[j] ? __builtin_fmaf(ds[j], uu[j], dDacc) : dDacc;
       }
@@ -764,9 +854,9 @@ void bwd_chunked_kernel(BwdArgs a) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       {
-        const uint32_t off = (t < L && l.i < N) ? static_cast<uint32_t>(((l.k * TC + j) * N + l.i) * 4) : chunk::kDropOffset;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sB), rpb, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sC), rpc, off, 0, 0);
+        const uint32_t off = tvs[j] ? bc_off : chunk::kDropOffset;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sB), rpb, off, j * pr, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sC), rpc, off, j * pr, 0);
       }
     }
     cur = nxt;
@@ -928,12 +1018,13 @@ int64_t bwd_split_part_len(int64_t seqlen, int rows, int parts) {
 // When the groups leave part of the last round of resident slots empty, split as the forward
 // does: the fewest parts within 5% of the best of max(1, ceil(groups * parts / slots) /
 // parts). The reverse kernel (~195 VGPRs) holds one 32-row or two 16-row workgroups per CU,
-// the checkpoint kernel (~140) one 32-row or three 16-row ones. At the 130M shape (768 groups
+// the checkpoint kernel (at most 128 VGPRs with 16 rows, 35 KB of LDS) one 32-row or four
+// 16-row ones. At the 130M shape (768 groups
 // of 16-row tiles) the reverse kernel's two parts took it from 569 to 526 us, and the
 // checkpoint kernel, which fills its 768 slots once, ran 9 us slower split; at 1024 groups
 // (two whole rounds of the reverse kernel) two parts measured 2% slower.
 int bwd_split_parts(int64_t groups, int rows, bool ckpt, int64_t seqlen, int cus) {
-  const int64_t slots = static_cast<int64_t>(rows == 32 ? 1 : (ckpt ? 3 : 2)) * cus;
+  const int64_t slots = static_cast<int64_t>(rows == 32 ? 1 : (ckpt ? 4 : 2)) * cus;
   if (groups <= slots || seqlen <= 0) return 1;
   auto time = [&](int p) {
     const double rounds = static_cast<double>((groups * p + slots - 1) / slots);

@@ -7,6 +7,8 @@
 // the update reads them through DPP row_newbcast:n folded into the consuming v_mul/v_fmac.
 #pragma once
 
+#include <type_traits>
+
 #include "ss_common.h"
 #include "ss_kernels.h"
 
@@ -167,6 +169,19 @@ __device__ __forceinline__ uint32_t ldb(uint16_t*, __amdgpu_buffer_rsrc_t r, uin
 template <typename T>
 __device__ __forceinline__ float as_f32(uint32_t w) {
   return __uint_as_float(sizeof(T) == 2 ? w << 16 : w);  // bf16 is the top half of an fp32
+}
+// Raw bits in the element's own width (u16 for bf16), for values carried across a loop: a
+// 32-bit copy of a 16-bit load is a zero-extension, which the compiler performs before the
+// loop's back edge, where it waits for the load; carried in its own width, the value is
+// widened only where it is used (as_f32 shifts the low half up, ignoring the rest).
+template <typename T>
+using Bits = std::conditional_t<sizeof(T) == 2, uint16_t, uint32_t>;
+template <typename T>
+__device__ __forceinline__ Bits<T> ldr(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (sizeof(T) == 2)
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  else
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 // An element widened to fp32 at the load (for loads consumed soon after).
 template <typename T>
