@@ -149,214 +149,53 @@ __device__ __forceinline__ void bwd_rlocal(float (&m)[16], const float (&e)[16],
 #undef BW_R
 
 // True reverse step of one token and its gradient terms (lam = m + ds C[n] in m[n]):
-//   g = lam (H[n] - dtu B[n])  (= lam abar h_prev);  dA[n] += dt g;  ga += A2[n] g;
-//   sb += B[n] lam;  LDS[ad + 64 n] = lam dtu (dB term);  LDS[ad + RC + 64 n] = ds H[n] (dC);
-//   m[n] = e[n] lam (the adjoint passed to the previous token).
-// The LDS data registers rotate over three temporaries.
+//   LDS[ad + 64 n] = lam dtu (dB term);  LDS[ad + RC + 64 n] = ds H[n] (dC term);
+//   sb += B[n] lam;  m[n] = e[n] lam (the adjoint passed to the previous token);
+//   g = m[n] P[n] (= lam abar h_prev, P the states entering the token);
+//   dA[n] += dt g;  ga += A2[n] g.
+// The LDS data registers rotate over three temporaries, g over two.
+#define BW_G(n, T, U, G, OB, OC)                                              \
+  "v_fmac_f32_dpp %[m" #n "], %[vc], %[ds]" SS_DPP_ROW(n)                     \
+  "v_mul_f32 %[" U "], %[ds], %[H" #n "]\n"                                   \
+  "v_mul_f32 %[" T "], %[m" #n "], %[dtu]\n"                                  \
+  "v_fmac_f32_dpp %[sb], %[vb], %[m" #n "]" SS_DPP_ROW(n)                     \
+  "ds_write_b32 %[ad], %[" T "] offset:" OB "\n"                              \
+  "ds_write_b32 %[ad], %[" U "] offset:" OC "\n"                              \
+  "v_mul_f32 %[m" #n "], %[e" #n "], %[m" #n "]\n"                            \
+  "v_mul_f32 %[" G "], %[m" #n "], %[P" #n "]\n"                              \
+  "v_fmac_f32 %[dA" #n "], %[dt], %[" G "]\n"                                 \
+  "v_fmac_f32 %[ga], %[a" #n "], %[" G "]\n"
+
 __device__ __forceinline__ void bwd_grad(float (&m)[16], float (&dA)[16], const float (&H)[16],
-                                         const float (&e)[16], const float (&a)[16], float dt, float dtu,
-                                         float ds, float vb, float vc, float& ga, float& sb, uint32_t ad) {
-  float t0, t1, t2, u0, u1, u2;
+                                         const float (&P)[16], const float (&e)[16], const float (&a)[16],
+                                         float dt, float dtu, float ds, float vb, float vc, float& ga,
+                                         float& sb, uint32_t ad) {
+  float t0, t1, t2, u0, u1, u2, g0, g1;
   asm volatile(
       "s_nop 1\n"
-      "v_fmac_f32_dpp %[m0], %[vc], %[ds]" SS_DPP_ROW(0)
-      "v_mul_f32_dpp %[t0], %[vb], %[dtu]" SS_DPP_ROW(0)
-      "v_sub_f32 %[t0], %[H0], %[t0]\n"
-      "v_mul_f32 %[t0], %[m0], %[t0]\n"
-      "v_fmac_f32 %[dA0], %[dt], %[t0]\n"
-      "v_fmac_f32 %[ga], %[a0], %[t0]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m0]" SS_DPP_ROW(0)
-      "v_mul_f32 %[t0], %[m0], %[dtu]\n"
-      "v_mul_f32 %[u0], %[ds], %[H0]\n"
-      "ds_write_b32 %[ad], %[t0] offset:0\n"
-      "ds_write_b32 %[ad], %[u0] offset:4352\n"
-      "v_mul_f32 %[m0], %[e0], %[m0]\n"
-      "v_fmac_f32_dpp %[m1], %[vc], %[ds]" SS_DPP_ROW(1)
-      "v_mul_f32_dpp %[t1], %[vb], %[dtu]" SS_DPP_ROW(1)
-      "v_sub_f32 %[t1], %[H1], %[t1]\n"
-      "v_mul_f32 %[t1], %[m1], %[t1]\n"
-      "v_fmac_f32 %[dA1], %[dt], %[t1]\n"
-      "v_fmac_f32 %[ga], %[a1], %[t1]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m1]" SS_DPP_ROW(1)
-      "v_mul_f32 %[t1], %[m1], %[dtu]\n"
-      "v_mul_f32 %[u1], %[ds], %[H1]\n"
-      "ds_write_b32 %[ad], %[t1] offset:64\n"
-      "ds_write_b32 %[ad], %[u1] offset:4416\n"
-      "v_mul_f32 %[m1], %[e1], %[m1]\n"
-      "v_fmac_f32_dpp %[m2], %[vc], %[ds]" SS_DPP_ROW(2)
-      "v_mul_f32_dpp %[t2], %[vb], %[dtu]" SS_DPP_ROW(2)
-      "v_sub_f32 %[t2], %[H2], %[t2]\n"
-      "v_mul_f32 %[t2], %[m2], %[t2]\n"
-      "v_fmac_f32 %[dA2], %[dt], %[t2]\n"
-      "v_fmac_f32 %[ga], %[a2], %[t2]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m2]" SS_DPP_ROW(2)
-      "v_mul_f32 %[t2], %[m2], %[dtu]\n"
-      "v_mul_f32 %[u2], %[ds], %[H2]\n"
-      "ds_write_b32 %[ad], %[t2] offset:128\n"
-      "ds_write_b32 %[ad], %[u2] offset:4480\n"
-      "v_mul_f32 %[m2], %[e2], %[m2]\n"
-      "v_fmac_f32_dpp %[m3], %[vc], %[ds]" SS_DPP_ROW(3)
-      "v_mul_f32_dpp %[t0], %[vb], %[dtu]" SS_DPP_ROW(3)
-      "v_sub_f32 %[t0], %[H3], %[t0]\n"
-      "v_mul_f32 %[t0], %[m3], %[t0]\n"
-      "v_fmac_f32 %[dA3], %[dt], %[t0]\n"
-      "v_fmac_f32 %[ga], %[a3], %[t0]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m3]" SS_DPP_ROW(3)
-      "v_mul_f32 %[t0], %[m3], %[dtu]\n"
-      "v_mul_f32 %[u0], %[ds], %[H3]\n"
-      "ds_write_b32 %[ad], %[t0] offset:192\n"
-      "ds_write_b32 %[ad], %[u0] offset:4544\n"
-      "v_mul_f32 %[m3], %[e3], %[m3]\n"
-      "v_fmac_f32_dpp %[m4], %[vc], %[ds]" SS_DPP_ROW(4)
-      "v_mul_f32_dpp %[t1], %[vb], %[dtu]" SS_DPP_ROW(4)
-      "v_sub_f32 %[t1], %[H4], %[t1]\n"
-      "v_mul_f32 %[t1], %[m4], %[t1]\n"
-      "v_fmac_f32 %[dA4], %[dt], %[t1]\n"
-      "v_fmac_f32 %[ga], %[a4], %[t1]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m4]" SS_DPP_ROW(4)
-      "v_mul_f32 %[t1], %[m4], %[dtu]\n"
-      "v_mul_f32 %[u1], %[ds], %[H4]\n"
-      "ds_write_b32 %[ad], %[t1] offset:256\n"
-      "ds_write_b32 %[ad], %[u1] offset:4608\n"
-      "v_mul_f32 %[m4], %[e4], %[m4]\n"
-      "v_fmac_f32_dpp %[m5], %[vc], %[ds]" SS_DPP_ROW(5)
-      "v_mul_f32_dpp %[t2], %[vb], %[dtu]" SS_DPP_ROW(5)
-      "v_sub_f32 %[t2], %[H5], %[t2]\n"
-      "v_mul_f32 %[t2], %[m5], %[t2]\n"
-      "v_fmac_f32 %[dA5], %[dt], %[t2]\n"
-      "v_fmac_f32 %[ga], %[a5], %[t2]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m5]" SS_DPP_ROW(5)
-      "v_mul_f32 %[t2], %[m5], %[dtu]\n"
-      "v_mul_f32 %[u2], %[ds], %[H5]\n"
-      "ds_write_b32 %[ad], %[t2] offset:320\n"
-      "ds_write_b32 %[ad], %[u2] offset:4672\n"
-      "v_mul_f32 %[m5], %[e5], %[m5]\n"
-      "v_fmac_f32_dpp %[m6], %[vc], %[ds]" SS_DPP_ROW(6)
-      "v_mul_f32_dpp %[t0], %[vb], %[dtu]" SS_DPP_ROW(6)
-      "v_sub_f32 %[t0], %[H6], %[t0]\n"
-      "v_mul_f32 %[t0], %[m6], %[t0]\n"
-      "v_fmac_f32 %[dA6], %[dt], %[t0]\n"
-      "v_fmac_f32 %[ga], %[a6], %[t0]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m6]" SS_DPP_ROW(6)
-      "v_mul_f32 %[t0], %[m6], %[dtu]\n"
-      "v_mul_f32 %[u0], %[ds], %[H6]\n"
-      "ds_write_b32 %[ad], %[t0] offset:384\n"
-      "ds_write_b32 %[ad], %[u0] offset:4736\n"
-      "v_mul_f32 %[m6], %[e6], %[m6]\n"
-      "v_fmac_f32_dpp %[m7], %[vc], %[ds]" SS_DPP_ROW(7)
-      "v_mul_f32_dpp %[t1], %[vb], %[dtu]" SS_DPP_ROW(7)
-      "v_sub_f32 %[t1], %[H7], %[t1]\n"
-      "v_mul_f32 %[t1], %[m7], %[t1]\n"
-      "v_fmac_f32 %[dA7], %[dt], %[t1]\n"
-      "v_fmac_f32 %[ga], %[a7], %[t1]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m7]" SS_DPP_ROW(7)
-      "v_mul_f32 %[t1], %[m7], %[dtu]\n"
-      "v_mul_f32 %[u1], %[ds], %[H7]\n"
-      "ds_write_b32 %[ad], %[t1] offset:448\n"
-      "ds_write_b32 %[ad], %[u1] offset:4800\n"
-      "v_mul_f32 %[m7], %[e7], %[m7]\n"
-      "v_fmac_f32_dpp %[m8], %[vc], %[ds]" SS_DPP_ROW(8)
-      "v_mul_f32_dpp %[t2], %[vb], %[dtu]" SS_DPP_ROW(8)
-      "v_sub_f32 %[t2], %[H8], %[t2]\n"
-      "v_mul_f32 %[t2], %[m8], %[t2]\n"
-      "v_fmac_f32 %[dA8], %[dt], %[t2]\n"
-      "v_fmac_f32 %[ga], %[a8], %[t2]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m8]" SS_DPP_ROW(8)
-      "v_mul_f32 %[t2], %[m8], %[dtu]\n"
-      "v_mul_f32 %[u2], %[ds], %[H8]\n"
-      "ds_write_b32 %[ad], %[t2] offset:512\n"
-      "ds_write_b32 %[ad], %[u2] offset:4864\n"
-      "v_mul_f32 %[m8], %[e8], %[m8]\n"
-      "v_fmac_f32_dpp %[m9], %[vc], %[ds]" SS_DPP_ROW(9)
-      "v_mul_f32_dpp %[t0], %[vb], %[dtu]" SS_DPP_ROW(9)
-      "v_sub_f32 %[t0], %[H9], %[t0]\n"
-      "v_mul_f32 %[t0], %[m9], %[t0]\n"
-      "v_fmac_f32 %[dA9], %[dt], %[t0]\n"
-      "v_fmac_f32 %[ga], %[a9], %[t0]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m9]" SS_DPP_ROW(9)
-      "v_mul_f32 %[t0], %[m9], %[dtu]\n"
-      "v_mul_f32 %[u0], %[ds], %[H9]\n"
-      "ds_write_b32 %[ad], %[t0] offset:576\n"
-      "ds_write_b32 %[ad], %[u0] offset:4928\n"
-      "v_mul_f32 %[m9], %[e9], %[m9]\n"
-      "v_fmac_f32_dpp %[m10], %[vc], %[ds]" SS_DPP_ROW(10)
-      "v_mul_f32_dpp %[t1], %[vb], %[dtu]" SS_DPP_ROW(10)
-      "v_sub_f32 %[t1], %[H10], %[t1]\n"
-      "v_mul_f32 %[t1], %[m10], %[t1]\n"
-      "v_fmac_f32 %[dA10], %[dt], %[t1]\n"
-      "v_fmac_f32 %[ga], %[a10], %[t1]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m10]" SS_DPP_ROW(10)
-      "v_mul_f32 %[t1], %[m10], %[dtu]\n"
-      "v_mul_f32 %[u1], %[ds], %[H10]\n"
-      "ds_write_b32 %[ad], %[t1] offset:640\n"
-      "ds_write_b32 %[ad], %[u1] offset:4992\n"
-      "v_mul_f32 %[m10], %[e10], %[m10]\n"
-      "v_fmac_f32_dpp %[m11], %[vc], %[ds]" SS_DPP_ROW(11)
-      "v_mul_f32_dpp %[t2], %[vb], %[dtu]" SS_DPP_ROW(11)
-      "v_sub_f32 %[t2], %[H11], %[t2]\n"
-      "v_mul_f32 %[t2], %[m11], %[t2]\n"
-      "v_fmac_f32 %[dA11], %[dt], %[t2]\n"
-      "v_fmac_f32 %[ga], %[a11], %[t2]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m11]" SS_DPP_ROW(11)
-      "v_mul_f32 %[t2], %[m11], %[dtu]\n"
-      "v_mul_f32 %[u2], %[ds], %[H11]\n"
-      "ds_write_b32 %[ad], %[t2] offset:704\n"
-      "ds_write_b32 %[ad], %[u2] offset:5056\n"
-      "v_mul_f32 %[m11], %[e11], %[m11]\n"
-      "v_fmac_f32_dpp %[m12], %[vc], %[ds]" SS_DPP_ROW(12)
-      "v_mul_f32_dpp %[t0], %[vb], %[dtu]" SS_DPP_ROW(12)
-      "v_sub_f32 %[t0], %[H12], %[t0]\n"
-      "v_mul_f32 %[t0], %[m12], %[t0]\n"
-      "v_fmac_f32 %[dA12], %[dt], %[t0]\n"
-      "v_fmac_f32 %[ga], %[a12], %[t0]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m12]" SS_DPP_ROW(12)
-      "v_mul_f32 %[t0], %[m12], %[dtu]\n"
-      "v_mul_f32 %[u0], %[ds], %[H12]\n"
-      "ds_write_b32 %[ad], %[t0] offset:768\n"
-      "ds_write_b32 %[ad], %[u0] offset:5120\n"
-      "v_mul_f32 %[m12], %[e12], %[m12]\n"
-      "v_fmac_f32_dpp %[m13], %[vc], %[ds]" SS_DPP_ROW(13)
-      "v_mul_f32_dpp %[t1], %[vb], %[dtu]" SS_DPP_ROW(13)
-      "v_sub_f32 %[t1], %[H13], %[t1]\n"
-      "v_mul_f32 %[t1], %[m13], %[t1]\n"
-      "v_fmac_f32 %[dA13], %[dt], %[t1]\n"
-      "v_fmac_f32 %[ga], %[a13], %[t1]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m13]" SS_DPP_ROW(13)
-      "v_mul_f32 %[t1], %[m13], %[dtu]\n"
-      "v_mul_f32 %[u1], %[ds], %[H13]\n"
-      "ds_write_b32 %[ad], %[t1] offset:832\n"
-      "ds_write_b32 %[ad], %[u1] offset:5184\n"
-      "v_mul_f32 %[m13], %[e13], %[m13]\n"
-      "v_fmac_f32_dpp %[m14], %[vc], %[ds]" SS_DPP_ROW(14)
-      "v_mul_f32_dpp %[t2], %[vb], %[dtu]" SS_DPP_ROW(14)
-      "v_sub_f32 %[t2], %[H14], %[t2]\n"
-      "v_mul_f32 %[t2], %[m14], %[t2]\n"
-      "v_fmac_f32 %[dA14], %[dt], %[t2]\n"
-      "v_fmac_f32 %[ga], %[a14], %[t2]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m14]" SS_DPP_ROW(14)
-      "v_mul_f32 %[t2], %[m14], %[dtu]\n"
-      "v_mul_f32 %[u2], %[ds], %[H14]\n"
-      "ds_write_b32 %[ad], %[t2] offset:896\n"
-      "ds_write_b32 %[ad], %[u2] offset:5248\n"
-      "v_mul_f32 %[m14], %[e14], %[m14]\n"
-      "v_fmac_f32_dpp %[m15], %[vc], %[ds]" SS_DPP_ROW(15)
-      "v_mul_f32_dpp %[t0], %[vb], %[dtu]" SS_DPP_ROW(15)
-      "v_sub_f32 %[t0], %[H15], %[t0]\n"
-      "v_mul_f32 %[t0], %[m15], %[t0]\n"
-      "v_fmac_f32 %[dA15], %[dt], %[t0]\n"
-      "v_fmac_f32 %[ga], %[a15], %[t0]\n"
-      "v_fmac_f32_dpp %[sb], %[vb], %[m15]" SS_DPP_ROW(15)
-      "v_mul_f32 %[t0], %[m15], %[dtu]\n"
-      "v_mul_f32 %[u0], %[ds], %[H15]\n"
-      "ds_write_b32 %[ad], %[t0] offset:960\n"
-      "ds_write_b32 %[ad], %[u0] offset:5312\n"
-      "v_mul_f32 %[m15], %[e15], %[m15]\n"
+      BW_G(0, "t0", "u0", "g0", "0", "4352")
+      BW_G(1, "t1", "u1", "g1", "64", "4416")
+      BW_G(2, "t2", "u2", "g0", "128", "4480")
+      BW_G(3, "t0", "u0", "g1", "192", "4544")
+      BW_G(4, "t1", "u1", "g0", "256", "4608")
+      BW_G(5, "t2", "u2", "g1", "320", "4672")
+      BW_G(6, "t0", "u0", "g0", "384", "4736")
+      BW_G(7, "t1", "u1", "g1", "448", "4800")
+      BW_G(8, "t2", "u2", "g0", "512", "4864")
+      BW_G(9, "t0", "u0", "g1", "576", "4928")
+      BW_G(10, "t1", "u1", "g0", "640", "4992")
+      BW_G(11, "t2", "u2", "g1", "704", "5056")
+      BW_G(12, "t0", "u0", "g0", "768", "5120")
+      BW_G(13, "t1", "u1", "g1", "832", "5184")
+      BW_G(14, "t2", "u2", "g0", "896", "5248")
+      BW_G(15, "t0", "u0", "g1", "960", "5312")
       : SS_OPS16(m, "+v"), SS_OPS16(dA, "+v"), [ga] "+v"(ga), [sb] "+v"(sb), [t0] "=&v"(t0), [t1] "=&v"(t1),
-        [t2] "=&v"(t2), [u0] "=&v"(u0), [u1] "=&v"(u1), [u2] "=&v"(u2)
-      : SS_OPS16(H, "v"), SS_OPS16(e, "v"), SS_OPS16(a, "v"), [dt] "v"(dt), [dtu] "v"(dtu), [ds] "v"(ds),
-        [vb] "v"(vb), [vc] "v"(vc), [ad] "v"(ad)
+        [t2] "=&v"(t2), [u0] "=&v"(u0), [u1] "=&v"(u1), [u2] "=&v"(u2), [g0] "=&v"(g0), [g1] "=&v"(g1)
+      : SS_OPS16(H, "v"), SS_OPS16(P, "v"), SS_OPS16(e, "v"), SS_OPS16(a, "v"), [dt] "v"(dt), [dtu] "v"(dtu),
+        [ds] "v"(ds), [vb] "v"(vb), [vc] "v"(vc), [ad] "v"(ad)
       : "memory");
 }
+#undef BW_G
 
 // LDS byte address of a __shared__ float (for the ds_write instructions of bwd_grad).
 __device__ __forceinline__ uint32_t lds_addr(float* p) {
@@ -819,7 +658,8 @@ void bwd_chunked_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = TC - 1; j >= 0; --j) {
       float sb = 0.0f, ga = 0.0f;
-      bwd_grad(mu, dAacc, H[j], ex[j], A2, dt[j], dtu[j], ds[j], vb[j], vc[j], ga, sb, rad);
+      bwd_grad(mu, dAacc, H[j], j == 0 ? q : H[j > 0 ? j - 1 : 0], ex[j], A2, dt[j], dtu[j], ds[j], vb[j],
+               vc[j], ga, sb, rad);
       {
         const uint32_t off = tvs[j] ? e_off : chunk::kDropOffset;
         const float ddt = __builtin_fmaf(uu[j], sb, ga * kLn2);
