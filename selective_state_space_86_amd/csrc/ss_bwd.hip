@@ -148,13 +148,111 @@ __device__ __forceinline__ void bwd_rlocal(float (&m)[16], const float (&e)[16],
 }
 #undef BW_R
 
-// True reverse step of one token and its gradient terms (lam = m + ds C[n] in m[n]):
+// True reverse step of one token and its gradient terms, the adjoint in m on entry:
+//   lam = m[n] + ds C[n] (kept in m[n]);  sb += B[n] lam;  o[n] = e[n] lam (the adjoint
+//   passed to the previous token);  g = o[n] P[n] (= lam abar h_prev, P the states entering
+//   the token);  dA[n] += dt g;  ga += A2[n] g;
+//   LDS: lam at row n of the dB block, H[n] at row n of the dC block (column: this lane's
+//   channel c, in the 16-byte quarter (c >> 2) ^ (n >> 2) of the row; ad[q] addresses the
+//   lane's word for the rows n with n >> 2 = q). The channel sums weight them by dtu and ds
+//   (bwd_rowsum). Written straight from lam and H, which nothing overwrites while the writes
+//   are in flight: the new adjoint goes to o, and the caller alternates m and o by token.
+#define BW_G(n, G, AD, OB, OC)                                                \
+  "v_fmac_f32_dpp %[m" #n "], %[vc], %[ds]" SS_DPP_ROW(n)                     \
+  "v_mul_f32 %[o" #n "], %[e" #n "], %[m" #n "]\n"                            \
+  "v_mul_f32 %[" G "], %[o" #n "], %[P" #n "]\n"                              \
+  "v_fmac_f32_dpp %[sb], %[vb], %[m" #n "]" SS_DPP_ROW(n)                     \
+  "ds_write_b32 %[" AD "], %[m" #n "] offset:" OB "\n"                        \
+  "ds_write_b32 %[" AD "], %[H" #n "] offset:" OC "\n"                        \
+  "v_fmac_f32 %[dA" #n "], %[dt], %[" G "]\n"                                 \
+  "v_fmac_f32 %[ga], %[a" #n "], %[" G "]\n"
+
+__device__ __forceinline__ void bwd_grad(float (&m)[16], float (&o)[16], float (&dA)[16], const float (&H)[16],
+                                         const float (&P)[16], const float (&e)[16], const float (&a)[16],
+                                         float dt, float ds, float vb, float vc, float& ga, float& sb,
+                                         const uint32_t (&ad)[4]) {
+  float g0, g1;
+  asm volatile(
+      "s_nop 1\n"
+      BW_G(0, "g0", "ad0", "0", "4352")
+      BW_G(1, "g1", "ad0", "64", "4416")
+      BW_G(2, "g0", "ad0", "128", "4480")
+      BW_G(3, "g1", "ad0", "192", "4544")
+      BW_G(4, "g0", "ad1", "256", "4608")
+      BW_G(5, "g1", "ad1", "320", "4672")
+      BW_G(6, "g0", "ad1", "384", "4736")
+      BW_G(7, "g1", "ad1", "448", "4800")
+      BW_G(8, "g0", "ad2", "512", "4864")
+      BW_G(9, "g1", "ad2", "576", "4928")
+      BW_G(10, "g0", "ad2", "640", "4992")
+      BW_G(11, "g1", "ad2", "704", "5056")
+      BW_G(12, "g0", "ad3", "768", "5120")
+      BW_G(13, "g1", "ad3", "832", "5184")
+      BW_G(14, "g0", "ad3", "896", "5248")
+      BW_G(15, "g1", "ad3", "960", "5312")
+      : SS_OPS16(m, "+v"), SS_OPS16(o, "=&v"), SS_OPS16(dA, "+v"), [ga] "+v"(ga), [sb] "+v"(sb),
+        [g0] "=&v"(g0), [g1] "=&v"(g1)
+      : SS_OPS16(H, "v"), SS_OPS16(P, "v"), SS_OPS16(e, "v"), SS_OPS16(a, "v"), [dt] "v"(dt), [ds] "v"(ds),
+        [vb] "v"(vb), [vc] "v"(vc), [ad0] "v"(ad[0]), [ad1] "v"(ad[1]), [ad2] "v"(ad[2]), [ad3] "v"(ad[3])
+      : "memory");
+}
+#undef BW_G
+
+// Channel sums of one token's dB and dC terms for state n (the reading lane's index in its
+// row): b0..b3 and c0..c3 are the logical channel quarters of row n of the dB and dC blocks;
+// channel c's terms are weighted by dtu and ds of channel c, broadcast from lane c of the row:
+//   sb = sum_c dtu_c lam_c[n],  sc = sum_c ds_c H_c[n].
+__device__ __forceinline__ void bwd_rowsum(float4 b0, float4 b1, float4 b2, float4 b3, float4 c0, float4 c1,
+                                           float4 c2, float4 c3, float dtu, float ds, float& sb, float& sc) {
+  sb = 0.0f;
+  sc = 0.0f;
+  asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b0x]" SS_DPP_ROW(0)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c0x]" SS_DPP_ROW(0)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b0y]" SS_DPP_ROW(1)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c0y]" SS_DPP_ROW(1)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b0z]" SS_DPP_ROW(2)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c0z]" SS_DPP_ROW(2)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b0w]" SS_DPP_ROW(3)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c0w]" SS_DPP_ROW(3)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b1x]" SS_DPP_ROW(4)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c1x]" SS_DPP_ROW(4)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b1y]" SS_DPP_ROW(5)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c1y]" SS_DPP_ROW(5)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b1z]" SS_DPP_ROW(6)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c1z]" SS_DPP_ROW(6)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b1w]" SS_DPP_ROW(7)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c1w]" SS_DPP_ROW(7)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b2x]" SS_DPP_ROW(8)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c2x]" SS_DPP_ROW(8)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b2y]" SS_DPP_ROW(9)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c2y]" SS_DPP_ROW(9)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b2z]" SS_DPP_ROW(10)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c2z]" SS_DPP_ROW(10)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b2w]" SS_DPP_ROW(11)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c2w]" SS_DPP_ROW(11)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b3x]" SS_DPP_ROW(12)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c3x]" SS_DPP_ROW(12)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b3y]" SS_DPP_ROW(13)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c3y]" SS_DPP_ROW(13)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b3z]" SS_DPP_ROW(14)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c3z]" SS_DPP_ROW(14)
+      "v_fmac_f32_dpp %[sb], %[dtu], %[b3w]" SS_DPP_ROW(15)
+      "v_fmac_f32_dpp %[sc], %[ds], %[c3w]" SS_DPP_ROW(15)
+      : [sb] "+v"(sb), [sc] "+v"(sc)
+      : [dtu] "v"(dtu), [ds] "v"(ds), [b0x] "v"(b0.x), [b0y] "v"(b0.y), [b0z] "v"(b0.z), [b0w] "v"(b0.w), [b1x] "v"(b1.x), [b1y] "v"(b1.y), [b1z] "v"(b1.z), [b1w] "v"(b1.w), [b2x] "v"(b2.x), [b2y] "v"(b2.y), [b2z] "v"(b2.z), [b2w] "v"(b2.w), [b3x] "v"(b3.x), [b3y] "v"(b3.y), [b3z] "v"(b3.z), [b3w] "v"(b3.w),
+        [c0x] "v"(c0.x), [c0y] "v"(c0.y), [c0z] "v"(c0.z), [c0w] "v"(c0.w), [c1x] "v"(c1.x), [c1y] "v"(c1.y), [c1z] "v"(c1.z), [c1w] "v"(c1.w), [c2x] "v"(c2.x), [c2y] "v"(c2.y), [c2z] "v"(c2.z), [c2w] "v"(c2.w), [c3x] "v"(c3.x), [c3y] "v"(c3.y), [c3z] "v"(c3.z), [c3w] "v"(c3.w));
+}
+
+// bwd_grad for the 32-row tiles, writing the weighted terms themselves (lam = m + ds C[n] in
+// m[n]):
 //   LDS[ad + 64 n] = lam dtu (dB term);  LDS[ad + RC + 64 n] = ds H[n] (dC term);
 //   sb += B[n] lam;  m[n] = e[n] lam (the adjoint passed to the previous token);
 //   g = m[n] P[n] (= lam abar h_prev, P the states entering the token);
 //   dA[n] += dt g;  ga += A2[n] g.
 // The LDS data registers rotate over three temporaries, g over two.
-#define BW_G(n, T, U, G, OB, OC)                                              \
+#define BW_GP(n, T, U, G, OB, OC)                                              \
   "v_fmac_f32_dpp %[m" #n "], %[vc], %[ds]" SS_DPP_ROW(n)                     \
   "v_mul_f32 %[" U "], %[ds], %[H" #n "]\n"                                   \
   "v_mul_f32 %[" T "], %[m" #n "], %[dtu]\n"                                  \
@@ -166,36 +264,36 @@ __device__ __forceinline__ void bwd_rlocal(float (&m)[16], const float (&e)[16],
   "v_fmac_f32 %[dA" #n "], %[dt], %[" G "]\n"                                 \
   "v_fmac_f32 %[ga], %[a" #n "], %[" G "]\n"
 
-__device__ __forceinline__ void bwd_grad(float (&m)[16], float (&dA)[16], const float (&H)[16],
+__device__ __forceinline__ void bwd_grad_products(float (&m)[16], float (&dA)[16], const float (&H)[16],
                                          const float (&P)[16], const float (&e)[16], const float (&a)[16],
                                          float dt, float dtu, float ds, float vb, float vc, float& ga,
                                          float& sb, uint32_t ad) {
   float t0, t1, t2, u0, u1, u2, g0, g1;
   asm volatile(
       "s_nop 1\n"
-      BW_G(0, "t0", "u0", "g0", "0", "4352")
-      BW_G(1, "t1", "u1", "g1", "64", "4416")
-      BW_G(2, "t2", "u2", "g0", "128", "4480")
-      BW_G(3, "t0", "u0", "g1", "192", "4544")
-      BW_G(4, "t1", "u1", "g0", "256", "4608")
-      BW_G(5, "t2", "u2", "g1", "320", "4672")
-      BW_G(6, "t0", "u0", "g0", "384", "4736")
-      BW_G(7, "t1", "u1", "g1", "448", "4800")
-      BW_G(8, "t2", "u2", "g0", "512", "4864")
-      BW_G(9, "t0", "u0", "g1", "576", "4928")
-      BW_G(10, "t1", "u1", "g0", "640", "4992")
-      BW_G(11, "t2", "u2", "g1", "704", "5056")
-      BW_G(12, "t0", "u0", "g0", "768", "5120")
-      BW_G(13, "t1", "u1", "g1", "832", "5184")
-      BW_G(14, "t2", "u2", "g0", "896", "5248")
-      BW_G(15, "t0", "u0", "g1", "960", "5312")
+      BW_GP(0, "t0", "u0", "g0", "0", "4352")
+      BW_GP(1, "t1", "u1", "g1", "64", "4416")
+      BW_GP(2, "t2", "u2", "g0", "128", "4480")
+      BW_GP(3, "t0", "u0", "g1", "192", "4544")
+      BW_GP(4, "t1", "u1", "g0", "256", "4608")
+      BW_GP(5, "t2", "u2", "g1", "320", "4672")
+      BW_GP(6, "t0", "u0", "g0", "384", "4736")
+      BW_GP(7, "t1", "u1", "g1", "448", "4800")
+      BW_GP(8, "t2", "u2", "g0", "512", "4864")
+      BW_GP(9, "t0", "u0", "g1", "576", "4928")
+      BW_GP(10, "t1", "u1", "g0", "640", "4992")
+      BW_GP(11, "t2", "u2", "g1", "704", "5056")
+      BW_GP(12, "t0", "u0", "g0", "768", "5120")
+      BW_GP(13, "t1", "u1", "g1", "832", "5184")
+      BW_GP(14, "t2", "u2", "g0", "896", "5248")
+      BW_GP(15, "t0", "u0", "g1", "960", "5312")
       : SS_OPS16(m, "+v"), SS_OPS16(dA, "+v"), [ga] "+v"(ga), [sb] "+v"(sb), [t0] "=&v"(t0), [t1] "=&v"(t1),
         [t2] "=&v"(t2), [u0] "=&v"(u0), [u1] "=&v"(u1), [u2] "=&v"(u2), [g0] "=&v"(g0), [g1] "=&v"(g1)
       : SS_OPS16(H, "v"), SS_OPS16(P, "v"), SS_OPS16(e, "v"), SS_OPS16(a, "v"), [dt] "v"(dt), [dtu] "v"(dtu),
         [ds] "v"(ds), [vb] "v"(vb), [vc] "v"(vc), [ad] "v"(ad)
       : "memory");
 }
-#undef BW_G
+#undef BW_GP
 
 // LDS byte address of a __shared__ float (for the ds_write instructions of bwd_grad).
 __device__ __forceinline__ uint32_t lds_addr(float* p) {
@@ -654,50 +752,119 @@ void bwd_chunked_kernel(BwdArgs a) {
     // true reverse recurrence and the gradient terms, token by token from the chunk end
     float* rB = &lds_eh[0][0] + w * (2 * 4 * kS) + rw * kS;  // this row's dB block; dC 4*kS on
     const float* rC = rB + 4 * kS;
-    const uint32_t rad = lds_addr(rB + l.i);
+    // Two ways to sum the dB and dC terms over the 16 channels of a row. With 16-row tiles
+    // (two workgroups per CU) the terms are written unweighted and the sums weight them by a
+    // DPP broadcast of each channel's dtu and ds, 2 VALU per update fewer (130M backward 0.673
+    // -> 0.630 ms, 1.4B 1.735 -> 1.648 ms). With 32-row tiles the eight waves of the CU's one
+    // workgroup reach their LDS bursts in step, and that layout made them wait 51% longer to
+    // issue LDS instructions (3B long context: 14.43 -> 15.14 ms), so they write the weighted
+    // terms and sum them with plain adds as each quarter arrives.
+    if constexpr (R == 32) {
+      const uint32_t rad = lds_addr(rB + l.i);
 #pragma unroll
-    for (int j = TC - 1; j >= 0; --j) {
-      float sb = 0.0f, ga = 0.0f;
-      bwd_grad(mu, dAacc, H[j], j == 0 ? q : H[j > 0 ? j - 1 : 0], ex[j], A2, dt[j], dtu[j], ds[j], vb[j],
-               vc[j], ga, sb, rad);
-      {
-        const uint32_t off = tvs[j] ? e_off : chunk::kDropOffset;
-        const float ddt = __builtin_fmaf(uu[j], sb, ga * kLn2);
-        const float dd = ddt * sg[j];
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__builtin_fmaf(ds[j], Dd, dt[j] * sb)), rdu, off, j * er, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dd), rdd, off, j * er, 0);
-        dbacc += ok[j] ? dd : 0.0f;
-        dDacc = ok[j] ? __builtin_fmaf(ds[j], uu[j], dDacc) : dDacc;
-      }
-      // sum the 16 channels of this row: lane i takes state n = i (the block is this row's
-      // own and LDS runs a wave's operations in order: the fences only keep the compiler
-      // from moving the accesses across the other lanes' writes)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      float sB = 0.0f, sC = 0.0f;
-      {
-        // (lane i reads the quarters of its 64-byte row in the order starting at i / 4: rows
-        // of lanes i and i + 4 sit 256 bytes apart, on the same banks, so in one 16-byte read
-        // the 16 lanes of a row touch 16 different bank groups only when their quarters differ)
-        const float4* qb = reinterpret_cast<const float4*>(rB + l.i * 16);
-        const float4* qc = reinterpret_cast<const float4*>(rC + l.i * 16);
+      for (int j = TC - 1; j >= 0; --j) {
+        float sb = 0.0f, ga = 0.0f;
+        bwd_grad_products(mu, dAacc, H[j], j == 0 ? q : H[j > 0 ? j - 1 : 0], ex[j], A2, dt[j], dtu[j], ds[j],
+                          vb[j], vc[j], ga, sb, rad);
+        {
+          const uint32_t off = tvs[j] ? e_off : chunk::kDropOffset;
+          const float ddt = __builtin_fmaf(uu[j], sb, ga * kLn2);
+          const float dd = ddt * sg[j];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__builtin_fmaf(ds[j], Dd, dt[j] * sb)), rdu, off, j * er, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dd), rdd, off, j * er, 0);
+          dbacc += ok[j] ? dd : 0.0f;
+          dDacc = ok[j] ? __builtin_fmaf(ds[j], uu[j], dDacc) : dDacc;
+        }
+        // sum the 16 channels of this row: lane i takes state n = i (the block is this row's
+        // own and LDS runs a wave's operations in order: the fences only keep the compiler
+        // from moving the accesses across the other lanes' writes)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float sB = 0.0f, sC = 0.0f;
+        {
+          // (lane i reads the quarters of its 64-byte row in the order starting at i / 4: rows
+          // of lanes i and i + 4 sit 256 bytes apart, on the same banks, so in one 16-byte read
+          // the 16 lanes of a row touch 16 different bank groups only when their quarters differ)
+          const float4* qb = reinterpret_cast<const float4*>(rB + l.i * 16);
+          const float4* qc = reinterpret_cast<const float4*>(rC + l.i * 16);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int mm = (m + (l.i >> 2)) & 3;
-          const float4 vb4 = qb[mm], vc4 = qc[mm];
-          sB += (vb4.x + vb4.y) + (vb4.z + vb4.w);
-          sC += (vc4.x + vc4.y) + (vc4.z + vc4.w);
+          for (int m = 0; m < 4; ++m) {
+            const int mm = (m + (l.i >> 2)) & 3;
+            const float4 vb4 = qb[mm], vc4 = qc[mm];
+            sB += (vb4.x + vb4.y) + (vb4.z + vb4.w);
+            sC += (vc4.x + vc4.y) + (vc4.z + vc4.w);
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        {
+          const uint32_t off = tvs[j] ? bc_off : chunk::kDropOffset;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sB), rpb, off, j * pr, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sC), rpc, off, j * pr, 0);
         }
       }
+    } else {
+      // write addresses of bwd_grad: this lane's channel c at quarter (c >> 2) ^ q of the rows n
+      // with n >> 2 = q (rows of lanes i and i + 4 lie 256 bytes apart, on the same banks: with the
+      // quarters swizzled by n >> 2, the 16 lanes of a row reading one logical quarter touch 16
+      // different bank groups, and every lane finds channel c at the same logical position, so
+      // the channel sums can take c's weights by a DPP broadcast from lane c)
+      uint32_t rad[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        rad[q4] = lds_addr(rB) + static_cast<uint32_t>(16 * ((l.i >> 2) ^ q4) + 4 * (l.i & 3));
+      const int sw = l.i >> 2;
+      float mo[16];  // the adjoint's second register set (bwd_grad alternates them by token)
+      static_assert(TC % 2 == 0, "the adjoint ends each tile in mu");
+      const float4* qb = reinterpret_cast<const float4*>(rB + l.i * 16);
+      const float4* qc = reinterpret_cast<const float4*>(rC + l.i * 16);
+      // Channel sums of the row (lane i takes state n = i), software-pipelined: a token's LDS
+      // reads are issued after its terms are written and summed only after the next token's
+      // gradient block, whose writes go to the same block but queue behind the reads (LDS runs
+      // a wave's operations in order; the block is this row's own). The fences only keep the
+      // compiler from moving the accesses across the other lanes' writes.
+      float4 qbv[4], qcv[4];  // the pending token's quarters
+      auto rowsum_store = [&](int jt) {
+        float sB, sC;
+        bwd_rowsum(qbv[0], qbv[1], qbv[2], qbv[3], qcv[0], qcv[1], qcv[2], qcv[3], dtu[jt], ds[jt], sB, sC);
+        const uint32_t off = tvs[jt] ? bc_off : chunk::kDropOffset;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sB), rpb, off, jt * pr, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sC), rpc, off, jt * pr, 0);
+      };
+#pragma unroll
+      for (int j = TC - 1; j >= 0; --j) {
+        float sb = 0.0f, ga = 0.0f;
+        if (((TC - 1 - j) & 1) == 0)
+          bwd_grad(mu, mo, dAacc, H[j], j == 0 ? q : H[j > 0 ? j - 1 : 0], ex[j], A2, dt[j], ds[j], vb[j], vc[j],
+                   ga, sb, rad);
+        else
+          bwd_grad(mo, mu, dAacc, H[j], j == 0 ? q : H[j > 0 ? j - 1 : 0], ex[j], A2, dt[j], ds[j], vb[j], vc[j],
+                   ga, sb, rad);
+        if (j < TC - 1) rowsum_store(j + 1);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+          qbv[m4] = qb[m4 ^ sw];
+          qcv[m4] = qc[m4 ^ sw];
+        }
+        {
+          const uint32_t off = tvs[j] ? e_off : chunk::kDropOffset;
+          const float ddt = __builtin_fmaf(uu[j], sb, ga * kLn2);
+          const float dd = ddt * sg[j];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__builtin_fmaf(ds[j], Dd, dt[j] * sb)), rdu, off, j * er, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dd), rdd, off, j * er, 0);
+          dbacc += ok[j] ? dd : 0.0f;
+          dDacc = ok[j] ? __builtin_fmaf(ds[j], uu[j], dDacc) : dDacc;
+        }
+      }
+      rowsum_store(0);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      {
-        const uint32_t off = tvs[j] ? bc_off : chunk::kDropOffset;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sB), rpb, off, j * pr, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sC), rpc, off, j * pr, 0);
-      }
     }
     cur = nxt;
     ck_cur = ck_nxt;
