@@ -108,6 +108,90 @@ __device__ __forceinline__ void bwd_local(float (&h)[16], float (&e)[16], const 
 #undef BW_L
 #undef BW_L_END
 
+// bwd_local for the first token of a chunk, whose state starts at zero: h[n] = dtu B[n],
+// e[n] = 2^(dt a2[n]) (no zero fill, no multiply by the decay). The block ends with a
+// non-transcendental instruction, so code after it may read e at once.
+__device__ __forceinline__ void bwd_local_first(float (&h)[16], float (&e)[16], const float (&a)[16], float dt,
+                                                float dtu, float vb) {
+  float x0, x1;
+  asm volatile(
+      "s_nop 1\n"
+      "v_mul_f32 %[x0], %[dt], %[a0]\n"
+      "v_exp_f32 %[e0], %[x0]\n"
+      "v_mul_f32_dpp %[h0], %[vb], %[dtu]" SS_DPP_ROW(0)
+      "v_mul_f32 %[x1], %[dt], %[a1]\n"
+      "v_exp_f32 %[e1], %[x1]\n"
+      "v_mul_f32_dpp %[h1], %[vb], %[dtu]" SS_DPP_ROW(1)
+      "v_mul_f32 %[x0], %[dt], %[a2]\n"
+      "v_exp_f32 %[e2], %[x0]\n"
+      "v_mul_f32_dpp %[h2], %[vb], %[dtu]" SS_DPP_ROW(2)
+      "v_mul_f32 %[x1], %[dt], %[a3]\n"
+      "v_exp_f32 %[e3], %[x1]\n"
+      "v_mul_f32_dpp %[h3], %[vb], %[dtu]" SS_DPP_ROW(3)
+      "v_mul_f32 %[x0], %[dt], %[a4]\n"
+      "v_exp_f32 %[e4], %[x0]\n"
+      "v_mul_f32_dpp %[h4], %[vb], %[dtu]" SS_DPP_ROW(4)
+      "v_mul_f32 %[x1], %[dt], %[a5]\n"
+      "v_exp_f32 %[e5], %[x1]\n"
+      "v_mul_f32_dpp %[h5], %[vb], %[dtu]" SS_DPP_ROW(5)
+      "v_mul_f32 %[x0], %[dt], %[a6]\n"
+      "v_exp_f32 %[e6], %[x0]\n"
+      "v_mul_f32_dpp %[h6], %[vb], %[dtu]" SS_DPP_ROW(6)
+      "v_mul_f32 %[x1], %[dt], %[a7]\n"
+      "v_exp_f32 %[e7], %[x1]\n"
+      "v_mul_f32_dpp %[h7], %[vb], %[dtu]" SS_DPP_ROW(7)
+      "v_mul_f32 %[x0], %[dt], %[a8]\n"
+      "v_exp_f32 %[e8], %[x0]\n"
+      "v_mul_f32_dpp %[h8], %[vb], %[dtu]" SS_DPP_ROW(8)
+      "v_mul_f32 %[x1], %[dt], %[a9]\n"
+      "v_exp_f32 %[e9], %[x1]\n"
+      "v_mul_f32_dpp %[h9], %[vb], %[dtu]" SS_DPP_ROW(9)
+      "v_mul_f32 %[x0], %[dt], %[a10]\n"
+      "v_exp_f32 %[e10], %[x0]\n"
+      "v_mul_f32_dpp %[h10], %[vb], %[dtu]" SS_DPP_ROW(10)
+      "v_mul_f32 %[x1], %[dt], %[a11]\n"
+      "v_exp_f32 %[e11], %[x1]\n"
+      "v_mul_f32_dpp %[h11], %[vb], %[dtu]" SS_DPP_ROW(11)
+      "v_mul_f32 %[x0], %[dt], %[a12]\n"
+      "v_exp_f32 %[e12], %[x0]\n"
+      "v_mul_f32_dpp %[h12], %[vb], %[dtu]" SS_DPP_ROW(12)
+      "v_mul_f32 %[x1], %[dt], %[a13]\n"
+      "v_exp_f32 %[e13], %[x1]\n"
+      "v_mul_f32_dpp %[h13], %[vb], %[dtu]" SS_DPP_ROW(13)
+      "v_mul_f32 %[x0], %[dt], %[a14]\n"
+      "v_exp_f32 %[e14], %[x0]\n"
+      "v_mul_f32_dpp %[h14], %[vb], %[dtu]" SS_DPP_ROW(14)
+      "v_mul_f32 %[x1], %[dt], %[a15]\n"
+      "v_exp_f32 %[e15], %[x1]\n"
+      "v_mul_f32_dpp %[h15], %[vb], %[dtu]" SS_DPP_ROW(15)
+      : SS_OPS16(h, "=&v"), SS_OPS16(e, "=&v"), [x0] "=&v"(x0), [x1] "=&v"(x1)
+      : SS_OPS16(a, "v"), [dt] "v"(dt), [dtu] "v"(dtu), [vb] "v"(vb));
+}
+
+// The state after a chunk's first token from zero when its decay is not needed: h[n] = dtu B[n].
+__device__ __forceinline__ void bwd_input_term(float (&h)[16], float dtu, float vb) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mul_f32_dpp %[h0], %[vb], %[dtu]" SS_DPP_ROW(0)
+      "v_mul_f32_dpp %[h1], %[vb], %[dtu]" SS_DPP_ROW(1)
+      "v_mul_f32_dpp %[h2], %[vb], %[dtu]" SS_DPP_ROW(2)
+      "v_mul_f32_dpp %[h3], %[vb], %[dtu]" SS_DPP_ROW(3)
+      "v_mul_f32_dpp %[h4], %[vb], %[dtu]" SS_DPP_ROW(4)
+      "v_mul_f32_dpp %[h5], %[vb], %[dtu]" SS_DPP_ROW(5)
+      "v_mul_f32_dpp %[h6], %[vb], %[dtu]" SS_DPP_ROW(6)
+      "v_mul_f32_dpp %[h7], %[vb], %[dtu]" SS_DPP_ROW(7)
+      "v_mul_f32_dpp %[h8], %[vb], %[dtu]" SS_DPP_ROW(8)
+      "v_mul_f32_dpp %[h9], %[vb], %[dtu]" SS_DPP_ROW(9)
+      "v_mul_f32_dpp %[h10], %[vb], %[dtu]" SS_DPP_ROW(10)
+      "v_mul_f32_dpp %[h11], %[vb], %[dtu]" SS_DPP_ROW(11)
+      "v_mul_f32_dpp %[h12], %[vb], %[dtu]" SS_DPP_ROW(12)
+      "v_mul_f32_dpp %[h13], %[vb], %[dtu]" SS_DPP_ROW(13)
+      "v_mul_f32_dpp %[h14], %[vb], %[dtu]" SS_DPP_ROW(14)
+      "v_mul_f32_dpp %[h15], %[vb], %[dtu]" SS_DPP_ROW(15)
+      : SS_OPS16(h, "=&v")
+      : [dtu] "v"(dtu), [vb] "v"(vb));
+}
+
 // True forward step of one token from the previous states P: H[n] = e[n] P[n] + dtu B[n];
 // s += C[n] H[n] (the DPP fmac of state n runs after state n+1's fma).
 #define BW_T(n, np)                                                           \
@@ -148,6 +232,46 @@ __device__ __forceinline__ void bwd_rlocal(float (&m)[16], const float (&e)[16],
       : SS_OPS16(e, "v"), [ds] "v"(ds), [vc] "v"(vc));
 }
 #undef BW_R
+
+// bwd_rlocal for the last token of a chunk, whose adjoint starts at zero: m[n] = e[n] ds C[n].
+__device__ __forceinline__ void bwd_rlocal_first(float (&m)[16], const float (&e)[16], float ds, float vc) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_mul_f32_dpp %[m0], %[vc], %[ds]" SS_DPP_ROW(0)
+      "v_mul_f32_dpp %[m1], %[vc], %[ds]" SS_DPP_ROW(1)
+      "v_mul_f32_dpp %[m2], %[vc], %[ds]" SS_DPP_ROW(2)
+      "v_mul_f32_dpp %[m3], %[vc], %[ds]" SS_DPP_ROW(3)
+      "v_mul_f32_dpp %[m4], %[vc], %[ds]" SS_DPP_ROW(4)
+      "v_mul_f32_dpp %[m5], %[vc], %[ds]" SS_DPP_ROW(5)
+      "v_mul_f32_dpp %[m6], %[vc], %[ds]" SS_DPP_ROW(6)
+      "v_mul_f32_dpp %[m7], %[vc], %[ds]" SS_DPP_ROW(7)
+      "v_mul_f32_dpp %[m8], %[vc], %[ds]" SS_DPP_ROW(8)
+      "v_mul_f32_dpp %[m9], %[vc], %[ds]" SS_DPP_ROW(9)
+      "v_mul_f32_dpp %[m10], %[vc], %[ds]" SS_DPP_ROW(10)
+      "v_mul_f32_dpp %[m11], %[vc], %[ds]" SS_DPP_ROW(11)
+      "v_mul_f32_dpp %[m12], %[vc], %[ds]" SS_DPP_ROW(12)
+      "v_mul_f32_dpp %[m13], %[vc], %[ds]" SS_DPP_ROW(13)
+      "v_mul_f32_dpp %[m14], %[vc], %[ds]" SS_DPP_ROW(14)
+      "v_mul_f32_dpp %[m15], %[vc], %[ds]" SS_DPP_ROW(15)
+      "v_mul_f32 %[m0], %[e0], %[m0]\n"
+      "v_mul_f32 %[m1], %[e1], %[m1]\n"
+      "v_mul_f32 %[m2], %[e2], %[m2]\n"
+      "v_mul_f32 %[m3], %[e3], %[m3]\n"
+      "v_mul_f32 %[m4], %[e4], %[m4]\n"
+      "v_mul_f32 %[m5], %[e5], %[m5]\n"
+      "v_mul_f32 %[m6], %[e6], %[m6]\n"
+      "v_mul_f32 %[m7], %[e7], %[m7]\n"
+      "v_mul_f32 %[m8], %[e8], %[m8]\n"
+      "v_mul_f32 %[m9], %[e9], %[m9]\n"
+      "v_mul_f32 %[m10], %[e10], %[m10]\n"
+      "v_mul_f32 %[m11], %[e11], %[m11]\n"
+      "v_mul_f32 %[m12], %[e12], %[m12]\n"
+      "v_mul_f32 %[m13], %[e13], %[m13]\n"
+      "v_mul_f32 %[m14], %[e14], %[m14]\n"
+      "v_mul_f32 %[m15], %[e15], %[m15]\n"
+      : SS_OPS16(m, "=&v")
+      : SS_OPS16(e, "v"), [ds] "v"(ds), [vc] "v"(vc));
+}
 
 // True reverse step of one token and its gradient terms, the adjoint in m on entry:
 //   lam = m[n] + ds C[n] (kept in m[n]);  sb += B[n] lam;  o[n] = e[n] lam (the adjoint
@@ -426,14 +550,15 @@ void bwd_ckpt_kernel(BwdArgs a) {
     fetch(nxt, t0 + TT < t_end ? t0 + TT : t0);
     float h[16], e[16], dsum = 0.0f;
 #pragma unroll
-    for (int n = 0; n < 16; ++n) h[n] = 0.0f;
-#pragma unroll
     for (int j = 0; j < CTC; ++j) {
       const float x = chunk::as_f32<T>(cur.x[j]) + bias;
       float dt = a.softplus ? softplus(x) : x;
       dt = (t0 + l.k * CTC + j < L) ? dt : 0.0f;  // a zero step is the identity
       dsum += dt;
-      bwd_local(h, e, A2, dt, dt * chunk::as_f32<T>(cur.u[j]), chunk::as_f32<T>(cur.b[j]));
+      if (j == 0)  // (the state starts at zero: the first token's decay does not enter it)
+        bwd_input_term(h, dt * chunk::as_f32<T>(cur.u[j]), chunk::as_f32<T>(cur.b[j]));
+      else
+        bwd_local(h, e, A2, dt, dt * chunk::as_f32<T>(cur.u[j]), chunk::as_f32<T>(cur.b[j]));
     }
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
@@ -670,19 +795,23 @@ void bwd_chunked_kernel(BwdArgs a) {
     // forward local pass from a zero state: decays and chunk aggregates
     float ex[TC][16], h[16], dsum = 0.0f;
 #pragma unroll
-    for (int n = 0; n < 16; ++n) h[n] = 0.0f;
-#pragma unroll
     for (int j = 0; j < TC; ++j) {
       dsum += dt[j];
-      bwd_local(h, ex[j], A2, dt[j], dtu[j], vb[j]);
+      if (j == 0)
+        bwd_local_first(h, ex[j], A2, dt[j], dtu[j], vb[j]);
+      else
+        bwd_local(h, ex[j], A2, dt[j], dtu[j], vb[j]);
     }
     // reverse local pass from a zero adjoint (it needs only the decays): the chunk
     // aggregate mu_loc, so both folds share one pair of barriers
     float mu[16];
 #pragma unroll
-    for (int n = 0; n < 16; ++n) mu[n] = 0.0f;
-#pragma unroll
-    for (int j = TC - 1; j >= 0; --j) bwd_rlocal(mu, ex[j], ds[j], vc[j]);
+    for (int j = TC - 1; j >= 0; --j) {
+      if (j == TC - 1)
+        bwd_rlocal_first(mu, ex[j], ds[j], vc[j]);
+      else
+        bwd_rlocal(mu, ex[j], ds[j], vc[j]);
+    }
 
     __syncthreads();  // the previous tile is done with every LDS array
 #pragma unroll
