@@ -638,15 +638,21 @@ void bwd_chunked_kernel(BwdArgs a) {
   for (int n = 0; n < 16; ++n) A2[n] = n < N ? a.A[l.cc * N + n] * kLog2e : 0.0f;
   float bias = a.delta_bias ? a.delta_bias[l.cc] : 0.0f;
   float Dd = a.D ? a.D[l.cc] : 0.0f;
-  // adjoint carried from later tiles: lane (k, i) owns state n = k of channel i
-  float rcarry = (a.dlast && (!SPLIT || part == a.parts - 1) && l.cvalid && l.k < N)
-                     ? a.dlast[(l.b * a.dim + l.c) * N + l.k] : 0.0f;
+  // Fold ownership: lane (k, i) owns state n = k & 15 of channel i. With 16 rows every lane
+  // runs both folds; with 32, rows 0..15 run the forward fold and rows 16..31 the reverse
+  // one, at the same time (the folds read the same chunk decays and write different arrays).
+  const int own_n = l.k & 15;
+  const bool fwd_owner = R == 16 || l.k < 16;
+  const bool rev_owner = R == 16 || l.k >= 16;
+  // adjoint carried from later tiles (the reverse fold's lanes)
+  float rcarry = (a.dlast && (!SPLIT || part == a.parts - 1) && l.cvalid && rev_owner && own_n < N)
+                     ? a.dlast[(l.b * a.dim + l.c) * N + own_n] : 0.0f;
   if (SPLIT && part < a.parts - 1) {  // start from the adjoint the later part publishes
     const int64_t slot = part * groups + gi;
     if (threadIdx.x == 0) seen_s = split::poll(a.split_ws, slot, a.split_wait_limit) ? 1u : 0u;
     __syncthreads();  // (the state loads are issued after thread 0 has seen the flag)
-    if (l.k < 16)
-      rcarry = __builtin_amdgcn_readfirstlane(seen_s) ? split::load_state(a.split_ws, a.split_cap, slot, l.k, l.i)
+    if (rev_owner)
+      rcarry = __builtin_amdgcn_readfirstlane(seen_s) ? split::load_state(a.split_ws, a.split_cap, slot, own_n, l.i)
                                                       : __builtin_nanf("");
   }
   float dAacc[16];
@@ -821,21 +827,23 @@ void bwd_chunked_kernel(BwdArgs a) {
       lds_m[l.k * kS + n * 16 + l.i] = mu[n];
     }
     __syncthreads();
-    {  // lane (k, i) owns state n = k of channel i: the forward fold from the checkpoint,
-       // then the reverse fold from the adjoint of the later tile; each lane overwrites
-       // exactly the words it read
-      if (R == 16 || l.k < 16) {
+    {  // the forward fold from the checkpoint and the reverse fold from the adjoint of the
+       // later tile, over state own_n of channel i; each lane overwrites exactly the words it
+       // read, and the two folds write different arrays
+      if (fwd_owner) {
         float carry = __uint_as_float(ck_cur);
 #pragma unroll
         for (int jj = 0; jj < R; ++jj) {
-          const int o = jj * kS + l.k * 16 + l.i;
+          const int o = jj * kS + own_n * 16 + l.i;
           const float pm = lds_eh[0][o], hv = lds_eh[1][o];
           lds_eh[1][o] = carry;  // state entering chunk jj
           carry = __builtin_fmaf(pm, carry, carry + hv);
         }
+      }
+      if (rev_owner) {
 #pragma unroll
         for (int jj = R - 1; jj >= 0; --jj) {
-          const int o = jj * kS + l.k * 16 + l.i;
+          const int o = jj * kS + own_n * 16 + l.i;
           const float pm = lds_eh[0][o], mv = lds_m[o];
           lds_m[o] = rcarry;  // adjoint entering chunk jj from its end
           rcarry = __builtin_fmaf(pm, rcarry, rcarry + mv);
@@ -1001,12 +1009,12 @@ void bwd_chunked_kernel(BwdArgs a) {
   }
   if (SPLIT && part > 0) {  // publish the adjoint entering this part for the earlier one
     const int64_t slot = (part - 1) * groups + gi;
-    if (l.k < 16) split::store_state(a.split_ws, a.split_cap, slot, l.k, l.i, rcarry);
+    if (rev_owner) split::store_state(a.split_ws, a.split_cap, slot, own_n, l.i, rcarry);
     split::finish_stores();
     __syncthreads();
     if (threadIdx.x == 0) split::publish(a.split_ws, slot);
-  } else if (a.dh0 && l.cvalid && l.k < N) {
-    a.dh0[(l.b * a.dim + l.c) * N + l.k] = rcarry;
+  } else if (a.dh0 && l.cvalid && rev_owner && own_n < N) {
+    a.dh0[(l.b * a.dim + l.c) * N + own_n] = rcarry;
   }
 
   // dA, dD and dbias of this workgroup: sum the R rows
