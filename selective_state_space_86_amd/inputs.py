@@ -2,9 +2,16 @@
 
 This module draws random tensors and nothing else: it holds none of the scan's
 arithmetic, so both the GPU path and the fp64 oracle can consume what it produces.
-Draws use ``torch.Generator`` on the requested device, in a fixed order
-(u, delta, z, B, C, D, bias), from a seed derived from the workload name and a
-caller seed. bf16 tensors are fp32 draws rounded to nearest even.
+
+Draws (the same on every host): numpy PCG64 streams keyed by
+``SeedSequence([86, config, tensor, chunk])`` (a caller seed other than 0 is appended),
+in the order u, delta, z, B, C, D, bias (tensor ids 0..6). Per-token tensors are drawn in
+chunks of 4096 tokens of one batch row (chunk = row * chunks_per_row + index), each chunk
+as (tokens, width) in token-major order, so a draw does not depend on how the tokens are
+later grouped into calls or launches, and a shorter sequence draws a prefix of a longer
+one. Values are drawn in fp64, rounded to fp32 (nearest even) and, for bf16 tensors, to
+bf16 (nearest even). Sequences of 2^19 tokens or more are drawn on the device with a
+seeded ``torch.Generator`` instead (host generation would take minutes there).
 
 Workload shapes are the per-layer scan shapes of Mamba models (d_inner channels,
 d_state = 16): 130M (batch 8, L 2048, 1536 ch), 1.4B (batch 4, L 4096, 4096 ch) and
@@ -17,7 +24,9 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
 import zlib
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -74,15 +83,128 @@ def _seed(name: str, seed: int) -> int:
     return (zlib.crc32(name.encode()) * 1000003 + 86 * 7919 + seed) % (2 ** 62)
 
 
+# configuration ids of the seed key: the tiny case 1, 130M 2, 1.4B 3, 3B long context 4 (and
+# its length sweep, which draws prefixes of the same streams), decode 5; other shapes (tests)
+# a number derived from their name
+CONFIG_IDS = {"tiny": 1, "tiny-lti": 1, "mamba130m": 2, "mamba130m-gated": 2, "mamba1.4b": 3,
+              "mamba3b-long": 4, "decode": 5}
+TENSOR_IDS = {"u": 0, "delta": 1, "z": 2, "B": 3, "C": 4, "D": 5, "bias": 6}
+CHUNK = 4096
+DEVICE_DRAW_L = 1 << 19  # sequences this long are drawn on the device
+
+
+def config_id(w: Workload) -> int:
+    if w.name in CONFIG_IDS:
+        return CONFIG_IDS[w.name]
+    if w.name.startswith("mamba3b-L"):
+        return 4
+    return 1000 + zlib.crc32(w.name.encode()) % 1_000_000
+
+
+def _rng(cfg: int, tensor: str, chunk: int, seed: int) -> np.random.Generator:
+    key = [86, cfg, TENSOR_IDS[tensor], chunk] + ([seed] if seed else [])
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(key)))
+
+
+def _draw(rng, dist, count):
+    """fp64 draws rounded to fp32 (nearest even)."""
+    kind, p, q = dist
+    v = rng.standard_normal(count) * q + p if kind == "normal" else rng.uniform(p, q, count)
+    return v.astype(np.float32)
+
+
+def _bf16_bits(f32: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, rounded to nearest even (finite inputs)."""
+    b = f32.view(np.uint32)
+    return ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def _host_tokens(w: Workload, cfg: int, tensor: str, dist, width: int, seed: int, pool) -> np.ndarray:
+    """A per-token tensor (batch, seqlen, width), drawn chunk by chunk, in the workload's
+    element type (bf16 as uint16 bit patterns)."""
+    b, L = w.batch, w.seqlen
+    nch = -(-L // CHUNK)
+    out = np.empty((b, L, width), dtype=np.uint16 if w.dtype == "bf16" else np.float32)
+
+    def one(job):
+        r, c = job
+        t0, t1 = c * CHUNK, min(L, (c + 1) * CHUNK)
+        v = _draw(_rng(cfg, tensor, r * nch + c, seed), dist, (t1 - t0) * width).reshape(t1 - t0, width)
+        out[r, t0:t1] = _bf16_bits(v) if w.dtype == "bf16" else v
+
+    list(pool.map(one, [(r, c) for r in range(b) for c in range(nch)]))
+    return out
+
+
+def _host_rows(w: Workload, cfg: int, tensor: str, dist, width: int, seed: int) -> np.ndarray:
+    """One draw per batch row, (batch, width) fp32 (the LTI case's per-row values)."""
+    return np.stack([_draw(_rng(cfg, tensor, r, seed), dist, width) for r in range(w.batch)])
+
+
+def _torch_of(a: np.ndarray, bf16: bool, dev) -> torch.Tensor:
+    t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
+    return t.to(dev)
+
+
 def make(w: Workload, seed: int = 0, device="cpu", time_major: bool = False) -> dict:
     """Draw every tensor of workload ``w``.
 
     Returns a dict with u, delta, z, B, C (w.dtype) and A, D, delta_bias (float32).
     With ``time_major`` the per-token tensors are laid out (seqlen, batch, dim) and
     (seqlen, batch, dstate) so that step t is a contiguous slice (decode streams);
-    otherwise (batch, seqlen, dim) and (batch, seqlen, dstate).
-    delta_bias is None when w.bias == "none"; z is always drawn (pass it or not).
+    otherwise (batch, seqlen, dim) and (batch, seqlen, dstate). The values do not depend
+    on the layout. delta_bias is None when w.bias == "none"; z is always drawn (pass it
+    or not).
     """
+    if w.seqlen >= DEVICE_DRAW_L:
+        return _make_device(w, seed, device, time_major)
+    dev = torch.device(device)
+    cfg = config_id(w)
+    b, L, d, n = w.batch, w.seqlen, w.dim, w.dstate
+    bf = w.dtype == "bf16"
+    normal = ("normal", 0.0, 1.0)
+    out = {}
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as pool:
+        if w.lti:
+            # one draw per (b, d) / (b, n), repeated along t
+            out["u"] = _host_tokens(w, cfg, "u", normal, d, seed, pool)
+            rows = {"delta": (w.delta_dist, d), "B": (normal, n), "C": (normal, n)}
+            for k in ("delta", "z", "B", "C"):
+                if k == "z":
+                    out[k] = _host_tokens(w, cfg, "z", normal, d, seed, pool)
+                    continue
+                dist, width = rows[k]
+                v = np.ascontiguousarray(np.broadcast_to(_host_rows(w, cfg, k, dist, width, seed)[:, None, :],
+                                                         (b, L, width)))
+                out[k] = _bf16_bits(v) if bf else v
+        else:
+            out["u"] = _host_tokens(w, cfg, "u", normal, d, seed, pool)
+            out["delta"] = _host_tokens(w, cfg, "delta", w.delta_dist, d, seed, pool)
+            out["z"] = _host_tokens(w, cfg, "z", normal, d, seed, pool)
+            out["B"] = _host_tokens(w, cfg, "B", normal, n, seed, pool)
+            out["C"] = _host_tokens(w, cfg, "C", normal, n, seed, pool)
+    res = {}
+    for k in ("u", "delta", "z", "B", "C"):
+        a = out[k]
+        if time_major:
+            a = np.ascontiguousarray(a.transpose(1, 0, 2))
+        res[k] = _torch_of(a, bf, dev)
+    res["D"] = torch.from_numpy(_draw(_rng(cfg, "D", 0, seed), normal, d)).to(dev)
+    if w.bias == "range":
+        res["delta_bias"] = torch.from_numpy(_draw(_rng(cfg, "bias", 0, seed), ("uniform", BIAS_LO, BIAS_HI),
+                                                   d)).to(dev)
+    elif w.bias == "zero":
+        res["delta_bias"] = torch.zeros((d,), dtype=torch.float32, device=dev)
+    else:
+        res["delta_bias"] = None
+    res["A"] = -torch.arange(1, n + 1, dtype=torch.float32, device=dev).repeat(d, 1).contiguous()
+    return {k: res[k] for k in ("u", "delta", "z", "B", "C", "A", "D", "delta_bias")}
+
+
+def _make_device(w: Workload, seed: int, device, time_major: bool) -> dict:
+    """The draws of ``make`` for sequences of 2^19 tokens or more: a seeded torch.Generator
+    on the device, in the same order and distributions (bf16: fp32 draws rounded to nearest
+    even)."""
     dev = torch.device(device)
     g = torch.Generator(device=dev)
     g.manual_seed(_seed(w.name, seed))
@@ -101,7 +223,6 @@ def make(w: Workload, seed: int = 0, device="cpu", time_major: bool = False) -> 
         return torch.rand(shape, **f32) * (q - p) + p
 
     if w.lti:
-        # one draw per (b, d) / (b, n), repeated along t
         u = normal(tok)
         if time_major:
             delta = delta_draw((1, b, d)).expand(tok).contiguous()
