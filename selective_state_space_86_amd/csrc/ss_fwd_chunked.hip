@@ -133,9 +133,11 @@ void fwd_chunked_kernel(FwdArgs a) {
   // drift apart because the SIMD issues from the oldest wave first: a younger wave's fix-up
   // runs beside an older wave's next local pass, takes about three times as long, and the
   // older wave then waits for it at the first barrier of every tile (8-wave 3B-layer tiles:
-  // 4.85 -> 4.25 ms with the raised fix-up).
+  // 4.85 -> 4.25 ms with the raised fix-up). The local pass steps down from 2 to 0 over its
+  // tokens and the fix-up runs at 1: at the 1.4B shape (split, 16 rows) 336 against 343-346
+  // us with the fix-up at 2 (341 at 3), the 3B shape unchanged.
 #ifndef SS_FIXUP_PRIO
-#define SS_FIXUP_PRIO 2
+#define SS_FIXUP_PRIO 1
 #endif
 #ifndef SS_LOCAL_RAMP
 #define SS_LOCAL_RAMP 1
