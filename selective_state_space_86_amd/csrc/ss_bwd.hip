@@ -761,12 +761,12 @@ void bwd_chunked_kernel(BwdArgs a) {
 #pragma unroll
   for (int n = 0; n < 16; ++n) asm volatile("" : "+v"(A2[n]));
   for (int64_t tile = tile_hi - 1; tile >= tile_lo; --tile) {
-    // wave priorities: progress priority unsplit; split, the local passes and folds at 0 and
-    // the gradient phase after them at 1, so a wave that fell behind catches up before the
-    // next tile's barriers (3B long context: 18.20-18.26 against 18.36-18.40 ms; the local
-    // phase raised instead ran 18.42-18.47)
-    if (!SPLIT) progress_priority(nt - 1 - tile, nt);
-    else __builtin_amdgcn_s_setprio(0);
+    // wave priorities: the local passes and folds at 0 and the gradient phase after them at
+    // 1, so a wave that fell behind catches up before the next tile's barriers (3B long
+    // context, split: 18.20-18.26 against 18.36-18.40 ms with none, and 18.42-18.47 with the
+    // local phase raised instead; 1.4B, unsplit: 1.448 against 1.555 ms with the progress
+    // priority the forward's unsplit plans use)
+    __builtin_amdgcn_s_setprio(0);
     const int64_t t0 = tile * TT;
     // the earlier tile, always a full one (the tile before the first re-reads tile 0, unused;
     // a sequence of one, partial, tile has no full tile to read: its loads are all dropped).
@@ -856,7 +856,7 @@ void bwd_chunked_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    if (SPLIT) __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(1);
     float q[16];
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
