@@ -10,7 +10,9 @@
 //   ddt_t = u_t sum_n lam_t[n] B_t[n] + sum_n A[n] lam_t[n] abar_t[n] h_{t-1}[n]
 //   dA[n] += dt_t lam_t[n] abar_t[n] h_{t-1}[n]                  (summed over batch and t)
 //   ddelta_t = ddt_t sigmoid(delta_t + bias) with softplus, dbias += ddelta_t, dD += ds_t u_t
-// and abar_t h_{t-1} = h_t - dt_t B_t u_t, so only the states h_t themselves are needed.
+// and lam_t[n] abar_t[n] h_{t-1}[n] = mu_t[n] h_{t-1}[n]: the adjoint passed back times the
+// state entering the token, which the reverse pass holds (the previous token's true state or
+// the chunk's carry-in), so only the states h_t themselves are needed.
 // The reverse recurrence mu_t = abar_t (ds_t C_t + mu_{t+1}) is linear with the same
 // decays as the forward one, so it is chunked the same way (an associative fold of chunk
 // aggregates, run from the end of the sequence).
@@ -19,7 +21,7 @@
 // the backward recomputes the expanded states instead of reading them from HBM), nothing
 // of size (batch, L, dim, N) is stored:
 //   1. bwd_ckpt_kernel runs the forward scan keeping only the state at the start of every
-//      tile of 16*TC tokens (workspace, 4*16/(16*TC) bytes per (b, t, d)).
+//      32 tokens (workspace, 2 bytes per (b, t, d)).
 //   2. bwd_chunked_kernel walks the tiles from last to first. Per tile it recomputes the
 //      states from the checkpoint (local pass, chunk fold, true recurrence kept in
 //      registers), then runs the adjoint: local reverse pass, reverse fold, and the true
@@ -28,7 +30,7 @@
 //      written as per-group partials; dA, dD, dbias are summed over the rows at the end.
 //   3. bwd_reduce_kernel adds the partials over channel groups (dB, dC) and batch rows
 //      (dA, dD, dbias). Every sum has a fixed order: results are deterministic.
-// Lane layout as in the forward: lane i of a row of 16 is channel c0+i, the 16 rows are 16
+// Lane layout as in the forward: lane i of a row of 16 is channel c0+i, the 16 or 32 rows are
 // consecutive chunks of TC tokens, and lane n of a row holds B_t[n], C_t[n], broadcast to
 // the row by DPP row_newbcast:n. dstate < 16 is padded: lanes n >= dstate read B = C = 0
 // and A = 0, which keeps those states at zero and their adjoint at zero.
@@ -1168,11 +1170,11 @@ int64_t bwd_split_part_len(int64_t seqlen, int rows, int parts) {
 
 // When the groups leave part of the last round of resident slots empty, split as the forward
 // does: the fewest parts within 5% of the best of max(1, ceil(groups * parts / slots) /
-// parts). The reverse kernel (~195 VGPRs) holds one 32-row or two 16-row workgroups per CU,
+// parts). The reverse kernel (~205-215 VGPRs) holds one 32-row or two 16-row workgroups per CU,
 // the checkpoint kernel (at most 128 VGPRs with 16 rows, 35 KB of LDS) one 32-row or four
 // 16-row ones. At the 130M shape (768 groups
 // of 16-row tiles) the reverse kernel's two parts took it from 569 to 526 us, and the
-// checkpoint kernel, which fills its 768 slots once, ran 9 us slower split; at 1024 groups
+// checkpoint kernel, whose slots hold all 768 groups at once, ran 9 us slower split; at 1024 groups
 // (two whole rounds of the reverse kernel) two parts measured 2% slower.
 int bwd_split_parts(int64_t groups, int rows, bool ckpt, int64_t seqlen, int cus) {
   const int64_t slots = static_cast<int64_t>(rows == 32 ? 1 : (ckpt ? 4 : 2)) * cus;
