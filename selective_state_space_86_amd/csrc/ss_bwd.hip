@@ -220,6 +220,48 @@ __device__ __forceinline__ void bwd_true(const float (&P)[16], float (&H)[16], c
 }
 #undef BW_T
 
+// bwd_true without s, for calls without the gate (s only feeds dz): H[n] = e[n] P[n] + dtu B[n].
+__device__ __forceinline__ void bwd_true_states(const float (&P)[16], float (&H)[16], const float (&e)[16],
+                                                float dtu, float vb) {
+  float t;
+  asm volatile(
+      "s_nop 1\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(0)
+      "v_fma_f32 %[H0], %[e0], %[P0], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(1)
+      "v_fma_f32 %[H1], %[e1], %[P1], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(2)
+      "v_fma_f32 %[H2], %[e2], %[P2], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(3)
+      "v_fma_f32 %[H3], %[e3], %[P3], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(4)
+      "v_fma_f32 %[H4], %[e4], %[P4], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(5)
+      "v_fma_f32 %[H5], %[e5], %[P5], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(6)
+      "v_fma_f32 %[H6], %[e6], %[P6], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(7)
+      "v_fma_f32 %[H7], %[e7], %[P7], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(8)
+      "v_fma_f32 %[H8], %[e8], %[P8], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(9)
+      "v_fma_f32 %[H9], %[e9], %[P9], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(10)
+      "v_fma_f32 %[H10], %[e10], %[P10], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(11)
+      "v_fma_f32 %[H11], %[e11], %[P11], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(12)
+      "v_fma_f32 %[H12], %[e12], %[P12], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(13)
+      "v_fma_f32 %[H13], %[e13], %[P13], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(14)
+      "v_fma_f32 %[H14], %[e14], %[P14], %[t]\n"
+      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(15)
+      "v_fma_f32 %[H15], %[e15], %[P15], %[t]\n"
+      : SS_OPS16(H, "=&v"), [t] "=&v"(t)
+      : SS_OPS16(P, "v"), SS_OPS16(e, "v"), [dtu] "v"(dtu), [vb] "v"(vb));
+}
+
 // Reverse local step of one token: m[n] = e[n] (m[n] + ds C[n]).
 #define BW_R(n)                                                               \
   "v_fmac_f32_dpp %[m" #n "], %[vc], %[ds]" SS_DPP_ROW(n)                     \
@@ -888,11 +930,14 @@ void bwd_chunked_kernel(BwdArgs a) {
     float H[TC][16];
 #pragma unroll
     for (int j = 0; j < TC; ++j) {
-      float s = Dd * uu[j];
-      bwd_true(j == 0 ? q : H[j > 0 ? j - 1 : 0], H[j], ex[j], dtu[j], vb[j], vc[j], s);
-      if (GATE)
+      if constexpr (GATE) {
+        float s = Dd * uu[j];
+        bwd_true(j == 0 ? q : H[j > 0 ? j - 1 : 0], H[j], ex[j], dtu[j], vb[j], vc[j], s);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dyv[j] * s * dsl[j]), rdz,
                                               tvs[j] ? e_off : chunk::kDropOffset, j * er, 0);
+      } else {
+        bwd_true_states(j == 0 ? q : H[j > 0 ? j - 1 : 0], H[j], ex[j], dtu[j], vb[j]);
+      }
     }
 
     // true reverse recurrence and the gradient terms, token by token from the chunk end
