@@ -110,64 +110,138 @@ __device__ __forceinline__ void bwd_local(float (&h)[16], float (&e)[16], const 
 #undef BW_L
 #undef BW_L_END
 
-// bwd_local for the first token of a chunk, whose state starts at zero: h[n] = dtu B[n],
-// e[n] = 2^(dt a2[n]) (no zero fill, no multiply by the decay). The block ends with a
-// non-transcendental instruction, so code after it may read e at once.
-__device__ __forceinline__ void bwd_local_first(float (&h)[16], float (&e)[16], const float (&a)[16], float dt,
-                                                float dtu, float vb) {
+// The reverse kernel's local pass over a chunk of two tokens, keeping each token's input
+// terms bu[n] = dtu B[n] for the true-state pass (which then needs no multiply of its own).
+// First token (state from zero): bu0 and e0, the state after it being bu0.
+__device__ __forceinline__ void bwd_local_first_bu(float (&bu)[16], float (&e)[16], const float (&a)[16],
+                                                   float dt, float dtu, float vb) {
   float x0, x1;
   asm volatile(
       "s_nop 1\n"
       "v_mul_f32 %[x0], %[dt], %[a0]\n"
       "v_exp_f32 %[e0], %[x0]\n"
-      "v_mul_f32_dpp %[h0], %[vb], %[dtu]" SS_DPP_ROW(0)
+      "v_mul_f32_dpp %[bu0], %[vb], %[dtu]" SS_DPP_ROW(0)
       "v_mul_f32 %[x1], %[dt], %[a1]\n"
       "v_exp_f32 %[e1], %[x1]\n"
-      "v_mul_f32_dpp %[h1], %[vb], %[dtu]" SS_DPP_ROW(1)
+      "v_mul_f32_dpp %[bu1], %[vb], %[dtu]" SS_DPP_ROW(1)
       "v_mul_f32 %[x0], %[dt], %[a2]\n"
       "v_exp_f32 %[e2], %[x0]\n"
-      "v_mul_f32_dpp %[h2], %[vb], %[dtu]" SS_DPP_ROW(2)
+      "v_mul_f32_dpp %[bu2], %[vb], %[dtu]" SS_DPP_ROW(2)
       "v_mul_f32 %[x1], %[dt], %[a3]\n"
       "v_exp_f32 %[e3], %[x1]\n"
-      "v_mul_f32_dpp %[h3], %[vb], %[dtu]" SS_DPP_ROW(3)
+      "v_mul_f32_dpp %[bu3], %[vb], %[dtu]" SS_DPP_ROW(3)
       "v_mul_f32 %[x0], %[dt], %[a4]\n"
       "v_exp_f32 %[e4], %[x0]\n"
-      "v_mul_f32_dpp %[h4], %[vb], %[dtu]" SS_DPP_ROW(4)
+      "v_mul_f32_dpp %[bu4], %[vb], %[dtu]" SS_DPP_ROW(4)
       "v_mul_f32 %[x1], %[dt], %[a5]\n"
       "v_exp_f32 %[e5], %[x1]\n"
-      "v_mul_f32_dpp %[h5], %[vb], %[dtu]" SS_DPP_ROW(5)
+      "v_mul_f32_dpp %[bu5], %[vb], %[dtu]" SS_DPP_ROW(5)
       "v_mul_f32 %[x0], %[dt], %[a6]\n"
       "v_exp_f32 %[e6], %[x0]\n"
-      "v_mul_f32_dpp %[h6], %[vb], %[dtu]" SS_DPP_ROW(6)
+      "v_mul_f32_dpp %[bu6], %[vb], %[dtu]" SS_DPP_ROW(6)
       "v_mul_f32 %[x1], %[dt], %[a7]\n"
       "v_exp_f32 %[e7], %[x1]\n"
-      "v_mul_f32_dpp %[h7], %[vb], %[dtu]" SS_DPP_ROW(7)
+      "v_mul_f32_dpp %[bu7], %[vb], %[dtu]" SS_DPP_ROW(7)
       "v_mul_f32 %[x0], %[dt], %[a8]\n"
       "v_exp_f32 %[e8], %[x0]\n"
-      "v_mul_f32_dpp %[h8], %[vb], %[dtu]" SS_DPP_ROW(8)
+      "v_mul_f32_dpp %[bu8], %[vb], %[dtu]" SS_DPP_ROW(8)
       "v_mul_f32 %[x1], %[dt], %[a9]\n"
       "v_exp_f32 %[e9], %[x1]\n"
-      "v_mul_f32_dpp %[h9], %[vb], %[dtu]" SS_DPP_ROW(9)
+      "v_mul_f32_dpp %[bu9], %[vb], %[dtu]" SS_DPP_ROW(9)
       "v_mul_f32 %[x0], %[dt], %[a10]\n"
       "v_exp_f32 %[e10], %[x0]\n"
-      "v_mul_f32_dpp %[h10], %[vb], %[dtu]" SS_DPP_ROW(10)
+      "v_mul_f32_dpp %[bu10], %[vb], %[dtu]" SS_DPP_ROW(10)
       "v_mul_f32 %[x1], %[dt], %[a11]\n"
       "v_exp_f32 %[e11], %[x1]\n"
-      "v_mul_f32_dpp %[h11], %[vb], %[dtu]" SS_DPP_ROW(11)
+      "v_mul_f32_dpp %[bu11], %[vb], %[dtu]" SS_DPP_ROW(11)
       "v_mul_f32 %[x0], %[dt], %[a12]\n"
       "v_exp_f32 %[e12], %[x0]\n"
-      "v_mul_f32_dpp %[h12], %[vb], %[dtu]" SS_DPP_ROW(12)
+      "v_mul_f32_dpp %[bu12], %[vb], %[dtu]" SS_DPP_ROW(12)
       "v_mul_f32 %[x1], %[dt], %[a13]\n"
       "v_exp_f32 %[e13], %[x1]\n"
-      "v_mul_f32_dpp %[h13], %[vb], %[dtu]" SS_DPP_ROW(13)
+      "v_mul_f32_dpp %[bu13], %[vb], %[dtu]" SS_DPP_ROW(13)
       "v_mul_f32 %[x0], %[dt], %[a14]\n"
       "v_exp_f32 %[e14], %[x0]\n"
-      "v_mul_f32_dpp %[h14], %[vb], %[dtu]" SS_DPP_ROW(14)
+      "v_mul_f32_dpp %[bu14], %[vb], %[dtu]" SS_DPP_ROW(14)
       "v_mul_f32 %[x1], %[dt], %[a15]\n"
       "v_exp_f32 %[e15], %[x1]\n"
-      "v_mul_f32_dpp %[h15], %[vb], %[dtu]" SS_DPP_ROW(15)
-      : SS_OPS16(h, "=&v"), SS_OPS16(e, "=&v"), [x0] "=&v"(x0), [x1] "=&v"(x1)
+      "v_mul_f32_dpp %[bu15], %[vb], %[dtu]" SS_DPP_ROW(15)
+      : SS_OPS16(bu, "=&v"), SS_OPS16(e, "=&v"), [x0] "=&v"(x0), [x1] "=&v"(x1)
       : SS_OPS16(a, "v"), [dt] "v"(dt), [dtu] "v"(dtu), [vb] "v"(vb));
+}
+// Second token from the state p after the first: bu, e and h[n] = e[n] p[n] + bu[n].
+__device__ __forceinline__ void bwd_local_next_bu(float (&h)[16], float (&bu)[16], float (&e)[16],
+                                                  const float (&p)[16], const float (&a)[16], float dt,
+                                                  float dtu, float vb) {
+  float x0, x1;
+  asm volatile(
+      "s_nop 1\n"
+      "v_mul_f32 %[x0], %[dt], %[a0]\n"
+      "v_exp_f32 %[e0], %[x0]\n"
+      "v_mul_f32 %[x1], %[dt], %[a1]\n"
+      "v_exp_f32 %[e1], %[x1]\n"
+      "v_mul_f32_dpp %[bu0], %[vb], %[dtu]" SS_DPP_ROW(0)
+      "v_fma_f32 %[h0], %[e0], %[p0], %[bu0]\n"
+      "v_mul_f32 %[x0], %[dt], %[a2]\n"
+      "v_exp_f32 %[e2], %[x0]\n"
+      "v_mul_f32_dpp %[bu1], %[vb], %[dtu]" SS_DPP_ROW(1)
+      "v_fma_f32 %[h1], %[e1], %[p1], %[bu1]\n"
+      "v_mul_f32 %[x1], %[dt], %[a3]\n"
+      "v_exp_f32 %[e3], %[x1]\n"
+      "v_mul_f32_dpp %[bu2], %[vb], %[dtu]" SS_DPP_ROW(2)
+      "v_fma_f32 %[h2], %[e2], %[p2], %[bu2]\n"
+      "v_mul_f32 %[x0], %[dt], %[a4]\n"
+      "v_exp_f32 %[e4], %[x0]\n"
+      "v_mul_f32_dpp %[bu3], %[vb], %[dtu]" SS_DPP_ROW(3)
+      "v_fma_f32 %[h3], %[e3], %[p3], %[bu3]\n"
+      "v_mul_f32 %[x1], %[dt], %[a5]\n"
+      "v_exp_f32 %[e5], %[x1]\n"
+      "v_mul_f32_dpp %[bu4], %[vb], %[dtu]" SS_DPP_ROW(4)
+      "v_fma_f32 %[h4], %[e4], %[p4], %[bu4]\n"
+      "v_mul_f32 %[x0], %[dt], %[a6]\n"
+      "v_exp_f32 %[e6], %[x0]\n"
+      "v_mul_f32_dpp %[bu5], %[vb], %[dtu]" SS_DPP_ROW(5)
+      "v_fma_f32 %[h5], %[e5], %[p5], %[bu5]\n"
+      "v_mul_f32 %[x1], %[dt], %[a7]\n"
+      "v_exp_f32 %[e7], %[x1]\n"
+      "v_mul_f32_dpp %[bu6], %[vb], %[dtu]" SS_DPP_ROW(6)
+      "v_fma_f32 %[h6], %[e6], %[p6], %[bu6]\n"
+      "v_mul_f32 %[x0], %[dt], %[a8]\n"
+      "v_exp_f32 %[e8], %[x0]\n"
+      "v_mul_f32_dpp %[bu7], %[vb], %[dtu]" SS_DPP_ROW(7)
+      "v_fma_f32 %[h7], %[e7], %[p7], %[bu7]\n"
+      "v_mul_f32 %[x1], %[dt], %[a9]\n"
+      "v_exp_f32 %[e9], %[x1]\n"
+      "v_mul_f32_dpp %[bu8], %[vb], %[dtu]" SS_DPP_ROW(8)
+      "v_fma_f32 %[h8], %[e8], %[p8], %[bu8]\n"
+      "v_mul_f32 %[x0], %[dt], %[a10]\n"
+      "v_exp_f32 %[e10], %[x0]\n"
+      "v_mul_f32_dpp %[bu9], %[vb], %[dtu]" SS_DPP_ROW(9)
+      "v_fma_f32 %[h9], %[e9], %[p9], %[bu9]\n"
+      "v_mul_f32 %[x1], %[dt], %[a11]\n"
+      "v_exp_f32 %[e11], %[x1]\n"
+      "v_mul_f32_dpp %[bu10], %[vb], %[dtu]" SS_DPP_ROW(10)
+      "v_fma_f32 %[h10], %[e10], %[p10], %[bu10]\n"
+      "v_mul_f32 %[x0], %[dt], %[a12]\n"
+      "v_exp_f32 %[e12], %[x0]\n"
+      "v_mul_f32_dpp %[bu11], %[vb], %[dtu]" SS_DPP_ROW(11)
+      "v_fma_f32 %[h11], %[e11], %[p11], %[bu11]\n"
+      "v_mul_f32 %[x1], %[dt], %[a13]\n"
+      "v_exp_f32 %[e13], %[x1]\n"
+      "v_mul_f32_dpp %[bu12], %[vb], %[dtu]" SS_DPP_ROW(12)
+      "v_fma_f32 %[h12], %[e12], %[p12], %[bu12]\n"
+      "v_mul_f32 %[x0], %[dt], %[a14]\n"
+      "v_exp_f32 %[e14], %[x0]\n"
+      "v_mul_f32_dpp %[bu13], %[vb], %[dtu]" SS_DPP_ROW(13)
+      "v_fma_f32 %[h13], %[e13], %[p13], %[bu13]\n"
+      "v_mul_f32 %[x1], %[dt], %[a15]\n"
+      "v_exp_f32 %[e15], %[x1]\n"
+      "v_mul_f32_dpp %[bu14], %[vb], %[dtu]" SS_DPP_ROW(14)
+      "v_fma_f32 %[h14], %[e14], %[p14], %[bu14]\n"
+      "v_mul_f32_dpp %[bu15], %[vb], %[dtu]" SS_DPP_ROW(15)
+      "v_fma_f32 %[h15], %[e15], %[p15], %[bu15]\n"
+      : SS_OPS16(h, "=&v"), SS_OPS16(bu, "=&v"), SS_OPS16(e, "=&v"), [x0] "=&v"(x0), [x1] "=&v"(x1)
+      : SS_OPS16(p, "v"), SS_OPS16(a, "v"), [dt] "v"(dt), [dtu] "v"(dtu), [vb] "v"(vb));
 }
 
 // The state after a chunk's first token from zero when its decay is not needed: h[n] = dtu B[n].
@@ -194,72 +268,70 @@ __device__ __forceinline__ void bwd_input_term(float (&h)[16], float dtu, float 
       : [dtu] "v"(dtu), [vb] "v"(vb));
 }
 
-// True forward step of one token from the previous states P: H[n] = e[n] P[n] + dtu B[n];
-// s += C[n] H[n] (the DPP fmac of state n runs after state n+1's fma).
-#define BW_T(n, np)                                                           \
-  "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(n)                           \
-  "v_fma_f32 %[H" #n "], %[e" #n "], %[P" #n "], %[t]\n"                      \
-  "v_fmac_f32_dpp %[s], %[vc], %[H" #np "]" SS_DPP_ROW(np)
-
-__device__ __forceinline__ void bwd_true(const float (&P)[16], float (&H)[16], const float (&e)[16],
-                                         float dtu, float vb, float vc, float& s) {
-  float t;
+// True forward step from the previous states P with the kept input terms:
+// H[n] = e[n] P[n] + bu[n]; s += C[n] H[n] (the DPP fmac of state n two fmas later).
+__device__ __forceinline__ void bwd_true_bu(const float (&P)[16], float (&H)[16], const float (&e)[16],
+                                            const float (&b)[16], float vc, float& s) {
   asm volatile(
       "s_nop 1\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(0)
-      "v_fma_f32 %[H0], %[e0], %[P0], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(1)
-      "v_fma_f32 %[H1], %[e1], %[P1], %[t]\n"
-      BW_T(2, 0) BW_T(3, 1) BW_T(4, 2) BW_T(5, 3) BW_T(6, 4) BW_T(7, 5) BW_T(8, 6) BW_T(9, 7)
-      BW_T(10, 8) BW_T(11, 9) BW_T(12, 10) BW_T(13, 11) BW_T(14, 12) BW_T(15, 13)
+      "v_fma_f32 %[H0], %[e0], %[P0], %[b0]\n"
+      "v_fma_f32 %[H1], %[e1], %[P1], %[b1]\n"
+      "v_fma_f32 %[H2], %[e2], %[P2], %[b2]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H0]" SS_DPP_ROW(0)
+      "v_fma_f32 %[H3], %[e3], %[P3], %[b3]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H1]" SS_DPP_ROW(1)
+      "v_fma_f32 %[H4], %[e4], %[P4], %[b4]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H2]" SS_DPP_ROW(2)
+      "v_fma_f32 %[H5], %[e5], %[P5], %[b5]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H3]" SS_DPP_ROW(3)
+      "v_fma_f32 %[H6], %[e6], %[P6], %[b6]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H4]" SS_DPP_ROW(4)
+      "v_fma_f32 %[H7], %[e7], %[P7], %[b7]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H5]" SS_DPP_ROW(5)
+      "v_fma_f32 %[H8], %[e8], %[P8], %[b8]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H6]" SS_DPP_ROW(6)
+      "v_fma_f32 %[H9], %[e9], %[P9], %[b9]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H7]" SS_DPP_ROW(7)
+      "v_fma_f32 %[H10], %[e10], %[P10], %[b10]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H8]" SS_DPP_ROW(8)
+      "v_fma_f32 %[H11], %[e11], %[P11], %[b11]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H9]" SS_DPP_ROW(9)
+      "v_fma_f32 %[H12], %[e12], %[P12], %[b12]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H10]" SS_DPP_ROW(10)
+      "v_fma_f32 %[H13], %[e13], %[P13], %[b13]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H11]" SS_DPP_ROW(11)
+      "v_fma_f32 %[H14], %[e14], %[P14], %[b14]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H12]" SS_DPP_ROW(12)
+      "v_fma_f32 %[H15], %[e15], %[P15], %[b15]\n"
+      "v_fmac_f32_dpp %[s], %[vc], %[H13]" SS_DPP_ROW(13)
+      "s_nop 1\n"
       "v_fmac_f32_dpp %[s], %[vc], %[H14]" SS_DPP_ROW(14)
-      "s_nop 1\n"
       "v_fmac_f32_dpp %[s], %[vc], %[H15]" SS_DPP_ROW(15)
-      : SS_OPS16(H, "=&v"), [s] "+v"(s), [t] "=&v"(t)
-      : SS_OPS16(P, "v"), SS_OPS16(e, "v"), [dtu] "v"(dtu), [vb] "v"(vb), [vc] "v"(vc));
+      : SS_OPS16(H, "=&v"), [s] "+v"(s)
+      : SS_OPS16(P, "v"), SS_OPS16(e, "v"), SS_OPS16(b, "v"), [vc] "v"(vc));
 }
-#undef BW_T
-
-// bwd_true without s, for calls without the gate (s only feeds dz): H[n] = e[n] P[n] + dtu B[n].
-__device__ __forceinline__ void bwd_true_states(const float (&P)[16], float (&H)[16], const float (&e)[16],
-                                                float dtu, float vb) {
-  float t;
+// Without s (no gate): H[n] = e[n] P[n] + bu[n].
+__device__ __forceinline__ void bwd_true_states_bu(const float (&P)[16], float (&H)[16], const float (&e)[16],
+                                                   const float (&b)[16]) {
   asm volatile(
-      "s_nop 1\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(0)
-      "v_fma_f32 %[H0], %[e0], %[P0], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(1)
-      "v_fma_f32 %[H1], %[e1], %[P1], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(2)
-      "v_fma_f32 %[H2], %[e2], %[P2], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(3)
-      "v_fma_f32 %[H3], %[e3], %[P3], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(4)
-      "v_fma_f32 %[H4], %[e4], %[P4], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(5)
-      "v_fma_f32 %[H5], %[e5], %[P5], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(6)
-      "v_fma_f32 %[H6], %[e6], %[P6], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(7)
-      "v_fma_f32 %[H7], %[e7], %[P7], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(8)
-      "v_fma_f32 %[H8], %[e8], %[P8], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(9)
-      "v_fma_f32 %[H9], %[e9], %[P9], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(10)
-      "v_fma_f32 %[H10], %[e10], %[P10], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(11)
-      "v_fma_f32 %[H11], %[e11], %[P11], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(12)
-      "v_fma_f32 %[H12], %[e12], %[P12], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(13)
-      "v_fma_f32 %[H13], %[e13], %[P13], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(14)
-      "v_fma_f32 %[H14], %[e14], %[P14], %[t]\n"
-      "v_mul_f32_dpp %[t], %[vb], %[dtu]" SS_DPP_ROW(15)
-      "v_fma_f32 %[H15], %[e15], %[P15], %[t]\n"
-      : SS_OPS16(H, "=&v"), [t] "=&v"(t)
-      : SS_OPS16(P, "v"), SS_OPS16(e, "v"), [dtu] "v"(dtu), [vb] "v"(vb));
+      "v_fma_f32 %[H0], %[e0], %[P0], %[b0]\n"
+      "v_fma_f32 %[H1], %[e1], %[P1], %[b1]\n"
+      "v_fma_f32 %[H2], %[e2], %[P2], %[b2]\n"
+      "v_fma_f32 %[H3], %[e3], %[P3], %[b3]\n"
+      "v_fma_f32 %[H4], %[e4], %[P4], %[b4]\n"
+      "v_fma_f32 %[H5], %[e5], %[P5], %[b5]\n"
+      "v_fma_f32 %[H6], %[e6], %[P6], %[b6]\n"
+      "v_fma_f32 %[H7], %[e7], %[P7], %[b7]\n"
+      "v_fma_f32 %[H8], %[e8], %[P8], %[b8]\n"
+      "v_fma_f32 %[H9], %[e9], %[P9], %[b9]\n"
+      "v_fma_f32 %[H10], %[e10], %[P10], %[b10]\n"
+      "v_fma_f32 %[H11], %[e11], %[P11], %[b11]\n"
+      "v_fma_f32 %[H12], %[e12], %[P12], %[b12]\n"
+      "v_fma_f32 %[H13], %[e13], %[P13], %[b13]\n"
+      "v_fma_f32 %[H14], %[e14], %[P14], %[b14]\n"
+      "v_fma_f32 %[H15], %[e15], %[P15], %[b15]\n"
+      : SS_OPS16(H, "=&v")
+      : SS_OPS16(P, "v"), SS_OPS16(e, "v"), SS_OPS16(b, "v"));
 }
 
 // Reverse local step of one token: m[n] = e[n] (m[n] + ds C[n]).
@@ -848,15 +920,11 @@ void bwd_chunked_kernel(BwdArgs a) {
     }
 
     // forward local pass from a zero state: decays and chunk aggregates
-    float ex[TC][16], h[16], dsum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < TC; ++j) {
-      dsum += dt[j];
-      if (j == 0)
-        bwd_local_first(h, ex[j], A2, dt[j], dtu[j], vb[j]);
-      else
-        bwd_local(h, ex[j], A2, dt[j], dtu[j], vb[j]);
-    }
+    static_assert(TC == 2, "the local pass keeps two tokens' input terms");
+    float ex[TC][16], bu[TC][16], h[16];
+    const float dsum = dt[0] + dt[1];
+    bwd_local_first_bu(bu[0], ex[0], A2, dt[0], dtu[0], vb[0]);
+    bwd_local_next_bu(h, bu[1], ex[1], bu[0], A2, dt[1], dtu[1], vb[1]);
     // reverse local pass from a zero adjoint (it needs only the decays): the chunk
     // aggregate mu_loc, so both folds share one pair of barriers
     float mu[16];
@@ -932,11 +1000,11 @@ void bwd_chunked_kernel(BwdArgs a) {
     for (int j = 0; j < TC; ++j) {
       if constexpr (GATE) {
         float s = Dd * uu[j];
-        bwd_true(j == 0 ? q : H[j > 0 ? j - 1 : 0], H[j], ex[j], dtu[j], vb[j], vc[j], s);
+        bwd_true_bu(j == 0 ? q : H[j > 0 ? j - 1 : 0], H[j], ex[j], bu[j], vc[j], s);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dyv[j] * s * dsl[j]), rdz,
                                               tvs[j] ? e_off : chunk::kDropOffset, j * er, 0);
       } else {
-        bwd_true_states(j == 0 ? q : H[j > 0 ? j - 1 : 0], H[j], ex[j], dtu[j], vb[j]);
+        bwd_true_states_bu(j == 0 ? q : H[j > 0 ? j - 1 : 0], H[j], ex[j], bu[j]);
       }
     }
 
