@@ -56,7 +56,8 @@ typedef enum {
   SS_ERR_HIP = 6,           /* a HIP runtime call or kernel launch failed */
   SS_ERR_DEVICE = 7,        /* the current device is not a gfx950 GPU */
   SS_ERR_WORKSPACE = 8,     /* workspace NULL or smaller than its size query returns */
-  SS_ERR_SPLIT_WAIT = 9     /* ss_workspace_status: a sequence-split hand-off wait gave up */
+  SS_ERR_SPLIT_WAIT = 9     /* a sequence-split hand-off wait gave up (the count that
+                               ss_workspace_status delivers is nonzero) */
 } ss_status;
 
 typedef enum {
@@ -159,14 +160,17 @@ int ss_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
                           const ss_fwd_options* opt, size_t* bytes);
 
 /*
- * ss_workspace_status -- whether a hand-off wait of the sequence split gave up in the most
- * recent split call that used this workspace (the workspace given to ss_fwd_ex / ss_fwd_conv,
- * or to ss_bwd). Waits hold until the previous part has published its state, which it always
- * does; this reports the bounded wait's safety net (or split_wait_limit < 0). Synchronises
- * `stream` (blocking the host) and reads a 4-byte counter. Returns SS_OK (no give-up) or
- * SS_ERR_SPLIT_WAIT, with the number of waits that gave up in *giveups (may be NULL).
- * Errors: SS_ERR_NULL_ARG (workspace NULL), SS_ERR_MISALIGNED (not 16-byte aligned),
- * SS_ERR_WORKSPACE (workspace_bytes < 1024), SS_ERR_HIP.
+ * ss_workspace_status -- enqueue on `stream` a copy of the number of sequence-split hand-off
+ * waits that gave up in the most recent split call that used this workspace (the workspace
+ * given to ss_fwd_ex / ss_fwd_conv, or to ss_bwd) into *giveups. Waits hold until the previous
+ * part has published its state, which it always does; the count reports the bounded wait's
+ * safety net (or split_wait_limit < 0): 0, or the number of waits that gave up, whose parts
+ * ran from a NaN state. Asynchronous like every other call: *giveups (4 bytes, 4-byte aligned;
+ * device memory, or pinned host memory for a copy that does not block) holds the count once
+ * `stream` has reached this point. A caller that reports the give-up as a status uses
+ * SS_ERR_SPLIT_WAIT. Errors: SS_ERR_NULL_ARG (workspace or giveups NULL), SS_ERR_MISALIGNED
+ * (workspace not 16-byte or giveups not 4-byte aligned), SS_ERR_WORKSPACE (workspace_bytes <
+ * 1024), SS_ERR_HIP (the copy could not be enqueued).
  */
 int ss_workspace_status(const void* workspace, size_t workspace_bytes, uint32_t* giveups, void* stream);
 

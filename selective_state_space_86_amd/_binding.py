@@ -69,7 +69,7 @@ def load_library():
     lib.ss_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(FwdOptions),
                                           ctypes.POINTER(ctypes.c_size_t)]
     lib.ss_workspace_status.restype = i32
-    lib.ss_workspace_status.argtypes = [vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_uint32), vp]
+    lib.ss_workspace_status.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.ss_step.restype = i32
     lib.ss_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i32, vp]
     lib.ss_step_ex.restype = i32
@@ -150,13 +150,16 @@ def fwd_workspace_size(batch, seqlen, dim, dstate, dtype=torch.float32, kernel=0
 
 def workspace_status(workspace, stream=None):
     """``ss_workspace_status``: (status, give-ups) of the most recent split call that used
-    this workspace; synchronises the stream. status is 0 or SS_ERR_SPLIT_WAIT (9)."""
-    n = ctypes.c_uint32(0)
+    this workspace. The library enqueues the count into a device word; reading it here waits
+    for the stream. status is SS_ERR_SPLIT_WAIT (9) when a wait gave up, else 0."""
+    n = torch.empty(1, dtype=torch.int32, device=workspace.device)  # (overwritten by the copy)
     rc = load_library().ss_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
-                                            ctypes.byref(n), _stream(workspace.device, stream))
-    if rc not in (0, SS_ERR_SPLIT_WAIT):
+                                            _ptr(n), _stream(workspace.device, stream))
+    if rc != 0:
         raise SSError(rc, "ss_workspace_status")
-    return rc, int(n.value)
+    torch.cuda.synchronize(workspace.device)  # (the copy runs on `stream`, not torch's current one)
+    count = int(n.item())
+    return (SS_ERR_SPLIT_WAIT if count else 0), count
 
 
 def _fwd_workspace(workspace, dev, batch, L, dim, N, dtype, **opt):

@@ -309,18 +309,15 @@ int ss_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t ds
 }
 
 int ss_workspace_status(const void* workspace, size_t workspace_bytes, uint32_t* giveups, void* stream) {
-  if (giveups) *giveups = 0;
-  if (!workspace) return SS_ERR_NULL_ARG;
-  if (!aligned(workspace, 16)) return SS_ERR_MISALIGNED;
+  if (!workspace || !giveups) return SS_ERR_NULL_ARG;
+  if (!aligned(workspace, 16) || !aligned(giveups, 4)) return SS_ERR_MISALIGNED;
   if (workspace_bytes < static_cast<size_t>(ss::split::kHeader) * 4) return SS_ERR_WORKSPACE;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  uint32_t count = 0;
   const uint32_t* word = static_cast<const uint32_t*>(workspace) + ss::split::kGiveUpWord;
-  if (hipMemcpyAsync(&count, word, sizeof(count), hipMemcpyDeviceToHost, s) != hipSuccess ||
-      hipStreamSynchronize(s) != hipSuccess)
+  // (hipMemcpyDefault: *giveups may be device memory or pinned host memory)
+  if (hipMemcpyAsync(giveups, word, sizeof(uint32_t), hipMemcpyDefault, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
     return SS_ERR_HIP;
-  if (giveups) *giveups = count;
-  return count == 0 ? SS_OK : SS_ERR_SPLIT_WAIT;
+  return SS_OK;
 }
 
 int ss_step_ex(float* state, const void* u, const void* delta, const float* A, const void* B,

@@ -325,13 +325,14 @@ def fwd_ex_call_opt(lib, opt, **kw):
                          ctypes.byref(opt), None)
 
 
-@pytest.mark.parametrize("ws,nbytes,code", [(None, 4096, 1), (FAKE + 4, 4096, 5), (FAKE, 1000, 8)])
-def test_workspace_status_validation(lib, ws, nbytes, code):
-    """ss_workspace_status: NULL, misaligned (16 bytes) and too-small (one 1 KiB header)
-    workspaces are refused before any device access; the give-up count is zeroed."""
-    n = ctypes.c_uint32(77)
-    assert lib.ss_workspace_status(ws, nbytes, ctypes.byref(n), None) == code
-    assert n.value == 0
+@pytest.mark.parametrize("ws,nbytes,out,code", [(None, 4096, FAKE, 1), (FAKE, 4096, None, 1),
+                                                (FAKE + 4, 4096, FAKE, 5), (FAKE, 4096, FAKE + 2, 5),
+                                                (FAKE, 1000, FAKE, 8)])
+def test_workspace_status_validation(lib, ws, nbytes, out, code):
+    """ss_workspace_status: a NULL workspace or count pointer, a workspace not 16-byte or a
+    count not 4-byte aligned, and a too-small workspace (one 1 KiB header) are refused before
+    anything is enqueued."""
+    assert lib.ss_workspace_status(ws, nbytes, out, None) == code
 
 
 def test_status_string_of_the_split_wait(lib):

@@ -187,6 +187,14 @@ def test_split_wait_give_up_is_reported(chunk, rows):
     groups = batch * ((dim + 15) // 16)
     rc, n = ss.workspace_status(ws)
     assert rc == 9 and n == groups * (parts - 1)
+    # the same count through the C ABI into pinned host memory, read after the stream
+    from selective_state_space_86_amd import _binding
+    host = torch.full((1,), -1, dtype=torch.int32, pin_memory=True)
+    s = torch.cuda.current_stream(DEV)
+    assert _binding.load_library().ss_workspace_status(ws.data_ptr(), ws.numel(), host.data_ptr(),
+                                                       s.cuda_stream) == 0
+    s.synchronize()
+    assert int(host[0]) == groups * (parts - 1)
     tile = rows * chunk
     part_len = -(-(-(-L // parts)) // tile) * tile
     assert torch.equal(got[0][:, :part_len], ref[0][:, :part_len])
