@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SS_ABI_VERSION 11
+#define SS_ABI_VERSION 12
 #define SS_MAX_DSTATE 16
 
 typedef enum {

@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ss_abi_version() == _binding.ABI_VERSION == 11
+    assert lib.ss_abi_version() == _binding.ABI_VERSION == 12
     for s in range(0, 10):
         assert lib.ss_status_string(s)
     assert b"unknown" in lib.ss_status_string(99)
