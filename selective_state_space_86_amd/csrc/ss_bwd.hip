@@ -69,11 +69,30 @@ __device__ __forceinline__ float sigmoid(float x) { return fast_rcp(1.0f + fast_
 // more. Where the exp is used (|x| >= 1/64) a carried value decays by e^-1 within 64
 // chunks, so its bias stays below ~5e-7 relative; the series' truncation, below
 // x^3/24 < 1.6e-7 relative to em1, adds up to less than that over the slow decays.
-// Cost: 6 VALU and an exp.
+// Cost: 6 VALU and an exp, without a branch: the exp is made opaque before the select, which
+// the compiler otherwise turned into a branch around it (an exec-mask branch per state and
+// chunk, both sides taken wherever the lanes disagree).
 __device__ __forceinline__ float chunk_em1(float x2) {
   constexpr float c1 = kLn2, c2 = kLn2 * kLn2 / 2.0f, c3 = kLn2 * kLn2 * kLn2 / 6.0f;
   const float p = x2 * __builtin_fmaf(x2, __builtin_fmaf(x2, c3, c2), c1);
-  return __builtin_fabsf(x2) < kLog2e / 64.0f ? p : fast_exp2(x2) - 1.0f;
+  float e = fast_exp2(x2);
+  asm("" : "+v"(e));
+  return __builtin_fabsf(x2) < kLog2e / 64.0f ? p : e - 1.0f;
+}
+
+// softplus as ss::softplus, with max(x, 0) as one v_max_f32: the step is computed only with the
+// softplus flag set (a runtime branch), so x comes from another basic block, and the builtin
+// fmax would first quiet a possible signalling NaN with a second instruction.
+__device__ __forceinline__ float softplus_b(float x) {
+  const float t = fast_exp2(-__builtin_fabsf(x) * kLog2e);
+  const float w = 1.0f + t;
+  const float m = w - 1.0f;
+  const float d = t - m;
+  const float corr = __builtin_fmaf(-d, m, d);
+  const float lp = __builtin_fmaf(fast_log2(w), kLn2, corr);
+  float mx;
+  asm("v_max_f32 %0, 0, %1" : "=v"(mx) : "v"(x));
+  return mx + lp;
 }
 
 // ---- hand-scheduled per-token blocks of the backward (16 states of one token) ----------
@@ -665,11 +684,13 @@ void bwd_ckpt_kernel(BwdArgs a) {
     // for all of them where the paths join)
     fetch(nxt, t0 + TT < t_end ? t0 + TT : t0);
     float h[16], e[16], dsum = 0.0f;
+    // tokens of this lane's chunk inside the sequence (32-bit, once per tile)
+    const int nval = static_cast<int>(min(L - t0, static_cast<int64_t>(TT))) - l.k * CTC;
 #pragma unroll
     for (int j = 0; j < CTC; ++j) {
       const float x = chunk::as_f32<T>(cur.x[j]) + bias;
-      float dt = a.softplus ? softplus(x) : x;
-      dt = (t0 + l.k * CTC + j < L) ? dt : 0.0f;  // a zero step is the identity
+      float dt = a.softplus ? softplus_b(x) : x;
+      dt = j < nval ? dt : 0.0f;  // a zero step is the identity
       dsum += dt;
       if (j == 0)  // (the state starts at zero: the first token's decay does not enter it)
         bwd_input_term(h, dt * chunk::as_f32<T>(cur.u[j]), chunk::as_f32<T>(cur.b[j]));
@@ -901,7 +922,7 @@ void bwd_chunked_kernel(BwdArgs a) {
       tvs[j] = tv;
       ok[j] = tv && l.cvalid;
       const float x = chunk::as_f32<T>(cur.x[j]) + bias;
-      dt[j] = tv ? (a.softplus ? softplus(x) : x) : 0.0f;
+      dt[j] = tv ? (a.softplus ? softplus_b(x) : x) : 0.0f;
       sg[j] = a.softplus ? sigmoid(x) : 1.0f;
       uu[j] = chunk::as_f32<T>(cur.u[j]);
       dtu[j] = dt[j] * uu[j];
