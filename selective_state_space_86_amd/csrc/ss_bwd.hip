@@ -80,21 +80,6 @@ __device__ __forceinline__ float chunk_em1(float x2) {
   return __builtin_fabsf(x2) < kLog2e / 64.0f ? p : e - 1.0f;
 }
 
-// softplus as ss::softplus, with max(x, 0) as one v_max_f32: the step is computed only with the
-// softplus flag set (a runtime branch), so x comes from another basic block, and the builtin
-// fmax would first quiet a possible signalling NaN with a second instruction.
-__device__ __forceinline__ float softplus_b(float x) {
-  const float t = fast_exp2(-__builtin_fabsf(x) * kLog2e);
-  const float w = 1.0f + t;
-  const float m = w - 1.0f;
-  const float d = t - m;
-  const float corr = __builtin_fmaf(-d, m, d);
-  const float lp = __builtin_fmaf(fast_log2(w), kLn2, corr);
-  float mx;
-  asm("v_max_f32 %0, 0, %1" : "=v"(mx) : "v"(x));
-  return mx + lp;
-}
-
 // ---- hand-scheduled per-token blocks of the backward (16 states of one token) ----------
 // Conventions as the forward's local_step: B_t[n] and C_t[n] are read from lane n of the
 // row by DPP row_newbcast:n folded into the consuming instruction; every VGPR a DPP
@@ -689,7 +674,7 @@ void bwd_ckpt_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < CTC; ++j) {
       const float x = chunk::as_f32<T>(cur.x[j]) + bias;
-      float dt = a.softplus ? softplus_b(x) : x;
+      float dt = a.softplus ? softplus(x) : x;
       dt = j < nval ? dt : 0.0f;  // a zero step is the identity
       dsum += dt;
       if (j == 0)  // (the state starts at zero: the first token's decay does not enter it)
@@ -922,7 +907,7 @@ void bwd_chunked_kernel(BwdArgs a) {
       tvs[j] = tv;
       ok[j] = tv && l.cvalid;
       const float x = chunk::as_f32<T>(cur.x[j]) + bias;
-      dt[j] = tv ? (a.softplus ? softplus_b(x) : x) : 0.0f;
+      dt[j] = tv ? (a.softplus ? softplus(x) : x) : 0.0f;
       sg[j] = a.softplus ? sigmoid(x) : 1.0f;
       uu[j] = chunk::as_f32<T>(cur.u[j]);
       dtu[j] = dt[j] * uu[j];

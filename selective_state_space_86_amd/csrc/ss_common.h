@@ -28,7 +28,10 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 // log1p(t) is log(w) for w = fl(1 + t) plus the rounding error of w: with m = w - 1 (exact
 // for w in [1, 2]) and d = t - m (exact), log(1 + t) = log(w) + log(1 + d/w) ~ log(w) + d/w,
 // and 1/w ~ 1 - m to the accuracy this tiny correction needs. When t < 2^-24, w = 1, m = 0
-// and the result is t itself. Cost: 2 transcendentals and 8 simple VALU ops.
+// and the result is t itself. max(x, 0) is one v_max_f32: the builtin fmax first quiets a
+// possible signalling NaN with a second instruction wherever x comes from another basic block
+// (the step is computed only with the softplus flag set, a runtime branch in every kernel); a
+// quiet NaN gives the same result either way. Cost: 2 transcendentals and 7 simple VALU ops.
 __device__ __forceinline__ float softplus(float x) {
   const float t = fast_exp2(-__builtin_fabsf(x) * kLog2e);
   const float w = 1.0f + t;
@@ -36,7 +39,9 @@ __device__ __forceinline__ float softplus(float x) {
   const float d = t - m;
   const float corr = __builtin_fmaf(-d, m, d);
   const float lp = __builtin_fmaf(fast_log2(w), kLn2, corr);
-  return __builtin_fmaxf(x, 0.0f) + lp;
+  float mx;
+  asm("v_max_f32 %0, 0, %1" : "=v"(mx) : "v"(x));
+  return mx + lp;
 }
 
 // Input coefficient of the exact zero-order hold, (e^x - 1)/A for x = dt*A, given
@@ -44,11 +49,16 @@ __device__ __forceinline__ float softplus(float x) {
 // dt*(1 + x/2 + x^2/6 + x^3/24 + x^4/120), whose truncation is below 1.3e-9 relative (and
 // which is dt at A = 0); otherwise (ab - 1)/A, where |ab - 1| > 0.06 keeps the rounding of
 // ab below 2e-6 relative. The subtraction ab - 1 alone would lose all accuracy as x -> 0.
+// Both sides are evaluated and one selected: the series is made opaque before the select,
+// which the compiler otherwise turned into an exec-mask branch per state (both sides taken
+// wherever the lanes of a wave disagree, plus the mask bookkeeping).
 __device__ __forceinline__ float zoh_coef(float dt, float x, float ab, float inv_a) {
   const float p = __builtin_fmaf(
       x, __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 120.0f, 1.0f / 24.0f), 1.0f / 6.0f), 0.5f),
       1.0f);
-  return __builtin_fabsf(x) < 0.0625f ? dt * p : (ab - 1.0f) * inv_a;
+  float small = dt * p;
+  asm("" : "+v"(small));
+  return __builtin_fabsf(x) < 0.0625f ? small : (ab - 1.0f) * inv_a;
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z), with the reciprocal on the transcendental unit.

@@ -49,21 +49,6 @@ using namespace chunk;
 
 constexpr int kLdsChunkStride = 16 * 16 + 16;  // [chunk][n][lane], padded against bank conflicts
 
-// softplus for the tile loop: as ss::softplus, with max(x, 0) as one v_max_f32 (the builtin
-// fmax quiets a signalling NaN first where x comes from another basic block, one more VALU
-// per element; a quiet NaN gives the same result either way).
-__device__ __forceinline__ float softplus_tile(float x) {
-  const float t = fast_exp2(-__builtin_fabsf(x) * kLog2e);
-  const float w = 1.0f + t;
-  const float m = w - 1.0f;
-  const float d = t - m;
-  const float corr = __builtin_fmaf(-d, m, d);
-  const float lp = __builtin_fmaf(fast_log2(w), kLn2, corr);
-  float mx;
-  asm("v_max_f32 %0, 0, %1" : "=v"(mx) : "v"(x));
-  return mx + lp;
-}
-
 // Sequence split (SPLIT): the work queue and state hand-off of ss_split.h. When the channel
 // groups do not fill the resident workgroup slots in whole rounds (the 3B long-context shape:
 // 320 groups for 256 one-workgroup CUs, so a second round of 64 would run on a quarter of
@@ -252,7 +237,7 @@ void fwd_chunked_kernel(FwdArgs a) {
       const float x = as_f32<T>(cur.raw[j]) + bias;
       const float vb = as_f32<T>(cur.vb[j]);
       vc[j] = as_f32<T>(cur.vc[j]);
-      float dt = a.softplus ? softplus_tile(x) : x;
+      float dt = a.softplus ? softplus(x) : x;
       if (TAIL) dt = j < nval ? dt : 0.0f;  // a zero step is the identity
       dsum += dt;
       y[j] = Dd * uu[j];
