@@ -636,22 +636,33 @@ void bwd_ckpt_kernel(BwdArgs a) {
   struct In {  // raw element bits, widened where used (a widening next to the load would wait for it)
     chunk::Bits<T> x[CTC], u[CTC], b[CTC];
   };
-  auto fetch = [&](In& r, int64_t t0) {
+  // The tile at t0: buffer resources and its last token (tokens past the end re-read it).
+  struct Src {
+    __amdgpu_buffer_rsrc_t rd, ru, rb;
+    int last;
+  };
+  auto src_of = [&](int64_t t0) {
+    Src r;
     const int64_t e0 = (l.b * L + t0) * a.dim + l.c0;
     const int64_t bc0 = (l.b * L + t0) * N;
     const int64_t left = (a.batch * L * a.dim - e0) * static_cast<int64_t>(sizeof(T));
     const int64_t bleft = (a.batch * L * N - bc0) * static_cast<int64_t>(sizeof(T));
-    const auto rd = chunk::rsrc(static_cast<const T*>(a.delta) + e0, left);
-    const auto ru = chunk::rsrc(static_cast<const T*>(a.u) + e0, left);
-    const auto rb = chunk::rsrc(static_cast<const T*>(a.B) + bc0, bleft);
-    const int last = static_cast<int>(min(L - 1 - t0, static_cast<int64_t>(TT - 1)));
+    r.rd = chunk::rsrc(static_cast<const T*>(a.delta) + e0, left);
+    r.ru = chunk::rsrc(static_cast<const T*>(a.u) + e0, left);
+    r.rb = chunk::rsrc(static_cast<const T*>(a.B) + bc0, bleft);
+    r.last = static_cast<int>(min(L - 1 - t0, static_cast<int64_t>(TT - 1)));
+    return r;
+  };
+  auto fetch_token = [&](In& r, const Src& sr, int j) {
+    const uint32_t tt = static_cast<uint32_t>(min(l.k * CTC + j, sr.last));  // past the end: last token
+    r.x[j] = chunk::ldr<T>(sr.rd, tt * tok_row + col, 0);
+    r.u[j] = chunk::ldr<T>(sr.ru, tt * tok_row + col, 0);
+    r.b[j] = chunk::ldr<T>(sr.rb, bcol == 0x7fffffffu ? bcol : tt * bc_row + bcol, 0);
+  };
+  auto fetch = [&](In& r, int64_t t0) {
+    const Src sr = src_of(t0);
 #pragma unroll
-    for (int j = 0; j < CTC; ++j) {
-      const uint32_t tt = static_cast<uint32_t>(min(l.k * CTC + j, last));  // past the end: last token
-      r.x[j] = chunk::ldr<T>(rd, tt * tok_row + col, 0);
-      r.u[j] = chunk::ldr<T>(ru, tt * tok_row + col, 0);
-      r.b[j] = chunk::ldr<T>(rb, bcol == 0x7fffffffu ? bcol : tt * bc_row + bcol, 0);
-    }
+    for (int j = 0; j < CTC; ++j) fetch_token(r, sr, j);
   };
   In cur, nxt;
   if (a.ntiles > 0) {
@@ -665,9 +676,11 @@ void bwd_ckpt_kernel(BwdArgs a) {
   asm volatile("" : "+v"(carry));  // (likewise the loaded initial state)
   for (int64_t t0 = t_begin; t0 < t_end; t0 += TT) {
     if (!SPLIT) progress_priority(t0, L);
-    // (the last tile re-requests itself, unused: loads under a branch make the compiler wait
-    // for all of them where the paths join)
-    fetch(nxt, t0 + TT < t_end ? t0 + TT : t0);
+    // The next tile's inputs, token by token: token j's loads are issued right after this
+    // tile's token j is consumed, so a tile's requests reach the memory pipeline spread over
+    // its local pass rather than all at its start (the last tile re-requests itself, unused:
+    // loads under a branch make the compiler wait for all of them where the paths join).
+    const Src nsrc = src_of(t0 + TT < t_end ? t0 + TT : t0);
     float h[16], e[16], dsum = 0.0f;
     // tokens of this lane's chunk inside the sequence (32-bit, once per tile)
     const int nval = static_cast<int>(min(L - t0, static_cast<int64_t>(TT))) - l.k * CTC;
@@ -681,6 +694,7 @@ void bwd_ckpt_kernel(BwdArgs a) {
         bwd_input_term(h, dt * chunk::as_f32<T>(cur.u[j]), chunk::as_f32<T>(cur.b[j]));
       else
         bwd_local(h, e, A2, dt, dt * chunk::as_f32<T>(cur.u[j]), chunk::as_f32<T>(cur.b[j]));
+      fetch_token(nxt, nsrc, j);
     }
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
