@@ -49,6 +49,42 @@ using namespace chunk;
 
 constexpr int kLdsChunkStride = 16 * 16 + 16;  // [chunk][n][lane], padded against bank conflicts
 
+// Fix-up weights, for the rows of a 32-row tile that own no state in the fold, computed while
+// the other rows fold: token j's stored decays become W_j[n] = C_j[n] P_j[n], with P_j[n] the
+// product of the chunk's decays up to token j (kept in p), so that once the carry-in q is
+// known the fix-up is y_j += sum_n W_j[n] q[n], one fma per update instead of two. With
+// `first`, p starts as the token's decays. (C_j[n] comes from lane n of the row by DPP
+// row_newbcast:n; every DPP source is written well before the block, which starts with
+// s_nop 1.)
+#define SS_PRE_M(n) "v_mul_f32 %[p" #n "], %[p" #n "], %[e" #n "]\n"
+#define SS_PRE_C(n) "v_mov_b32 %[p" #n "], %[e" #n "]\n"
+#define SS_PRE_W(n) "v_mul_f32_dpp %[e" #n "], %[vc], %[p" #n "]" SS_DPP_ROW(n)
+#define SS_PRE(M)                                                                              \
+  asm volatile("s_nop 1\n" M(0) M(1) SS_PRE_W(0) M(2) SS_PRE_W(1) M(3) SS_PRE_W(2) M(4)         \
+               SS_PRE_W(3) M(5) SS_PRE_W(4) M(6) SS_PRE_W(5) M(7) SS_PRE_W(6) M(8) SS_PRE_W(7)     \
+               M(9) SS_PRE_W(8) M(10) SS_PRE_W(9) M(11) SS_PRE_W(10) M(12) SS_PRE_W(11) M(13)      \
+               SS_PRE_W(12) M(14) SS_PRE_W(13) M(15) SS_PRE_W(14) SS_PRE_W(15)                     \
+               : SS_OPS16(p, "+v"), SS_OPS16(e, "+v")                                              \
+               : [vc] "v"(vc))
+__device__ __forceinline__ void fixup_weights(float (&p)[16], float (&e)[16], float vc, bool first) {
+  if (first)
+    SS_PRE(SS_PRE_C);
+  else
+    SS_PRE(SS_PRE_M);
+}
+#undef SS_PRE
+// y += sum_n w[n] q[n] (even and odd states in separate sums, as fixup_step)
+__device__ __forceinline__ void fixup_weighted(const float (&w)[16], const float (&q)[16], float& y) {
+  float y2 = w[1] * q[1];
+  y = __builtin_fmaf(w[0], q[0], y);
+#pragma unroll
+  for (int n = 2; n < 16; n += 2) {
+    y = __builtin_fmaf(w[n], q[n], y);
+    y2 = __builtin_fmaf(w[n + 1], q[n + 1], y2);
+  }
+  y += y2;
+}
+
 // Sequence split (SPLIT): the work queue and state hand-off of ss_split.h. When the channel
 // groups do not fill the resident workgroup slots in whole rounds (the 3B long-context shape:
 // 320 groups for 256 one-workgroup CUs, so a second round of 64 would run on a quarter of
@@ -305,8 +341,14 @@ void fwd_chunked_kernel(FwdArgs a) {
         }
       }
     }
+    // (32-row tiles: rows 16..31 are waves 4..7, so the test is uniform per wave)
+    const bool weighted = R == 32 && wave_tid0 >= 256;
+    float q[16];  // this chunk's carry-in (before it, the running decay product of the weights)
+    if (weighted) {
+#pragma unroll
+      for (int j = 0; j < TC; ++j) fixup_weights(q, ex[j], vc[j], j == 0);
+    }
     __syncthreads();
-    float q[16];  // this chunk's carry-in
     {
       const float* lc = lds_a + k_t * kLdsChunkStride + i_t;
 #pragma unroll
@@ -321,12 +363,23 @@ void fwd_chunked_kernel(FwdArgs a) {
     const auto ry = rsrc_tile(a.y + y0);
     uint32_t yr = y_row;  // (token steps formed per tile, as in the loads)
     asm volatile("" : "+s"(yr));
-#pragma unroll
-    for (int j = 0; j < TC; ++j) {
-      fixup_step(q, ex[j], vc[j], y[j]);
+    auto store = [&](int j) {
       const uint32_t vo = TAIL ? ((cvalid && j < nval) ? y_off : kDropOffset) : y_voff;
       const float g = ZT ? silu(as_f32<T>(zb[j])) : gate[j];
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[j] * g), ry, vo, j * yr, 0);
+    };
+    if (weighted) {  // (one branch around the whole fix-up: q stays one set of registers)
+#pragma unroll
+      for (int j = 0; j < TC; ++j) {
+        fixup_weighted(ex[j], q, y[j]);
+        store(j);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TC; ++j) {
+        fixup_step(q, ex[j], vc[j], y[j]);
+        store(j);
+      }
     }
     buf ^= 1;
   };
