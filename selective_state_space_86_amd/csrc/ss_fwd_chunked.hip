@@ -528,13 +528,17 @@ int fwd_split_parts(const FwdArgs& a, ChunkPlan plan, int cus) {
     const int64_t len = fwd_split_part_len(a.seqlen, plan, p);
     return (a.seqlen + len - 1) / len == p;
   };
+  // Among the part counts whose modelled time is within 5% of the best, the largest whose
+  // parts still span 40 tiles: shorter parts even out the workgroups' finishing times, and
+  // each part pays a start (its first tile's loads, the hand-off); at most 12 parts, whose
+  // hand-off slots the fixed scratch of ss_fwd_noalloc holds at the 3B layer's 320 groups.
   double tbest = time(1);
-  for (int p = 2; p <= 8; ++p)
+  for (int p = 2; p <= 12; ++p)
     if (fits(p)) tbest = std::min(tbest, time(p));
   int best = 1;
-  for (int p = 2; p <= 8; ++p) {
+  for (int p = 2; p <= 12; ++p) {
     if (!fits(p) || time(p) > tbest / 0.95) continue;
-    if (best == 1 || fwd_split_part_len(a.seqlen, plan, p) >= 32 * tile) best = p;
+    if (best == 1 || fwd_split_part_len(a.seqlen, plan, p) >= 40 * tile) best = p;
   }
   return best;
 }

@@ -310,13 +310,14 @@ def test_split_from_several_host_threads():
     assert not errors, errors
 
 
-@pytest.mark.parametrize("batch,L,dim,dt,parts", [(1, 131072, 5120, torch.bfloat16, 8),
+@pytest.mark.parametrize("batch,L,dim,dt,parts", [(1, 131072, 5120, torch.bfloat16, 12),
                                                  (4, 4096, 4096, torch.bfloat16, 3),
                                                  (8, 2048, 1536, torch.float32, 1)])
 def test_automatic_part_count_at_the_layer_shapes(batch, L, dim, dt, parts):
     """The automatic plan's part count on this chip (256 CUs), read from the workspace it asks
-    for: 8 at the 3B long-context shape (4, 8 and 12 parts model the same rounds; the largest
-    whose parts span 32 tiles is taken), 3 at the 1.4B shape, none at the 130M shape."""
+    for: 12 at the 3B long-context shape (4, 8, 12 and 16 parts model the same rounds; the
+    largest of at most 12 whose parts span 40 tiles is taken), 3 at the 1.4B shape, none at
+    the 130M shape."""
     auto = ss.fwd_workspace_size(batch, L, dim, 16, dt)
     if parts == 1:
         assert auto == 0
