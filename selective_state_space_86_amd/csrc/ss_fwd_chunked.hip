@@ -355,7 +355,15 @@ void fwd_chunked_kernel(FwdArgs a) {
       for (int n = 0; n < 16; ++n) q[n] = lc[n * 16];
     }
 
-    if (!kProgressPrio) __builtin_amdgcn_s_setprio(kFixupPrio);
+    // (32-row tiles: the rows that folded have the longer fix-up, two VALU per update against
+    // one for the rows with weights, and run it at priority 3: 3B 3.500/3.504/3.511 ->
+    // 3.481/3.487/3.482 ms on one box)
+    if (!kProgressPrio) {
+      if (R == 32 && wave_tid0 < 256)
+        __builtin_amdgcn_s_setprio(3);
+      else
+        __builtin_amdgcn_s_setprio(kFixupPrio);
+    }
     // fix-up with the carry-in, gate, store (unconditionally: a masked lane's store goes to an
     // offset past the buffer range and is dropped, so the compiler sees a fixed number of
     // outstanding stores and never waits for them when the prefetched loads are consumed)
