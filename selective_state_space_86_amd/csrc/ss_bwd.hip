@@ -602,9 +602,15 @@ void bwd_ckpt_kernel(BwdArgs a) {
   static_assert(CTC * 4 == 32 || CTC * 8 == 32 || CTC * 16 == 32, "checkpoints every 32 tokens");
   static_assert(R == 16 || R == 32, "16 or 32 chunks per tile");
   constexpr int kPer = 32 / CTC;  // chunks per checkpoint interval
-  __shared__ float lds_p[R * kS];
-  __shared__ float lds_h[R * kS];
+  // With 32 rows, rows 16..31 own no state in the fold: the aggregate arrays alternate by
+  // tile, so those rows go on to the next tile's local pass while rows 0..15 fold (a tile's
+  // arrays are written again two tiles later, after every row has passed the first barrier
+  // of the tile between, which the folding rows reach only after their fold).
+  constexpr int NB = R == 32 ? 2 : 1;
+  __shared__ float lds_p2[NB][R * kS];
+  __shared__ float lds_h2[NB][R * kS];
   __shared__ uint32_t item_s, seen_s;
+  int buf = 0;
   int64_t gi, part;
   work_item<SPLIT>(a, false, item_s, gi, part);
   const Lane l = lane_at(a, gi);
@@ -696,6 +702,8 @@ void bwd_ckpt_kernel(BwdArgs a) {
         bwd_local(h, e, A2, dt, dt * chunk::as_f32<T>(cur.u[j]), chunk::as_f32<T>(cur.b[j]));
       fetch_token(nxt, nsrc, j);
     }
+    float* lds_p = lds_p2[buf];
+    float* lds_h = lds_h2[buf];
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
       lds_p[l.k * kS + n * 16 + l.i] = chunk_em1(A2[n] * dsum);
@@ -729,7 +737,8 @@ void bwd_ckpt_kernel(BwdArgs a) {
       for (int m = 0; m < kCk; ++m)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ckv[m]), rck, voff, m * ck_row, 0);
     }
-    __syncthreads();
+    if (NB == 1) __syncthreads();  // (one set of arrays: the next tile writes it)
+    buf = NB == 2 ? buf ^ 1 : 0;
     cur = nxt;
   }
   if (SPLIT && part < a.parts - 1) {  // publish the end state for the next part
