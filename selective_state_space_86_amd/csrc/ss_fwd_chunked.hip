@@ -488,10 +488,14 @@ bool fwd_chunked_supported(const FwdArgs& a) { return a.dstate == 16 && a.seqlen
 //    slower at steady clock (420 against 398 us at 1.4B, 169 against 136 us at 130M): in a
 //    12-row tile a quarter of the folding lanes fold two states. They stay available through
 //    ss_fwd_options.chunk_rows.
-// The zero-order-hold variant runs at two waves per SIMD either way and keeps 16 rows.
+// The zero-order-hold variant keeps chunk length 4 (it spills registers at 8) and takes 32
+// rows where the plain one does (3B long-context shape: 6.31 against 10.35 ms with 16 rows,
+// whose 320 groups of 4 waves left most SIMDs one wave).
 ChunkPlan fwd_chunked_pick(const FwdArgs& a, int cus) {
   const int64_t groups = a.batch * ((a.dim + 15) / 16);
-  if (a.zoh) return {4, 16};  // the zero-order-hold variant spills registers at 8
+  if (a.zoh)
+    return (groups <= 2 * static_cast<int64_t>(cus) && 128 * a.dim * 4 < (1LL << 31)) ? ChunkPlan{4, 32}
+                                                                                       : ChunkPlan{4, 16};
   // (32 rows of 8 tokens span 256 tokens of the (.., dim) arrays from one 32-bit tile offset)
   if (groups <= 2 * static_cast<int64_t>(cus)) return (256 * a.dim * 4 < (1LL << 31)) ? ChunkPlan{8, 32} : ChunkPlan{8, 16};
   return ChunkPlan{4, 16};
