@@ -10,8 +10,9 @@ chunks of 4096 tokens of one batch row (chunk = row * chunks_per_row + index), e
 as (tokens, width) in token-major order, so a draw does not depend on how the tokens are
 later grouped into calls or launches, and a shorter sequence draws a prefix of a longer
 one. Values are drawn in fp64, rounded to fp32 (nearest even) and, for bf16 tensors, to
-bf16 (nearest even). Sequences of 2^19 tokens or more are drawn on the device with a
-seeded ``torch.Generator`` instead (host generation would take minutes there).
+bf16 (nearest even). Every length is drawn this way, the longest sweep point (2^20 tokens of
+5120 channels) included, chunks in parallel on up to 16 host threads. The projection inputs
+(``make_proj``) follow the same recipe with tensor ids 7..9.
 
 Workload shapes are the per-layer scan shapes of Mamba models (d_inner channels,
 d_state = 16): 130M (batch 8, L 2048, 1536 ch), 1.4B (batch 4, L 4096, 4096 ch) and
@@ -79,18 +80,14 @@ def sweep_workload(seqlen: int) -> Workload:
     return WORKLOADS["mamba3b-long"].replace(name=f"mamba3b-L{seqlen}", seqlen=seqlen)
 
 
-def _seed(name: str, seed: int) -> int:
-    return (zlib.crc32(name.encode()) * 1000003 + 86 * 7919 + seed) % (2 ** 62)
-
-
 # configuration ids of the seed key: the tiny case 1, 130M 2, 1.4B 3, 3B long context 4 (and
 # its length sweep, which draws prefixes of the same streams), decode 5; other shapes (tests)
 # a number derived from their name
 CONFIG_IDS = {"tiny": 1, "tiny-lti": 1, "mamba130m": 2, "mamba130m-gated": 2, "mamba1.4b": 3,
               "mamba3b-long": 4, "decode": 5}
-TENSOR_IDS = {"u": 0, "delta": 1, "z": 2, "B": 3, "C": 4, "D": 5, "bias": 6}
+TENSOR_IDS = {"u": 0, "delta": 1, "z": 2, "B": 3, "C": 4, "D": 5, "bias": 6,
+              "proj_u": 7, "W_x": 8, "W_dt": 9}
 CHUNK = 4096
-DEVICE_DRAW_L = 1 << 19  # sequences this long are drawn on the device
 
 
 def config_id(w: Workload) -> int:
@@ -156,8 +153,6 @@ def make(w: Workload, seed: int = 0, device="cpu", time_major: bool = False) -> 
     on the layout. delta_bias is None when w.bias == "none"; z is always drawn (pass it
     or not).
     """
-    if w.seqlen >= DEVICE_DRAW_L:
-        return _make_device(w, seed, device, time_major)
     dev = torch.device(device)
     cfg = config_id(w)
     b, L, d, n = w.batch, w.seqlen, w.dim, w.dstate
@@ -201,58 +196,6 @@ def make(w: Workload, seed: int = 0, device="cpu", time_major: bool = False) -> 
     return {k: res[k] for k in ("u", "delta", "z", "B", "C", "A", "D", "delta_bias")}
 
 
-def _make_device(w: Workload, seed: int, device, time_major: bool) -> dict:
-    """The draws of ``make`` for sequences of 2^19 tokens or more: a seeded torch.Generator
-    on the device, in the same order and distributions (bf16: fp32 draws rounded to nearest
-    even)."""
-    dev = torch.device(device)
-    g = torch.Generator(device=dev)
-    g.manual_seed(_seed(w.name, seed))
-    b, L, d, n = w.batch, w.seqlen, w.dim, w.dstate
-    tok = (L, b, d) if time_major else (b, L, d)
-    st = (L, b, n) if time_major else (b, L, n)
-    f32 = dict(dtype=torch.float32, device=dev, generator=g)
-
-    def normal(shape, mean=0.0, std=1.0):
-        return torch.randn(shape, **f32) * std + mean
-
-    def delta_draw(shape):
-        kind, p, q = w.delta_dist
-        if kind == "normal":
-            return normal(shape, p, q)
-        return torch.rand(shape, **f32) * (q - p) + p
-
-    if w.lti:
-        u = normal(tok)
-        if time_major:
-            delta = delta_draw((1, b, d)).expand(tok).contiguous()
-        else:
-            delta = delta_draw((b, 1, d)).expand(tok).contiguous()
-        z = normal(tok)
-        one = (1, b, n) if time_major else (b, 1, n)
-        B = normal(one).expand(st).contiguous()
-        C = normal(one).expand(st).contiguous()
-    else:
-        u = normal(tok)
-        delta = delta_draw(tok)
-        z = normal(tok)
-        B = normal(st)
-        C = normal(st)
-    D = normal((d,))
-    if w.bias == "range":
-        bias = torch.rand((d,), **f32) * (BIAS_HI - BIAS_LO) + BIAS_LO
-    elif w.bias == "zero":
-        bias = torch.zeros((d,), dtype=torch.float32, device=dev)
-    else:
-        bias = None
-    A = -torch.arange(1, n + 1, dtype=torch.float32, device=dev).repeat(d, 1).contiguous()
-    out = dict(u=u, delta=delta, z=z, B=B, C=C, A=A, D=D, delta_bias=bias)
-    if w.dtype == "bf16":
-        for k in ("u", "delta", "z", "B", "C"):
-            out[k] = out[k].to(torch.bfloat16)
-    return out
-
-
 def proj_rank(dim: int) -> int:
     """Rank of the step projection in the projection workloads: dim / 32 rounded up to a
     multiple of 8 (1536 -> 48, 4096 -> 128, 5120 -> 160)."""
@@ -262,18 +205,21 @@ def proj_rank(dim: int) -> int:
 def make_proj(w: Workload, rank: int, seed: int = 0, device="cpu") -> dict:
     """Inputs of the projections for workload ``w``: u (batch, seqlen, dim) ~ N(0, 1),
     W_x (rank + 2 dstate, dim) ~ N(0, 1/dim) and W_dt (dim, rank) ~ N(0, 1/rank), so every
-    output is O(1); all in w.dtype (bf16: fp32 draws rounded to nearest even)."""
+    output is O(1); all in w.dtype (bf16: fp32 draws rounded to nearest even). Host PCG64
+    streams as in ``make`` (u in 4096-token chunks, tensor ids 7, 8, 9; each weight matrix
+    one stream, row-major)."""
     dev = torch.device(device)
-    g = torch.Generator(device=dev)
-    g.manual_seed(_seed(w.name + "/proj", seed))
-    f32 = dict(dtype=torch.float32, device=dev, generator=g)
+    cfg = config_id(w)
     d, n = w.dim, w.dstate
-    out = dict(u=torch.randn((w.batch, w.seqlen, d), **f32),
-               W_x=torch.randn((rank + 2 * n, d), **f32) / math.sqrt(d),
-               W_dt=torch.randn((d, rank), **f32) / math.sqrt(rank))
-    if w.dtype == "bf16":
-        out = {k: v.to(torch.bfloat16) for k, v in out.items()}
-    return out
+    bf = w.dtype == "bf16"
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as pool:
+        u = _host_tokens(w, cfg, "proj_u", ("normal", 0.0, 1.0), d, seed, pool)
+    wx = _draw(_rng(cfg, "W_x", 0, seed), ("normal", 0.0, 1.0 / math.sqrt(d)),
+               (rank + 2 * n) * d).reshape(rank + 2 * n, d)
+    wdt = _draw(_rng(cfg, "W_dt", 0, seed), ("normal", 0.0, 1.0 / math.sqrt(rank)), d * rank).reshape(d, rank)
+    if bf:
+        wx, wdt = _bf16_bits(wx), _bf16_bits(wdt)
+    return dict(u=_torch_of(u, bf, dev), W_x=_torch_of(wx, bf, dev), W_dt=_torch_of(wdt, bf, dev))
 
 
 def to_numpy(t):

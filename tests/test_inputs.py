@@ -74,3 +74,33 @@ def test_lti_values_are_constant_along_the_sequence():
 def test_sweep_shapes_share_the_long_context_streams():
     assert inputs.config_id(inputs.sweep_workload(1 << 13)) == inputs.config_id(inputs.WORKLOADS["mamba3b-long"]) == 4
     assert inputs.config_id(inputs.WORKLOADS["decode"]) == 5
+
+
+def test_long_sequences_draw_the_same_host_streams():
+    # 2^20 tokens (the longest sweep point's length) on a narrow shape: the same chunked
+    # streams as any other length, so a long sequence's prefix is the short one's draw
+    w = inputs.WORKLOADS["mamba3b-long"].replace(name="long-narrow", seqlen=1 << 20, dim=2, dstate=1)
+    x = inputs.make(w, seed=2)
+    short = inputs.make(w.replace(seqlen=9000), seed=2)
+    for k in ("u", "delta", "z", "B", "C"):
+        assert torch.equal(short[k], x[k][:, :9000]), k
+    cfg = inputs.config_id(w)
+    last = 256 - 1  # the last 4096-token chunk of the row
+    f32 = _stream([86, cfg, 0, last, 2]).standard_normal(4096 * 2).astype(np.float32)
+    ref = torch.from_numpy(f32).to(torch.bfloat16).reshape(4096, 2)
+    assert torch.equal(x["u"][0, -4096:], ref)
+
+
+def test_projection_inputs_follow_the_seed_key():
+    w = inputs.WORKLOADS["tiny"].replace(name="projin", batch=2, seqlen=70, dim=24, dstate=3)
+    rank = 8
+    x = inputs.make_proj(w, rank, seed=4)
+    cfg = inputs.config_id(w)
+    u = _stream([86, cfg, 7, 1, 4]).standard_normal(70 * 24).astype(np.float32).reshape(70, 24)
+    assert np.array_equal(x["u"][1].numpy(), u)
+    wx = (_stream([86, cfg, 8, 0, 4]).standard_normal((rank + 6) * 24) * (1 / np.sqrt(24))).astype(np.float32)
+    assert np.array_equal(x["W_x"].numpy(), wx.reshape(rank + 6, 24))
+    wdt = (_stream([86, cfg, 9, 0, 4]).standard_normal(24 * rank) * (1 / np.sqrt(rank))).astype(np.float32)
+    assert np.array_equal(x["W_dt"].numpy(), wdt.reshape(24, rank))
+    again = inputs.make_proj(w, rank, seed=4)
+    assert all(torch.equal(again[k], x[k]) for k in x)
