@@ -222,6 +222,28 @@ def make_proj(w: Workload, rank: int, seed: int = 0, device="cpu") -> dict:
     return dict(u=_torch_of(u, bf, dev), W_x=_torch_of(wx, bf, dev), W_dt=_torch_of(wdt, bf, dev))
 
 
+class HostStream:
+    """A seeded host stream for a test's own extra tensors (initial states, output
+    gradients, conv taps, shapes of its own): numpy PCG64 keyed by
+    ``SeedSequence([86, 99, *key])``, drawn in fp64 and rounded to fp32, then copied to the
+    device, so every such draw is also the same on every host. Successive calls continue
+    the one stream in call order."""
+
+    def __init__(self, *key: int):
+        self._rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([86, 99, *key])))
+
+    def _out(self, v: np.ndarray, shape, device) -> torch.Tensor:
+        return torch.from_numpy(v.astype(np.float32).reshape(shape)).to(device)
+
+    def randn(self, shape, device="cpu") -> torch.Tensor:
+        """N(0, 1) values of the given shape, float32."""
+        return self._out(self._rng.standard_normal(math.prod(shape)), shape, device)
+
+    def rand(self, shape, device="cpu") -> torch.Tensor:
+        """U[0, 1) values of the given shape, float32."""
+        return self._out(self._rng.random(math.prod(shape)), shape, device)
+
+
 def to_numpy(t):
     """A host numpy view of a tensor for the oracle: float32 stays float32, bfloat16
     becomes uint16 bit patterns. None stays None."""

@@ -24,9 +24,8 @@ def _announce(msg):
 
 
 def _dy(shape, seed):
-    g = torch.Generator(device=DEV)
-    g.manual_seed(seed)
-    return torch.randn(shape, generator=g, device=DEV)
+    g = inputs.HostStream(seed)
+    return g.randn(shape, DEV)
 
 
 def _oracle(x, dy, gated=True, use_D=True, use_bias=True, softplus=True, h0=None, dlast=None, channels=None):

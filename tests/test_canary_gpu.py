@@ -77,7 +77,7 @@ def test_forward_outputs_stay_in_bounds(batch, L, dim, N, dt, plan):
         pytest.skip("the chunked kernel is for dstate 16")
     x = _make(batch, L, dim, N, dt, seed=501)
     _announce(f"fwd {batch}x{L}x{dim}x{N} {dt} plan={plan}")
-    h0 = torch.randn((batch, dim, N), device=DEV) if L % 2 else None
+    h0 = inputs.HostStream(500, L).randn((batch, dim, N), DEV) if L % 2 else None
     kw = dict(kernel=kernel, chunk_len=chunk, chunk_rows=rows, split_parts=parts, h0=h0)
     y_ref, st_ref = pu.gpu_fwd(x, True, **kw)
     need = ss.fwd_workspace_size(batch, L, dim, N, x["u"].dtype, kernel=kernel, chunk_len=chunk,
@@ -98,11 +98,10 @@ def test_forward_outputs_stay_in_bounds(batch, L, dim, N, dt, plan):
 def test_conv_forward_outputs_stay_in_bounds(batch, L, dim, N, dt, K, kernel, chunk, rows, parts):
     x = _make(batch, L, dim, N, dt, seed=502)
     _announce(f"fwd_conv {batch}x{L}x{dim}x{N} {dt} K={K} plan={(kernel, chunk, rows, parts)}")
-    g = torch.Generator(device=DEV)
-    g.manual_seed(503)
-    w = (torch.randn((dim, K), generator=g, device=DEV) * 0.5).contiguous()
-    b = torch.randn((dim,), generator=g, device=DEV) * 0.1
-    cs = torch.randn((batch, dim, K - 1), generator=g, device=DEV)
+    g = inputs.HostStream(503)
+    w = (g.randn((dim, K), DEV) * 0.5).contiguous()
+    b = g.randn((dim,), DEV) * 0.1
+    cs = g.randn((batch, dim, K - 1), DEV)
 
     def run(**out):
         return ss.fwd_conv(x["u"], w, x["delta"], x["A"], x["B"], x["C"], conv_b=b, conv_state=cs, D=x["D"],
@@ -125,7 +124,7 @@ def test_decode_step_outputs_stay_in_bounds(batch, dim, N, dt, zoh):
                                            dstate=N, dtype=dt)
     x = inputs.make(w, seed=504, device=DEV, time_major=True)
     _announce(f"step {batch}x{dim}x{N} {dt} zoh={zoh}")
-    st0 = torch.randn((batch, dim, N), device=DEV)
+    st0 = inputs.HostStream(505).randn((batch, dim, N), DEV)
     ref = st0.clone()
     st = Padded((batch, dim, N), init=st0)
     for t in range(x["u"].shape[0]):
@@ -148,11 +147,10 @@ BWD_KEYS = ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0")
 def test_backward_gradients_stay_in_bounds(batch, L, dim, N, dt):
     x = _make(batch, L, dim, N, dt, seed=505)
     _announce(f"bwd {batch}x{L}x{dim}x{N} {dt}")
-    g = torch.Generator(device=DEV)
-    g.manual_seed(506)
-    dy = torch.randn((batch, L, dim), generator=g, device=DEV)
-    h0 = torch.randn((batch, dim, N), generator=g, device=DEV)
-    dlast = torch.randn((batch, dim, N), generator=g, device=DEV)
+    g = inputs.HostStream(506)
+    dy = g.randn((batch, L, dim), DEV)
+    h0 = g.randn((batch, dim, N), DEV)
+    dlast = g.randn((batch, dim, N), DEV)
 
     def run(**kw):
         return ss.bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"],
@@ -177,7 +175,7 @@ def test_backward_split_gradients_stay_in_bounds():
     batch, L, dim, N = 1, 700, 16 * int(cus * 1.2) - 5, 16
     x = _make(batch, L, dim, N, "bf16", seed=507)
     _announce(f"bwd split {batch}x{L}x{dim}x{N}")
-    dy = torch.randn((batch, L, dim), device=DEV)
+    dy = inputs.HostStream(507).randn((batch, L, dim), DEV)
 
     def run(**kw):
         return ss.bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"],
@@ -206,9 +204,8 @@ def test_projection_outputs_stay_in_bounds(batch, L, dim, N, rank, dt, K):
     _announce(f"proj {w.name} K={K}")
     tdt = x["u"].dtype
     if K:
-        g = torch.Generator(device=DEV)
-        g.manual_seed(509)
-        cw = (torch.randn((dim, K), generator=g, device=DEV) * 0.5).contiguous()
+        g = inputs.HostStream(509)
+        cw = (g.randn((dim, K), DEV) * 0.5).contiguous()
 
         def run(**o):
             return ss.proj_conv(x["u"], cw, x["W_x"], x["W_dt"], rank, **o)

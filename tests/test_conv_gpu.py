@@ -22,11 +22,10 @@ def _announce(msg):
 
 
 def conv_params(batch, dim, K, seed, bias=True, state=True):
-    g = torch.Generator(device=DEV)
-    g.manual_seed(seed)
-    w = (torch.randn((dim, K), generator=g, device=DEV) * 0.5).contiguous()
-    b = torch.randn((dim,), generator=g, device=DEV) * 0.1 if bias else None
-    st = torch.randn((batch, dim, K - 1), generator=g, device=DEV) if state and K > 1 else None
+    g = inputs.HostStream(seed)
+    w = (g.randn((dim, K), DEV) * 0.5).contiguous()
+    b = g.randn((dim,), DEV) * 0.1 if bias else None
+    st = g.randn((batch, dim, K - 1), DEV) if state and K > 1 else None
     return w, b, st
 
 
@@ -74,7 +73,7 @@ def test_conv_with_initial_state_and_zoh():
     w = inputs.WORKLOADS["mamba130m"].replace(name="cz", batch=2, seqlen=200, dim=48)
     x = inputs.make(w, seed=83, device=DEV)
     cw, cb, cs = conv_params(2, 48, 4, 84)
-    h0 = torch.randn((2, 48, 16), device=DEV)
+    h0 = inputs.HostStream(82).randn((2, 48, 16), DEV)
     got = gpu_conv(x, cw, cb, cs, True, h0=h0, zoh=True)
     torch.cuda.synchronize()
     check(x, got, oracle_conv(x, cw, cb, cs, True, h0=h0, zoh=True), "h0 + zoh")

@@ -104,3 +104,16 @@ def test_projection_inputs_follow_the_seed_key():
     assert np.array_equal(x["W_dt"].numpy(), wdt.reshape(24, rank))
     again = inputs.make_proj(w, rank, seed=4)
     assert all(torch.equal(again[k], x[k]) for k in x)
+
+
+def test_host_stream_for_extra_tensors():
+    # a test's own extra tensors: one PCG64 stream keyed by [86, 99, *key], fp64 rounded
+    # to fp32, continued across calls in call order
+    g = inputs.HostStream(503, 2)
+    a = g.randn((3, 4))
+    b = g.rand((5,))
+    r = _stream([86, 99, 503, 2])
+    assert np.array_equal(a.numpy(), r.standard_normal(12).astype(np.float32).reshape(3, 4))
+    assert np.array_equal(b.numpy(), r.random(5).astype(np.float32))
+    assert a.dtype == torch.float32 and b.dtype == torch.float32
+    assert not torch.equal(inputs.HostStream(503, 3).randn((3, 4)), a)

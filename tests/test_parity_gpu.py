@@ -204,9 +204,8 @@ def test_initial_state(kernel, chunk, rows, batch, L, dim, N, dt):
     w = inputs.WORKLOADS["mamba130m"].replace(name=f"h{batch}{L}{dim}{N}{dt}", batch=batch, seqlen=L, dim=dim,
                                               dstate=N, dtype=dt)
     x = inputs.make(w, seed=12, device=DEV)
-    g = torch.Generator(device=DEV)
-    g.manual_seed(5)
-    h0 = torch.randn((batch, dim, N), generator=g, device=DEV)
+    g = inputs.HostStream(5)
+    h0 = g.randn((batch, dim, N), DEV)
     y, st = pu.gpu_fwd(x, True, kernel=kernel, chunk_len=chunk, chunk_rows=rows, h0=h0)
     torch.cuda.synchronize()
     n = {k: inputs.to_numpy(v) for k, v in x.items()}
@@ -221,7 +220,7 @@ def test_initial_state(kernel, chunk, rows, batch, L, dim, N, dt):
 def test_empty_sequence_returns_initial_state():
     w = inputs.WORKLOADS["mamba130m"].replace(name="empty-h0", batch=2, seqlen=0, dim=80, dstate=16)
     x = inputs.make(w, seed=5, device=DEV)
-    h0 = torch.randn((2, 80, 16), device=DEV)
+    h0 = inputs.HostStream(6).randn((2, 80, 16), DEV)
     _, st = pu.gpu_fwd(x, True, h0=h0)
     torch.cuda.synchronize()
     assert torch.equal(st, h0)

@@ -169,11 +169,10 @@ def test_proj_then_scan_matches_oracle():
 # ---- the fused prologue (ss_proj_conv) ----------------------------------------------------------
 
 def conv_params(batch, dim, K, seed, bias=True, state=True):
-    g = torch.Generator(device=DEV)
-    g.manual_seed(seed)
-    w = (torch.randn((dim, K), generator=g, device=DEV) * 0.5).contiguous()
-    b = torch.randn((dim,), generator=g, device=DEV) * 0.1 if bias else None
-    st = torch.randn((batch, dim, K - 1), generator=g, device=DEV) if state and K > 1 else None
+    g = inputs.HostStream(seed)
+    w = (g.randn((dim, K), DEV) * 0.5).contiguous()
+    b = g.randn((dim,), DEV) * 0.1 if bias else None
+    st = g.randn((batch, dim, K - 1), DEV) if state and K > 1 else None
     return w, b, st
 
 

@@ -46,9 +46,8 @@ def _inputs(c, seed):
     if not c["softplus"]:  # the raw step (plus bias) is used as is: keep it positive and small
         x["delta"] = (x["delta"].float().abs() * 0.05).to(x["delta"].dtype)
         x["delta_bias"] = x["delta_bias"].abs() * 0.01
-    g = torch.Generator(device=DEV)
-    g.manual_seed(seed)
-    h0 = torch.randn((c["batch"], c["dim"], c["N"]), generator=g, device=DEV) if c["h0"] else None
+    g = inputs.HostStream(seed)
+    h0 = g.randn((c["batch"], c["dim"], c["N"]), DEV) if c["h0"] else None
     return x, h0
 
 
@@ -75,10 +74,9 @@ def test_random_backward_case(seed):
     c["zoh"] = False  # the backward is of the default input term
     print(f"\n[random] bwd seed={seed} {c}", flush=True)
     x, h0 = _inputs(c, 100 + seed)
-    g = torch.Generator(device=DEV)
-    g.manual_seed(200 + seed)
-    dy = torch.randn((c["batch"], c["L"], c["dim"]), generator=g, device=DEV)
-    dlast = torch.randn((c["batch"], c["dim"], c["N"]), generator=g, device=DEV) if seed % 2 else None
+    g = inputs.HostStream(200 + seed)
+    dy = g.randn((c["batch"], c["L"], c["dim"]), DEV)
+    dlast = g.randn((c["batch"], c["dim"], c["N"]), DEV) if seed % 2 else None
     got = ss.bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"] if c["use_D"] else None,
                  z=x["z"] if c["gated"] else None, delta_bias=x["delta_bias"] if c["use_bias"] else None,
                  softplus=c["softplus"], h0=h0, dlast=dlast)

@@ -61,9 +61,8 @@ def test_split_matches_oracle_and_unsplit(chunk, rows, batch, L, dim, dt, parts)
 def test_split_with_initial_state(chunk, rows):
     w = _workload(2, 1500, 50, "f32", "h")
     x = inputs.make(w, seed=22, device=DEV)
-    g = torch.Generator(device=DEV)
-    g.manual_seed(9)
-    h0 = torch.randn((2, 50, 16), generator=g, device=DEV)
+    g = inputs.HostStream(9)
+    h0 = g.randn((2, 50, 16), DEV)
     _announce(f"h0 chunk={chunk} rows={rows}")
     got = pu.gpu_fwd(x, True, kernel=2, chunk_len=chunk, chunk_rows=rows, split_parts=4, h0=h0)
     one = pu.gpu_fwd(x, True, kernel=2, chunk_len=chunk, chunk_rows=rows, split_parts=1, h0=h0)

@@ -77,13 +77,14 @@ def test_decode_stream_full_size():
 
 def test_step_zero_step_size_keeps_state():
     batch, dim, N = 4, 128, 16
-    st0 = torch.randn((batch, dim, N), device=DEV)
+    g = inputs.HostStream(87)
+    st0 = g.randn((batch, dim, N), DEV)
     st = st0.clone()
     z = torch.zeros((batch, dim), device=DEV)
     A = -torch.arange(1, N + 1, dtype=torch.float32, device=DEV).repeat(dim, 1).contiguous()
-    B = torch.randn((batch, N), device=DEV)
-    C = torch.randn((batch, N), device=DEV)
-    u = torch.randn((batch, dim), device=DEV)
+    B = g.randn((batch, N), DEV)
+    C = g.randn((batch, N), DEV)
+    u = g.randn((batch, dim), DEV)
     ss.step(st, u, z, A, B, C, softplus=False)
     torch.cuda.synchronize()
     assert torch.equal(st, st0)

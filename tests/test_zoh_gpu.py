@@ -54,20 +54,18 @@ def _wide_range_inputs(batch, L, dim, seed):
     """Step sizes from ~1e-6 to ~5 and |A| from 1e-4 to 20, so dt*A runs from ~1e-10 to
     ~100 across the series / difference switch at 1/16; a few A are exactly 0 (limit dt)
     and a few small positive A grow the state."""
-    g = torch.Generator(device=DEV)
-    g.manual_seed(seed)
-    f = dict(device=DEV, dtype=torch.float32, generator=g)
+    g = inputs.HostStream(seed)
     N = 16
-    u = torch.randn((batch, L, dim), **f)
-    delta = torch.rand((batch, L, dim), **f) * 15.0 - 13.0       # softplus: ~2e-6 .. ~2
-    B = torch.randn((batch, L, N), **f)
-    C = torch.randn((batch, L, N), **f)
-    z = torch.randn((batch, L, dim), **f)
-    A = -torch.pow(10.0, torch.rand((dim, N), **f) * 5.3 - 4.0)   # -1e-4 .. -20
+    u = g.randn((batch, L, dim), DEV)
+    delta = g.rand((batch, L, dim), DEV) * 15.0 - 13.0       # softplus: ~2e-6 .. ~2
+    B = g.randn((batch, L, N), DEV)
+    C = g.randn((batch, L, N), DEV)
+    z = g.randn((batch, L, dim), DEV)
+    A = -torch.pow(10.0, g.rand((dim, N), DEV) * 5.3 - 4.0)   # -1e-4 .. -20
     A[::7, 3] = 0.0
     A[1::11, 5] = 0.002
-    D = torch.randn((dim,), **f)
-    bias = torch.rand((dim,), **f) * 2.0 - 1.0
+    D = g.randn((dim,), DEV)
+    bias = g.rand((dim,), DEV) * 2.0 - 1.0
     return dict(u=u, delta=delta, z=z, B=B, C=C, A=A.contiguous(), D=D, delta_bias=bias)
 
 
@@ -84,7 +82,7 @@ def test_zoh_step_sizes_across_the_series_switch(kernel, chunk, rows):
 def test_zoh_initial_state(kernel, chunk, rows):
     w = inputs.WORKLOADS["mamba1.4b"].replace(name="zh0", batch=2, seqlen=333, dim=80)
     x = inputs.make(w, seed=33, device=DEV)
-    h0 = torch.randn((2, 80, 16), device=DEV)
+    h0 = inputs.HostStream(86).randn((2, 80, 16), DEV)
     y, st = pu.gpu_fwd(x, True, kernel=kernel, chunk_len=chunk, chunk_rows=rows, zoh=True, h0=h0)
     torch.cuda.synchronize()
     _check(x, y, st, True, h0=h0, what="zoh from h0")
