@@ -568,11 +568,15 @@ __device__ __forceinline__ Lane lane_at(const BwdArgs& a, int64_t g) {
 }
 
 // The workgroup's group index gi and sequence part: with SPLIT a work item from the queue
-// (ss_split.h), the chain running from the last part to the first when `reverse`.
+// (ss_split.h), the chain running from the last part to the first when `reverse`; without,
+// the forward's mapping, which keeps neighbouring groups (sharing 128-byte lines of the
+// (.., dim) arrays) on one XCD: with the workgroup id as the group, two (fp32) or four (bf16)
+// XCDs each fetched every line (130M checkpoint kernel: 0.41 GB read per call for 0.20 GB
+// of inputs).
 template <bool SPLIT>
 __device__ __forceinline__ void work_item(const BwdArgs& a, bool reverse, uint32_t& item_s, int64_t& gi,
                                           int64_t& part) {
-  gi = blockIdx.x;
+  gi = SPLIT ? static_cast<int64_t>(blockIdx.x) : chunk::group_of(blockIdx.x, a.batch * a.ngroups);
   part = 0;
   if (SPLIT) {
     const int64_t groups = a.batch * a.ngroups;
